@@ -1,0 +1,202 @@
+/*
+ * moeq.h - C ABI of libmoeq.so: the affine group-quantized mixture-of-experts
+ * FFN step on AMD MI355X (gfx950).
+ *
+ * The step (markbaseengine MOE_ROUTER_WORKS_BREAKTHROUGH, "Forward Pass
+ * Sequence"; flash-moe-inference skill page, per-layer pipeline listing):
+ *   router projection -> softmax -> top-K -> for each selected expert a fused
+ *   dequantize gate/up matvec -> SwiGLU -> down projection -> weighted combine,
+ *   with an optional shared expert scaled by a sigmoid gate.
+ * The many-token form runs the expert products as gather_qmm (ml-explore/mlx
+ * issue #3856, minimal repro: rows sorted by expert, x_i @ deq(W[idx_i])^T).
+ *
+ * Weight format (danveloper/flash-moe issue thread, quantization config and
+ * the 8-bit gate diagnosis; flash-moe-inference skill page, matvec_4bit_fma):
+ *   a matrix [rows][cols] ("out" x "in") stores codes of `bits` bits packed
+ *   along the input dimension into uint32 words, low bits first: column k is
+ *   field k % (32/bits) of word k / (32/bits).  Each group of `group_size`
+ *   consecutive input columns has one bf16 scale and one bf16 bias and the
+ *   dequantized weight is  w = scale * code + bias.  The bit width is a
+ *   property of each tensor (router and shared-expert gates may be 8-bit while
+ *   experts are 4-bit).
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller; the library
+ *    allocates nothing, keeps no global mutable state besides what lives in the
+ *    caller's workspace, and only enqueues work on `stream` (no host sync).
+ *  - Every argument is validated on the host BEFORE anything is launched; on
+ *    a bad argument the call returns a negative moeq_status and launches
+ *    nothing.  A kernel launch failure returns MOEQ_ERR_LAUNCH.
+ *  - Shapes are int32 and every derived index fits int32 (checked:
+ *    MOEQ_ERR_OVERFLOW); rows, tokens and pairs need not be multiples of any
+ *    tile size (ragged tails are computed exactly).
+ *  - Device pointers must be 16-byte aligned (MOEQ_ERR_ALIGN).
+ *  - Inputs are finite; with NaN/Inf inputs the outputs are unspecified.
+ *  - Outputs never alias inputs.
+ *  - Workspaces: sized by moe_workspace_size().  A workspace must hold zeros
+ *    before its first use (e.g. torch.zeros); every call leaves its counters
+ *    at zero again.  Calls that share one workspace must be ordered on one
+ *    stream; concurrent calls need separate workspaces.
+ */
+#ifndef MOEQ_H
+#define MOEQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void *moeq_stream_t; /* a hipStream_t (NULL = the null stream) */
+
+typedef enum moeq_status {
+  MOEQ_OK = 0,
+  MOEQ_ERR_NULL_PTR = -1,    /* a required pointer is NULL                      */
+  MOEQ_ERR_BAD_BITS = -2,    /* bits not in {2, 4, 8}                           */
+  MOEQ_ERR_BAD_GROUP = -3,   /* group_size != 64                                 */
+  MOEQ_ERR_K_TAIL = -4,      /* cols not a multiple of group_size               */
+  MOEQ_ERR_SHAPE = -5,       /* inconsistent shapes (hidden/inter/experts, top-K) */
+  MOEQ_ERR_OVERFLOW = -6,    /* a size or an index would not fit int32          */
+  MOEQ_ERR_ALIGN = -7,       /* a device pointer is not 16-byte aligned         */
+  MOEQ_ERR_WORKSPACE = -8,   /* workspace missing or smaller than required      */
+  MOEQ_ERR_UNSUPPORTED = -9, /* valid request outside what this build computes  */
+  MOEQ_ERR_LAUNCH = -10      /* the HIP runtime rejected a kernel launch        */
+} moeq_status;
+
+/* One quantized matrix [rows][cols], or a stack of `batch` such matrices laid
+ * out back to back (expert e starts at q + e*rows*(cols*bits/32)).
+ *   q      : uint32 [batch][rows][cols*bits/32], codes low bits first
+ *   scales : bf16 bit patterns [batch][rows][cols/group_size]
+ *   biases : bf16 bit patterns, same shape as scales
+ * `group_size` is the number of input columns per group (64), not a group
+ * count: the markbaseengine expert kernel hung when this parameter was missing
+ * or garbage (MOE_FIX_SUCCESS_EXPERT_WORKS, "Bug Details"), so it is an
+ * explicit, validated field here. */
+typedef struct moeq_qtensor {
+  const uint32_t *q;
+  const uint16_t *scales;
+  const uint16_t *biases;
+  int32_t batch;
+  int32_t rows;
+  int32_t cols;
+  int32_t bits;
+  int32_t group_size;
+} moeq_qtensor;
+
+/* One MoE layer.  router [1][E][H]; gate, up [E][I][H]; down [E][H][I].
+ * has_shared != 0 adds a shared expert: sh_gate, sh_up [1][Is][H],
+ * sh_down [1][H][Is] and the one-row shared_expert_gate [1][1][H], whose
+ * sigmoid scales the shared expert's output (flash-moe-inference skill page,
+ * moe_combine_residual: combine + residual + sigmoid gate). */
+typedef struct moeq_moe {
+  moeq_qtensor router;
+  moeq_qtensor gate;
+  moeq_qtensor up;
+  moeq_qtensor down;
+  int32_t has_shared;
+  moeq_qtensor sh_gate;
+  moeq_qtensor sh_up;
+  moeq_qtensor sh_down;
+  moeq_qtensor sh_expert_gate;
+} moeq_moe;
+
+/* Workspace paths for moe_workspace_size(). */
+#define MOEQ_PATH_ROUTE 0   /* moe_route                                   */
+#define MOEQ_PATH_DECODE 1  /* moe_expert_forward                          */
+#define MOEQ_PATH_GATHER 2  /* moe_gather_qmm                              */
+#define MOEQ_PATH_GQMM 3    /* gather_qmm (single projection; K is unused) */
+
+/* Human-readable text for a status code (static storage). */
+const char *moeq_status_string(int status);
+
+/* Library version string (static storage). */
+const char *moeq_version(void);
+
+/* Workspace bytes needed by the given path for a layer, M tokens and top-K.
+ * For MOEQ_PATH_GQMM pass the stacked weight as L->gate and n rows as M.
+ * Returns 0 when the arguments are invalid. */
+size_t moe_workspace_size(const moeq_moe *L, int32_t M, int32_t K, int32_t path);
+
+/* qdequant: unpack and dequantize a whole (stacked) quantized tensor.
+ *   codes : nullable, uint8 [batch][rows][cols], the integer codes
+ *   deq   : nullable, fp32  [batch][rows][cols], fp32(scale*code + bias)
+ * Defines: the unpack / dequantize step itself (flash-moe-inference,
+ * matvec_4bit_fma: (nibble*scale + bias)).  Both outputs are exact: the
+ * bf16*code product is exact in fp32, so deq is the single rounding of
+ * scale*code + bias. */
+int qdequant(const moeq_qtensor *W, uint8_t *codes, float *deq, moeq_stream_t stream);
+
+/* qmatvec: y[m][r] = sum_k deq(W)[r][k] * x[m][k]  (fp32 in, fp32 out, fp32
+ * accumulation) for one matrix (W->batch == 1), M >= 1 tokens.
+ *   x : fp32 [M][cols];  y : fp32 [M][rows]
+ * Defines: the dequantizing matrix-vector product of the flash-moe
+ * matvec_4bit_fma sketch (weights, scales, biases, x, out) with explicit
+ * in/out dimensions and group parameter (markbaseengine expert kernel). */
+int qmatvec(const moeq_qtensor *W, const float *x, int32_t M, float *y,
+            moeq_stream_t stream);
+
+/* moe_route: router projection, softmax over all E experts, top-K by
+ * (score descending, index ascending), weights p[idx] / sum(p[idx]) when
+ * renorm != 0, else p[idx].
+ *   gate      : the router [1][E][H]; NULL selects logits-in mode, where
+ *               x_or_logits holds fp32 logits [M][E]
+ *   x_or_logits : fp32 [M][H] activations (or [M][E] logits)
+ *   topk_idx  : int32 [M][K] out, in selection order
+ *   topk_w    : fp32  [M][K] out
+ *   logits_out: nullable fp32 [M][E] out (router mode only)
+ *   ws        : workspace of moe_workspace_size(L, M, K, MOEQ_PATH_ROUTE)
+ * The router logits are accumulated in fp64 on the GPU so the top-K decision
+ * is taken on fp64 values.  1 <= K <= min(E, 16), E <= 1024.
+ * Defines: "Forward Pass Sequence" steps 1-4 (markbaseengine) and "softmax +
+ * topK routing" (flash-moe pipeline), kept on the device. */
+int moe_route(const moeq_qtensor *gate, const float *x_or_logits, int32_t M, int32_t E,
+              int32_t K, int32_t renorm, int32_t *topk_idx, float *topk_w,
+              float *logits_out, void *ws, size_t ws_bytes, moeq_stream_t stream);
+
+/* moe_expert_forward: the expert part of the step for fp32 activations
+ * (decode, any M >= 1):
+ *   y[t] = sum_{k<K} topk_w[t][k] * down_e(silu(gate_e x_t) * up_e x_t),
+ *          e = topk_idx[t][k]
+ *        + sigmoid(sh_expert_gate . x_t) * FFN_shared(x_t)   (if has_shared)
+ *        + residual[t]                                          (if non-NULL)
+ * with fp32 accumulation; the K terms are added in slot order, so results are
+ * bitwise reproducible run to run.
+ *   x : fp32 [M][H];  topk_idx int32 [M][K] (each in [0, E));  topk_w fp32 [M][K]
+ *   residual : nullable fp32 [M][H];  y : fp32 [M][H]
+ * Defines: "Forward Pass Sequence" step 5-6 (markbaseengine), flash-moe swiglu
+ * and moe_combine_residual sketches. */
+int moe_expert_forward(const moeq_moe *L, const float *x, const int32_t *topk_idx,
+                       const float *topk_w, int32_t M, int32_t K, const float *residual,
+                       float *y, void *ws, size_t ws_bytes, moeq_stream_t stream);
+
+/* moe_gather_qmm: the expert part for many bf16 tokens (prefill).  Pairs
+ * (token, slot) are sorted by expert on the device; per expert the gathered
+ * rows run through a bf16 MFMA gate/up GEMM with a SwiGLU epilogue (h kept in
+ * bf16) and a down GEMM scaled by the routing weight; each token then sums its
+ * K pairs in slot order.  fp32 output; any M >= 1 (no tile-size alignment).
+ *   x_bf16 : bf16 bit patterns [M][H];  topk_idx, topk_w as above;  y : fp32 [M][H]
+ * has_shared must be 0 (MOEQ_ERR_UNSUPPORTED otherwise).
+ * Defines: mlx-lm SwitchGLU through gather_qmm with sorted indices
+ * (ml-explore/mlx issue #3856), with exact handling of ragged row counts. */
+int moe_gather_qmm(const moeq_moe *L, const uint16_t *x_bf16, const int32_t *topk_idx,
+                   const float *topk_w, int32_t M, int32_t K, float *y, void *ws,
+                   size_t ws_bytes, moeq_stream_t stream);
+
+/* gather_qmm: one projection per row, the weight picked per row:
+ *   out[i] = x[i] @ deq(W[rhs_idx[i]])^T       (transpose=True)
+ *   W : stacked [E][N][Kd];  x_bf16 : bf16 [n][Kd];  rhs_idx : int32 [n] in [0, E)
+ *   sorted : nonzero if rhs_idx is non-decreasing (rows are then used in
+ *            place); otherwise rows are grouped by expert on the device
+ *   out : fp32 [n][N]
+ * Defines: mx.gather_qmm(x, w, scales, biases, rhs_indices, transpose=True,
+ * sorted_indices) of the ml-explore/mlx issue #3856 minimal repro. */
+int gather_qmm(const moeq_qtensor *W, const uint16_t *x_bf16, const int32_t *rhs_idx,
+               int32_t n, int32_t sorted, float *out, void *ws, size_t ws_bytes,
+               moeq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOEQ_H */

@@ -1,0 +1,316 @@
+"""CPU oracle for the affine-quantized mixture-of-experts FFN step.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import, call or
+execute this module: only the tests, the smoke check in ``__graft_entry__``
+and the ``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code with
+the HIP path (no kernels, headers, helpers, tables or generators) and it
+imports nothing from the package.
+
+What it computes is the plain definition of the step, written out the slow
+and obvious way: dequantize every weight fully to fp32, widen to fp64, and do
+fp64 matrix-vector products, an fp64 softmax, an explicit top-K with ties
+broken towards the lower expert index, SwiGLU, the down projection and the
+weighted combine.  This is the "dequantize, then dense fp32/fp64 math"
+arbiter that the MLX issue thread uses to judge ``gather_qmm`` (ml-explore/mlx
+issue #3856, "Silent numerical corruption in single long forward on quantized
+MoE ...", the minimal pure-mlx repro: ``mx.dequantize`` then a dense matmul),
+and the CPU-only path that the flash-moe thread used as ground truth
+(danveloper/flash-moe issue thread, "Definitive finding": the ``g_metal = NULL``
+CPU path matched the MLX gate scores).
+
+Sources, cited by page title and section:
+
+* Affine group quantization, per-tensor bit width, codes packed along the
+  input dimension into uint32 words: danveloper/flash-moe issue thread, the
+  quantization-config excerpt (``group_size 64, bits 4, mode affine`` with
+  8-bit overrides for ``mlp.gate`` and ``mlp.shared_expert_gate``) and the
+  ``[512, 512] U32`` gate-shape remark (packed width x codes per word =
+  in_dim).
+* Dequantized weight = scale * code + bias: flash-moe-inference skill page,
+  the ``matvec_4bit_fma`` kernel sketch (the naive form ``(nibble * scale +
+  bias) * x`` and the fused ``fma(nibble, scale*x, bias*x)``).
+* Router projection, softmax, top-K, per-expert fused gate/up, down,
+  accumulate: markbaseengine MOE_ROUTER_WORKS_BREAKTHROUGH, "Forward Pass
+  Sequence"; flash-moe-inference skill page, the per-layer pipeline listing
+  (CMD2 routing, CPU softmax + topK, CMD3 expert forward + combine).
+* SwiGLU ``g / (1 + exp(-g)) * up``: flash-moe-inference skill page, the
+  ``swiglu`` kernel sketch.
+* Shared expert scaled by a sigmoid gate, fused into the combine:
+  flash-moe-inference skill page, ``moe_combine_residual`` ("MoE combine +
+  residual + sigmoid gate"), and the 8-bit ``shared_expert_gate`` of the
+  flash-moe quantization config.
+* gather_qmm: row i computes ``x_i @ dequant(W[rhs_indices[i]])^T``
+  (``transpose=True``): ml-explore/mlx issue #3856, minimal repro.
+
+Readings where the pages are silent (each is listed with its reason in the
+design notes): codes sit low bits first inside a word; scales and biases are
+bf16; the group parameter is the number of elements per group; renormalized
+top-K weights ``p[idx] / sum(p[idx])``; ties go to the lower index; the
+combine adds the K experts in slot order.
+
+Every function here is pinned by the CPU tests (``tests/test_oracle_*.py``)
+against hand-packed words, closed forms, invariants and brute force with
+exactly rounded sums; none is "parity unpinned".
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "bf16_bits_to_f32",
+    "unpack_codes",
+    "dequantize",
+    "expert_slice",
+    "qmatvec",
+    "softmax",
+    "top_k",
+    "route",
+    "silu",
+    "swiglu",
+    "moe_experts",
+    "moe_layer",
+    "gather_qmm",
+    "expert_bytes",
+]
+
+
+# --------------------------------------------------------------------------
+# Format: unpack and dequantize
+# --------------------------------------------------------------------------
+
+def bf16_bits_to_f32(bits) -> np.ndarray:
+    """Widen bf16 bit patterns (uint16) to float32.
+
+    bf16 is the upper half of an IEEE float32, so the widening is exact: the
+    16 bits move to the top of a 32-bit word and the low half is zero.
+    """
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32)
+    return (b << np.uint32(16)).view(np.float32)
+
+
+def unpack_codes(words, bits: int, cols: int) -> np.ndarray:
+    """Unpack uint32 words into integer codes, one code per input column.
+
+    Each word holds ``32 / bits`` codes.  Column ``k`` of a row lives in word
+    ``k // (32 / bits)`` at bit offset ``bits * (k % (32 / bits))``: low bits
+    first.  For 4-bit this is "8 nibbles per uint32", for 8-bit "4 bytes per
+    uint32" (danveloper/flash-moe issue thread, the 8-bit gate diagnosis).
+    """
+    if bits not in (2, 4, 8):
+        raise ValueError(f"bits must be 2, 4 or 8, got {bits}")
+    w = np.asarray(words, dtype=np.uint32)
+    per_word = 32 // bits
+    if w.shape[-1] * per_word != cols:
+        raise ValueError(
+            f"packed width {w.shape[-1]} x {per_word} codes/word != cols {cols}")
+    mask = np.uint32((1 << bits) - 1)
+    shifts = np.arange(per_word, dtype=np.uint32) * np.uint32(bits)
+    codes = (w[..., :, None] >> shifts) & mask          # [..., words, per_word]
+    return codes.reshape(w.shape[:-1] + (cols,)).astype(np.uint8)
+
+
+def dequantize(qt: dict) -> np.ndarray:
+    """Dequantize a quantized matrix (or a stack of them) to float32.
+
+    ``w = scale * code + bias`` per group of ``group_size`` consecutive input
+    columns.  The product of a bf16 scale (8 significant bits) and a code of at
+    most 8 bits is exact in float32, so the float32 result is the single
+    rounding of ``scale * code + bias``.
+    """
+    bits, gs, cols = int(qt["bits"]), int(qt["group_size"]), int(qt["cols"])
+    if cols % gs:
+        raise ValueError("cols must be a multiple of group_size")
+    codes = unpack_codes(qt["q"], bits, cols).astype(np.float32)
+    s = np.repeat(bf16_bits_to_f32(qt["scales"]), gs, axis=-1)
+    b = np.repeat(bf16_bits_to_f32(qt["biases"]), gs, axis=-1)
+    if s.shape != codes.shape:
+        raise ValueError(f"scales shape {s.shape} does not match codes {codes.shape}")
+    prod = s * codes                                   # exact in float32
+    return (prod + b).astype(np.float32)               # one rounding
+
+
+def expert_slice(qt: dict, e: int) -> dict:
+    """The quantized matrix of expert ``e`` out of a stacked ``[E, rows, ...]``
+    tensor.  The arrays may be numpy arrays or lazy stacks indexable by ``e``."""
+    out = dict(qt)
+    out["q"] = qt["q"][e]
+    out["scales"] = qt["scales"][e]
+    out["biases"] = qt["biases"][e]
+    return out
+
+
+# --------------------------------------------------------------------------
+# Quantized matrix-vector product
+# --------------------------------------------------------------------------
+
+def qmatvec(qt: dict, x) -> np.ndarray:
+    """``y[m, r] = sum_k deq(W)[r, k] * x[m, k]`` in fp64.
+
+    ``qt`` is one matrix ``[rows, cols]``; ``x`` is ``[M, cols]`` (fp32 or a
+    widened bf16; both are exact in fp64).  Returns fp64 ``[M, rows]``.
+    """
+    w = dequantize(qt).astype(np.float64)
+    x64 = np.asarray(x, dtype=np.float64)
+    return x64 @ w.T
+
+
+# --------------------------------------------------------------------------
+# Routing: softmax, top-K, renormalization
+# --------------------------------------------------------------------------
+
+def softmax(logits) -> np.ndarray:
+    """Row-wise softmax in fp64, max-subtracted."""
+    z = np.asarray(logits, dtype=np.float64)
+    z = z - z.max(axis=-1, keepdims=True)
+    e = np.exp(z)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+def top_k(scores, k: int):
+    """Explicit top-K: K rounds of "take the largest remaining score, the
+    lowest index on ties, then remove it".
+
+    Returns ``(idx int32 [M, k], values [M, k])`` in selection order, i.e.
+    descending score with ties in ascending index.
+    """
+    s = np.array(scores, dtype=np.float64, copy=True)
+    if s.ndim == 1:
+        s = s[None, :]
+    m, e = s.shape
+    if not 1 <= k <= e:
+        raise ValueError(f"top-k {k} outside [1, {e}]")
+    idx = np.empty((m, k), dtype=np.int32)
+    val = np.empty((m, k), dtype=np.float64)
+    rows = np.arange(m)
+    for j in range(k):
+        a = np.argmax(s, axis=1)          # numpy returns the first maximum
+        idx[:, j] = a
+        val[:, j] = s[rows, a]
+        s[rows, a] = -np.inf
+    return idx, val
+
+
+def route(logits, k: int, renorm: bool = True):
+    """Softmax over all experts, explicit top-K, optional renormalization.
+
+    Returns ``(idx int32 [M, K], w fp64 [M, K], p fp64 [M, E])``.  With
+    ``renorm`` the weights are ``p[idx] / sum(p[idx])``.
+    """
+    p = softmax(logits)
+    if p.ndim == 1:
+        p = p[None, :]
+    idx, pv = top_k(p, k)
+    w = pv / pv.sum(axis=1, keepdims=True) if renorm else pv
+    return idx, w, p
+
+
+# --------------------------------------------------------------------------
+# Expert FFN and combine
+# --------------------------------------------------------------------------
+
+def silu(g) -> np.ndarray:
+    """``g / (1 + exp(-g))`` (the flash-moe ``swiglu`` kernel sketch)."""
+    g = np.asarray(g, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu(g, u) -> np.ndarray:
+    return silu(g) * np.asarray(u, dtype=np.float64)
+
+
+def _deq64(qt: dict, e: int | None = None) -> np.ndarray:
+    return dequantize(qt if e is None else expert_slice(qt, e)).astype(np.float64)
+
+
+def moe_experts(layer: dict, x, idx, w, residual=None) -> np.ndarray:
+    """Expert part of the step for given routing.
+
+    ``y[t] = sum_k w[t,k] * down_e(swiglu(gate_e x_t, up_e x_t))`` with
+    ``e = idx[t,k]``, plus ``sigmoid(shared_expert_gate . x_t) * FFN_shared(x_t)``
+    when the layer has a shared expert, plus ``residual[t]`` when given.
+
+    The per-expert products run over all rows routed to that expert at once
+    (fp64 matmuls), which is the same arithmetic per row as a loop over
+    tokens.  The K expert outputs of a token are summed in slot order.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    idx = np.asarray(idx)
+    w64 = np.asarray(w, dtype=np.float64)
+    m, k = idx.shape
+    hidden = int(layer["down"]["rows"])
+    per_slot = np.zeros((m, k, hidden), dtype=np.float64)
+    flat = idx.reshape(-1)
+    for e in np.unique(flat):
+        pairs = np.nonzero(flat == e)[0]
+        toks, slots = pairs // k, pairs % k
+        xe = x64[toks]
+        g = xe @ _deq64(layer["gate"], int(e)).T
+        u = xe @ _deq64(layer["up"], int(e)).T
+        h = swiglu(g, u)
+        per_slot[toks, slots] = h @ _deq64(layer["down"], int(e)).T
+    y = np.zeros((m, hidden), dtype=np.float64)
+    for j in range(k):                     # combine in slot order
+        y += w64[:, j:j + 1] * per_slot[:, j]
+    sh = layer.get("shared")
+    if sh is not None:
+        sg = qmatvec(sh["expert_gate"], x64)[:, 0]
+        gate_scale = 1.0 / (1.0 + np.exp(-sg))
+        g = x64 @ _deq64(sh["gate"]).T
+        u = x64 @ _deq64(sh["up"]).T
+        y_sh = swiglu(g, u) @ _deq64(sh["down"]).T
+        y += gate_scale[:, None] * y_sh
+    if residual is not None:
+        y += np.asarray(residual, dtype=np.float64).reshape(m, hidden)
+    return y
+
+
+def moe_layer(layer: dict, x, k: int, renorm: bool = True, residual=None,
+              logits=None):
+    """The whole step: router logits (or given logits), route, experts.
+
+    Returns ``(y, idx, w, logits)``.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    if logits is None:
+        logits = qmatvec(layer["router"], x64)
+    idx, w, _ = route(logits, k, renorm)
+    y = moe_experts(layer, x64, idx, w, residual)
+    return y, idx, w, np.asarray(logits, dtype=np.float64)
+
+
+# --------------------------------------------------------------------------
+# gather_qmm: one projection per row, weight matrix picked per row
+# --------------------------------------------------------------------------
+
+def gather_qmm(qt_stack: dict, x, rhs_idx) -> np.ndarray:
+    """``out[i] = x[i] @ deq(W[rhs_idx[i]])^T`` in fp64 (``transpose=True``).
+
+    ``x`` is ``[n, cols]``, ``rhs_idx`` is ``[n]``; the order of rows does not
+    matter (sorted or not gives the same rows).
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    ridx = np.asarray(rhs_idx).reshape(-1)
+    out = np.zeros((x64.shape[0], int(qt_stack["rows"])), dtype=np.float64)
+    for e in np.unique(ridx):
+        rows = np.nonzero(ridx == e)[0]
+        out[rows] = x64[rows] @ _deq64(qt_stack, int(e)).T
+    return out
+
+
+# --------------------------------------------------------------------------
+# Byte accounting
+# --------------------------------------------------------------------------
+
+def expert_bytes(hidden: int, inter: int, bits: int, group_size: int = 64,
+                 scale_bytes: int = 2) -> int:
+    """Bytes of one expert (gate, up: ``[inter, hidden]``; down:
+    ``[hidden, inter]``): packed codes plus one scale and one bias per group.
+    """
+    n = 3 * hidden * inter
+    return n * bits // 8 + 2 * scale_bytes * (n // group_size)

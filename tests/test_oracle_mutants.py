@@ -1,0 +1,169 @@
+"""The oracle's pins catch plausible mistakes.
+
+Each case plants one mistake in the oracle (on the CPU, via monkeypatch), runs
+the pins that should notice it, and requires at least one of them to fail.
+This is what makes the pins worth trusting: a dropped term, a wrong sign or
+index, a transposed operand or a wrong tie rule cannot slip through.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import oracle.moe_oracle as mo
+from tests import test_oracle_format as tf
+from tests import test_oracle_route_ffn as tr
+from tests.conftest import golden_rows
+
+
+def _patch(monkeypatch, name, fn):
+    monkeypatch.setattr(mo, name, fn)
+    monkeypatch.setattr(oracle, name, fn)
+
+
+def _fails(*checks):
+    for chk in checks:
+        try:
+            chk()
+        except (AssertionError, ValueError, IndexError):
+            return True
+    return False
+
+
+_unpack = mo.unpack_codes
+_dequant = mo.dequantize
+_route = mo.route
+_top_k = mo.top_k
+_silu = mo.silu
+_moe_experts = mo.moe_experts
+
+
+def _format_pins():
+    for row in golden_rows("hand_packed_words.txt"):
+        tf.test_unpack_hand_packed_words(row)
+    tf.test_unpack_multiword_rows_keep_column_order()
+    for row in golden_rows("dequant_values.txt"):
+        tf.test_dequant_closed_form(row)
+    tf.test_dequant_group_boundaries()
+    tf.test_qmatvec_one_hot_x_reads_codes()
+    tf.test_qmatvec_constant_codes_group_sums()
+
+
+def _route_pins():
+    tr.test_topk_matches_sort_based_brute_force(16, 4)
+    tr.test_route_weights_sum_to_one_and_equal_topk_only_softmax()
+    tr.test_route_special_cases()
+
+
+def _layer_pins():
+    tr.test_layer_matches_python_brute_force(True, 4)
+    tr.test_silu_values()
+
+
+def test_pins_pass_on_the_real_oracle():
+    _format_pins()
+    _route_pins()
+    _layer_pins()
+
+
+def test_high_bits_first_unpack_is_caught(monkeypatch):
+    def bad(words, bits, cols):
+        c = _unpack(words, bits, cols)
+        per = 32 // bits
+        return c.reshape(c.shape[:-1] + (cols // per, per))[..., ::-1].reshape(c.shape)
+    _patch(monkeypatch, "unpack_codes", bad)
+    assert _fails(_format_pins)
+
+
+def test_bias_inside_the_product_is_caught(monkeypatch):
+    def bad(qt):
+        codes = mo.unpack_codes(qt["q"], qt["bits"], qt["cols"]).astype(np.float32)
+        s = np.repeat(mo.bf16_bits_to_f32(qt["scales"]), qt["group_size"], axis=-1)
+        b = np.repeat(mo.bf16_bits_to_f32(qt["biases"]), qt["group_size"], axis=-1)
+        return (s * (codes + b)).astype(np.float32)
+    _patch(monkeypatch, "dequantize", bad)
+    assert _fails(_format_pins)
+
+
+def test_dropped_bias_is_caught(monkeypatch):
+    def bad(qt):
+        q2 = dict(qt)
+        q2["biases"] = np.zeros_like(np.asarray(qt["biases"]))
+        return _dequant(q2)
+    _patch(monkeypatch, "dequantize", bad)
+    assert _fails(_format_pins)
+
+
+def test_scales_tiled_instead_of_repeated_is_caught(monkeypatch):
+    def bad(qt):
+        codes = mo.unpack_codes(qt["q"], qt["bits"], qt["cols"]).astype(np.float32)
+        s = np.tile(mo.bf16_bits_to_f32(qt["scales"]), qt["group_size"])
+        b = np.tile(mo.bf16_bits_to_f32(qt["biases"]), qt["group_size"])
+        return (s * codes + b).astype(np.float32)
+    _patch(monkeypatch, "dequantize", bad)
+    assert _fails(_format_pins)
+
+
+def test_transposed_weight_in_matvec_is_caught(monkeypatch):
+    def bad(qt, x):
+        w = mo.dequantize(qt).astype(np.float64)
+        x64 = np.asarray(x, np.float64)
+        if w.shape[0] == w.shape[1]:
+            return x64 @ w
+        return x64[:, : w.shape[0]] @ w[:, : w.shape[0]]
+    _patch(monkeypatch, "qmatvec", bad)
+    assert _fails(_format_pins)
+
+
+def test_ties_to_higher_index_are_caught(monkeypatch):
+    def bad(scores, k):
+        s = np.asarray(scores, np.float64)
+        if s.ndim == 1:
+            s = s[None, :]
+        e = s.shape[1]
+        idx, val = _top_k(s[:, ::-1], k)
+        return (e - 1 - idx).astype(np.int32), val
+    _patch(monkeypatch, "top_k", bad)
+    assert _fails(_route_pins)
+
+
+def test_missing_renormalization_is_caught(monkeypatch):
+    _patch(monkeypatch, "route", lambda logits, k, renorm=True: _route(logits, k, False))
+    assert _fails(_route_pins)
+
+
+def test_silu_sign_error_is_caught(monkeypatch):
+    def bad(g):
+        g = np.asarray(g, np.float64)
+        with np.errstate(over="ignore"):
+            return g / (1.0 + np.exp(g))
+    _patch(monkeypatch, "silu", bad)
+    assert _fails(_layer_pins)
+
+
+def test_swapped_slot_weights_are_caught(monkeypatch):
+    def bad(layer, x, idx, w, residual=None):
+        return _moe_experts(layer, x, idx, np.asarray(w)[:, ::-1], residual)
+    _patch(monkeypatch, "moe_experts", bad)
+    assert _fails(_layer_pins)
+
+
+def test_shared_expert_without_sigmoid_is_caught(monkeypatch):
+    def bad(layer, x, idx, w, residual=None):
+        sh = layer.get("shared")
+        if sh is None:
+            return _moe_experts(layer, x, idx, w, residual)
+        lay = dict(layer)
+        lay["shared"] = None
+        y = _moe_experts(lay, x, idx, w, residual)
+        x64 = np.asarray(x, np.float64).reshape(-1, np.asarray(x).shape[-1])
+        g = x64 @ mo._deq64(sh["gate"]).T
+        u = x64 @ mo._deq64(sh["up"]).T
+        return y + mo.swiglu(g, u) @ mo._deq64(sh["down"]).T     # gate scale dropped
+    _patch(monkeypatch, "moe_experts", bad)
+    assert _fails(_layer_pins)
+
+
+@pytest.mark.parametrize("name", ["unpack_codes", "dequantize", "route", "moe_experts"])
+def test_each_patch_target_exists(name):
+    assert callable(getattr(mo, name))
