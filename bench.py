@@ -1,0 +1,369 @@
+#!/usr/bin/env python3
+"""Throughput of the quantized MoE step on one MI355X.
+
+Default workload (``--config c2``): 30B-A3B-shaped decode at batch 1 -- hidden
+2048, 128 experts, top-8, expert intermediate 768, router and experts 8-bit
+affine group 64 -- through 48 independent resident layers.  One step is one
+token through all 48 layers: per layer the router projection with softmax and
+top-K (moe_route) and the expert forward (moe_expert_forward), strictly one
+layer after the other on one stream.  The 48-layer sweep of each of 64 token
+slots is captured once in a HIP graph and replayed; the token slots rotate
+so the routed experts change from step to step.  All weights and activations
+are resident in HBM before the timed region.
+
+Other workloads: ``c3`` (397B-A17B-shaped decode, 4-bit experts + shared
+expert, 8 layers), ``c5`` / ``c5_4bit`` (the same shapes at 2 / 4 bits, 64
+tokens per step), ``c4`` (prefill gather_qmm, M=16384 tokens, one layer).
+
+Prints one JSON line.  ``roofline`` rates the dominant launch against the HBM
+(decode) or bf16 MFMA (prefill) peak, timed live with HIP events on the stream
+it runs on; ``cpu_baseline`` times the CPU oracle on a bounded sample of the
+same workload on this host.
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill) vs peak"
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2516.6
+TOKEN_SLOTS = 64
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_bytes(cfg, touched: float) -> float:
+    """Algorithmic bytes of one layer: the router, every distinct touched
+    expert (codes + bf16 scale/bias) and the shared expert."""
+    def mat(rows, cols, bits):
+        return rows * cols * bits // 8 + rows * (cols // cfg.group_size) * 4
+    router = mat(cfg.experts, cfg.hidden, cfg.router_bits)
+    expert = 2 * mat(cfg.inter, cfg.hidden, cfg.expert_bits) + mat(cfg.hidden, cfg.inter, cfg.expert_bits)
+    shared = 0
+    if cfg.has_shared:
+        shared = (2 * mat(cfg.shared_inter, cfg.hidden, cfg.shared_bits)
+                  + mat(cfg.hidden, cfg.shared_inter, cfg.shared_bits)
+                  + mat(1, cfg.hidden, cfg.shared_gate_bits))
+    acts = 2 * cfg.tokens * cfg.hidden * 4          # x in, y out (fp32)
+    return router + touched * expert + shared + acts
+
+
+def expert_launch_bytes(cfg, touched: float) -> float:
+    """Bytes one moe_expert_forward launch must move: touched experts, the
+    shared expert, x, y and the routing (the router is not part of it)."""
+    def mat(rows, cols, bits):
+        return rows * cols * bits // 8 + rows * (cols // cfg.group_size) * 4
+    expert = 2 * mat(cfg.inter, cfg.hidden, cfg.expert_bits) + mat(cfg.hidden, cfg.inter, cfg.expert_bits)
+    shared = 0
+    if cfg.has_shared:
+        shared = (2 * mat(cfg.shared_inter, cfg.hidden, cfg.shared_bits)
+                  + mat(cfg.hidden, cfg.shared_inter, cfg.shared_bits)
+                  + mat(1, cfg.hidden, cfg.shared_gate_bits))
+    return touched * expert + shared + 2 * cfg.tokens * cfg.hidden * 4 + cfg.tokens * cfg.top_k * 8
+
+
+# --------------------------------------------------------------------------
+# CPU oracle baseline
+# --------------------------------------------------------------------------
+
+class _Picked:
+    """Stack view holding only pre-drawn experts (draw time stays out of the
+    timed oracle call)."""
+
+    def __init__(self, arrays):
+        self.arrays = arrays
+
+    def __getitem__(self, e):
+        return self.arrays[int(e)]
+
+
+def cpu_baseline_decode(cfg, tokens_per_layer, n_layers):
+    import oracle
+    from quantized_moe_expert_unpack_amd import synth
+    try:
+        from threadpoolctl import threadpool_limits
+    except ImportError:  # pragma: no cover
+        threadpool_limits = None
+    cores = min(16, len(os.sched_getaffinity(0)))
+    lim = threadpool_limits(cores) if threadpool_limits else None
+    total = 0.0
+    ntok = 0
+    try:
+        for l in range(n_layers):
+            small = synth._small_tensors(cfg, l)
+            x = np.concatenate([synth.decode_x(cfg, l, t) for t in range(tokens_per_layer)])
+            # pre-draw exactly the experts the oracle will route to (untimed)
+            lg = oracle.qmatvec(small["router"], x)
+            idx, _, _ = oracle.route(lg, cfg.top_k)
+            need = sorted(set(int(e) for e in idx.reshape(-1)))
+            layer = dict(small)
+            for name, tid, rows, cols in (("gate", synth.T_GATE, cfg.inter, cfg.hidden),
+                                          ("up", synth.T_UP, cfg.inter, cfg.hidden),
+                                          ("down", synth.T_DOWN, cfg.hidden, cfg.inter)):
+                drawn = {e: synth.draw_weight(cfg, l, e, tid, rows, cols, cfg.expert_bits) for e in need}
+                layer[name] = {"q": _Picked({e: d[0] for e, d in drawn.items()}),
+                               "scales": _Picked({e: d[1] for e, d in drawn.items()}),
+                               "biases": _Picked({e: d[2] for e, d in drawn.items()}),
+                               "rows": rows, "cols": cols, "bits": cfg.expert_bits,
+                               "group_size": cfg.group_size, "batch": cfg.experts}
+            t0 = time.perf_counter()
+            oracle.moe_layer(layer, x, cfg.top_k, cfg.renorm)
+            total += time.perf_counter() - t0
+            ntok += tokens_per_layer
+    finally:
+        if lim is not None:
+            lim.restore_original_limits()
+    # a token passes through every layer: oracle tokens/s over the full stack
+    per_token_layer = total / ntok
+    value = 1.0 / (per_token_layer * cfg.layers)
+    return {"value": value, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{tokens_per_layer} token(s) x {n_layers} of {cfg.layers} layers "
+                      f"(router + top-K + {cfg.top_k} experts{' + shared' if cfg.has_shared else ''}, "
+                      f"fp64 numpy); {total:.1f} s of oracle time, scaled to {cfg.layers} layers/token"}
+
+
+def cpu_baseline_prefill(cfg, host, m_sample):
+    import oracle
+    from quantized_moe_expert_unpack_amd import synth
+    cores = min(16, len(os.sched_getaffinity(0)))
+    try:
+        from threadpoolctl import threadpool_limits
+        lim = threadpool_limits(cores)
+    except ImportError:  # pragma: no cover
+        lim = None
+    xb = synth.prefill_x_bf16(cfg, m_sample)
+    xf = (xb.astype(np.uint32) << 16).view(np.float32)
+    lg = synth.zipf_logits(cfg, m_sample)
+    t0 = time.perf_counter()
+    idx, w, _ = oracle.route(lg.astype(np.float64), cfg.top_k)
+    oracle.moe_experts(host, xf, idx, w)
+    dt = time.perf_counter() - t0
+    if lim is not None:
+        lim.restore_original_limits()
+    return {"value": m_sample / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{m_sample} of {cfg.tokens} prefill tokens, one layer (fp64 numpy); {dt:.1f} s"}
+
+
+# --------------------------------------------------------------------------
+# decode workloads
+# --------------------------------------------------------------------------
+
+def run_decode(args, cfg):
+    import torch
+    from quantized_moe_expert_unpack_amd import moeq, synth
+
+    dev = torch.device("cuda:0")
+    n_layers = args.layers or cfg.layers
+    m, K, H = cfg.tokens, cfg.top_k, cfg.hidden
+    t0 = time.time()
+    layers = []
+    for l in range(n_layers):
+        host = synth.host_layer(cfg, l, threads=16)
+        layers.append(moeq.MoELayer.from_host(host, dev))
+        del host
+    log(f"[bench] {n_layers} layers resident ({sum(L.gate.nbytes + L.up.nbytes + L.down.nbytes for L in layers) / 1e9:.1f} GB experts) in {time.time() - t0:.0f}s")
+    slots = args.slots
+    x = torch.empty((n_layers, slots, m, H), dtype=torch.float32, device=dev)
+    for l in range(n_layers):
+        for t in range(slots):
+            x[l, t] = torch.from_numpy(synth.decode_x(cfg, l, t, m=m))
+    idx = torch.zeros((n_layers, m, K), dtype=torch.int32, device=dev)
+    w = torch.zeros((n_layers, m, K), dtype=torch.float32, device=dev)
+    y = torch.zeros((n_layers, m, H), dtype=torch.float32, device=dev)
+    ws_route = torch.zeros(8 * m * cfg.experts + 4096, dtype=torch.uint8, device=dev)
+    ws_dec = moeq.workspace(layers[0], m, K, moeq.PATH_DECODE, dev)
+
+    def step(t):
+        for l, L in enumerate(layers):
+            moeq.moe_route(L.router, x[l, t], cfg.experts, K, cfg.renorm, ws=ws_route,
+                           idx=idx[l], w=w[l])
+            moeq.moe_expert_forward(L, x[l, t], idx[l], w[l], ws=ws_dec, y=y[l])
+
+    # eager warm-up (also checks the path runs), then capture one graph per slot
+    for t in range(min(2, slots)):
+        step(t)
+    torch.cuda.synchronize()
+    capture_stream = torch.cuda.Stream()
+    graphs = []
+    for t in range(slots):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=capture_stream):
+            step(t)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    # touched experts per layer (distinct experts over the step's tokens)
+    touched = []
+    for t in range(slots):
+        graphs[t].replay()
+        torch.cuda.synchronize()
+        ii = idx.cpu().numpy()
+        touched.append(np.mean([len(np.unique(ii[l])) for l in range(n_layers)]))
+    touched = float(np.mean(touched))
+
+    for s in range(args.warmup):
+        graphs[s % slots].replay()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for s in range(args.steps):
+        graphs[s % slots].replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    log(f"[bench] timed {args.steps} steps: {ms * 1e3:.1f} us/step")
+
+    bytes_step = n_layers * layer_bytes(cfg, touched)
+    gbps = bytes_step / (ms * 1e-3) / 1e9
+
+    # dominant launch: moe_expert_forward, timed live with HIP events recorded
+    # on the stream it is launched on (eager launches, same buffers)
+    s_ = torch.cuda.current_stream()
+    reps = max(1, args.launch_reps)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(reps * n_layers)]
+    k = 0
+    for r in range(reps):
+        t = r % slots
+        for l, L in enumerate(layers):
+            moeq.moe_route(L.router, x[l, t], cfg.experts, K, cfg.renorm, ws=ws_route,
+                           idx=idx[l], w=w[l])
+            evs[k][0].record(s_)
+            moeq.moe_expert_forward(L, x[l, t], idx[l], w[l], ws=ws_dec, y=y[l])
+            evs[k][1].record(s_)
+            k += 1
+    torch.cuda.synchronize()
+    launch_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    lbytes = expert_launch_bytes(cfg, touched)
+    achieved = lbytes / (launch_us * 1e-6) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": args.traffic, "kernel": "moe_expert_forward",
+                "launch_us": round(launch_us, 2), "bytes_per_launch": int(lbytes)}
+
+    out = {
+        "metric": METRIC, "value": round(m * 1e3 / ms, 2), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "layers": n_layers, "tokens_per_step": m,
+                   "hidden": H, "experts": cfg.experts, "top_k": K, "inter": cfg.inter,
+                   "expert_bits": cfg.expert_bits, "router_bits": cfg.router_bits,
+                   "shared_expert": cfg.has_shared, "group_size": cfg.group_size,
+                   "token_slots": slots, "graph": True},
+        "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+        "bytes_per_step": int(bytes_step), "touched_experts_per_layer": round(touched, 2),
+        "roofline": roofline,
+    }
+    return out
+
+
+# --------------------------------------------------------------------------
+# prefill workload
+# --------------------------------------------------------------------------
+
+def run_prefill(args, cfg):
+    import torch
+    from quantized_moe_expert_unpack_amd import moeq, synth
+
+    dev = torch.device("cuda:0")
+    m = args.tokens or cfg.tokens
+    host = synth.host_layer(cfg, 0, threads=16)
+    L = moeq.MoELayer.from_host(host, dev)
+    xb = torch.from_numpy(synth.prefill_x_bf16(cfg, m).view(np.int16)).to(dev)
+    lg = torch.from_numpy(synth.zipf_logits(cfg, m)).to(dev)
+    K = cfg.top_k
+    idx = torch.empty((m, K), dtype=torch.int32, device=dev)
+    w = torch.empty((m, K), dtype=torch.float32, device=dev)
+    y = torch.empty((m, cfg.hidden), dtype=torch.float32, device=dev)
+    ws = moeq.workspace(L, m, K, moeq.PATH_GATHER, dev)
+
+    def step():
+        moeq.moe_route(None, lg, cfg.experts, K, cfg.renorm, idx=idx, w=w)
+        moeq.moe_gather_qmm(L, xb, idx, w, ws=ws, y=y)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        step()
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    flops = 2.0 * m * K * 3 * cfg.inter * cfg.hidden
+    tflops = flops / (ms * 1e-3) / 1e12
+    out = {
+        "metric": METRIC, "value": round(m * 1e3 / ms, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "tokens": m, "hidden": cfg.hidden,
+                   "experts": cfg.experts, "top_k": K, "inter": cfg.inter,
+                   "expert_bits": cfg.expert_bits, "logits": "zipf(1.1)+gumbel"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": args.traffic, "kernel": "moe_route + moe_gather_qmm",
+                     "flops_per_launch": flops},
+    }
+    out["_host"] = host
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c5_4bit"])
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (decode)")
+    ap.add_argument("--tokens", type=int, default=0, help="override M (prefill)")
+    ap.add_argument("--slots", type=int, default=TOKEN_SLOTS)
+    ap.add_argument("--launch-reps", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-layers", type=int, default=0)
+    ap.add_argument("--traffic", type=float, default=None,
+                    help="HBM bytes per launch from rocprofv3 counters, if taken")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+
+    from quantized_moe_expert_unpack_amd import synth
+    cfg = synth.CONFIGS[args.config]
+    if args.config == "c4":
+        out = run_prefill(args, cfg)
+        host = out.pop("_host")
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_prefill(cfg, host, 1024)
+    else:
+        out = run_decode(args, cfg)
+        if not args.no_cpu_baseline:
+            # bounded samples of ~10-30 s of oracle time: one whole token of the
+            # 48-layer stack, two tokens of the 8-layer stack, one 64-token layer
+            n, tok = {"c2": (48, 1), "c3": (8, 2), "c5": (1, 64), "c5_4bit": (1, 64)}[args.config]
+            out["cpu_baseline"] = cpu_baseline_decode(cfg, tok, args.cpu_layers or n)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

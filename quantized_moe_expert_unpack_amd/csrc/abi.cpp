@@ -1,0 +1,309 @@
+// C-ABI front end of libmoeq: argument validation (before any launch),
+// workspace carve-up and dispatch to the HIP kernels.  See include/moeq.h for
+// the contract of every entry point.
+#include "moeq.h"
+
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cstdint>
+
+#include "launch.h"
+
+using moeq::QT;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxE = 1024;
+constexpr int kMaxK = 16;
+
+inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool fits_i32(int64_t v) { return v >= 0 && v <= INT32_MAX; }
+
+// Validate one quantized tensor; expected dims < 0 are not checked.
+int check_qt(const moeq_qtensor* t, int batch, int rows, int cols) {
+  if (!t) return MOEQ_ERR_NULL_PTR;
+  if (!t->q || !t->scales || !t->biases) return MOEQ_ERR_NULL_PTR;
+  if (t->bits != 2 && t->bits != 4 && t->bits != 8) return MOEQ_ERR_BAD_BITS;
+  if (t->group_size != 64) return MOEQ_ERR_BAD_GROUP;
+  if (t->batch <= 0 || t->rows <= 0 || t->cols <= 0) return MOEQ_ERR_SHAPE;
+  if (t->cols % t->group_size) return MOEQ_ERR_K_TAIL;
+  if (batch >= 0 && t->batch != batch) return MOEQ_ERR_SHAPE;
+  if (rows >= 0 && t->rows != rows) return MOEQ_ERR_SHAPE;
+  if (cols >= 0 && t->cols != cols) return MOEQ_ERR_SHAPE;
+  if (!fits_i32((int64_t)t->batch * t->rows) ||
+      !fits_i32((int64_t)t->batch * t->rows * (t->cols / (32 / t->bits))) ||
+      !fits_i32((int64_t)t->batch * t->rows * t->cols / 4))
+    return MOEQ_ERR_OVERFLOW;
+  if (!aligned16(t->q) || !aligned16(t->scales) || !aligned16(t->biases)) return MOEQ_ERR_ALIGN;
+  return MOEQ_OK;
+}
+
+QT to_qt(const moeq_qtensor& t) {
+  return QT{t.q, t.scales, t.biases, t.batch, t.rows, t.cols, t.bits, t.group_size};
+}
+
+int launch_status() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? MOEQ_OK : MOEQ_ERR_LAUNCH;
+}
+
+// ---- layer validation -----------------------------------------------------
+struct LayerDims {
+  int E, H, I, Is;
+};
+
+int check_experts(const moeq_moe* L, LayerDims* d) {
+  if (!L) return MOEQ_ERR_NULL_PTR;
+  const moeq_qtensor& g = L->gate;
+  int st = check_qt(&g, -1, -1, -1);
+  if (st) return st;
+  d->E = g.batch;
+  d->I = g.rows;
+  d->H = g.cols;
+  if (d->E > kMaxE) return MOEQ_ERR_SHAPE;
+  if ((st = check_qt(&L->up, d->E, d->I, d->H))) return st;
+  if ((st = check_qt(&L->down, d->E, d->H, d->I))) return st;
+  if (L->up.bits != g.bits || L->down.bits != g.bits) return MOEQ_ERR_UNSUPPORTED;
+  d->Is = 0;
+  if (L->has_shared) {
+    if ((st = check_qt(&L->sh_gate, 1, -1, d->H))) return st;
+    d->Is = L->sh_gate.rows;
+    if ((st = check_qt(&L->sh_up, 1, d->Is, d->H))) return st;
+    if ((st = check_qt(&L->sh_down, 1, d->H, d->Is))) return st;
+    if ((st = check_qt(&L->sh_expert_gate, 1, 1, d->H))) return st;
+    if (L->sh_up.bits != L->sh_gate.bits || L->sh_down.bits != L->sh_gate.bits)
+      return MOEQ_ERR_UNSUPPORTED;
+  }
+  return MOEQ_OK;
+}
+
+// ---- workspace layouts ----------------------------------------------------
+size_t route_ws_bytes(int M, int E) { return align_up(sizeof(double) * (size_t)M * E); }
+
+size_t decode_ws_bytes(const LayerDims& d, int M, int K) {
+  return align_up(sizeof(float) * ((size_t)M * K * d.I + (size_t)M * d.Is + (size_t)M));
+}
+
+int max_tiles_for(int n, int E) { return (n + moeq::kGemmBM - 1) / moeq::kGemmBM + E; }
+
+// carve the gather workspace; with base == nullptr only the size is computed
+size_t gather_ws(char* base, int E, int n, int I, int H, bool full, moeq::GatherWs* ws) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  moeq::GatherWs w{};
+  w.max_tiles = max_tiles_for(n, E);
+  w.counts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * E));
+  w.offsets = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
+  w.tile_off = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
+  w.n_tiles = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
+  w.tiles = reinterpret_cast<int4*>(take(sizeof(int4) * (size_t)w.max_tiles));
+  w.sorted = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)n));
+  if (full) {
+    w.h = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * (size_t)n * I));
+    w.ypair = reinterpret_cast<float*>(take(sizeof(float) * (size_t)n * H));
+  }
+  if (ws) *ws = w;
+  return off;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moeq_status_string(int status) {
+  switch (status) {
+    case MOEQ_OK: return "ok";
+    case MOEQ_ERR_NULL_PTR: return "a required pointer is NULL";
+    case MOEQ_ERR_BAD_BITS: return "bits must be 2, 4 or 8";
+    case MOEQ_ERR_BAD_GROUP: return "group_size must be 64";
+    case MOEQ_ERR_K_TAIL: return "cols must be a multiple of group_size";
+    case MOEQ_ERR_SHAPE: return "inconsistent shapes";
+    case MOEQ_ERR_OVERFLOW: return "a size or index does not fit int32";
+    case MOEQ_ERR_ALIGN: return "device pointers must be 16-byte aligned";
+    case MOEQ_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOEQ_ERR_UNSUPPORTED: return "unsupported combination";
+    case MOEQ_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+const char* moeq_version(void) { return "moeq 0.1 gfx950"; }
+
+size_t moe_workspace_size(const moeq_moe* L, int32_t M, int32_t K, int32_t path) {
+  if (!L || M < 0) return 0;
+  if (path == MOEQ_PATH_ROUTE) {
+    const int E = L->router.q ? L->router.rows : L->gate.batch;
+    if (E <= 0) return 0;
+    return route_ws_bytes(M, E) + kAlign;
+  }
+  if (path == MOEQ_PATH_GQMM) {
+    if (check_qt(&L->gate, -1, -1, -1)) return 0;
+    return gather_ws(nullptr, L->gate.batch, M, 0, 0, false, nullptr) + kAlign;
+  }
+  LayerDims d;
+  if (check_experts(L, &d)) return 0;
+  if (K < 1 || K > kMaxK || K > d.E) return 0;
+  if (path == MOEQ_PATH_DECODE) return decode_ws_bytes(d, M, K) + kAlign;
+  if (path == MOEQ_PATH_GATHER) {
+    if (!fits_i32((int64_t)M * K)) return 0;
+    return gather_ws(nullptr, d.E, M * K, d.I, d.H, true, nullptr) + kAlign;
+  }
+  return 0;
+}
+
+int qdequant(const moeq_qtensor* W, uint8_t* codes, float* deq, moeq_stream_t stream) {
+  int st = check_qt(W, -1, -1, -1);
+  if (st) return st;
+  if (!codes && !deq) return MOEQ_ERR_NULL_PTR;
+  if ((codes && !aligned16(codes)) || (deq && !aligned16(deq))) return MOEQ_ERR_ALIGN;
+  moeq::launch_qdequant(to_qt(*W), codes, deq, (hipStream_t)stream);
+  return launch_status();
+}
+
+int qmatvec(const moeq_qtensor* W, const float* x, int32_t M, float* y, moeq_stream_t stream) {
+  int st = check_qt(W, 1, -1, -1);
+  if (st) return st;
+  if (M < 0) return MOEQ_ERR_SHAPE;
+  if (M == 0) return MOEQ_OK;
+  if (!x || !y) return MOEQ_ERR_NULL_PTR;
+  if (!fits_i32((int64_t)M * W->cols) || !fits_i32((int64_t)M * W->rows)) return MOEQ_ERR_OVERFLOW;
+  if (!aligned16(x) || !aligned16(y)) return MOEQ_ERR_ALIGN;
+  moeq::launch_qmatvec(to_qt(*W), x, M, y, (hipStream_t)stream);
+  return launch_status();
+}
+
+int moe_route(const moeq_qtensor* gate, const float* x_or_logits, int32_t M, int32_t E, int32_t K,
+              int32_t renorm, int32_t* topk_idx, float* topk_w, float* logits_out, void* ws,
+              size_t ws_bytes, moeq_stream_t stream) {
+  if (M < 0 || E <= 0 || E > kMaxE || K < 1 || K > kMaxK || K > E) return MOEQ_ERR_SHAPE;
+  if (gate) {
+    int st = check_qt(gate, 1, E, -1);
+    if (st) return st;
+  }
+  if (M == 0) return MOEQ_OK;
+  if (!x_or_logits || !topk_idx || !topk_w) return MOEQ_ERR_NULL_PTR;
+  if (!fits_i32((int64_t)M * E) || !fits_i32((int64_t)M * K) ||
+      (gate && !fits_i32((int64_t)M * gate->cols)))
+    return MOEQ_ERR_OVERFLOW;
+  if (!aligned16(x_or_logits) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+      (logits_out && !aligned16(logits_out)))
+    return MOEQ_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  if (gate) {
+    if (!ws) return MOEQ_ERR_WORKSPACE;
+    if (ws_bytes < route_ws_bytes(M, E)) return MOEQ_ERR_WORKSPACE;
+    if (!aligned16(ws)) return MOEQ_ERR_ALIGN;
+    double* l64 = reinterpret_cast<double*>(ws);
+    moeq::launch_router_f64(to_qt(*gate), x_or_logits, M, l64, logits_out, s);
+    moeq::launch_topk(l64, nullptr, M, E, K, renorm, topk_idx, topk_w, s);
+  } else {
+    if (logits_out) return MOEQ_ERR_UNSUPPORTED;
+    moeq::launch_topk(nullptr, x_or_logits, M, E, K, renorm, topk_idx, topk_w, s);
+  }
+  return launch_status();
+}
+
+int moe_expert_forward(const moeq_moe* L, const float* x, const int32_t* topk_idx,
+                       const float* topk_w, int32_t M, int32_t K, const float* residual, float* y,
+                       void* ws, size_t ws_bytes, moeq_stream_t stream) {
+  LayerDims d;
+  int st = check_experts(L, &d);
+  if (st) return st;
+  if (M < 0 || K < 1 || K > kMaxK || K > d.E) return MOEQ_ERR_SHAPE;
+  if (M == 0) return MOEQ_OK;
+  if (!x || !topk_idx || !topk_w || !y) return MOEQ_ERR_NULL_PTR;
+  if (!fits_i32((int64_t)M * d.H) || !fits_i32((int64_t)M * K * d.I + (int64_t)M * d.Is + M))
+    return MOEQ_ERR_OVERFLOW;
+  if (!aligned16(x) || !aligned16(topk_idx) || !aligned16(topk_w) || !aligned16(y) ||
+      (residual && !aligned16(residual)))
+    return MOEQ_ERR_ALIGN;
+  if (!ws || ws_bytes < decode_ws_bytes(d, M, K)) return MOEQ_ERR_WORKSPACE;
+  if (!aligned16(ws)) return MOEQ_ERR_ALIGN;
+  moeq::DecodeLayer dl;
+  dl.gate = to_qt(L->gate);
+  dl.up = to_qt(L->up);
+  dl.down = to_qt(L->down);
+  dl.has_shared = L->has_shared ? 1 : 0;
+  if (dl.has_shared) {
+    dl.sh_gate = to_qt(L->sh_gate);
+    dl.sh_up = to_qt(L->sh_up);
+    dl.sh_down = to_qt(L->sh_down);
+    dl.sh_eg = to_qt(L->sh_expert_gate);
+  } else {
+    dl.sh_gate = dl.sh_up = dl.sh_down = dl.sh_eg = dl.gate;
+  }
+  dl.E = d.E;
+  dl.H = d.H;
+  dl.I = d.I;
+  dl.Is = d.Is;
+  if (moeq::decode_lds_bytes(dl, K) > 160 * 1024) return MOEQ_ERR_UNSUPPORTED;
+  st = moeq::launch_decode_forward(dl, x, topk_idx, topk_w, M, K, residual, y,
+                                   reinterpret_cast<float*>(ws), (hipStream_t)stream);
+  if (st) return MOEQ_ERR_UNSUPPORTED;
+  return launch_status();
+}
+
+int moe_gather_qmm(const moeq_moe* L, const uint16_t* x_bf16, const int32_t* topk_idx,
+                   const float* topk_w, int32_t M, int32_t K, float* y, void* ws, size_t ws_bytes,
+                   moeq_stream_t stream) {
+  LayerDims d;
+  int st = check_experts(L, &d);
+  if (st) return st;
+  if (L->has_shared) return MOEQ_ERR_UNSUPPORTED;
+  if (M < 0 || K < 1 || K > kMaxK || K > d.E) return MOEQ_ERR_SHAPE;
+  if (M == 0) return MOEQ_OK;
+  if (!x_bf16 || !topk_idx || !topk_w || !y) return MOEQ_ERR_NULL_PTR;
+  const int64_t n = (int64_t)M * K;
+  if (!fits_i32(n) || !fits_i32((int64_t)M * d.H) || !fits_i32(n * d.I) || !fits_i32(n * d.H / 4) ||
+      !fits_i32(max_tiles_for((int)n, d.E)))
+    return MOEQ_ERR_OVERFLOW;
+  if (!aligned16(x_bf16) || !aligned16(topk_idx) || !aligned16(topk_w) || !aligned16(y))
+    return MOEQ_ERR_ALIGN;
+  moeq::GatherWs g;
+  const size_t need = gather_ws(nullptr, d.E, (int)n, d.I, d.H, true, nullptr);
+  if (!ws || ws_bytes < need) return MOEQ_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOEQ_ERR_ALIGN;
+  gather_ws(reinterpret_cast<char*>(ws), d.E, (int)n, d.I, d.H, true, &g);
+  hipStream_t s = (hipStream_t)stream;
+  moeq::launch_sort_pairs(topk_idx, (int)n, d.E, g, s);
+  moeq::launch_gemm_gate_up(to_qt(L->gate), to_qt(L->up), x_bf16, K, g, (int)n, s);
+  moeq::launch_gemm_down(to_qt(L->down), topk_w, g, (int)n, s);
+  moeq::launch_combine(g.ypair, topk_idx, M, K, d.H, d.E, y, s);
+  return launch_status();
+}
+
+int gather_qmm(const moeq_qtensor* W, const uint16_t* x_bf16, const int32_t* rhs_idx, int32_t n,
+               int32_t sorted, float* out, void* ws, size_t ws_bytes, moeq_stream_t stream) {
+  (void)sorted;  // both cases group rows on the device; sorted input keeps its order
+  int st = check_qt(W, -1, -1, -1);
+  if (st) return st;
+  if (W->batch > kMaxE) return MOEQ_ERR_SHAPE;
+  if (n < 0) return MOEQ_ERR_SHAPE;
+  if (n == 0) return MOEQ_OK;
+  if (!x_bf16 || !rhs_idx || !out) return MOEQ_ERR_NULL_PTR;
+  if (!fits_i32((int64_t)n * W->cols) || !fits_i32((int64_t)n * W->rows) ||
+      !fits_i32(max_tiles_for(n, W->batch)))
+    return MOEQ_ERR_OVERFLOW;
+  if (!aligned16(x_bf16) || !aligned16(rhs_idx) || !aligned16(out)) return MOEQ_ERR_ALIGN;
+  moeq::GatherWs g;
+  const size_t need = gather_ws(nullptr, W->batch, n, 0, 0, false, nullptr);
+  if (!ws || ws_bytes < need) return MOEQ_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOEQ_ERR_ALIGN;
+  gather_ws(reinterpret_cast<char*>(ws), W->batch, n, 0, 0, false, &g);
+  hipStream_t s = (hipStream_t)stream;
+  moeq::launch_sort_pairs(rhs_idx, n, W->batch, g, s);
+  moeq::launch_gemm_plain(to_qt(*W), x_bf16, out, g, n, s);
+  moeq::launch_mark_invalid_rows(rhs_idx, n, W->batch, W->rows, out, s);
+  return launch_status();
+}
+
+}  // extern "C"

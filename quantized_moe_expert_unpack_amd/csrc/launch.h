@@ -1,0 +1,68 @@
+// Internal interface between the C-ABI front end (abi.cpp) and the kernel
+// translation units.  Launchers assume validated arguments.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace moeq {
+
+// A validated quantized tensor (see moeq_qtensor in include/moeq.h).
+struct QT {
+  const uint32_t* q;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  int batch, rows, cols, bits, group_size;
+};
+
+// Decode (fp32 activations) layer description.
+struct DecodeLayer {
+  QT gate, up, down;   // [E][I][H], [E][I][H], [E][H][I]
+  int has_shared;
+  QT sh_gate, sh_up, sh_down, sh_eg;  // [1][Is][H] x2, [1][H][Is], [1][1][H]
+  int E, H, I, Is;
+};
+
+// Workspace carve-up for the gather (prefill) path; every pointer is
+// 256-byte aligned inside the caller's workspace.
+struct GatherWs {
+  int32_t* counts;     // [E]
+  int32_t* offsets;    // [E+1]  sorted row offset per expert
+  int32_t* tile_off;   // [E+1]  first tile per expert
+  int32_t* n_tiles;    // [1]
+  int4* tiles;         // [max_tiles] {expert, row0, rows, 0}
+  int32_t* sorted;     // [n] pair id at each sorted position
+  uint16_t* h;         // [n][I] bf16 (moe_gather_qmm only)
+  float* ypair;        // [n][H] fp32 (moe_gather_qmm only)
+  int max_tiles;
+};
+
+constexpr int kGemmBM = 128;  // rows per gather-GEMM tile
+
+int launch_qdequant(const QT& W, uint8_t* codes, float* deq, hipStream_t s);
+int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s);
+int launch_router_f64(const QT& W, const float* x, int M, double* logits, float* logits32,
+                      hipStream_t s);
+int launch_topk(const double* l64, const float* l32, int M, int E, int K, int renorm, int32_t* idx,
+                float* w, hipStream_t s);
+
+// decode expert forward; ws_f32 holds M*K*I + M*Is + M floats
+int launch_decode_forward(const DecodeLayer& L, const float* x, const int32_t* idx, const float* w,
+                          int M, int K, const float* residual, float* y, float* ws_f32,
+                          hipStream_t s);
+size_t decode_lds_bytes(const DecodeLayer& L, int K);
+
+// gather path
+int launch_sort_pairs(const int32_t* idx, int n, int E, const GatherWs& ws, hipStream_t s);
+int launch_gemm_gate_up(const QT& gate, const QT& up, const uint16_t* x, int K, const GatherWs& ws,
+                        int n, hipStream_t s);
+int launch_gemm_down(const QT& down, const float* w, const GatherWs& ws, int n, hipStream_t s);
+int launch_gemm_plain(const QT& W, const uint16_t* x, float* out, const GatherWs& ws, int n,
+                      hipStream_t s);
+// rows whose expert index is outside [0, E) become NaN (gather_qmm output)
+int launch_mark_invalid_rows(const int32_t* idx, int n, int E, int N, float* out, hipStream_t s);
+int launch_combine(const float* ypair, const int32_t* idx, int M, int K, int H, int E, float* y,
+                   hipStream_t s);
+
+}  // namespace moeq

@@ -1,0 +1,293 @@
+"""ctypes binding of libmoeq.so (argument marshalling only).
+
+Every computation happens in the HIP kernels behind the C ABI declared in
+``include/moeq.h``; this module only turns torch device tensors into the
+ABI's plain pointers and sizes, allocates outputs and workspaces with torch,
+and passes torch's current HIP stream.  If the library is missing the first
+call raises: there is no fallback path.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libmoeq.so")
+
+PATH_ROUTE, PATH_DECODE, PATH_GATHER, PATH_GQMM = 0, 1, 2, 3
+
+STATUS = {
+    0: "MOEQ_OK", -1: "MOEQ_ERR_NULL_PTR", -2: "MOEQ_ERR_BAD_BITS", -3: "MOEQ_ERR_BAD_GROUP",
+    -4: "MOEQ_ERR_K_TAIL", -5: "MOEQ_ERR_SHAPE", -6: "MOEQ_ERR_OVERFLOW", -7: "MOEQ_ERR_ALIGN",
+    -8: "MOEQ_ERR_WORKSPACE", -9: "MOEQ_ERR_UNSUPPORTED", -10: "MOEQ_ERR_LAUNCH",
+}
+
+
+class MoeqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {STATUS.get(status, status)} ({_text(status)})")
+
+
+class QTensorStruct(ctypes.Structure):
+    _fields_ = [("q", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
+                ("batch", ctypes.c_int32), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
+                ("bits", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+
+
+class MoEStruct(ctypes.Structure):
+    _fields_ = [("router", QTensorStruct), ("gate", QTensorStruct), ("up", QTensorStruct),
+                ("down", QTensorStruct), ("has_shared", ctypes.c_int32),
+                ("sh_gate", QTensorStruct), ("sh_up", QTensorStruct), ("sh_down", QTensorStruct),
+                ("sh_expert_gate", QTensorStruct)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "moeq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "moeq_version": (ctypes.c_char_p, []),
+    "moe_workspace_size": (_SZ, [ctypes.POINTER(MoEStruct), _I, _I, _I]),
+    "qdequant": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _P, _P]),
+    "qmatvec": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _I, _P, _P]),
+    "moe_route": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _I, _I, _I, _I, _P, _P, _P,
+                                 _P, _SZ, _P]),
+    "moe_expert_forward": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _P, _P, _I, _I, _P, _P,
+                                          _P, _SZ, _P]),
+    "moe_gather_qmm": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _P, _P, _I, _I, _P, _P, _SZ,
+                                      _P]),
+    "gather_qmm": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _P, _I, _I, _P, _P, _SZ, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoeq.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m quantized_moe_expert_unpack_amd.build` (there is no fallback path)")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _text(status: int) -> str:
+    try:
+        return lib().moeq_status_string(status).decode()
+    except Exception:  # noqa: BLE001 - message only
+        return "?"
+
+
+def _check(status: int, what: str) -> None:
+    if status != 0:
+        raise MoeqError(status, what)
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libmoeq takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libmoeq takes contiguous tensors")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+# --------------------------------------------------------------------------
+# tensors
+# --------------------------------------------------------------------------
+
+@dataclass
+class QTensor:
+    """A quantized matrix (or stack) resident on the device.  ``q`` holds the
+    uint32 words as int32, ``scales``/``biases`` the bf16 bit patterns as int16."""
+    q: torch.Tensor
+    scales: torch.Tensor
+    biases: torch.Tensor
+    batch: int
+    rows: int
+    cols: int
+    bits: int
+    group_size: int = 64
+
+    def struct(self) -> QTensorStruct:
+        return QTensorStruct(_ptr(self.q), _ptr(self.scales), _ptr(self.biases), self.batch,
+                             self.rows, self.cols, self.bits, self.group_size)
+
+    @property
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in (self.q, self.scales, self.biases))
+
+    @staticmethod
+    def from_host(d: dict, device="cuda") -> "QTensor":
+        q = np.ascontiguousarray(d["q"]).view(np.int32)
+        s = np.ascontiguousarray(d["scales"]).view(np.int16)
+        b = np.ascontiguousarray(d["biases"]).view(np.int16)
+        return QTensor(torch.from_numpy(q).to(device), torch.from_numpy(s).to(device),
+                       torch.from_numpy(b).to(device), int(d.get("batch", 1)), int(d["rows"]),
+                       int(d["cols"]), int(d["bits"]), int(d.get("group_size", 64)))
+
+
+def _empty_qt() -> QTensorStruct:
+    return QTensorStruct(None, None, None, 0, 0, 0, 0, 0)
+
+
+@dataclass
+class MoELayer:
+    """One MoE layer on the device (router, expert stacks, optional shared expert)."""
+    router: Optional[QTensor]
+    gate: QTensor
+    up: QTensor
+    down: QTensor
+    shared: Optional[dict] = None      # {"gate","up","down","expert_gate"} -> QTensor
+    _struct: Optional[MoEStruct] = field(default=None, repr=False)
+
+    def struct(self) -> MoEStruct:
+        if self._struct is None:
+            sh = self.shared
+            self._struct = MoEStruct(
+                self.router.struct() if self.router is not None else _empty_qt(),
+                self.gate.struct(), self.up.struct(), self.down.struct(), 1 if sh else 0,
+                sh["gate"].struct() if sh else _empty_qt(),
+                sh["up"].struct() if sh else _empty_qt(),
+                sh["down"].struct() if sh else _empty_qt(),
+                sh["expert_gate"].struct() if sh else _empty_qt())
+        return self._struct
+
+    @property
+    def experts(self) -> int:
+        return self.gate.batch
+
+    @property
+    def hidden(self) -> int:
+        return self.gate.cols
+
+    @staticmethod
+    def from_host(layer: dict, device="cuda") -> "MoELayer":
+        sh = None
+        if layer.get("shared") is not None:
+            sh = {k: QTensor.from_host(v, device) for k, v in layer["shared"].items()}
+        router = QTensor.from_host(layer["router"], device) if layer.get("router") is not None else None
+        return MoELayer(router, QTensor.from_host(layer["gate"], device),
+                        QTensor.from_host(layer["up"], device),
+                        QTensor.from_host(layer["down"], device), sh)
+
+
+# --------------------------------------------------------------------------
+# entry points
+# --------------------------------------------------------------------------
+
+def version() -> str:
+    return lib().moeq_version().decode()
+
+
+def workspace_size(layer: MoELayer, m: int, k: int, path: int) -> int:
+    return int(lib().moe_workspace_size(ctypes.byref(layer.struct()), m, k, path))
+
+
+def workspace(layer: MoELayer, m: int, k: int, path: int, device="cuda") -> torch.Tensor:
+    """A zeroed workspace of the size the library asks for (256-byte aligned:
+    torch's caching allocator returns 512-byte aligned blocks)."""
+    n = workspace_size(layer, m, k, path)
+    if n == 0:
+        raise MoeqError(-5, "moe_workspace_size")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def qdequant(W: QTensor, codes: bool = True, deq: bool = True, stream=None):
+    dev = W.q.device
+    shape = (W.batch, W.rows, W.cols)
+    c = torch.empty(shape, dtype=torch.uint8, device=dev) if codes else None
+    d = torch.empty(shape, dtype=torch.float32, device=dev) if deq else None
+    _check(lib().qdequant(ctypes.byref(W.struct()), _ptr(c), _ptr(d), _stream(stream)), "qdequant")
+    return c, d
+
+
+def qmatvec(W: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None):
+    m = x.shape[0]
+    if y is None:
+        y = torch.empty((m, W.rows), dtype=torch.float32, device=x.device)
+    _check(lib().qmatvec(ctypes.byref(W.struct()), _ptr(x), m, _ptr(y), _stream(stream)), "qmatvec")
+    return y
+
+
+def moe_route(gate: Optional[QTensor], x_or_logits: torch.Tensor, experts: int, k: int,
+              renorm: bool = True, ws: Optional[torch.Tensor] = None,
+              idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+              logits_out: Optional[torch.Tensor] = None, stream=None):
+    m = x_or_logits.shape[0]
+    dev = x_or_logits.device
+    if idx is None:
+        idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((m, k), dtype=torch.float32, device=dev)
+    if gate is not None and ws is None:
+        n = 8 * m * experts + 512
+        ws = torch.zeros(n, dtype=torch.uint8, device=dev)
+    gs = ctypes.byref(gate.struct()) if gate is not None else None
+    _check(lib().moe_route(gs, _ptr(x_or_logits), m, experts, k, 1 if renorm else 0, _ptr(idx),
+                           _ptr(w), _ptr(logits_out), _ptr(ws),
+                           ws.numel() if ws is not None else 0, _stream(stream)), "moe_route")
+    return idx, w
+
+
+def moe_expert_forward(layer: MoELayer, x: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
+                       residual: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                       y: Optional[torch.Tensor] = None, stream=None):
+    m, k = idx.shape
+    if ws is None:
+        ws = workspace(layer, m, k, PATH_DECODE, x.device)
+    if y is None:
+        y = torch.empty((m, layer.hidden), dtype=torch.float32, device=x.device)
+    _check(lib().moe_expert_forward(ctypes.byref(layer.struct()), _ptr(x), _ptr(idx), _ptr(w), m,
+                                    k, _ptr(residual), _ptr(y), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "moe_expert_forward")
+    return y
+
+
+def moe_gather_qmm(layer: MoELayer, x_bf16: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,
+                   ws: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                   stream=None):
+    m, k = idx.shape
+    if ws is None:
+        ws = workspace(layer, m, k, PATH_GATHER, x_bf16.device)
+    if y is None:
+        y = torch.empty((m, layer.hidden), dtype=torch.float32, device=x_bf16.device)
+    _check(lib().moe_gather_qmm(ctypes.byref(layer.struct()), _ptr(x_bf16), _ptr(idx), _ptr(w), m,
+                                k, _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
+           "moe_gather_qmm")
+    return y
+
+
+def gather_qmm(W: QTensor, x_bf16: torch.Tensor, rhs_idx: torch.Tensor, sorted_indices=False,
+               ws: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None, stream=None):
+    n = rhs_idx.shape[0]
+    if ws is None:
+        probe = MoELayer(None, W, W, W)
+        ws = workspace(probe, n, 1, PATH_GQMM, x_bf16.device)
+    if out is None:
+        out = torch.empty((n, W.rows), dtype=torch.float32, device=x_bf16.device)
+    _check(lib().gather_qmm(ctypes.byref(W.struct()), _ptr(x_bf16), _ptr(rhs_idx), n,
+                            1 if sorted_indices else 0, _ptr(out), _ptr(ws), ws.numel(),
+                            _stream(stream)), "gather_qmm")
+    return out

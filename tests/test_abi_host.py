@@ -1,0 +1,156 @@
+"""Host-side checks of libmoeq.so, no GPU needed: it loads, exports every
+function that include/moeq.h declares, and rejects every invalid argument
+with its status code before anything is launched (all pointers below are
+fake, aligned addresses that no call may touch)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_moe_expert_unpack_amd import moeq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moeq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(moeq.LIB_PATH),
+                                reason="libmoeq.so not built (run __graft_entry__.build())")
+
+FAKE = 0x7F0000000000            # 16-byte aligned, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*([A-Za-z_][A-Za-z0-9_]*)\s*\(",
+                       text, flags=re.M)
+    return sorted(set(n for n in names if n not in ("if", "while")))
+
+
+def test_header_declares_the_four_calls_and_helpers():
+    names = declared_functions()
+    for n in ("qmatvec", "moe_route", "moe_expert_forward", "moe_gather_qmm", "qdequant",
+              "gather_qmm", "moe_workspace_size", "moeq_status_string", "moeq_version"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moeq.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n), n
+    assert moeq.version().startswith("moeq")
+
+
+def test_status_strings():
+    for code, name in moeq.STATUS.items():
+        assert moeq.lib().moeq_status_string(code)
+    assert moeq.lib().moeq_status_string(12345) == b"unknown status"
+
+
+def _qt(bits=4, batch=1, rows=64, cols=256, gs=64, q=FAKE, s=FAKE + 4096, b=FAKE + 8192):
+    return moeq.QTensorStruct(q, s, b, batch, rows, cols, bits, gs)
+
+
+def _layer(E=8, H=256, I=128, bits=4, shared=False, **over):
+    router = _qt(8, 1, E, H)
+    gate = _qt(bits, E, I, H)
+    up = _qt(bits, E, I, H)
+    down = _qt(bits, E, H, I)
+    L = moeq.MoEStruct(router, gate, up, down, 1 if shared else 0,
+                       _qt(bits, 1, 64, H), _qt(bits, 1, 64, H), _qt(bits, 1, H, 64),
+                       _qt(8, 1, 1, H))
+    for k, v in over.items():
+        setattr(L, k, v)
+    return L
+
+
+def _qmatvec(W, M=1, x=FAKE, y=FAKE):
+    return moeq.lib().qmatvec(ctypes.byref(W), x, M, y, None)
+
+
+@pytest.mark.parametrize("bits,code", [(3, -2), (16, -2), (1, -2), (0, -2)])
+def test_bad_bits(bits, code):
+    assert _qmatvec(_qt(bits=bits)) == code
+
+
+@pytest.mark.parametrize("gs,code", [(32, -3), (128, -3), (0, -3)])
+def test_bad_group(gs, code):
+    assert _qmatvec(_qt(gs=gs)) == code
+
+
+def test_k_tail_and_shapes():
+    assert _qmatvec(_qt(cols=100)) == -4           # cols % 64 != 0 (reduction-dim tail)
+    assert _qmatvec(_qt(rows=0)) == -5
+    assert _qmatvec(_qt(batch=2)) == -5            # qmatvec takes one matrix
+    assert _qmatvec(_qt(), M=-1) == -5
+
+
+def test_null_and_align():
+    assert _qmatvec(_qt(q=0)) == -1
+    assert _qmatvec(_qt(s=0)) == -1
+    assert _qmatvec(_qt(), x=0) == -1
+    assert _qmatvec(_qt(q=FAKE + 4)) == -7
+    assert _qmatvec(_qt(), y=FAKE + 8) == -7
+
+
+def test_overflow():
+    assert _qmatvec(_qt(rows=1 << 20, cols=1 << 16, bits=8)) == -6
+    assert _qmatvec(_qt(cols=1 << 16), M=1 << 16) == -6
+
+
+def test_empty_inputs_are_ok_without_launch():
+    assert _qmatvec(_qt(), M=0, x=0, y=0) == 0
+    L = _layer()
+    assert moeq.lib().moe_expert_forward(ctypes.byref(L), 0, 0, 0, 0, 2, 0, 0, 0, 0, None) == 0
+    assert moeq.lib().moe_gather_qmm(ctypes.byref(L), 0, 0, 0, 0, 2, 0, 0, 0, None) == 0
+    assert moeq.lib().gather_qmm(ctypes.byref(_qt(batch=8)), 0, 0, 0, 0, 0, 0, 0, None) == 0
+
+
+def test_route_validation():
+    f = moeq.lib().moe_route
+    g = _qt(8, 1, 8, 256)
+    assert f(ctypes.byref(g), FAKE, 1, 8, 9, 1, FAKE, FAKE, None, FAKE, 1 << 20, None) == -5  # K > E
+    assert f(ctypes.byref(g), FAKE, 1, 8, 0, 1, FAKE, FAKE, None, FAKE, 1 << 20, None) == -5
+    assert f(ctypes.byref(g), FAKE, 1, 8, 17, 1, FAKE, FAKE, None, FAKE, 1 << 20, None) == -5
+    assert f(ctypes.byref(g), FAKE, 1, 16, 2, 1, FAKE, FAKE, None, FAKE, 1 << 20, None) == -5  # rows != E
+    assert f(None, FAKE, 1, 2048, 2, 1, FAKE, FAKE, None, None, 0, None) == -5                 # E > 1024
+    assert f(ctypes.byref(g), FAKE, 1, 8, 2, 1, FAKE, FAKE, None, None, 0, None) == -8          # no workspace
+    assert f(ctypes.byref(g), FAKE, 1, 8, 2, 1, FAKE, FAKE, None, FAKE, 16, None) == -8         # too small
+    assert f(ctypes.byref(g), FAKE, 1, 8, 2, 1, 0, FAKE, None, FAKE, 1 << 20, None) == -1
+    assert f(None, FAKE, 1, 8, 2, 1, FAKE, FAKE, FAKE, None, 0, None) == -9                     # logits_out in logits mode
+
+
+def test_layer_validation():
+    f = moeq.lib().moe_expert_forward
+
+    def call(L, K=2, ws=1 << 30):
+        return f(ctypes.byref(L), FAKE, FAKE, FAKE, 1, K, None, FAKE, FAKE, ws, None)
+
+    assert call(_layer(), K=9) == -5                                    # K > E
+    assert call(_layer(), K=17) == -5
+    assert call(_layer(up=_qt(4, 8, 128, 512))) == -5                   # up shape mismatch
+    assert call(_layer(down=_qt(4, 8, 128, 256))) == -5                 # down not [E][H][I]
+    assert call(_layer(down=_qt(8, 8, 256, 128))) == -9                 # mixed expert bits
+    assert call(_layer(shared=True, sh_down=_qt(4, 1, 256, 128))) == -5 # shared down [H][Is]
+    assert call(_layer(shared=True, sh_expert_gate=_qt(8, 1, 2, 256))) == -5
+    assert call(_layer(), ws=16) == -8
+    g = moeq.lib().moe_gather_qmm
+    assert g(ctypes.byref(_layer(shared=True)), FAKE, FAKE, FAKE, 4, 2, FAKE, FAKE, 1 << 30, None) == -9
+
+
+def test_workspace_sizes():
+    L = _layer()
+    ws = moeq.lib().moe_workspace_size
+    assert ws(ctypes.byref(L), 1, 2, moeq.PATH_DECODE) >= 4 * (2 * 128 + 1)
+    g = ws(ctypes.byref(L), 1000, 2, moeq.PATH_GATHER)
+    assert g >= 2000 * 128 * 2 + 2000 * 256 * 4
+    assert ws(ctypes.byref(L), 1, 9, moeq.PATH_DECODE) == 0             # K > E
+    assert ws(None, 1, 2, moeq.PATH_DECODE) == 0
+
+
+def test_binding_fails_loudly_without_the_library(monkeypatch):
+    monkeypatch.setattr(moeq, "_lib", None)
+    monkeypatch.setattr(moeq, "LIB_PATH", "/nonexistent/libmoeq.so")
+    with pytest.raises(RuntimeError, match="no fallback"):
+        moeq.lib()

@@ -1,0 +1,136 @@
+"""GPU parity: the bf16-MFMA gather path (moe_gather_qmm, gather_qmm).
+
+Acceptance: max per-row relative L2 <= 2e-2 against the fp64 oracle; one-shot
+equals 2048-token chunks; no row left unwritten under two poison patterns;
+reruns bitwise identical; zero bad rows at the row counts of the pages'
+seam list.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_moe_expert_unpack_amd import moeq, synth
+from tests.gpu_util import bf16_bits_to_f32, bf16_dev, dev, rel_l2_rows, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+POISON = (float("nan"), 3.0e38)
+
+
+@functools.lru_cache(maxsize=1)
+def _c4_layer():
+    cfg = synth.CONFIGS["c4"]
+    host = synth.host_layer(cfg, 0, threads=16)
+    return cfg, host, moeq.MoELayer.from_host(host, dev())
+
+
+def _prefill(cfg, L, xb, lg, chunk=None, poison=None):
+    m = xb.shape[0]
+    x = bf16_dev(xb)
+    idx, w = moeq.moe_route(None, to_dev(lg), cfg.experts, cfg.top_k)
+    y = torch.empty((m, cfg.hidden), dtype=torch.float32, device=dev())
+    if poison is not None:
+        y.fill_(poison)
+    step = chunk or m
+    for s in range(0, m, step):
+        e = min(m, s + step)
+        moeq.moe_gather_qmm(L, x[s:e], idx[s:e], w[s:e], y=y[s:e])
+    torch.cuda.synchronize()
+    return y, idx, w
+
+
+@pytest.mark.parametrize("m", [1, 7, 300, 1000])
+def test_moe_gather_small_m_vs_oracle(m):
+    cfg, host, L = _c4_layer()
+    say(f"moe_gather_qmm M={m}")
+    xb = synth.prefill_x_bf16(cfg, m)
+    lg = synth.zipf_logits(cfg, m)
+    y, idx, w = _prefill(cfg, L, xb, lg, poison=POISON[0])
+    ridx, rw, _ = oracle.route(lg.astype(np.float64), cfg.top_k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    ref = oracle.moe_experts(host, bf16_bits_to_f32(xb), ridx, rw)
+    err = rel_l2_rows(y.cpu().numpy(), ref)
+    say(f"  max rel-L2 {err.max():.3e}")
+    assert np.isfinite(y.cpu().numpy()).all()
+    assert err.max() <= TOL
+
+
+@pytest.mark.parametrize("m", [16068, 16384])
+def test_c4_full_size_sampled_rows_chunks_poison(m):
+    cfg, host, L = _c4_layer()
+    say(f"c4 prefill M={m}")
+    xb = synth.prefill_x_bf16(cfg, m)
+    lg = synth.zipf_logits(cfg, m)
+    y1, idx, w = _prefill(cfg, L, xb, lg, poison=POISON[0])
+    y2, _, _ = _prefill(cfg, L, xb, lg, poison=POISON[1])
+    assert torch.equal(y1, y2)                  # nothing unwritten, bitwise rerun
+    yc, _, _ = _prefill(cfg, L, xb, lg, chunk=2048, poison=POISON[0])
+    assert torch.equal(y1, yc)                  # one-shot == 2048-token chunks
+    # sampled tokens against the oracle: the tail, both ends and random rows
+    rng = np.random.default_rng(m)
+    rows = np.unique(np.concatenate([np.arange(8), np.arange(m - 40, m),
+                                     rng.choice(m, 120, replace=False)]))
+    ridx, rw, _ = oracle.route(lg[rows].astype(np.float64), cfg.top_k)
+    assert np.array_equal(idx.cpu().numpy()[rows], ridx)
+    ref = oracle.moe_experts(host, bf16_bits_to_f32(xb[rows]), ridx, rw)
+    err = rel_l2_rows(y1.cpu().numpy()[rows], ref)
+    say(f"  sampled {len(rows)} rows: max rel-L2 {err.max():.3e}")
+    assert err.max() <= TOL
+
+
+def _gqmm_case(n, bits=4, E=8, N=64, Kd=64, seed=0):
+    q, s, b = synth.draw_matrix((77, bits, E, N), E * N, Kd, bits)
+    host = {"q": q.reshape(E, N, -1), "scales": s.reshape(E, N, -1), "biases": b.reshape(E, N, -1),
+            "batch": E, "rows": N, "cols": Kd, "bits": bits, "group_size": 64}
+    rng = np.random.default_rng(seed)
+    x = synth.f32_to_bf16_bits((rng.standard_normal((n, Kd)) * 0.5).astype(np.float32))
+    ridx = np.sort(rng.integers(0, E, n)).astype(np.int32)
+    return host, x, ridx
+
+
+# the seam list: the row counts the pages print (clean and corrupt ones)
+SEAMS = [32768, 32769, 32802, 32833, 32896, 40000, 40002]
+
+
+@pytest.mark.parametrize("n", SEAMS)
+@pytest.mark.parametrize("bits", [4, 8])
+def test_gather_qmm_seams_have_no_bad_rows(n, bits):
+    say(f"gather_qmm seam n={n} bits={bits}")
+    host, xb, ridx = _gqmm_case(n, bits)
+    W = moeq.QTensor.from_host(host, dev())
+    x, r = bf16_dev(xb), to_dev(ridx)
+    outs = []
+    for p in POISON:
+        out = torch.full((n, 64), p, dtype=torch.float32, device=dev())
+        moeq.gather_qmm(W, x, r, sorted_indices=True, out=out)
+        outs.append(out)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    ref = oracle.gather_qmm(host, bf16_bits_to_f32(xb), ridx)
+    got = outs[0].cpu().numpy()
+    abs_err = np.abs(got - ref).max(axis=1)
+    rel = rel_l2_rows(got, ref)
+    # a row is bad when it is not finite or off by more than the bf16 tolerance;
+    # the issue's unwritten rows are ~1e3x above the noise floor, so a relative
+    # per-row criterion separates them from rounding at any weight scale
+    bad = int((~np.isfinite(rel) | (rel > TOL)).sum())
+    say(f"  max|err| {np.nanmax(abs_err):.4f} max rel-L2 {np.nanmax(rel):.2e} bad rows {bad}/{n}")
+    assert bad == 0
+
+
+def test_gather_qmm_unsorted_equals_sorted_and_invalid_rows_are_nan():
+    host, xb, ridx = _gqmm_case(1000, 8, E=16, N=192, Kd=256, seed=3)
+    W = moeq.QTensor.from_host(host, dev())
+    perm = np.random.default_rng(0).permutation(1000)
+    out_s = moeq.gather_qmm(W, bf16_dev(xb), to_dev(ridx), sorted_indices=True)
+    out_u = moeq.gather_qmm(W, bf16_dev(xb[perm]), to_dev(ridx[perm]), sorted_indices=False)
+    assert torch.equal(out_s[perm], out_u)
+    bad = ridx.copy()
+    bad[5] = 99
+    out_b = moeq.gather_qmm(W, bf16_dev(xb), to_dev(bad)).cpu().numpy()
+    assert np.isnan(out_b[5]).all() and np.isfinite(np.delete(out_b, 5, axis=0)).all()

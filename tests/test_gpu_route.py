@@ -1,0 +1,87 @@
+"""GPU parity: router projection + softmax + top-K (indices bit-exact)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from quantized_moe_expert_unpack_amd import moeq, synth
+from tests.gpu_util import dev, gapped_tokens, say, to_dev, topk_gaps_ok
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3"])
+def test_route_router_mode_matches_oracle(name):
+    cfg = synth.CONFIGS[name]
+    say(f"route {name}")
+    small = synth._small_tensors(cfg, 0)
+    router = small["router"]
+    x = gapped_tokens(cfg, small, 0, 16)[:, 0]              # 16 tokens, gaps >= 1e-4
+    idx, w = moeq.moe_route(moeq.QTensor.from_host(router, dev()), to_dev(x), cfg.experts,
+                            cfg.top_k)
+    torch.cuda.synchronize()
+    lg = oracle.qmatvec(router, x)
+    ridx, rw, _ = oracle.route(lg, cfg.top_k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    assert np.abs(w.cpu().numpy().sum(axis=1) - 1).max() <= 1e-6
+
+
+def test_route_batched_m64_and_logits_out():
+    cfg = synth.CONFIGS["c5"]
+    small = synth._small_tensors(cfg, 0)
+    x = gapped_tokens(cfg, small, 0, 64)[:, 0]
+    lo = torch.empty((64, cfg.experts), dtype=torch.float32, device=dev())
+    idx, w = moeq.moe_route(moeq.QTensor.from_host(small["router"], dev()), to_dev(x),
+                            cfg.experts, cfg.top_k, logits_out=lo)
+    lg = oracle.qmatvec(small["router"], x)
+    ridx, rw, _ = oracle.route(lg, cfg.top_k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    assert np.abs(lo.cpu().numpy() - lg).max() <= 1e-5 * np.abs(lg).max()
+
+
+@pytest.mark.parametrize("m", [1, 5, 16068])
+def test_route_logits_mode_zipf(m):
+    cfg = synth.CONFIGS["c4"]
+    lg = synth.zipf_logits(cfg, m)
+    idx, w = moeq.moe_route(None, to_dev(lg), cfg.experts, cfg.top_k)
+    ridx, rw, _ = oracle.route(lg.astype(np.float64), cfg.top_k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+
+
+def test_route_ties_and_special_cases():
+    # all-equal logits: indices 0..K-1 and uniform weights (lower index wins ties)
+    lg = np.zeros((3, 128), np.float32)
+    lg[1, ::3] = 1.0                     # many exact ties at the top
+    lg[2] = np.round(np.random.default_rng(0).standard_normal(128)).astype(np.float32)
+    idx, w = moeq.moe_route(None, to_dev(lg), 128, 8)
+    ridx, rw, _ = oracle.route(lg.astype(np.float64), 8)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert idx.cpu().numpy()[0].tolist() == list(range(8))
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    # K = E: the whole sorted softmax; E = 2, K = 1: argmax
+    lg2 = np.random.default_rng(1).standard_normal((4, 16)).astype(np.float32)
+    idx, w = moeq.moe_route(None, to_dev(lg2), 16, 16)
+    ridx, rw, _ = oracle.route(lg2.astype(np.float64), 16)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    idx, w = moeq.moe_route(None, to_dev(lg2[:, :2].copy()), 2, 1)
+    assert np.array_equal(idx.cpu().numpy()[:, 0], np.argmax(lg2[:, :2], axis=1))
+    assert np.all(w.cpu().numpy() == 1.0)
+
+
+def test_route_without_renorm():
+    lg = np.random.default_rng(3).standard_normal((8, 64)).astype(np.float32) * 3
+    idx, w = moeq.moe_route(None, to_dev(lg), 64, 4, renorm=False)
+    ridx, rw, _ = oracle.route(lg.astype(np.float64), 4, renorm=False)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+
+
+def test_gap_filter_is_satisfied_by_generated_tokens():
+    cfg = synth.CONFIGS["c2"]
+    small = synth._small_tensors(cfg, 3)
+    x = gapped_tokens(cfg, small, 3, 4)[:, 0]
+    assert topk_gaps_ok(oracle.qmatvec(small["router"], x), cfg.top_k).all()
