@@ -83,10 +83,25 @@ int check_experts(const moeq_moe* L, LayerDims* d) {
 }
 
 // ---- workspace layouts ----------------------------------------------------
-size_t route_ws_bytes(int M, int E) { return align_up(sizeof(double) * (size_t)M * E); }
-
-size_t decode_ws_bytes(const LayerDims& d, int M, int K) {
-  return align_up(sizeof(float) * ((size_t)M * K * d.I + (size_t)M * d.Is + (size_t)M));
+moeq::DecodeLayer to_decode_layer(const moeq_moe* L, const LayerDims& d) {
+  moeq::DecodeLayer dl;
+  dl.gate = to_qt(L->gate);
+  dl.up = to_qt(L->up);
+  dl.down = to_qt(L->down);
+  dl.has_shared = L->has_shared ? 1 : 0;
+  if (dl.has_shared) {
+    dl.sh_gate = to_qt(L->sh_gate);
+    dl.sh_up = to_qt(L->sh_up);
+    dl.sh_down = to_qt(L->sh_down);
+    dl.sh_eg = to_qt(L->sh_expert_gate);
+  } else {
+    dl.sh_gate = dl.sh_up = dl.sh_down = dl.sh_eg = dl.gate;
+  }
+  dl.E = d.E;
+  dl.H = d.H;
+  dl.I = d.I;
+  dl.Is = d.Is;
+  return dl;
 }
 
 int max_tiles_for(int n, int E) { return (n + moeq::kGemmBM - 1) / moeq::kGemmBM + E; }
@@ -143,7 +158,7 @@ size_t moe_workspace_size(const moeq_moe* L, int32_t M, int32_t K, int32_t path)
   if (path == MOEQ_PATH_ROUTE) {
     const int E = L->router.q ? L->router.rows : L->gate.batch;
     if (E <= 0) return 0;
-    return route_ws_bytes(M, E) + kAlign;
+    return moeq::route_ws_bytes(M, E) + kAlign;
   }
   if (path == MOEQ_PATH_GQMM) {
     if (check_qt(&L->gate, -1, -1, -1)) return 0;
@@ -152,7 +167,7 @@ size_t moe_workspace_size(const moeq_moe* L, int32_t M, int32_t K, int32_t path)
   LayerDims d;
   if (check_experts(L, &d)) return 0;
   if (K < 1 || K > kMaxK || K > d.E) return 0;
-  if (path == MOEQ_PATH_DECODE) return decode_ws_bytes(d, M, K) + kAlign;
+  if (path == MOEQ_PATH_DECODE) return moeq::decode_ws_bytes(to_decode_layer(L, d), M, K) + kAlign;
   if (path == MOEQ_PATH_GATHER) {
     if (!fits_i32((int64_t)M * K)) return 0;
     return gather_ws(nullptr, d.E, M * K, d.I, d.H, true, nullptr) + kAlign;
@@ -197,18 +212,17 @@ int moe_route(const moeq_qtensor* gate, const float* x_or_logits, int32_t M, int
   if (!aligned16(x_or_logits) || !aligned16(topk_idx) || !aligned16(topk_w) ||
       (logits_out && !aligned16(logits_out)))
     return MOEQ_ERR_ALIGN;
-  hipStream_t s = (hipStream_t)stream;
   if (gate) {
     if (!ws) return MOEQ_ERR_WORKSPACE;
-    if (ws_bytes < route_ws_bytes(M, E)) return MOEQ_ERR_WORKSPACE;
-    if (!aligned16(ws)) return MOEQ_ERR_ALIGN;
-    double* l64 = reinterpret_cast<double*>(ws);
-    moeq::launch_router_f64(to_qt(*gate), x_or_logits, M, l64, logits_out, s);
-    moeq::launch_topk(l64, nullptr, M, E, K, renorm, topk_idx, topk_w, s);
-  } else {
-    if (logits_out) return MOEQ_ERR_UNSUPPORTED;
-    moeq::launch_topk(nullptr, x_or_logits, M, E, K, renorm, topk_idx, topk_w, s);
+    if (ws_bytes < moeq::route_ws_bytes(M, E)) return MOEQ_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOEQ_ERR_ALIGN;
+  } else if (logits_out) {
+    return MOEQ_ERR_UNSUPPORTED;
   }
+  moeq::QT g;
+  if (gate) g = to_qt(*gate);
+  moeq::launch_route(gate ? &g : nullptr, x_or_logits, M, E, K, renorm, topk_idx, topk_w,
+                     logits_out, ws, (hipStream_t)stream);
   return launch_status();
 }
 
@@ -226,28 +240,12 @@ int moe_expert_forward(const moeq_moe* L, const float* x, const int32_t* topk_id
   if (!aligned16(x) || !aligned16(topk_idx) || !aligned16(topk_w) || !aligned16(y) ||
       (residual && !aligned16(residual)))
     return MOEQ_ERR_ALIGN;
-  if (!ws || ws_bytes < decode_ws_bytes(d, M, K)) return MOEQ_ERR_WORKSPACE;
-  if (!aligned16(ws)) return MOEQ_ERR_ALIGN;
-  moeq::DecodeLayer dl;
-  dl.gate = to_qt(L->gate);
-  dl.up = to_qt(L->up);
-  dl.down = to_qt(L->down);
-  dl.has_shared = L->has_shared ? 1 : 0;
-  if (dl.has_shared) {
-    dl.sh_gate = to_qt(L->sh_gate);
-    dl.sh_up = to_qt(L->sh_up);
-    dl.sh_down = to_qt(L->sh_down);
-    dl.sh_eg = to_qt(L->sh_expert_gate);
-  } else {
-    dl.sh_gate = dl.sh_up = dl.sh_down = dl.sh_eg = dl.gate;
-  }
-  dl.E = d.E;
-  dl.H = d.H;
-  dl.I = d.I;
-  dl.Is = d.Is;
-  if (moeq::decode_lds_bytes(dl, K) > 160 * 1024) return MOEQ_ERR_UNSUPPORTED;
-  st = moeq::launch_decode_forward(dl, x, topk_idx, topk_w, M, K, residual, y,
-                                   reinterpret_cast<float*>(ws), (hipStream_t)stream);
+  const moeq::DecodeLayer dl = to_decode_layer(L, d);
+  if (!moeq::decode_supported(dl, K)) return MOEQ_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < moeq::decode_ws_bytes(dl, M, K)) return MOEQ_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOEQ_ERR_ALIGN;
+  st = moeq::launch_decode_forward(dl, x, topk_idx, topk_w, M, K, residual, y, ws,
+                                   (hipStream_t)stream);
   if (st) return MOEQ_ERR_UNSUPPORTED;
   return launch_status();
 }

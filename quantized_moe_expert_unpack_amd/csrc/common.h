@@ -49,4 +49,30 @@ __device__ __forceinline__ double wave_max(double v) {
 
 __device__ __forceinline__ float silu(float g) { return g / (1.0f + __expf(-g)); }
 
+// ---- arrival counting ------------------------------------------------------
+// Device-scope atomics on one address serialize across the chip (about 11 ns
+// each, measured on MI355X), so many arrivals are spread over kFan counters on
+// separate 128-byte lines; whoever completes a sub-counter counts once in a top
+// counter.  arrive() returns true for exactly one caller: the one completing
+// all `total` arrivals.  Every counter is reset by the caller that completes
+// it (no later arrival can touch it within the same launch), so the lines are
+// zero again when the launch ends.
+constexpr int kLineInts = 32;   // ints per 128-byte line
+constexpr int kFan = 16;
+
+// lines: (1 + kFan) * kLineInts ints: [0] top counter, [1 + s] sub-counter s
+__device__ __forceinline__ bool arrive(int* lines, int slot, int total) {
+  const int sub = slot % kFan;
+  const int n_sub = total / kFan + (sub < total % kFan ? 1 : 0);
+  int* c = lines + (1 + sub) * kLineInts;
+  if (__hip_atomic_fetch_add(c, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n_sub - 1)
+    return false;
+  __hip_atomic_store(c, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const int n_top = total < kFan ? total : kFan;
+  if (__hip_atomic_fetch_add(lines, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != n_top - 1)
+    return false;
+  __hip_atomic_store(lines, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
 }  // namespace moeq

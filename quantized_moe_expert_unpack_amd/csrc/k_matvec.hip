@@ -97,137 +97,177 @@ __global__ void __launch_bounds__(256) k_qmatvec(const uint32_t* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// Router projection in fp64: logits[m][e] = sum_k w_e,k * x_m,k with the fp32
-// dequantized weight widened exactly and fp64 products/accumulation, so the
-// top-K decision is taken on fp64 values.
+// Routing: softmax over all E experts, top-K by (score descending, index
+// ascending), weights p[idx]/sum p[idx] (renorm) or p[idx].
+// markbaseengine MOE_ROUTER_WORKS_BREAKTHROUGH "Forward Pass Sequence" steps
+// 1-4 and the flash-moe pipeline's "softmax + topK routing", on the device.
+//
+// Selection works on unique 64-bit keys: the fp64 logit's order-preserving bit
+// pattern with its 10 lowest fraction bits replaced by (1023 - expert), so one
+// integer compare orders by value and breaks ties towards the lower index
+// (logits closer than 2^-42 relative compare as a tie; fp32 logits widened to
+// fp64 have those bits zero and are ordered exactly).  A block of 4 waves
+// first ranks each quarter of the keys inside its wave, keeps every key whose
+// rank in its quarter is < K (at most 4K candidates), then ranks the
+// candidates.  The softmax itself is evaluated in fp64 on the exact logits.
 // ---------------------------------------------------------------------------
-template <int BITS>
-__global__ void __launch_bounds__(256) k_router_f64(const uint32_t* __restrict__ q,
-                                                    const uint16_t* __restrict__ sc,
-                                                    const uint16_t* __restrict__ bi, int rows,
-                                                    int cols, const float* __restrict__ x, int M,
-                                                    double* __restrict__ logits,
-                                                    float* __restrict__ logits32) {
-  constexpr int kCpc = 128 / BITS;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int r = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-  if (r >= rows) return;
-  const int chunks = cols / kCpc;
-  const int groups = cols / kGroup;
-  const uint4* rq = reinterpret_cast<const uint4*>(q + (size_t)r * (cols / (32 / BITS)));
-  const uint16_t* rs = sc + (size_t)r * groups;
-  const uint16_t* rb = bi + (size_t)r * groups;
-  for (int m0 = 0; m0 < M; m0 += 2) {
-    const int mn = min(2, M - m0);
-    double acc[2] = {0.0, 0.0};
-    for (int c = lane; c < chunks; c += kWave) {
-      const uint4 v = rq[c];
-      const int g = (c * kCpc) / kGroup;
-      const float s = bf16_to_f32(rs[g]);
-      const float b = bf16_to_f32(rb[g]);
-      const float* xc = x + (size_t)m0 * cols + (size_t)c * kCpc;
-#pragma unroll
-      for (int j = 0; j < kCpc; j += 4) {
-        double w[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) w[u] = (double)fmaf(s, (float)chunk_code<BITS>(v, j + u), b);
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          if (mm < mn) {
-            const float4 xv = *reinterpret_cast<const float4*>(xc + (size_t)mm * cols + j);
-            acc[mm] = fma(w[0], (double)xv.x, acc[mm]);
-            acc[mm] = fma(w[1], (double)xv.y, acc[mm]);
-            acc[mm] = fma(w[2], (double)xv.z, acc[mm]);
-            acc[mm] = fma(w[3], (double)xv.w, acc[mm]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int mm = 0; mm < 2; ++mm) {
-      const double t = wave_sum(acc[mm]);
-      if (lane == 0 && mm < mn) {
-        logits[(size_t)(m0 + mm) * rows + r] = t;
-        if (logits32) logits32[(size_t)(m0 + mm) * rows + r] = (float)t;
-      }
-    }
-  }
+constexpr int kRouteThreads = 256;
+constexpr int kMaxE = 1024;
+
+__device__ __forceinline__ uint64_t route_key(double v, int e) {
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+  return (u & ~0x3FFull) | (uint64_t)(1023 - e);
 }
 
-// ---------------------------------------------------------------------------
-// Softmax + explicit top-K, one wave per token.  K rounds of "largest
-// remaining logit, lowest index on ties"; weights exp(l_k - max) over the sum
-// of the chosen ones (renorm) or over all E (softmax values).  fp64 math.
-// ---------------------------------------------------------------------------
-constexpr int kMaxPerLane = 16;  // E <= 1024
-
-__device__ __forceinline__ bool better(double v, int i, double ov, int oi) {
-  return v > ov || (v == ov && i < oi);
-}
-
-__global__ void __launch_bounds__(256) k_topk(const double* __restrict__ l64,
-                                              const float* __restrict__ l32, int M, int E, int K,
-                                              int renorm, int32_t* __restrict__ idx,
-                                              float* __restrict__ wout) {
-  const int lane = threadIdx.x & (kWave - 1);
-  const int t = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
-  if (t >= M) return;
-  double v[kMaxPerLane];
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) {
-    const int e = lane + kWave * i;
-    double val = -INFINITY;
-    if (e < E) val = l64 ? l64[(size_t)t * E + e] : (double)l32[(size_t)t * E + e];
-    v[i] = val;
+// keys/vals in LDS for one token; writes K indices and weights
+__device__ void block_topk(const uint64_t* keys, const double* vals, int E, int K, int renorm,
+                           int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
+  __shared__ uint64_t cand[4 * 16];
+  __shared__ int ncand;
+  __shared__ int sel[16];
+  __shared__ double red[kRouteThreads / kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  if (tid == 0) ncand = 0;
+  __syncthreads();
+  const int q = (E + 3) / 4;
+  const int lo = wid * q, hi = min(E, lo + q);
+  for (int a = lo + lane; a < hi; a += kWave) {
+    const uint64_t ka = keys[a];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = lo; j < hi; ++j) rank += keys[j] > ka;
+    if (rank < K) cand[atomicAdd(&ncand, 1)] = ka;
   }
-  double mx = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < kMaxPerLane; ++i) mx = fmax(mx, v[i]);
-  mx = wave_max(mx);
+  __syncthreads();
+  const int nc = ncand;
+  if (tid < nc) {
+    const uint64_t kt = cand[tid];
+    int rank = 0;
+#pragma unroll 8
+    for (int j = 0; j < nc; ++j) rank += cand[j] > kt;
+    if (rank < K) sel[rank] = 1023 - (int)(kt & 0x3FFull);
+  }
+  __syncthreads();
+  const double mx = vals[sel[0]];
   double total = 0.0;
   if (!renorm) {
     double part = 0.0;
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
-      if (lane + kWave * i < E) part += exp(v[i] - mx);
-    total = wave_sum(part);
+    for (int e = tid; e < E; e += kRouteThreads) part += exp(vals[e] - mx);
+    part = wave_sum(part);
+    if (lane == 0) red[wid] = part;
+    __syncthreads();
+    for (int w = 0; w < kRouteThreads / kWave; ++w) total += red[w];
+  } else {
+    for (int k = 0; k < K; ++k) total += exp(vals[sel[k]] - mx);   // slot order
   }
-  double selv[16];
-  int seli[16];
-  double selsum = 0.0;
-  for (int k = 0; k < K; ++k) {
-    double bv = -INFINITY;
-    int bi = 0x7fffffff;
+  if (tid < K) {
+    const int e = sel[tid];
+    idx_out[tid] = e;
+    w_out[tid] = (float)(exp(vals[e] - mx) / total);
+  }
+  __syncthreads();
+}
+
+// Router projection in fp64 (the fp32 dequantized weight widened exactly,
+// fp64 products and sums), one wave per router row and token.  With
+// LAST_TOPK the block that finishes last (arrival counter) runs top-K for all
+// M tokens and resets the counter; otherwise logits stay in the workspace for
+// k_topk_rows.
+template <int BITS, bool LAST_TOPK>
+__global__ void __launch_bounds__(kRouteThreads) k_router(QT W, const float* __restrict__ x, int M,
+                                                          int K, int renorm,
+                                                          double* __restrict__ logits,
+                                                          int* __restrict__ ctr,
+                                                          float* __restrict__ logits32,
+                                                          int32_t* __restrict__ idx,
+                                                          float* __restrict__ wout) {
+  __shared__ uint64_t keys[kMaxE];
+  __shared__ double vals[kMaxE];
+  __shared__ int s_last;
+  constexpr int kCpc = 128 / BITS;
+  const int rows = W.rows, cols = W.cols;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = blockIdx.x * (kRouteThreads / kWave) + (threadIdx.x / kWave);
+  if (r < rows) {
+    const int chunks = cols / kCpc;
+    const int groups = cols / kGroup;
+    const uint4* rq = reinterpret_cast<const uint4*>(W.q + (size_t)r * (cols / (32 / BITS)));
+    const uint16_t* rs = W.scales + (size_t)r * groups;
+    const uint16_t* rb = W.biases + (size_t)r * groups;
+    for (int m = 0; m < M; ++m) {
+      double acc = 0.0;
+      const float* xm = x + (size_t)m * cols;
+      for (int c = lane; c < chunks; c += kWave) {
+        const uint4 v = rq[c];
+        const int g = (c * kCpc) / kGroup;
+        const float s = bf16_to_f32(rs[g]);
+        const float b = bf16_to_f32(rb[g]);
+        const float* xc = xm + (size_t)c * kCpc;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) {
-      const int e = lane + kWave * i;
-      if (e < E && better(v[i], e, bv, bi)) { bv = v[i]; bi = e; }
+        for (int j = 0; j < kCpc; j += 4) {
+          const float4 xv = *reinterpret_cast<const float4*>(xc + j);
+          acc = fma((double)fmaf(s, (float)chunk_code<BITS>(v, j + 0), b), (double)xv.x, acc);
+          acc = fma((double)fmaf(s, (float)chunk_code<BITS>(v, j + 1), b), (double)xv.y, acc);
+          acc = fma((double)fmaf(s, (float)chunk_code<BITS>(v, j + 2), b), (double)xv.z, acc);
+          acc = fma((double)fmaf(s, (float)chunk_code<BITS>(v, j + 3), b), (double)xv.w, acc);
+        }
+      }
+      acc = wave_sum(acc);
+      if (lane == 0) {
+        __hip_atomic_store(logits + (size_t)m * rows + r, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (logits32) logits32[(size_t)m * rows + r] = (float)acc;
+      }
+    }
+  }
+  if (!LAST_TOPK) return;
+  // logits went out with coherent (agent-scope) stores: drain, then announce
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) s_last = arrive(ctr, blockIdx.x, gridDim.x);
+  __syncthreads();
+  if (!s_last) return;
+  for (int m = 0; m < M; ++m) {
+    double v[kMaxE / kRouteThreads];               // all loads in flight first
+#pragma unroll
+    for (int j = 0; j < kMaxE / kRouteThreads; ++j) {
+      const int e = threadIdx.x + kRouteThreads * j;
+      v[j] = e < rows ? __hip_atomic_load(logits + (size_t)m * rows + e, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT)
+                      : 0.0;
     }
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const double ov = __shfl_xor(bv, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    for (int j = 0; j < kMaxE / kRouteThreads; ++j) {
+      const int e = threadIdx.x + kRouteThreads * j;
+      if (e < rows) {
+        vals[e] = v[j];
+        keys[e] = route_key(v[j], e);
+      }
     }
-#pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
-      if (lane + kWave * i == bi) v[i] = -INFINITY;
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-      if (kk == k) { selv[kk] = bv; seli[kk] = bi; }
-    selsum += exp(bv - mx);
-  }
-  if (renorm) total = selsum;
-  if (lane < K) {
-    double sv = 0.0;
-    int si = 0;
-#pragma unroll
-    for (int kk = 0; kk < 16; ++kk)
-      if (kk == lane) { sv = selv[kk]; si = seli[kk]; }
-    idx[(size_t)t * K + lane] = si;
-    wout[(size_t)t * K + lane] = (float)(exp(sv - mx) / total);
+    __syncthreads();
+    block_topk(keys, vals, rows, K, renorm, idx + (size_t)m * K, wout + (size_t)m * K);
   }
 }
+
+// top-K for many tokens: one block per token, logits fp64 (router) or fp32 (given)
+__global__ void __launch_bounds__(kRouteThreads) k_topk_rows(const double* __restrict__ l64,
+                                                             const float* __restrict__ l32, int M,
+                                                             int E, int K, int renorm,
+                                                             int32_t* __restrict__ idx,
+                                                             float* __restrict__ wout) {
+  __shared__ uint64_t keys[kMaxE];
+  __shared__ double vals[kMaxE];
+  const int t = blockIdx.x;
+  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
+    const double v = l64 ? l64[(size_t)t * E + e] : (double)l32[(size_t)t * E + e];
+    vals[e] = v;
+    keys[e] = route_key(v, e);
+  }
+  __syncthreads();
+  block_topk(keys, vals, E, K, renorm, idx + (size_t)t * K, wout + (size_t)t * K);
+}
+
+constexpr int kLastTopkMaxM = 4;
 
 // ---------------------------------------------------------------------------
 // host launchers
@@ -257,18 +297,40 @@ int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s) 
   return 0;
 }
 
-int launch_router_f64(const QT& W, const float* x, int M, double* logits, float* logits32,
-                      hipStream_t s) {
-  const int blocks = (W.rows + 3) / 4;
-  MOEQ_BITS_LAUNCH(W.bits, k_router_f64, dim3(blocks), s, W.q, W.scales, W.biases, W.rows, W.cols,
-                   x, M, logits, logits32);
-  return 0;
+constexpr size_t kRouteCtrBytes = sizeof(int) * kLineInts * (1 + kFan);
+
+size_t route_ws_bytes(int M, int E) {
+  return ((sizeof(double) * (size_t)M * E + 255) / 256) * 256 + kRouteCtrBytes;
 }
 
-int launch_topk(const double* l64, const float* l32, int M, int E, int K, int renorm, int32_t* idx,
-                float* w, hipStream_t s) {
-  const int blocks = (M + 3) / 4;
-  hipLaunchKernelGGL(k_topk, dim3(blocks), dim3(256), 0, s, l64, l32, M, E, K, renorm, idx, w);
+int launch_route(const QT* router, const float* x_or_logits, int M, int E, int K, int renorm,
+                 int32_t* idx, float* w, float* logits32, void* ws, hipStream_t s) {
+  if (!router) {
+    hipLaunchKernelGGL(k_topk_rows, dim3(M), dim3(kRouteThreads), 0, s, (const double*)nullptr,
+                       x_or_logits, M, E, K, renorm, idx, w);
+    return 0;
+  }
+  double* l64 = reinterpret_cast<double*>(ws);
+  int* ctr = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + route_ws_bytes(M, E) - kRouteCtrBytes);
+  const dim3 grid((E + 3) / 4);
+  const QT& W = *router;
+  const bool last = M <= kLastTopkMaxM;
+#define MOEQ_ROUTER(B_)                                                                           \
+  if (W.bits == B_) {                                                                             \
+    if (last)                                                                                     \
+      hipLaunchKernelGGL((k_router<B_, true>), grid, dim3(kRouteThreads), 0, s, W, x_or_logits, M, \
+                         K, renorm, l64, ctr, logits32, idx, w);                                   \
+    else                                                                                          \
+      hipLaunchKernelGGL((k_router<B_, false>), grid, dim3(kRouteThreads), 0, s, W, x_or_logits,  \
+                         M, K, renorm, l64, ctr, logits32, idx, w);                               \
+  }
+  MOEQ_ROUTER(8)
+  MOEQ_ROUTER(4)
+  MOEQ_ROUTER(2)
+#undef MOEQ_ROUTER
+  if (!last)
+    hipLaunchKernelGGL(k_topk_rows, dim3(M), dim3(kRouteThreads), 0, s, l64, (const float*)nullptr,
+                       M, E, K, renorm, idx, w);
   return 0;
 }
 

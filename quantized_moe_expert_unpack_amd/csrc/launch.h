@@ -24,6 +24,16 @@ struct DecodeLayer {
   int E, H, I, Is;
 };
 
+// Decode plan: unit counts and the workspace carve-up of the fused decode
+// expert kernel (counters are zero between calls).
+struct DecPlan {
+  int M, K, S, P, Imax;
+  int ng_routed, ng_shared, g_units, nc, d_units;
+  int* ctr;      // 128-byte lines: error word, then per token gdone, ready, ddone
+  float* h;      // [P][Imax] (pair p = token * S + slot)
+  float* sg;     // [M]
+};
+
 // Workspace carve-up for the gather (prefill) path; every pointer is
 // 256-byte aligned inside the caller's workspace.
 struct GatherWs {
@@ -42,16 +52,18 @@ constexpr int kGemmBM = 128;  // rows per gather-GEMM tile
 
 int launch_qdequant(const QT& W, uint8_t* codes, float* deq, hipStream_t s);
 int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s);
-int launch_router_f64(const QT& W, const float* x, int M, double* logits, float* logits32,
-                      hipStream_t s);
-int launch_topk(const double* l64, const float* l32, int M, int E, int K, int renorm, int32_t* idx,
-                float* w, hipStream_t s);
+// routing: router projection (fp64) + softmax/top-K; ws holds the fp64 logits
+// and a counter (zero between calls)
+size_t route_ws_bytes(int M, int E);
+int launch_route(const QT* router, const float* x_or_logits, int M, int E, int K, int renorm,
+                 int32_t* idx, float* w, float* logits32, void* ws, hipStream_t s);
 
-// decode expert forward; ws_f32 holds M*K*I + M*Is + M floats
+// decode expert forward (one launch)
 int launch_decode_forward(const DecodeLayer& L, const float* x, const int32_t* idx, const float* w,
-                          int M, int K, const float* residual, float* y, float* ws_f32,
-                          hipStream_t s);
+                          int M, int K, const float* residual, float* y, void* ws, hipStream_t s);
+size_t decode_ws_bytes(const DecodeLayer& L, int M, int K);
 size_t decode_lds_bytes(const DecodeLayer& L, int K);
+bool decode_supported(const DecodeLayer& L, int K);
 
 // gather path
 int launch_sort_pairs(const int32_t* idx, int n, int E, const GatherWs& ws, hipStream_t s);

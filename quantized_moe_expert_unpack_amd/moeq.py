@@ -242,7 +242,7 @@ def moe_route(gate: Optional[QTensor], x_or_logits: torch.Tensor, experts: int, 
     if w is None:
         w = torch.empty((m, k), dtype=torch.float32, device=dev)
     if gate is not None and ws is None:
-        n = 8 * m * experts + 512
+        n = 8 * m * experts + 4096
         ws = torch.zeros(n, dtype=torch.uint8, device=dev)
     gs = ctypes.byref(gate.struct()) if gate is not None else None
     _check(lib().moe_route(gs, _ptr(x_or_logits), m, experts, k, 1 if renorm else 0, _ptr(idx),
