@@ -118,13 +118,14 @@ size_t gather_ws(char* base, int E, int n, int I, int H, bool full, moeq::Gather
   w.max_tiles = max_tiles_for(n, E);
   w.counts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * E));
   w.offsets = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
+  w.cursor = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * E));
   w.tile_off = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
   w.n_tiles = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
   w.tiles = reinterpret_cast<int4*>(take(sizeof(int4) * (size_t)w.max_tiles));
   w.sorted = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)n));
   if (full) {
     w.h = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * (size_t)n * I));
-    w.ypair = reinterpret_cast<float*>(take(sizeof(float) * (size_t)n * H));
+    w.ypair = reinterpret_cast<uint16_t*>(take(sizeof(uint16_t) * (size_t)n * H));
   }
   if (ws) *ws = w;
   return off;

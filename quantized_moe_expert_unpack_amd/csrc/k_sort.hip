@@ -1,39 +1,51 @@
-// Group (token, slot) pairs by expert on the device, stably by pair id, and
-// build the per-expert tile list of the gather GEMMs.
+// Group (token, slot) pairs by expert on the device and build the per-expert
+// tile list of the gather GEMMs.
 //
 // ml-explore/mlx issue #3856 (minimal repro and the mlx-lm SwitchGLU path)
 // sorts the expert indices before gather_qmm; the unsort reads back only the
 // original rows.  All row counts and offsets here are int32 and every tile
 // records its exact row count, so ragged tails of any length are covered (the
 // issue's defect came from narrowing a remaining-row count to 16 bits).
+//
+// Three launches: a histogram (LDS counts per block, one global add per
+// (block, expert)), a one-block scan (expert offsets, tile offsets, the tile
+// list, and per-expert cursors initialised to the offsets; it also clears the
+// counts for the next call) and a scatter (LDS ranks per block, one global
+// cursor add per (block, expert)).  Within an expert the pair order depends on
+// atomic order; a pair's GEMM output does not depend on its position in a
+// tile, so results are bitwise reproducible all the same.
 #include "common.h"
 #include "launch.h"
 
 namespace moeq {
 
-// counts[e] = #{p : idx[p] == e}; one block per expert.
-__global__ void __launch_bounds__(256) k_count(const int32_t* __restrict__ idx, int n,
-                                               int32_t* __restrict__ counts) {
-  __shared__ int part[256 / kWave];
-  const int e = blockIdx.x;
-  int c = 0;
-  for (int p = threadIdx.x; p < n; p += blockDim.x) c += idx[p] == e;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o, kWave);
-  if ((threadIdx.x & (kWave - 1)) == 0) part[threadIdx.x / kWave] = c;
+constexpr int kSortThreads = 256;
+constexpr int kSortChunk = 4096;   // pairs per block
+constexpr int kSortMaxE = 1024;
+
+__global__ void __launch_bounds__(kSortThreads) k_hist(const int32_t* __restrict__ idx, int n, int E,
+                                                       int32_t* __restrict__ counts) {
+  __shared__ int h[kSortMaxE];
+  for (int e = threadIdx.x; e < E; e += kSortThreads) h[e] = 0;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int s = 0;
-    for (int w = 0; w < (int)(blockDim.x / kWave); ++w) s += part[w];
-    counts[e] = s;
+  const int p0 = blockIdx.x * kSortChunk;
+  const int p1 = min(n, p0 + kSortChunk);
+  for (int p = p0 + threadIdx.x; p < p1; p += kSortThreads) {
+    const int e = idx[p];
+    if (e >= 0 && e < E) atomicAdd(&h[e], 1);
   }
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kSortThreads)
+    if (h[e]) atomicAdd(&counts[e], h[e]);
 }
 
-// Exclusive scans of counts and of tiles per expert; one block of 1024.
-__global__ void __launch_bounds__(1024) k_scan(const int32_t* __restrict__ counts, int E, int bm,
+// one block of 1024 threads; E <= 1024
+__global__ void __launch_bounds__(1024) k_scan(int32_t* __restrict__ counts, int E, int bm,
                                                int32_t* __restrict__ offsets,
+                                               int32_t* __restrict__ cursor,
                                                int32_t* __restrict__ tile_off,
-                                               int32_t* __restrict__ n_tiles) {
+                                               int32_t* __restrict__ n_tiles,
+                                               int4* __restrict__ tiles) {
   __shared__ int sc[1024];
   __shared__ int st[1024];
   const int e = threadIdx.x;
@@ -50,60 +62,54 @@ __global__ void __launch_bounds__(1024) k_scan(const int32_t* __restrict__ count
     __syncthreads();
   }
   if (e < E) {
+    const int off = sc[e] - c;
+    const int toff = st[e] - (c + bm - 1) / bm;
+    offsets[e] = off;
     offsets[e + 1] = sc[e];
+    cursor[e] = off;
+    tile_off[e] = toff;
     tile_off[e + 1] = st[e];
+    counts[e] = 0;                       // clean for the next call
+    for (int j = 0; j * bm < c; ++j) tiles[toff + j] = make_int4(e, off + j * bm, min(bm, c - j * bm), 0);
   }
-  if (e == 0) {
-    offsets[0] = 0;
-    tile_off[0] = 0;
-    n_tiles[0] = st[E - 1];
-  }
+  if (e == 0) n_tiles[0] = st[E - 1];
 }
 
-// Stable scatter: block e walks the pairs in order and appends those routed to
-// e; then writes e's tiles {e, first sorted row, rows, 0}.
-__global__ void __launch_bounds__(256) k_scatter(const int32_t* __restrict__ idx, int n, int bm,
-                                                 const int32_t* __restrict__ offsets,
-                                                 const int32_t* __restrict__ tile_off,
-                                                 int32_t* __restrict__ sorted,
-                                                 int4* __restrict__ tiles) {
-  __shared__ int wave_tot[256 / kWave];
-  const int e = blockIdx.x;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wid = threadIdx.x / kWave;
-  const int nw = blockDim.x / kWave;
-  const int base0 = offsets[e];
-  int run = 0;
-  for (int p0 = 0; p0 < n; p0 += blockDim.x) {
-    const int p = p0 + threadIdx.x;
-    const bool hit = p < n && idx[p] == e;
-    const unsigned long long m = __ballot(hit);
-    const int pre = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_tot[wid] = __popcll(m);
-    __syncthreads();
-    int before = 0, tot = 0;
-    for (int w = 0; w < nw; ++w) {
-      before += w < wid ? wave_tot[w] : 0;
-      tot += wave_tot[w];
-    }
-    if (hit) sorted[base0 + run + before + pre] = p;
-    run += tot;
-    __syncthreads();
+__global__ void __launch_bounds__(kSortThreads) k_scatter(const int32_t* __restrict__ idx, int n, int E,
+                                                          int32_t* __restrict__ cursor,
+                                                          int32_t* __restrict__ sorted) {
+  __shared__ int h[kSortMaxE];
+  __shared__ int base[kSortMaxE];
+  for (int e = threadIdx.x; e < E; e += kSortThreads) h[e] = 0;
+  __syncthreads();
+  const int p0 = blockIdx.x * kSortChunk;
+  const int p1 = min(n, p0 + kSortChunk);
+  constexpr int kPer = kSortChunk / kSortThreads;
+  int rank[kPer];
+  int ev[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int p = p0 + threadIdx.x + j * kSortThreads;
+    ev[j] = p < p1 ? idx[p] : -1;
+    rank[j] = (ev[j] >= 0 && ev[j] < E) ? atomicAdd(&h[ev[j]], 1) : -1;
   }
-  const int cnt = offsets[e + 1] - base0;
-  const int t0 = tile_off[e];
-  for (int j = threadIdx.x; j * bm < cnt; j += blockDim.x) {
-    const int r0 = j * bm;
-    tiles[t0 + j] = make_int4(e, base0 + r0, min(bm, cnt - r0), 0);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kSortThreads)
+    if (h[e]) base[e] = atomicAdd(&cursor[e], h[e]);
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (rank[j] >= 0) sorted[base[ev[j]] + rank[j]] = p0 + threadIdx.x + j * kSortThreads;
   }
 }
 
 int launch_sort_pairs(const int32_t* idx, int n, int E, const GatherWs& ws, hipStream_t s) {
-  hipLaunchKernelGGL(k_count, dim3(E), dim3(256), 0, s, idx, n, ws.counts);
+  const int blocks = (n + kSortChunk - 1) / kSortChunk;
+  hipLaunchKernelGGL(k_hist, dim3(blocks), dim3(kSortThreads), 0, s, idx, n, E, ws.counts);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, ws.counts, E, kGemmBM, ws.offsets,
-                     ws.tile_off, ws.n_tiles);
-  hipLaunchKernelGGL(k_scatter, dim3(E), dim3(256), 0, s, idx, n, kGemmBM, ws.offsets, ws.tile_off,
-                     ws.sorted, ws.tiles);
+                     ws.cursor, ws.tile_off, ws.n_tiles, ws.tiles);
+  hipLaunchKernelGGL(k_scatter, dim3(blocks), dim3(kSortThreads), 0, s, idx, n, E, ws.cursor,
+                     ws.sorted);
   return 0;
 }
 

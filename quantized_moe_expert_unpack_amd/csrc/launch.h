@@ -37,18 +37,19 @@ struct DecPlan {
 // Workspace carve-up for the gather (prefill) path; every pointer is
 // 256-byte aligned inside the caller's workspace.
 struct GatherWs {
-  int32_t* counts;     // [E]
+  int32_t* counts;     // [E]    zero between calls
   int32_t* offsets;    // [E+1]  sorted row offset per expert
+  int32_t* cursor;     // [E]    scatter cursors
   int32_t* tile_off;   // [E+1]  first tile per expert
   int32_t* n_tiles;    // [1]
   int4* tiles;         // [max_tiles] {expert, row0, rows, 0}
   int32_t* sorted;     // [n] pair id at each sorted position
   uint16_t* h;         // [n][I] bf16 (moe_gather_qmm only)
-  float* ypair;        // [n][H] fp32 (moe_gather_qmm only)
+  uint16_t* ypair;     // [n][H] bf16 (moe_gather_qmm only)
   int max_tiles;
 };
 
-constexpr int kGemmBM = 128;  // rows per gather-GEMM tile
+constexpr int kGemmBM = 256;  // rows per gather-GEMM tile
 
 int launch_qdequant(const QT& W, uint8_t* codes, float* deq, hipStream_t s);
 int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s);
@@ -74,7 +75,7 @@ int launch_gemm_plain(const QT& W, const uint16_t* x, float* out, const GatherWs
                       hipStream_t s);
 // rows whose expert index is outside [0, E) become NaN (gather_qmm output)
 int launch_mark_invalid_rows(const int32_t* idx, int n, int E, int N, float* out, hipStream_t s);
-int launch_combine(const float* ypair, const int32_t* idx, int M, int K, int H, int E, float* y,
+int launch_combine(const uint16_t* ypair, const int32_t* idx, int M, int K, int H, int E, float* y,
                    hipStream_t s);
 
 }  // namespace moeq

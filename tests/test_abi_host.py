@@ -144,7 +144,7 @@ def test_workspace_sizes():
     ws = moeq.lib().moe_workspace_size
     assert ws(ctypes.byref(L), 1, 2, moeq.PATH_DECODE) >= 4 * (2 * 128 + 1)
     g = ws(ctypes.byref(L), 1000, 2, moeq.PATH_GATHER)
-    assert g >= 2000 * 128 * 2 + 2000 * 256 * 4
+    assert g >= 2000 * 128 * 2 + 2000 * 256 * 2     # bf16 h and bf16 per-pair outputs
     assert ws(ctypes.byref(L), 1, 9, moeq.PATH_DECODE) == 0             # K > E
     assert ws(None, 1, 2, moeq.PATH_DECODE) == 0
 
