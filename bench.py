@@ -76,6 +76,48 @@ def expert_launch_bytes(cfg, touched: float) -> float:
 
 
 # --------------------------------------------------------------------------
+# HBM traffic measured with rocprofv3 counters
+# --------------------------------------------------------------------------
+
+KERNEL_SOURCES = {
+    "k_moe_decode": ["k_decode.hip", "common.h", "topk.h", "launch.h"],
+    "k_gqmm": ["k_gemm.hip", "common.h", "launch.h"],
+}
+
+
+def kernel_source_hash(kernel):
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "quantized_moe_expert_unpack_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(args, kernel):
+    """HBM bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel
+    calibration) from profiles/traffic_<kernel>_<workload>.md, or null when
+    those counters were taken on a different version of the kernel's sources."""
+    if args.traffic is not None:
+        return args.traffic
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{args.config}.md")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and line.startswith("- "):
+                k, v = line[2:].split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_hash") != kernel_source_hash(kernel):
+        return None
+    try:
+        return int(float(vals["hbm_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# --------------------------------------------------------------------------
 # CPU oracle baseline
 # --------------------------------------------------------------------------
 
@@ -183,14 +225,25 @@ def run_decode(args, cfg):
     idx = torch.zeros((n_layers, m, K), dtype=torch.int32, device=dev)
     w = torch.zeros((n_layers, m, K), dtype=torch.float32, device=dev)
     y = torch.zeros((n_layers, m, H), dtype=torch.float32, device=dev)
+    # one launch per layer (router + top-K + experts) when the library can
+    # route inside the launch (8-bit router, M <= 4); else route, then experts
+    one_launch = cfg.router_bits == 8 and m <= 4
+    ws_fwd = moeq.workspace(layers[0], m, K, moeq.PATH_FORWARD, dev)
     ws_route = torch.zeros(8 * m * cfg.experts + 4096, dtype=torch.uint8, device=dev)
     ws_dec = moeq.workspace(layers[0], m, K, moeq.PATH_DECODE, dev)
 
-    def step(t):
-        for l, L in enumerate(layers):
+    def layer_call(l, t):
+        L = layers[l]
+        if one_launch:
+            moeq.moe_forward(L, x[l, t], K, cfg.renorm, ws=ws_fwd, y=y[l], idx=idx[l], w=w[l])
+        else:
             moeq.moe_route(L.router, x[l, t], cfg.experts, K, cfg.renorm, ws=ws_route,
                            idx=idx[l], w=w[l])
             moeq.moe_expert_forward(L, x[l, t], idx[l], w[l], ws=ws_dec, y=y[l])
+
+    def step(t):
+        for l in range(n_layers):
+            layer_call(l, t)
 
     # eager warm-up (also checks the path runs), then capture one graph per slot
     for t in range(min(2, slots)):
@@ -230,8 +283,10 @@ def run_decode(args, cfg):
     bytes_step = n_layers * layer_bytes(cfg, touched)
     gbps = bytes_step / (ms * 1e-3) / 1e9
 
-    # dominant launch: moe_expert_forward, timed live with HIP events recorded
-    # on the stream it is launched on (eager launches, same buffers)
+    # dominant launch, timed live with HIP events recorded on the stream it is
+    # launched on (eager launches, same buffers): the one-launch layer
+    # (moe_forward), or the expert launch (moe_expert_forward) of the
+    # two-launch form
     s_ = torch.cuda.current_stream()
     reps = max(1, args.launch_reps)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -240,19 +295,26 @@ def run_decode(args, cfg):
     for r in range(reps):
         t = r % slots
         for l, L in enumerate(layers):
-            moeq.moe_route(L.router, x[l, t], cfg.experts, K, cfg.renorm, ws=ws_route,
-                           idx=idx[l], w=w[l])
-            evs[k][0].record(s_)
-            moeq.moe_expert_forward(L, x[l, t], idx[l], w[l], ws=ws_dec, y=y[l])
-            evs[k][1].record(s_)
+            if one_launch:
+                evs[k][0].record(s_)
+                moeq.moe_forward(L, x[l, t], K, cfg.renorm, ws=ws_fwd, y=y[l], idx=idx[l], w=w[l])
+                evs[k][1].record(s_)
+            else:
+                moeq.moe_route(L.router, x[l, t], cfg.experts, K, cfg.renorm, ws=ws_route,
+                               idx=idx[l], w=w[l])
+                evs[k][0].record(s_)
+                moeq.moe_expert_forward(L, x[l, t], idx[l], w[l], ws=ws_dec, y=y[l])
+                evs[k][1].record(s_)
             k += 1
     torch.cuda.synchronize()
     launch_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
-    lbytes = expert_launch_bytes(cfg, touched)
+    lbytes = (layer_bytes(cfg, touched) + m * K * 8) if one_launch else expert_launch_bytes(cfg, touched)
     achieved = lbytes / (launch_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": args.traffic, "kernel": "moe_expert_forward",
+                "traffic": traffic_for(args, "k_moe_decode"),
+                "kernel": "k_moe_decode (moe_forward: router + top-K + experts)" if one_launch
+                          else "k_moe_decode (moe_expert_forward)",
                 "launch_us": round(launch_us, 2), "bytes_per_launch": int(lbytes)}
 
     out = {
@@ -264,7 +326,8 @@ def run_decode(args, cfg):
                    "hidden": H, "experts": cfg.experts, "top_k": K, "inter": cfg.inter,
                    "expert_bits": cfg.expert_bits, "router_bits": cfg.router_bits,
                    "shared_expert": cfg.has_shared, "group_size": cfg.group_size,
-                   "token_slots": slots, "graph": True},
+                   "token_slots": slots, "graph": True,
+                   "launches_per_layer": 1 if one_launch else 2},
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "bytes_per_step": int(bytes_step), "touched_experts_per_layer": round(touched, 2),
         "roofline": roofline,
@@ -319,7 +382,7 @@ def run_prefill(args, cfg):
                    "expert_bits": cfg.expert_bits, "logits": "zipf(1.1)+gumbel"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": args.traffic, "kernel": "moe_route + moe_gather_qmm",
+                     "traffic": traffic_for(args, "k_gqmm"), "kernel": "moe_route + moe_gather_qmm",
                      "flops_per_launch": flops},
     }
     out["_host"] = host

@@ -106,6 +106,7 @@ typedef struct moeq_moe {
 #define MOEQ_PATH_DECODE 1  /* moe_expert_forward                          */
 #define MOEQ_PATH_GATHER 2  /* moe_gather_qmm                              */
 #define MOEQ_PATH_GQMM 3    /* gather_qmm (single projection; K is unused) */
+#define MOEQ_PATH_FORWARD 4 /* moe_forward                                 */
 
 /* Human-readable text for a status code (static storage). */
 const char *moeq_status_string(int status);
@@ -169,6 +170,24 @@ int moe_route(const moeq_qtensor *gate, const float *x_or_logits, int32_t M, int
 int moe_expert_forward(const moeq_moe *L, const float *x, const int32_t *topk_idx,
                        const float *topk_w, int32_t M, int32_t K, const float *residual,
                        float *y, void *ws, size_t ws_bytes, moeq_stream_t stream);
+
+/* moe_forward: the whole step for fp32 activations (decode): moe_route on
+ * L->router (router mode) followed by moe_expert_forward, with the same
+ * results as that pair of calls.
+ *   x : fp32 [M][H];  renorm as in moe_route;  residual : nullable fp32 [M][H]
+ *   y : fp32 [M][H] out;  topk_idx int32 [M][K] and topk_w fp32 [M][K] out
+ *   ws : workspace of moe_workspace_size(L, M, K, MOEQ_PATH_FORWARD)
+ * With an 8-bit router and M <= 4 the whole step is ONE launch: the router
+ * rows, the top-K selection and the experts run in one grid, the expert units
+ * starting their weight loads as soon as the selection is published, so the
+ * routing round trip through the host or a second launch disappears; other
+ * cases run the two launches.
+ * Defines: the per-layer pipeline of the flash-moe skill page (router
+ * projection, softmax + topK, expert forward, combine) and the markbaseengine
+ * "Forward Pass Sequence", kept on the device. */
+int moe_forward(const moeq_moe *L, const float *x, int32_t M, int32_t K, int32_t renorm,
+                const float *residual, float *y, int32_t *topk_idx, float *topk_w, void *ws,
+                size_t ws_bytes, moeq_stream_t stream);
 
 /* moe_gather_qmm: the expert part for many bf16 tokens (prefill).  Pairs
  * (token, slot) are sorted by expert on the device; per expert the gathered

@@ -131,6 +131,14 @@ size_t gather_ws(char* base, int E, int n, int I, int H, bool full, moeq::Gather
   return off;
 }
 
+// moe_forward: one launch (routing in the launch) or moe_route's workspace
+// followed by moe_expert_forward's; room for either
+size_t forward_ws_bytes(const moeq::DecodeLayer& dl, int E, int M, int K) {
+  const size_t one = moeq::decode_ws_bytes(dl, M, K, true);
+  const size_t two = align_up(moeq::route_ws_bytes(M, E)) + moeq::decode_ws_bytes(dl, M, K);
+  return one > two ? one : two;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,6 +177,10 @@ size_t moe_workspace_size(const moeq_moe* L, int32_t M, int32_t K, int32_t path)
   if (check_experts(L, &d)) return 0;
   if (K < 1 || K > kMaxK || K > d.E) return 0;
   if (path == MOEQ_PATH_DECODE) return moeq::decode_ws_bytes(to_decode_layer(L, d), M, K) + kAlign;
+  if (path == MOEQ_PATH_FORWARD) {
+    if (!L->router.q || L->router.rows != d.E) return 0;
+    return forward_ws_bytes(to_decode_layer(L, d), d.E, M, K) + kAlign;
+  }
   if (path == MOEQ_PATH_GATHER) {
     if (!fits_i32((int64_t)M * K)) return 0;
     return gather_ws(nullptr, d.E, M * K, d.I, d.H, true, nullptr) + kAlign;
@@ -247,6 +259,41 @@ int moe_expert_forward(const moeq_moe* L, const float* x, const int32_t* topk_id
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOEQ_ERR_ALIGN;
   st = moeq::launch_decode_forward(dl, x, topk_idx, topk_w, M, K, residual, y, ws,
                                    (hipStream_t)stream);
+  if (st) return MOEQ_ERR_UNSUPPORTED;
+  return launch_status();
+}
+
+int moe_forward(const moeq_moe* L, const float* x, int32_t M, int32_t K, int32_t renorm,
+                const float* residual, float* y, int32_t* topk_idx, float* topk_w, void* ws,
+                size_t ws_bytes, moeq_stream_t stream) {
+  LayerDims d;
+  int st = check_experts(L, &d);
+  if (st) return st;
+  if ((st = check_qt(&L->router, 1, d.E, d.H))) return st;
+  if (M < 0 || K < 1 || K > kMaxK || K > d.E) return MOEQ_ERR_SHAPE;
+  if (M == 0) return MOEQ_OK;
+  if (!x || !y || !topk_idx || !topk_w) return MOEQ_ERR_NULL_PTR;
+  if (!fits_i32((int64_t)M * d.H) || !fits_i32((int64_t)M * d.E) ||
+      !fits_i32((int64_t)M * K * d.I + (int64_t)M * d.Is + M))
+    return MOEQ_ERR_OVERFLOW;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+      (residual && !aligned16(residual)))
+    return MOEQ_ERR_ALIGN;
+  const moeq::DecodeLayer dl = to_decode_layer(L, d);
+  if (!moeq::decode_supported(dl, K)) return MOEQ_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < forward_ws_bytes(dl, d.E, M, K)) return MOEQ_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOEQ_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const QT router = to_qt(L->router);
+  if (moeq::fused_supported(dl, router, M, K)) {
+    const moeq::RouteIn R{router, renorm, topk_idx, topk_w};
+    st = moeq::launch_moe_forward(dl, R, x, M, K, residual, y, ws, s);
+  } else {
+    char* wsr = reinterpret_cast<char*>(ws);
+    char* wsd = wsr + align_up(moeq::route_ws_bytes(M, d.E));
+    moeq::launch_route(&router, x, M, d.E, K, renorm, topk_idx, topk_w, nullptr, wsr, s);
+    st = moeq::launch_decode_forward(dl, x, topk_idx, topk_w, M, K, residual, y, wsd, s);
+  }
   if (st) return MOEQ_ERR_UNSUPPORTED;
   return launch_status();
 }

@@ -1,47 +1,66 @@
-// Decode expert forward (fp32 activations, small M) as ONE launch.
+// Decode step (fp32 activations, small M) as ONE launch: router, top-K and
+// the selected experts, or the experts alone for given indices.
 //
-// The step per selected expert (markbaseengine MOE_ROUTER_WORKS_BREAKTHROUGH,
-// "Forward Pass Sequence": expertFusedGateUp, expertDown, accumulateResults;
-// flash-moe-inference kernels swiglu and moe_combine_residual):
+// The step (markbaseengine MOE_ROUTER_WORKS_BREAKTHROUGH, "Forward Pass
+// Sequence": router projection, softmax, top-K, expertFusedGateUp,
+// expertDown, accumulateResults; flash-moe-inference kernels swiglu and
+// moe_combine_residual):
 //   h_k = silu(Gate_e x) * (Up_e x),   y = sum_k w_k Down_e h_k
 //         (+ sigmoid(sg . x) * FFN_shared(x)) (+ residual).
 //
-// Work units by block index (G units first, then D units):
+// Work units by block index, every unit 8 waves:
+//   R units  (routing in the launch only; 8 router rows each): fp64 logits of
+//            all M tokens, published one by one; the last R unit collects
+//            them, selects the top-K of every token and publishes each
+//            (expert + 1, weight) pair as one 64-bit word (0 means "not yet").
 //   G units  (pair p = token*S + slot, 16 intermediate rows): gate and up rows
 //            of the pair's expert against x, SwiGLU, h[p][i]; the first G unit
 //            of a shared-expert pair also computes the shared_expert_gate
-//            logit.  Each G unit counts its arrival for token t; the one that
-//            completes the count raises ready[t].
+//            logit.  With routing in the launch a G unit stages x and its chunk
+//            sums while it waits for its expert index.  Each G unit counts its
+//            arrival for token t; the one that completes the count raises
+//            ready[t].
 //   D units  (token t, 8 output rows): issue the weight loads of their rows
-//            for all S slots at once, wait for ready[t], stage h of all S
-//            pairs in LDS and produce whole output rows,
+//            for all S slots (the shared expert's before the routed experts'
+//            indices are known), wait for ready[t], stage h of all S pairs in
+//            LDS and produce whole output rows,
 //            y = sum_k w_k Down_k h_k (+ sigmoid(sg) Down_sh h_sh) (+ residual),
 //            with one fixed reduction order, so results are bitwise
 //            reproducible and no data crosses blocks twice.  The last D unit of
-//            a token to arrive lowers ready[t] for the next launch.
-// Workgroups are dispatched in index order within each XCD, so when a D unit
-// runs, every G unit of its XCD has been dispatched, and G units never wait:
-// each wait ends.  Waits are bounded anyway: one that exceeds its spin limit
-// records an error word in the workspace and gives up instead of hanging.
-// Arrivals are counted with two-level counters (see arrive()).
+//            a token to arrive lowers ready[t] and clears the token's published
+//            indices for the next launch.
+// Workgroups are dispatched in index order within each XCD, so when a unit
+// runs, every unit of a lower index on its XCD has been dispatched; a unit
+// only ever waits for units of lower index, so each wait ends.  Waits are
+// bounded anyway: one that exceeds its spin limit records an error word in the
+// workspace and gives up instead of hanging.  Arrivals are counted with
+// two-level counters (see arrive()).
 //
 // Latency is what bounds a decode layer, so every unit issues all of its HBM
 // loads (weight rows, and the rows' bf16 scales and biases, staged through
-// LDS) before it touches any result, and units are sized so that a whole
-// layer's blocks are resident at once.  Rows are streamed in 16-byte chunks
-// (128/BITS codes, never straddling a 64-column group); a chunk contributes
-// s*(sum_j q_j a_j) + b*(sum_j a_j) with the activation's chunk sums
-// precomputed once per block in LDS.
+// LDS) as soon as their addresses are known and before it touches any result,
+// and units are sized so that a whole layer's blocks are resident at once.
+// Rows are streamed in 16-byte chunks (128/BITS codes, never straddling a
+// 64-column group); a chunk contributes s*(sum_j q_j a_j) + b*(sum_j a_j)
+// with the activation's chunk sums precomputed once per block in LDS.
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 namespace moeq {
 
-constexpr int kGRows = 16;    // intermediate rows per G unit (four per wave)
-constexpr int kDRows = 8;     // output rows per D unit (two per wave)
+constexpr int kThreads = 512;              // every unit is 8 waves
+constexpr int kWaves = kThreads / kWave;
+constexpr int kGRows = 16;                 // intermediate rows per G unit (two per wave)
+constexpr int kDRows = kWaves;             // output rows per D unit (one per wave)
+constexpr int kRRows = kWaves;             // router rows per R unit (one per wave)
 constexpr int kSpinLimit = 1 << 26;
 constexpr int kLine = kLineInts;
-constexpr int kCtrLines = 2 * (1 + kFan) + 1;   // per token: G counter, D counter, ready
+constexpr int kRep = 64;      // copies of every flag that many units poll
+// per token: G arrival counter lines, D arrival counter lines
+constexpr int kCtrLines = 2 * (1 + kFan);
+constexpr int kHCopies = 8;   // copies of h (D unit d reads copy d % kHCopies): spreads the
+                              // reads of all D units of a token over more memory channels
 
 // ---- coherent (agent-scope) loads/stores for data crossing blocks ----------
 __device__ __forceinline__ void st_coh(float* p, float v) {
@@ -59,13 +78,89 @@ __device__ __forceinline__ uint64_t ld_coh64(const uint64_t* p) {
 // the counter update that announces them.
 __device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
 
+
+__device__ __forceinline__ int ld_coh_i(const int* p) {
+  return __hip_atomic_load(const_cast<int*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_i(int* p, int v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Polling.  Every poll is a coherent load that the memory side serves; many
+// units polling one line at a high rate would take a share of that line's
+// memory channel away from the weight stream.  So every flag that many units
+// wait on exists in kRep copies, one copy per block of flags, the blocks 4 KB
+// + 256 B apart so that the copies fall on different channels (a unit polls
+// copy unit % kRep), and polls are spaced by s_sleep.
+
+__device__ __forceinline__ uint64_t ld_coh_u64(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coh_u64(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// lanes < n of one wave wait until p[lane] != 0; returns the lane's value
+// (0, and an error bit, if the spin limit hit)
+__device__ __forceinline__ uint64_t wave_wait_nonzero(const uint64_t* p, int n, int lane, int* err) {
+  uint64_t v = 0;
+  for (int i = 0; i < kSpinLimit; ++i) {
+    if (lane < n) v = ld_coh_u64(p + lane);
+    if (__all(lane >= n || v != 0)) return v;
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if (lane == 0) atomicOr(err, 2);
+  return v;
+}
+
 // wait (one thread) until *flag != 0; returns false if the spin limit hit
 __device__ __forceinline__ bool wait_flag(int* flag) {
   for (int i = 0; i < kSpinLimit; ++i) {
     if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) return true;
-    __builtin_amdgcn_s_sleep(4);
+    __builtin_amdgcn_s_sleep(2);
   }
   return false;
+}
+
+// the token's route line in copy `rep`: word k = (expert + 1) << 32 | the
+// routing weight's fp32 bits, 0 while not routed (one 64-bit store publishes
+// both halves together)
+__device__ __forceinline__ uint64_t* route_line(const DecPlan& P, int rep, int t) {
+  return reinterpret_cast<uint64_t*>(P.idx_c + (size_t)rep * P.rstride + (size_t)t * kLine);
+}
+__device__ __forceinline__ int* ready_line(const DecPlan& P, int rep, int t) {
+  return P.ready + (size_t)rep * P.rstride + (size_t)t * kLine;
+}
+
+// ---- fp64 wave sum on VALU exchanges (DPP and gfx950 permlane swaps) -------
+template <int M>
+__device__ __forceinline__ double xchg_d(double v) {
+  const uint64_t u = (uint64_t)__double_as_longlong(v);
+  uint32_t lo = (uint32_t)u, hi = (uint32_t)(u >> 32);
+  if constexpr (M >= 16) {
+    const auto rl = M == 32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                            : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto rh = M == 32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                            : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    // r[0], r[1]: this lane's and its partner's value, in lane order
+    const double a = __longlong_as_double((long long)(((uint64_t)rh[0] << 32) | rl[0]));
+    const double b = __longlong_as_double((long long)(((uint64_t)rh[1] << 32) | rl[1]));
+    return a + b;
+  } else {
+    constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : M == 4 ? 0x141 : 0x140;
+    lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, ctrl, 0xF, 0xF, false);
+    hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, ctrl, 0xF, 0xF, false);
+    return v + __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  }
+}
+// every lane gets the sum of the wave's 64 values (mirror steps: see treduce)
+__device__ __forceinline__ double wave_sum_d(double v) {
+  v = xchg_d<32>(v);
+  v = xchg_d<16>(v);
+  v = xchg_d<8>(v);
+  v = xchg_d<4>(v);
+  v = xchg_d<2>(v);
+  return xchg_d<1>(v);
 }
 
 // Activations live in LDS chunk-interleaved: float4 number f of chunk c sits at
@@ -175,352 +270,535 @@ __device__ __forceinline__ int tindex(int lane) {
   return r;
 }
 
-// LDS of a block: [activation][its chunk sums (n/16 floats max)][the unit's
-// bf16 scales and biases]
-template <int BITS, int CPL, int DCH>
-__global__ void __launch_bounds__(256) k_dec_fused(DecodeLayer L, DecPlan P,
-                                                   const float* __restrict__ x,
-                                                   const int32_t* __restrict__ idx,
-                                                   const float* __restrict__ wts,
-                                                   const float* __restrict__ residual,
-                                                   float* __restrict__ y) {
+
+// ------------------------------------------------------------------ R unit
+// top-K of token m from keys/vals in LDS (E <= 1024), all threads of the
+// block: selection by rank as in topk.h, candidates ranked by four threads
+// each; publishes the weights into every route-line copy, drains, then the
+// indices, and writes the caller's outputs.
+__device__ __forceinline__ void route_select(const uint64_t* keys, const double* vals, int E,
+                                             int K, int renorm, const DecPlan& P, const RouteIn& R,
+                                             int m) {
+  __shared__ uint64_t cand[kWaves * kMaxTopK];
+  __shared__ int sel[kMaxTopK];
+  __shared__ double ex[kMaxTopK];
+  __shared__ double red[kWaves];
+  __shared__ double s_tot;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int nc = kWaves * K;             // candidate slots, K per wave
+  if (tid < nc) cand[tid] = 0ull;        // 0 is below every key
+  __syncthreads();
+  // 1) per wave: the keys of its part whose rank inside the part is < K, at
+  //    their rank (keys are unique, so the positions are too)
+  const int q = (E + kWaves - 1) / kWaves;
+  const int lo = min(E, wid * q), hi = min(E, lo + q);
+  for (int a = lo + lane; a < hi; a += kWave) {
+    const uint64_t ka = keys[a];
+    int rank = 0;
+#pragma unroll 4
+    for (int j = lo; j < hi; ++j) rank += keys[j] > ka;
+    if (rank < K) cand[wid * K + rank] = ka;
+  }
+  __syncthreads();
+  // 2) rank of every candidate among the candidates: four threads (one quad)
+  //    per candidate, each over a quarter, summed across the quad
+  {
+    const int c = tid >> 2, part = tid & 3;
+    const uint64_t kc = c < nc ? cand[c] : 0ull;
+    int rank = 0;
+#pragma unroll 4
+    for (int j = part; j < nc; j += 4) rank += cand[j] > kc;
+    rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, false);
+    rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, false);
+    if (part == 0 && c < nc && kc != 0ull && rank < K) sel[rank] = 1023 - (int)(kc & 0x3FFull);
+  }
+  __syncthreads();
+  // 3) weights in fp64: p[idx] / sum p[idx] (renorm, summed in slot order) or
+  //    p[idx] / sum over all E (fixed order), with p relative to the maximum
+  const double mx = vals[sel[0]];
+  if (tid < K) ex[tid] = exp(vals[sel[tid]] - mx);
+  if (!renorm) {
+    double part = 0.0;
+    for (int e = tid; e < E; e += kThreads) part += exp(vals[e] - mx);
+    part = wave_sum_d(part);
+    if (lane == 0) red[wid] = part;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    double tot = 0.0;
+    if (renorm)
+      for (int k = 0; k < K; ++k) tot += ex[k];
+    else
+      for (int w = 0; w < kWaves; ++w) tot += red[w];
+    s_tot = tot;
+  }
+  __syncthreads();
+  for (int i = tid; i < kRep * K; i += kThreads) {
+    const int rep = i / K, k = i - rep * K;
+    const float w = (float)(ex[k] / s_tot);
+    if (rep == 0) {
+      R.idx_out[(size_t)m * K + k] = sel[k];
+      R.w_out[(size_t)m * K + k] = w;
+    }
+    st_coh_u64(route_line(P, rep, m) + k, ((uint64_t)(sel[k] + 1) << 32) | __float_as_uint(w));
+  }
+}
+
+// Router rows (8-bit) against x for all M tokens in fp64: the fp32
+// dequantized weight widened exactly, fp64 products and sums, as the oracle
+// defines the logits.  The R unit completing the arrivals selects.
+__device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P, const RouteIn R,
+                                           const float* __restrict__ x, int u) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  __shared__ int s_last;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int E = L.E, H = L.H, M = P.M, K = P.K;
+  const int e = u * kRRows + wid;
+  const int nch = H / 16;                 // 16 codes per chunk at 8 bits
+  const int gpr = H / kGroup;
+  const bool row_ok = e < E;
+  // Loads use clamped, always valid addresses and no branches, so they all
+  // issue back to back; lanes past the row's end are never used.
+  const int er = min(e, E - 1);
+  uint4 rv[4];
+  uint32_t rsb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = min(lane + kWave * j, nch - 1);
+    rv[j] = reinterpret_cast<const uint4*>(R.W.q + (size_t)er * (H / 4))[c];
+    rsb[j] = (uint32_t)R.W.scales[(size_t)er * gpr + c / 4] |
+             ((uint32_t)R.W.biases[(size_t)er * gpr + c / 4] << 16);
+  }
+  // x of every token in LDS, chunk-interleaved (float4 f of chunk c at f*nch+c)
+  float4* xl = reinterpret_cast<float4*>(smem);
+  for (int i = tid; i < M * (H / 4); i += kThreads) {
+    const int m = i / (H / 4), ii = i - m * (H / 4);
+    xl[m * (H / 4) + (ii % 4) * nch + ii / 4] = reinterpret_cast<const float4*>(x)[i];
+  }
+  float rs[4], rb[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    rs[j] = bf16_to_f32(rsb[j] & 0xFFFFu);
+    rb[j] = bf16_to_f32(rsb[j] >> 16);
+  }
+  __syncthreads();
+  for (int m = 0; m < M; ++m) {
+    // the lane's chunks as independent fp64 chains, elements in order
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll 1
+    for (int f = 0; f < 4; ++f) {     // rolled: keeps the fp64 operands out of registers
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = lane + kWave * j;
+        if (row_ok && c < nch) {
+          const float4 xv = xl[m * (H / 4) + f * nch + c];
+          acc[j] = fma((double)fmaf(rs[j], (float)chunk_code<8>(rv[j], 4 * f + 0), rb[j]), (double)xv.x, acc[j]);
+          acc[j] = fma((double)fmaf(rs[j], (float)chunk_code<8>(rv[j], 4 * f + 1), rb[j]), (double)xv.y, acc[j]);
+          acc[j] = fma((double)fmaf(rs[j], (float)chunk_code<8>(rv[j], 4 * f + 2), rb[j]), (double)xv.z, acc[j]);
+          acc[j] = fma((double)fmaf(rs[j], (float)chunk_code<8>(rv[j], 4 * f + 3), rb[j]), (double)xv.w, acc[j]);
+        }
+      }
+    }
+    const double tot = wave_sum_d((acc[0] + acc[1]) + (acc[2] + acc[3]));
+    // published as the complement of its bits: zero means "not written yet"
+    // (the complement of a finite double is never zero)
+    if (lane == 0 && row_ok)
+      st_coh_u64(P.logits + (size_t)m * E + e, ~(uint64_t)__double_as_longlong(tot));
+  }
+  // the last R unit selects: it polls every logit (no counter round trips),
+  // clears them for the next launch, and runs the top-K of each token
+  if (u != P.r_units - 1) return;
+  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
+  double* vals = reinterpret_cast<double*>(keys + E);
+  __syncthreads();                       // x in LDS is no longer read
+  for (int m = 0; m < M; ++m) {
+    for (int ee = tid; ee < E; ee += kThreads) {
+      uint64_t* src = P.logits + (size_t)m * E + ee;
+      uint64_t v = 0;
+      for (int i = 0; i < kSpinLimit && v == 0; ++i) {
+        v = ld_coh_u64(src);
+        if (v == 0) __builtin_amdgcn_s_sleep(1);
+      }
+      if (v == 0) atomicOr(P.ctr, 4);
+      st_coh_u64(src, 0);
+      const double lg = __longlong_as_double((long long)~v);
+      vals[ee] = lg;
+      keys[ee] = route_key(lg, ee);
+    }
+    __syncthreads();
+    route_select(keys, vals, E, K, R.renorm, P, R, m);
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------------ G unit
+// LDS: [x, chunk-interleaved][its chunk sums (<= H/16 floats)][bf16 scales and
+// biases of the unit's gate and up rows]
+template <int BITS, int CPL, bool FUSED>
+__device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan P,
+                                             const float* __restrict__ x,
+                                             const int32_t* __restrict__ idx, int u) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ int s_e;
   constexpr int kCpc = 128 / BITS;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  // counter lines: [0] error word, then per token kCtrLines lines: the G
-  // arrival counter, the D arrival counter and the ready flag
-  int* err = P.ctr;
-  auto tok_lines = [&](int tt) { return P.ctr + (size_t)kLine * (1 + (size_t)tt * kCtrLines); };
-  const int u = blockIdx.x;
   const int S = P.S, K = P.K, H = L.H;
+  const int upt = K * P.ng_routed + (L.has_shared ? P.ng_shared : 0);
+  const int t = u / upt;
+  const int r = u - t * upt;
+  const bool shared = r >= K * P.ng_routed;
+  const int k = shared ? K : r / P.ng_routed;
+  const int g = shared ? r - K * P.ng_routed : r - k * P.ng_routed;
+  const int p = t * S + k;
+  const int I = shared ? L.Is : L.I;
+  const QT Gq = shared ? L.sh_gate : L.gate;
+  const QT Uq = shared ? L.sh_up : L.up;
+  const int i_base = g * kGRows;                    // the unit's first row
+  const int nrows = min(kGRows, I - i_base);
+  const int nch = H / kCpc;                         // chunks per row
+  const int wpr = H / (32 / BITS);                  // words per row
+  const int gpr = H / kGroup;                       // groups per row
+  const int x16 = H / 4;
+  const int sb16 = kGRows * gpr * 2 / 16;           // 16-byte words per scale/bias tensor
+  float* xs = smem;
+  float* xsum = xs + H;
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(xsum + H / 16);   // [4][kGRows * gpr]
+  float4* x4 = reinterpret_cast<float4*>(xs);
 
-  if (u < P.g_units) {
-    // ------------------------------------------------------------ G unit
-    const int upt = K * P.ng_routed + (L.has_shared ? P.ng_shared : 0);
-    const int t = u / upt;
-    const int r = u - t * upt;
-    const bool shared = r >= K * P.ng_routed;
-    const int k = shared ? K : r / P.ng_routed;
-    const int g = shared ? r - K * P.ng_routed : r - k * P.ng_routed;
-    const int p = t * S + k;
-    const int I = shared ? L.Is : L.I;
-    const QT& Gq = shared ? L.sh_gate : L.gate;
-    const QT& Uq = shared ? L.sh_up : L.up;
-    bool valid = true;
-    size_t erow = 0;                                  // first row of the expert
+  uint4 xr[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = tid + j * kThreads;
+    xr[j] = reinterpret_cast<const uint4*>(x + (size_t)t * H)[min(i, x16 - 1)];
+  }
+  bool valid = true;
+  size_t erow = 0;                                  // first row of the expert
+  if constexpr (FUSED) {
+    // x and its chunk sums while the router runs, then the expert index
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = tid + j * kThreads;
+      if (i < x16) x4[ilv<kCpc>(i, nch)] = reinterpret_cast<const float4&>(xr[j]);
+    }
+    __syncthreads();
+    chunk_sums<kCpc>(x4, xsum, nch);
+    if (wid == 0 && !shared) {
+      const uint64_t v = wave_wait_nonzero(route_line(P, u % kRep, t) + k, 1, lane, P.ctr);
+      if (lane == 0) s_e = (int)(v >> 32) - 1;
+    }
+    __syncthreads();
+    if (!shared) erow = (size_t)min(max(s_e, 0), L.E - 1) * L.I;
+  } else {
     if (!shared) {
       const int e = idx[(size_t)t * K + k];
       valid = e >= 0 && e < L.E;
       erow = (size_t)(valid ? e : 0) * L.I;
     }
-    const int i_base = g * kGRows;                    // the unit's first row
-    const int nrows = min(kGRows, I - i_base);
-    const int nch = H / kCpc;                         // chunks per row
-    const int wpr = H / (32 / BITS);                  // words per row
-    const int gpr = H / kGroup;                       // groups per row
-    // 1) issue every HBM load, first what is needed first: x and the unit's
-    //    scales/biases (contiguous: rows x groups bf16), then 4 rows x (gate,
-    //    up) per wave
-    const int x16 = H / 4;
-    uint4 xr[4];
+  }
+  // every HBM load of the unit, scales/biases first (rows x groups bf16,
+  // contiguous per tensor), then 2 rows x (gate, up) per wave; clamped,
+  // always valid addresses and no branches, so they all issue back to back
+  uint4 sbr;
+  {
+    const size_t o = (erow + i_base) * gpr;
+    const int qq = min(tid, 4 * sb16 - 1);
+    const int q = qq / sb16, w = qq - q * sb16;
+    const uint16_t* src = q == 0 ? Gq.scales : q == 1 ? Gq.biases : q == 2 ? Uq.scales : Uq.biases;
+    sbr = reinterpret_cast<const uint4*>(src + o)[w];
+  }
+  uint4 wg[2][CPL], wu[2][CPL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = tid + j * 256;
-      xr[j] = i < x16 ? reinterpret_cast<const uint4*>(x + (size_t)t * H)[i] : make_uint4(0, 0, 0, 0);
-    }
-    const int sb16 = nrows * gpr * 2 / 16;            // 16-byte words per tensor
-    uint4 sbr[4];
-    {
-      const size_t o = (erow + i_base) * gpr;
-      const uint4* src[4] = {reinterpret_cast<const uint4*>(Gq.scales + o),
-                             reinterpret_cast<const uint4*>(Gq.biases + o),
-                             reinterpret_cast<const uint4*>(Uq.scales + o),
-                             reinterpret_cast<const uint4*>(Uq.biases + o)};
+  for (int rr = 0; rr < 2; ++rr) {
+    const int i = wid * 2 + rr;
+    const size_t row = erow + i_base + min(i, nrows - 1);
+    const uint4* g4 = reinterpret_cast<const uint4*>(Gq.q + row * wpr);
+    const uint4* u4 = reinterpret_cast<const uint4*>(Uq.q + row * wpr);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sbr[q] = tid < sb16 ? src[q][tid] : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < CPL; ++j) {
+      const int c = min(lane + kWave * j, nch - 1);
+      wg[rr][j] = g4[c];
+      wu[rr][j] = u4[c];
     }
-    uint4 wg[4][CPL], wu[4][CPL];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int i = wid * 4 + rr;
-      const size_t row = erow + i_base + (i < nrows ? i : 0);
-      const uint4* g4 = reinterpret_cast<const uint4*>(Gq.q + row * wpr);
-      const uint4* u4 = reinterpret_cast<const uint4*>(Uq.q + row * wpr);
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const int c = lane + kWave * j;
-        const bool ok = i < nrows && c < nch;
-        wg[rr][j] = ok ? g4[c] : make_uint4(0, 0, 0, 0);
-        wu[rr][j] = ok ? u4[c] : make_uint4(0, 0, 0, 0);
-      }
-    }
-    // 2) stage x, its chunk sums and the scales/biases in LDS
-    float* xs = smem;
-    float* xsum = xs + H;
-    uint16_t* sbl = reinterpret_cast<uint16_t*>(xsum + H / 16);   // [4][kGRows*gpr]
-    float4* x4 = reinterpret_cast<float4*>(xs);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int i = tid + j * 256;
-      if (i < x16) x4[ilv<kCpc>(i, nch)] = reinterpret_cast<const float4&>(xr[j]);
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (tid < sb16) reinterpret_cast<uint4*>(sbl + q * kGRows * gpr)[tid] = sbr[q];
-    __syncthreads();
-    chunk_sums<kCpc>(x4, xsum, nch);
-    __syncthreads();
-    // 3) the wave's four rows: per-lane partials, then one transposed reduction
-    float pg[4], pu[4];
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-      const int i = wid * 4 + rr;
-      float ag = 0.f, au = 0.f;
-#pragma unroll
-      for (int j = 0; j < CPL; ++j) {
-        const int c = lane + kWave * j;
-        if (c < nch) {
-          const int grp = i * gpr + (c * kCpc) / kGroup;
-          const float dg = chunk_dot<BITS>(wg[rr][j], x4 + c, nch);
-          const float du = chunk_dot<BITS>(wu[rr][j], x4 + c, nch);
-          ag = fmaf(bf16_to_f32(sbl[grp]), dg, fmaf(bf16_to_f32(sbl[kGRows * gpr + grp]), xsum[c], ag));
-          au = fmaf(bf16_to_f32(sbl[2 * kGRows * gpr + grp]), du,
-                    fmaf(bf16_to_f32(sbl[3 * kGRows * gpr + grp]), xsum[c], au));
-        }
-      }
-      pg[rr] = ag;
-      pu[rr] = au;
-    }
-    const float gsum = treduce<4, 32>(pg, lane);
-    const float usum = treduce<4, 32>(pu, lane);
-    if ((lane & 15) == 0) {
-      const int i = wid * 4 + tindex<4, 32>(lane);
-      if (i < nrows)
-        st_coh(P.h + (size_t)p * P.Imax + i_base + i, valid ? silu(gsum) * usum : __builtin_nanf(""));
-    }
-    if (shared && g == 0 && wid == 0) {
-      // the shared_expert_gate logit of token t (one row of H, its own bits)
-      const int eb = L.sh_eg.bits;
-      const int cpce = 128 / eb;
-      const int nche = H / cpce;
-      float a = 0.f;
-      for (int c = lane; c < nche; c += kWave) {
-        const uint4 v = reinterpret_cast<const uint4*>(L.sh_eg.q)[c];
-        const int gg = (c * cpce) / kGroup;
-        float d = 0.f, xsm = 0.f;
-        for (int q = 0; q < cpce; ++q) {
-          const int col = c * cpce + q;          // element of x in the interleaved layout
-          const float xv = xs[4 * ilv<kCpc>(col / 4, nch) + col % 4];
-          const uint32_t word = q / (32 / eb) == 0 ? v.x : q / (32 / eb) == 1 ? v.y : q / (32 / eb) == 2 ? v.z : v.w;
-          const uint32_t code = (word >> (eb * (q % (32 / eb)))) & ((1u << eb) - 1u);
-          d = fmaf((float)code, xv, d);
-          xsm += xv;
-        }
-        a = fmaf(bf16_to_f32(L.sh_eg.scales[gg]), d, fmaf(bf16_to_f32(L.sh_eg.biases[gg]), xsm, a));
-      }
-      a = wave_sum(a);
-      if (lane == 0) st_coh(P.sg + t, a);
-    }
-    drain();
-    __syncthreads();
-    if (tid == 0) {
-      int* tl = tok_lines(t);
-      if (arrive(tl, r, upt))
-        __hip_atomic_store(tl + 2 * (1 + kFan) * kLine, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  } else {
-    // ------------------------------------------------------------ D unit
-    const int d = u - P.g_units;
-    const int t = d / P.nc;
-    const int c = d - t * P.nc;
-    const int r0 = c * kDRows;
-    const int nrows = min(kDRows, H - r0);
-    const int I = L.I, Is = L.Is;
-    const int cpr = I / kCpc;                    // chunks per routed down row
-    const int cps = L.has_shared ? Is / kCpc : 0;
-    const int tot = K * cpr + cps;               // chunks per output row, all slots
-    // slot of every chunk position and the row bases, per lane (chunks q = lane + 64 j)
-    int eoff[DCH];                          // expert (or shared) row base, in rows
-    int kq[DCH];                            // slot of the chunk, -1 if none
-    int cq[DCH];                            // chunk within the slot's row
-#pragma unroll
-    for (int j = 0; j < DCH; ++j) {
-      const int q = lane + kWave * j;
-      kq[j] = -1;
-      cq[j] = 0;
-      eoff[j] = 0;
-      if (q < tot) {
-        const int k = q < K * cpr ? q / cpr : K;
-        kq[j] = k;
-        cq[j] = k < K ? q - k * cpr : q - K * cpr;
-        if (k < K) {
-          const int e = idx[(size_t)t * K + k];
-          eoff[j] = (e >= 0 && e < L.E ? e : 0) * H;
-        }
-      }
-    }
-    // 1) issue every HBM load: the unit's scales and biases for every slot
-    //    (per slot kDRows rows x groups bf16, contiguous), then 2 rows x up to
-    //    DCH chunks per lane
-    const int gr = I / kGroup, gs = L.has_shared ? Is / kGroup : 0;
-    const int sb_r = kDRows * gr * 2 / 16;       // 16-byte words per slot and tensor
-    const int sb_s = kDRows * gs * 2 / 16;
-    const int n_sb = 2 * (K * sb_r + sb_s);      // all slots, scales and biases
-    uint4 sbr[2];
+  }
+  if constexpr (!FUSED) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int q = tid + 256 * j;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (q < n_sb) {
-        const int half = q < K * sb_r + sb_s ? 0 : 1;          // 0: scales, 1: biases
-        const int qq = q - half * (K * sb_r + sb_s);
-        const int k = qq < K * sb_r ? qq / sb_r : K;
-        const int w = k < K ? qq - k * sb_r : qq - K * sb_r;
-        size_t base;
-        const uint16_t* src;
-        if (k < K) {
-          const int e = idx[(size_t)t * K + k];
-          base = ((size_t)(e >= 0 && e < L.E ? e : 0) * H + r0) * gr;
-          src = half ? L.down.biases : L.down.scales;
-        } else {
-          base = (size_t)r0 * gs;
-          src = half ? L.sh_down.biases : L.sh_down.scales;
-        }
-        if (r0 + kDRows <= H || w * 8 < (H - r0) * (k < K ? gr : gs))
-          v = reinterpret_cast<const uint4*>(src + base)[w];
-      }
-      sbr[j] = v;
+      const int i = tid + j * kThreads;
+      if (i < x16) x4[ilv<kCpc>(i, nch)] = reinterpret_cast<const float4&>(xr[j]);
     }
-    uint4 wv[2][DCH];
+  }
+  if (tid < 4 * sb16) reinterpret_cast<uint4*>(sbl)[tid] = sbr;
+  __syncthreads();
+  if constexpr (!FUSED) {
+    chunk_sums<kCpc>(x4, xsum, nch);
+    __syncthreads();
+  }
+  // the wave's two rows: per-lane partials, then one transposed reduction
+  float pg[2], pu[2];
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int rl = wid * 2 + rr;
+  for (int rr = 0; rr < 2; ++rr) {
+    const int i = wid * 2 + rr;
+    float ag = 0.f, au = 0.f;
 #pragma unroll
-      for (int j = 0; j < DCH; ++j) {
-        const bool ok = kq[j] >= 0 && rl < nrows;
-        const bool sh = kq[j] == K;
-        const uint32_t* base = sh ? L.sh_down.q : L.down.q;
-        const int wpr = (sh ? Is : I) / (32 / BITS);
-        wv[rr][j] = ok ? reinterpret_cast<const uint4*>(base + (size_t)(eoff[j] + r0 + rl) * wpr)[cq[j]]
-                       : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < CPL; ++j) {
+      const int c = lane + kWave * j;
+      if (c < nch) {
+        const int grp = i * gpr + (c * kCpc) / kGroup;
+        const float dg = chunk_dot<BITS>(wg[rr][j], x4 + c, nch);
+        const float du = chunk_dot<BITS>(wu[rr][j], x4 + c, nch);
+        ag = fmaf(bf16_to_f32(sbl[grp]), dg, fmaf(bf16_to_f32(sbl[kGRows * gpr + grp]), xsum[c], ag));
+        au = fmaf(bf16_to_f32(sbl[2 * kGRows * gpr + grp]), du,
+                  fmaf(bf16_to_f32(sbl[3 * kGRows * gpr + grp]), xsum[c], au));
       }
     }
-    // per-slot weights (routing weights; sigmoid(sg) for the shared slot) and
-    // whether the token has an out-of-range expert index (its rows become NaN)
-    __shared__ float wk[17];
-    __shared__ int bad;
-    if (tid == 0) bad = 0;
+    pg[rr] = ag;
+    pu[rr] = au;
+  }
+  const float gsum = treduce<2, 32>(pg, lane);
+  const float usum = treduce<2, 32>(pu, lane);
+  if ((lane & 31) < kHCopies) {         // every lane of a half holds its row's sum
+    const int i = wid * 2 + tindex<2, 32>(lane);
+    if (i < nrows)
+      st_coh(P.h + (size_t)(lane & 31) * P.P * P.Imax + (size_t)p * P.Imax + i_base + i,
+             valid ? silu(gsum) * usum : __builtin_nanf(""));
+  }
+  if (shared && g == 0 && wid == 0) {
+    // the shared_expert_gate logit of token t (one row of H, its own bits)
+    const int eb = L.sh_eg.bits;
+    const int cpce = 128 / eb;
+    const int nche = H / cpce;
+    float a = 0.f;
+    for (int c = lane; c < nche; c += kWave) {
+      const uint4 v = reinterpret_cast<const uint4*>(L.sh_eg.q)[c];
+      const int gg = (c * cpce) / kGroup;
+      float d = 0.f, xsm = 0.f;
+      for (int q = 0; q < cpce; ++q) {
+        const int col = c * cpce + q;          // element of x in the interleaved layout
+        const float xv = xs[4 * ilv<kCpc>(col / 4, nch) + col % 4];
+        const uint32_t word = q / (32 / eb) == 0 ? v.x : q / (32 / eb) == 1 ? v.y : q / (32 / eb) == 2 ? v.z : v.w;
+        const uint32_t code = (word >> (eb * (q % (32 / eb)))) & ((1u << eb) - 1u);
+        d = fmaf((float)code, xv, d);
+        xsm += xv;
+      }
+      a = fmaf(bf16_to_f32(L.sh_eg.scales[gg]), d, fmaf(bf16_to_f32(L.sh_eg.biases[gg]), xsm, a));
+    }
+    a = wave_sum(a);
+    if (lane == 0) st_coh(P.sg + t, a);
+  }
+  drain();
+  __syncthreads();
+  __shared__ int s_done;
+  if (tid == 0) s_done = arrive(P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines), r, upt);
+  __syncthreads();
+  if (s_done && tid < kRep) st_coh_i(ready_line(P, tid, t), 1);
+}
+
+// ------------------------------------------------------------------ D unit
+// LDS: [h of all S slots, chunk-interleaved per slot][their chunk sums][bf16
+// scales then biases of the unit's rows, slot by slot]
+template <int BITS, int DCH, bool FUSED>
+__device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
+                                          const int32_t* __restrict__ idx,
+                                          const float* __restrict__ wts,
+                                          const float* __restrict__ residual,
+                                          float* __restrict__ y, int d) {
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  __shared__ float wk[kMaxTopK + 1];
+  __shared__ int s_ex[kMaxTopK];
+  __shared__ int bad;
+  constexpr int kCpc = 128 / BITS;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int K = P.K, H = L.H;
+  const int t = d / P.nc;
+  const int c = d - t * P.nc;
+  const int r0 = c * kDRows;
+  const int nrows = min(kDRows, H - r0);
+  const int rl = wid;                          // the wave's row
+  const int I = L.I, Is = L.Is;
+  const int cpr = I / kCpc;                    // chunks per routed down row
+  const int cps = L.has_shared ? Is / kCpc : 0;
+  const int tot = K * cpr + cps;               // chunks per output row, all slots
+  int* tl = P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines);
+  // slot and chunk of every chunk position of the lane (q = lane + 64 j)
+  int kq[DCH], cq[DCH];
+#pragma unroll
+  for (int j = 0; j < DCH; ++j) {
+    const int q = lane + kWave * j;
+    kq[j] = -1;
+    cq[j] = 0;
+    if (q < tot) {
+      const int k = q < K * cpr ? q / cpr : K;
+      kq[j] = k;
+      cq[j] = k < K ? q - k * cpr : q - K * cpr;
+    }
+  }
+  if (tid == 0) bad = 0;
+  if constexpr (!FUSED) {
     __syncthreads();
     if (tid < K) {
       const int e = idx[(size_t)t * K + tid];
+      const bool ok = e >= 0 && e < L.E;
+      s_ex[tid] = ok ? e : 0;
       wk[tid] = wts[(size_t)t * K + tid];
-      if (e < 0 || e >= L.E) atomicOr(&bad, 1);
+      if (!ok) atomicOr(&bad, 1);
     }
-    // 2) wait for token t's h, then stage it (coherent loads) with chunk sums
-    if (tid == 0) {
-      if (!wait_flag(tok_lines(t) + 2 * (1 + kFan) * kLine)) atomicOr(err, 1);
-      if (L.has_shared) wk[K] = 1.0f / (1.0f + __expf(-ld_coh(P.sg + t)));
+  }
+  if constexpr (FUSED) {
+    if (wid == 0) {
+      const uint64_t v = wave_wait_nonzero(route_line(P, d % kRep, t), K, lane, P.ctr);
+      if (lane < K) {
+        s_ex[lane] = min(max((int)(v >> 32) - 1, 0), L.E - 1);
+        wk[lane] = __uint_as_float((uint32_t)v);
+      }
     }
-    __syncthreads();
-    float* hs = smem;                            // [S][Imax]
-    float* hsum = hs + (size_t)P.S * P.Imax;     // [S][Imax/kCpc]
-    // bf16 scales then biases: slot k < K at k*kDRows*gr, shared after them
-    uint16_t* sbl = reinterpret_cast<uint16_t*>(hsum + (size_t)P.S * P.Imax / 16);
+  }
+  __syncthreads();
+  // scales and biases of every slot (per slot kDRows rows x groups bf16,
+  // contiguous), then the routed chunks
+  const int gr = I / kGroup, gs = L.has_shared ? Is / kGroup : 0;
+  const int sb_r = kDRows * gr * 2 / 16;       // 16-byte words per slot and tensor
+  const int sb_s = kDRows * gs * 2 / 16;
+  const int n_sb = 2 * (K * sb_r + sb_s);      // all slots, scales and biases
+  // (clamped, always valid addresses and no branches: the loads issue back
+  // to back; H is a multiple of kDRows, so every unit has full rows)
+  uint4 sbr;
+  {
+    const int tq = min(tid, n_sb - 1);
+    const int half = tq < K * sb_r + sb_s ? 0 : 1;           // 0: scales, 1: biases
+    const int qq = tq - half * (K * sb_r + sb_s);
+    const int k = qq < K * sb_r ? qq / sb_r : K;
+    const int w = k < K ? qq - k * sb_r : qq - K * sb_r;
+    const uint16_t* src = k < K ? (half ? L.down.biases : L.down.scales)
+                                : (half ? L.sh_down.biases : L.sh_down.scales);
+    const size_t base = k < K ? ((size_t)s_ex[k] * H + r0) * gr : (size_t)r0 * gs;
+    sbr = reinterpret_cast<const uint4*>(src + base)[w];
+  }
+  uint4 wv[DCH];
+  const int rlc = min(rl, nrows - 1);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int q = tid + 256 * j;
-      if (q < n_sb) reinterpret_cast<uint4*>(sbl)[q] = sbr[j];
-    }
-    {
-      // all coherent loads of a batch in flight before any is consumed
-      const uint64_t* h2 = reinterpret_cast<const uint64_t*>(P.h + (size_t)t * P.S * P.Imax);
-      const int n2 = P.S * P.Imax / 2;
-      constexpr int kB = 16;
-      for (int b0 = 0; b0 < n2; b0 += 256 * kB) {
-        uint64_t r[kB];
+  for (int j = 0; j < DCH; ++j) {
+    const bool sh = kq[j] == K;
+    const uint32_t* base = sh ? L.sh_down.q
+                              : L.down.q + ((size_t)s_ex[max(kq[j], 0)] * H) * (I / (32 / BITS));
+    const int wpr = (sh ? Is : I) / (32 / BITS);
+    wv[j] = reinterpret_cast<const uint4*>(base + (size_t)(r0 + rlc) * wpr)[cq[j]];
+  }
+  // wait for token t's h (and the routing weights, the shared gate)
+  if (wid == 0) {
+    if (lane == 0 && !wait_flag(ready_line(P, d % kRep, t))) atomicOr(P.ctr, 1);
+    // lane K: the shared expert's gate
+    if (L.has_shared && lane == K) wk[K] = 1.0f / (1.0f + __expf(-ld_coh(P.sg + t)));
+  }
+  __syncthreads();
+  // this unit is done with the token's flags and route words: count it; the
+  // last unit of the token clears them for the next launch (below)
+  __shared__ int s_done;
+  if (tid == 0) s_done = arrive(tl + (1 + kFan) * kLine, c, P.nc);
+  float* hs = smem;                            // [S][Imax]
+  float* hsum = hs + (size_t)P.S * P.Imax;     // [S][Imax/kCpc]
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(hsum + (size_t)P.S * P.Imax / 16);
+  if (tid < n_sb) reinterpret_cast<uint4*>(sbl)[tid] = sbr;
+  {
+    // all coherent loads of a batch in flight before any is consumed
+    const uint64_t* h2 = reinterpret_cast<const uint64_t*>(P.h + (size_t)(d % kHCopies) * P.P * P.Imax +
+                                                           (size_t)t * P.S * P.Imax);
+    const int n2 = P.S * P.Imax / 2;
+    constexpr int kB = 8;
+    for (int b0 = 0; b0 < n2; b0 += kThreads * kB) {
+      uint64_t rg[kB];
 #pragma unroll
-        for (int j = 0; j < kB; ++j) {
-          const int i = b0 + tid + 256 * j;
-          r[j] = i < n2 ? ld_coh64(h2 + i) : 0ull;
-        }
+      for (int j = 0; j < kB; ++j) {
+        const int i = b0 + tid + kThreads * j;
+        rg[j] = ld_coh64(h2 + min(i, n2 - 1));
+      }
 #pragma unroll
-        for (int j = 0; j < kB; ++j) {
-          const int i = b0 + tid + 256 * j;      // floats 2i, 2i+1 of the token's h
-          if (i < n2) {
-            const int k = (2 * i) / P.Imax;
-            const int e = 2 * i - k * P.Imax;    // element within the slot
-            const int nk = (k == K ? Is : I) / kCpc;
-            if (e < nk * kCpc) {
-              float* dst = hs + (size_t)k * P.Imax + 4 * ilv<kCpc>(e / 4, nk) + e % 4;
-              *reinterpret_cast<uint64_t*>(dst) = r[j];
-            }
+      for (int j = 0; j < kB; ++j) {
+        const int i = b0 + tid + kThreads * j;   // floats 2i, 2i+1 of the token's h
+        if (i < n2) {
+          const int k = (2 * i) / P.Imax;
+          const int e = 2 * i - k * P.Imax;      // element within the slot
+          const int nk = (k == K ? Is : I) / kCpc;
+          if (e < nk * kCpc) {
+            float* dst = hs + (size_t)k * P.Imax + 4 * ilv<kCpc>(e / 4, nk) + e % 4;
+            *reinterpret_cast<uint64_t*>(dst) = rg[j];
           }
         }
       }
     }
-    __syncthreads();
-    // chunk sums of every slot, one (slot, chunk) pair per thread
-    for (int q = tid; q < tot; q += blockDim.x) {
-      const int k = q < K * cpr ? q / cpr : K;
-      const int cc = k < K ? q - k * cpr : q - K * cpr;
-      const int nk = k < K ? cpr : cps;
-      const float4* a4 = reinterpret_cast<const float4*>(hs + (size_t)k * P.Imax);
-      float sum = 0.f;
+  }
+  __syncthreads();
+  if (s_done) {
+    if (tid < kRep) st_coh_i(ready_line(P, tid, t), 0);
+    if constexpr (FUSED)
+      for (int i = tid; i < kRep * K; i += kThreads) st_coh_u64(route_line(P, i / K, t) + i % K, 0);
+  }
+  // chunk sums of every slot, one (slot, chunk) pair per thread
+  for (int q = tid; q < tot; q += kThreads) {
+    const int k = q < K * cpr ? q / cpr : K;
+    const int cc = k < K ? q - k * cpr : q - K * cpr;
+    const int nk = k < K ? cpr : cps;
+    const float4* a4 = reinterpret_cast<const float4*>(hs + (size_t)k * P.Imax);
+    float sum = 0.f;
 #pragma unroll
-      for (int f = 0; f < kCpc / 4; ++f) {
-        const float4 v = a4[f * nk + cc];
-        sum += (v.x + v.y) + (v.z + v.w);
-      }
-      hsum[(size_t)k * (P.Imax / kCpc) + cc] = sum;
+    for (int f = 0; f < kCpc / 4; ++f) {
+      const float4 v = a4[f * nk + cc];
+      sum += (v.x + v.y) + (v.z + v.w);
     }
-    __syncthreads();
-    // 3) two rows per wave: per-lane partials over the lane's chunks, then
-    //    one transposed reduction
-    float pv[2];
+    hsum[(size_t)k * (P.Imax / kCpc) + cc] = sum;
+  }
+  __syncthreads();
+  // the wave's row: per-lane partials over the lane's chunks, then the wave sum
+  float pv[1];
+  {
+    float acc = 0.f;
 #pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int rl = wid * 2 + rr;
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < DCH; ++j) {
-        const int k = kq[j];
-        if (k >= 0 && rl < nrows) {
-          const bool sh = k == K;
-          const int Ik = sh ? Is : I;
-          const int gpr = Ik / kGroup;
-          const float4* hk = reinterpret_cast<const float4*>(hs + (size_t)k * P.Imax);
-          const float dd = chunk_dot<BITS>(wv[rr][j], hk + cq[j], Ik / kCpc);
-          const int gi = (sh ? K * kDRows * gr : k * kDRows * gr) + rl * gpr + (cq[j] * kCpc) / kGroup;
-          const int boff = K * kDRows * gr + kDRows * gs;    // biases follow all scales
-          const float part = fmaf(bf16_to_f32(sbl[gi]), dd,
-                                  bf16_to_f32(sbl[boff + gi]) * hsum[(size_t)k * (P.Imax / kCpc) + cq[j]]);
-          acc = fmaf(wk[k], part, acc);
-        }
-      }
-      pv[rr] = acc;
-    }
-    const float tsum = treduce<2, 32>(pv, lane);
-    if ((lane & 31) == 0) {
-      const int rl = wid * 2 + tindex<2, 32>(lane);
-      if (rl < nrows) {
-        float v = bad ? __builtin_nanf("") : tsum;
-        if (residual) v += residual[(size_t)t * H + r0 + rl];
-        y[(size_t)t * H + r0 + rl] = v;
+    for (int j = 0; j < DCH; ++j) {
+      const int k = kq[j];
+      if (k >= 0 && rl < nrows) {
+        const bool sh = k == K;
+        const int Ik = sh ? Is : I;
+        const int gpr = Ik / kGroup;
+        const float4* hk = reinterpret_cast<const float4*>(hs + (size_t)k * P.Imax);
+        const float dd = chunk_dot<BITS>(wv[j], hk + cq[j], Ik / kCpc);
+        const int gi = (sh ? K * kDRows * gr : k * kDRows * gr) + rl * gpr + (cq[j] * kCpc) / kGroup;
+        const int boff = K * kDRows * gr + kDRows * gs;    // biases follow all scales
+        const float part = fmaf(bf16_to_f32(sbl[gi]), dd,
+                                bf16_to_f32(sbl[boff + gi]) * hsum[(size_t)k * (P.Imax / kCpc) + cq[j]]);
+        acc = fmaf(wk[k], part, acc);
       }
     }
-    // the last D unit of token t to arrive lowers the ready flag (every D unit
-    // of the token has finished waiting on it)
-    __syncthreads();
-    if (tid == 0) {
-      int* tl = tok_lines(t);
-      if (arrive(tl + (1 + kFan) * kLine, c, P.nc))
-        __hip_atomic_store(tl + 2 * (1 + kFan) * kLine, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    pv[0] = acc;
+  }
+  const float tsum = treduce<1, 32>(pv, lane);
+  if (lane == 0 && rl < nrows) {
+    float v = bad ? __builtin_nanf("") : tsum;
+    if (residual) v += residual[(size_t)t * H + r0 + rl];
+    y[(size_t)t * H + r0 + rl] = v;
   }
 }
 
-DecPlan make_dec_plan(const DecodeLayer& L, int M, int K, void* ws, size_t* bytes) {
+// 8-bit layers of up to 2048 columns: at most 80 VGPRs, so three units fit per
+// CU (24 waves) and a 30B-A3B-shaped layer's units are all resident at once
+template <int BITS, int CPL, int DCH, bool FUSED>
+__global__ void __launch_bounds__(kThreads)
+    __attribute__((amdgpu_waves_per_eu(BITS == 8 && CPL <= 2 && DCH <= 6 ? 6 : 1))) k_moe_decode(DecodeLayer L, DecPlan P, RouteIn R,
+                                                        const float* __restrict__ x,
+                                                        const int32_t* __restrict__ idx,
+                                                        const float* __restrict__ wts,
+                                                        const float* __restrict__ residual,
+                                                        float* __restrict__ y) {
+  int u = blockIdx.x;
+  if constexpr (FUSED) {
+    if (u < P.r_units) {
+      route_unit(L, P, R, x, u);
+      return;
+    }
+    u -= P.r_units;
+  }
+  if (u < P.g_units) gate_up_unit<BITS, CPL, FUSED>(L, P, x, idx, u);
+  else down_unit<BITS, DCH, FUSED>(L, P, idx, wts, residual, y, u - P.g_units);
+}
+
+static DecPlan make_dec_plan(const DecodeLayer& L, int M, int K, bool routed, void* ws, size_t* bytes) {
   DecPlan P{};
   P.M = M;
   P.K = K;
@@ -532,35 +810,50 @@ DecPlan make_dec_plan(const DecodeLayer& L, int M, int K, void* ws, size_t* byte
   P.g_units = M * (K * P.ng_routed + P.ng_shared);
   P.nc = (L.H + kDRows - 1) / kDRows;
   P.d_units = M * P.nc;
+  P.r_units = routed ? (L.E + kRRows - 1) / kRRows : 0;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   size_t off = 0;
-  const size_t n_ctr = (size_t)kLine * (1 + (size_t)kCtrLines * M);
   char* base = reinterpret_cast<char*>(ws);
-  P.ctr = reinterpret_cast<int*>(base + off);
-  off += al(sizeof(int) * n_ctr);
-  P.h = reinterpret_cast<float*>(base + off);
-  off += al(sizeof(float) * (size_t)P.P * P.Imax);
-  P.sg = reinterpret_cast<float*>(base + off);
-  off += al(sizeof(float) * (size_t)M);
+  auto take = [&](size_t n) { char* p = base ? base + off : nullptr; off += al(n); return p; };
+  P.ctr = reinterpret_cast<int*>(take(sizeof(int) * (size_t)kLine * (1 + (size_t)kCtrLines * M)));
+  // flag copies: kRep blocks of M lines, 4 KB + 256 B apart at least
+  P.rstride = (int)((((size_t)M * kLine * sizeof(int) + 4095) / 4096 * 4096 + 256) / sizeof(int));
+  P.ready = reinterpret_cast<int*>(take(sizeof(int) * (size_t)kRep * P.rstride));
+  P.h = reinterpret_cast<float*>(take(sizeof(float) * kHCopies * (size_t)P.P * P.Imax));
+  P.sg = reinterpret_cast<float*>(take(sizeof(float) * (size_t)M));
+  if (routed) {
+    P.logits = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)M * L.E));
+    P.idx_c = reinterpret_cast<int32_t*>(take(sizeof(int) * (size_t)kRep * P.rstride));
+  }
   if (bytes) *bytes = off;
   return P;
 }
 
-size_t decode_ws_bytes(const DecodeLayer& L, int M, int K) {
+size_t decode_ws_bytes(const DecodeLayer& L, int M, int K, bool routed) {
   size_t b = 0;
-  make_dec_plan(L, M, K, nullptr, &b);
+  make_dec_plan(L, M, K, routed, nullptr, &b);
   return b;
 }
 
-size_t decode_lds_bytes(const DecodeLayer& L, int K) {
+// scale/bias words (16 bytes) a D unit stages: all slots, scales and biases
+static int d_sb_words(const DecodeLayer& L, int K) {
+  return 2 * kDRows * (K * (L.I / kGroup) + (L.has_shared ? L.Is / kGroup : 0)) * 2 / 16;
+}
+
+static size_t dec_lds_bytes(const DecodeLayer& L, int K, bool routed) {
   // G: x (H floats) + chunk sums (<= H/16) + 4 x 16 rows x groups bf16;
   // D: h of all S slots (S x Imax floats) + their chunk sums (<= 1/16 of that)
+  //    + the staged scale/bias words;
+  // R (last unit only): E keys and E fp64 logits
   const size_t g = sizeof(float) * (L.H + L.H / 16) + 2 * 4 * kGRows * (L.H / kGroup);
   const int S = K + (L.has_shared ? 1 : 0);
   const int Im = L.has_shared && L.Is > L.I ? L.Is : L.I;
-  const size_t d = sizeof(float) * ((size_t)S * Im + (size_t)S * Im / 16) +
-                   2 * 2 * (size_t)kDRows * (K * (L.I / kGroup) + (L.has_shared ? L.Is / kGroup : 0));
-  return (g > d ? g : d) + 64;
+  const size_t d = sizeof(float) * ((size_t)S * Im + (size_t)S * Im / 16) + 16 * (size_t)d_sb_words(L, K);
+  const size_t r = routed ? 16 * (size_t)L.E : 0;        // + x of kFusedMaxM tokens below
+  const size_t rx = routed ? sizeof(float) * (size_t)kFusedMaxM * L.H : 0;
+  size_t m = g > d ? g : d;
+  m = m > r ? m : r;
+  return m > rx ? m : rx;
 }
 
 // 16-byte chunks per lane of a D row (all slots), rounded up to 1,2,3,4,6,8
@@ -577,43 +870,49 @@ static int g_cpl(int H, int bits) {
   return nch <= kWave ? 1 : nch <= 2 * kWave ? 2 : nch <= 4 * kWave ? 4 : 0;
 }
 
-// limits of this kernel: x at most 4096 floats (one 16-byte word per thread
-// per 1024), G rows of at most 4 chunks per lane, D rows (all slots) of at
-// most 8 chunks per lane, the shared expert at the routed experts' bit width,
-// a G unit's scales/biases within one 16-byte word per thread, and the LDS
+// limits of this kernel: x at most 4096 floats (two 16-byte words per
+// thread), G rows of at most 4 chunks per lane, D rows (all slots) of at most
+// 8 chunks per lane, the shared expert at the routed experts' bit width, the
+// scale/bias words of a G or D unit within one 16-byte word per thread, and
+// the LDS
 bool decode_supported(const DecodeLayer& L, int K) {
   const int b = L.gate.bits;
   if (L.H > 4096 || !g_cpl(L.H, b)) return false;
-  if (kGRows * (L.H / kGroup) * 2 / 16 > 256) return false;
+  if (4 * kGRows * (L.H / kGroup) * 2 / 16 > kThreads) return false;
   if (L.has_shared) {
     if (L.sh_gate.bits != b) return false;
     if (L.sh_eg.bits != 2 && L.sh_eg.bits != 4 && L.sh_eg.bits != 8) return false;
   }
   if (!d_ch(L, K)) return false;
-  // the D unit stages its scales/biases with at most two 16-byte words per thread
-  const int words = 2 * kDRows * (K * (L.I / kGroup) + (L.has_shared ? L.Is / kGroup : 0)) * 2 / 16;
-  if (words > 2 * 256) return false;
-  return decode_lds_bytes(L, K) <= 160 * 1024;
+  if (d_sb_words(L, K) > kThreads) return false;
+  return dec_lds_bytes(L, K, false) <= 160 * 1024;
 }
 
-template <int B, int CPL, int DCH>
-static void run_fused(const DecodeLayer& L, const DecPlan& P, const float* x, const int32_t* idx,
-                      const float* w, const float* residual, float* y, hipStream_t s) {
-  const size_t lds = decode_lds_bytes(L, P.K);
-  hipLaunchKernelGGL((k_dec_fused<B, CPL, DCH>), dim3(P.g_units + P.d_units), dim3(256), lds, s,
-                     L, P, x, idx, w, residual, y);
+bool fused_supported(const DecodeLayer& L, const QT& router, int M, int K) {
+  return decode_supported(L, K) && router.bits == 8 && router.rows == L.E && router.cols == L.H &&
+         M >= 1 && M <= kFusedMaxM && L.E <= kMaxExperts && dec_lds_bytes(L, K, true) <= 160 * 1024;
 }
 
-int launch_decode_forward(const DecodeLayer& L, const float* x, const int32_t* idx, const float* w,
-                          int M, int K, const float* residual, float* y, void* ws, hipStream_t s) {
-  const DecPlan P = make_dec_plan(L, M, K, ws, nullptr);
+template <int B, int CPL, int DCH, bool FUSED>
+static void run_dec(const DecodeLayer& L, const DecPlan& P, const RouteIn& R, const float* x,
+                    const int32_t* idx, const float* w, const float* residual, float* y,
+                    hipStream_t s) {
+  const size_t lds = dec_lds_bytes(L, P.K, FUSED);
+  hipLaunchKernelGGL((k_moe_decode<B, CPL, DCH, FUSED>), dim3(P.r_units + P.g_units + P.d_units),
+                     dim3(kThreads), lds, s, L, P, R, x, idx, w, residual, y);
+}
+
+template <bool FUSED>
+static int dispatch_dec(const DecodeLayer& L, const DecPlan& P, const RouteIn& R, const float* x,
+                        const int32_t* idx, const float* w, const float* residual, float* y,
+                        hipStream_t s) {
   const int b = L.gate.bits;
   const int cpl = g_cpl(L.H, b);
-  const int dch = d_ch(L, K);
-#define MOEQ_DEC(B_, C_, D_)                                    \
-  if (b == B_ && cpl == C_ && dch == D_) {                     \
-    run_fused<B_, C_, D_>(L, P, x, idx, w, residual, y, s);    \
-    return 0;                                                  \
+  const int dch = d_ch(L, P.K);
+#define MOEQ_DEC(B_, C_, D_)                                              \
+  if (b == B_ && cpl == C_ && dch == D_) {                               \
+    run_dec<B_, C_, D_, FUSED>(L, P, R, x, idx, w, residual, y, s);      \
+    return 0;                                                            \
   }
 #define MOEQ_DEC_PW(B_, C_) MOEQ_DEC(B_, C_, 1) MOEQ_DEC(B_, C_, 2) MOEQ_DEC(B_, C_, 3) \
   MOEQ_DEC(B_, C_, 4) MOEQ_DEC(B_, C_, 6) MOEQ_DEC(B_, C_, 8)
@@ -625,6 +924,19 @@ int launch_decode_forward(const DecodeLayer& L, const float* x, const int32_t* i
 #undef MOEQ_DEC_PW
 #undef MOEQ_DEC
   return -9;
+}
+
+int launch_decode_forward(const DecodeLayer& L, const float* x, const int32_t* idx, const float* w,
+                          int M, int K, const float* residual, float* y, void* ws, hipStream_t s) {
+  const DecPlan P = make_dec_plan(L, M, K, false, ws, nullptr);
+  const RouteIn R{};
+  return dispatch_dec<false>(L, P, R, x, idx, w, residual, y, s);
+}
+
+int launch_moe_forward(const DecodeLayer& L, const RouteIn& R, const float* x, int M, int K,
+                       const float* residual, float* y, void* ws, hipStream_t s) {
+  const DecPlan P = make_dec_plan(L, M, K, true, ws, nullptr);
+  return dispatch_dec<true>(L, P, R, x, nullptr, nullptr, residual, y, s);
 }
 
 }  // namespace moeq

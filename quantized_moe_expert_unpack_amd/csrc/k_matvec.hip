@@ -9,6 +9,7 @@
 // a group because a group is 8*BITS bytes (a multiple of 16).
 #include "common.h"
 #include "launch.h"
+#include "topk.h"
 
 namespace moeq {
 
@@ -97,77 +98,10 @@ __global__ void __launch_bounds__(256) k_qmatvec(const uint32_t* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
-// Routing: softmax over all E experts, top-K by (score descending, index
-// ascending), weights p[idx]/sum p[idx] (renorm) or p[idx].
-// markbaseengine MOE_ROUTER_WORKS_BREAKTHROUGH "Forward Pass Sequence" steps
-// 1-4 and the flash-moe pipeline's "softmax + topK routing", on the device.
-//
-// Selection works on unique 64-bit keys: the fp64 logit's order-preserving bit
-// pattern with its 10 lowest fraction bits replaced by (1023 - expert), so one
-// integer compare orders by value and breaks ties towards the lower index
-// (logits closer than 2^-42 relative compare as a tie; fp32 logits widened to
-// fp64 have those bits zero and are ordered exactly).  A block of 4 waves
-// first ranks each quarter of the keys inside its wave, keeps every key whose
-// rank in its quarter is < K (at most 4K candidates), then ranks the
-// candidates.  The softmax itself is evaluated in fp64 on the exact logits.
+// Routing (selection in topk.h)
 // ---------------------------------------------------------------------------
 constexpr int kRouteThreads = 256;
-constexpr int kMaxE = 1024;
-
-__device__ __forceinline__ uint64_t route_key(double v, int e) {
-  uint64_t u = (uint64_t)__double_as_longlong(v);
-  u = (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-  return (u & ~0x3FFull) | (uint64_t)(1023 - e);
-}
-
-// keys/vals in LDS for one token; writes K indices and weights
-__device__ void block_topk(const uint64_t* keys, const double* vals, int E, int K, int renorm,
-                           int32_t* __restrict__ idx_out, float* __restrict__ w_out) {
-  __shared__ uint64_t cand[4 * 16];
-  __shared__ int ncand;
-  __shared__ int sel[16];
-  __shared__ double red[kRouteThreads / kWave];
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  if (tid == 0) ncand = 0;
-  __syncthreads();
-  const int q = (E + 3) / 4;
-  const int lo = wid * q, hi = min(E, lo + q);
-  for (int a = lo + lane; a < hi; a += kWave) {
-    const uint64_t ka = keys[a];
-    int rank = 0;
-#pragma unroll 8
-    for (int j = lo; j < hi; ++j) rank += keys[j] > ka;
-    if (rank < K) cand[atomicAdd(&ncand, 1)] = ka;
-  }
-  __syncthreads();
-  const int nc = ncand;
-  if (tid < nc) {
-    const uint64_t kt = cand[tid];
-    int rank = 0;
-#pragma unroll 8
-    for (int j = 0; j < nc; ++j) rank += cand[j] > kt;
-    if (rank < K) sel[rank] = 1023 - (int)(kt & 0x3FFull);
-  }
-  __syncthreads();
-  const double mx = vals[sel[0]];
-  double total = 0.0;
-  if (!renorm) {
-    double part = 0.0;
-    for (int e = tid; e < E; e += kRouteThreads) part += exp(vals[e] - mx);
-    part = wave_sum(part);
-    if (lane == 0) red[wid] = part;
-    __syncthreads();
-    for (int w = 0; w < kRouteThreads / kWave; ++w) total += red[w];
-  } else {
-    for (int k = 0; k < K; ++k) total += exp(vals[sel[k]] - mx);   // slot order
-  }
-  if (tid < K) {
-    const int e = sel[tid];
-    idx_out[tid] = e;
-    w_out[tid] = (float)(exp(vals[e] - mx) / total);
-  }
-  __syncthreads();
-}
+constexpr int kMaxE = kMaxExperts;
 
 // Router projection in fp64 (the fp32 dequantized weight widened exactly,
 // fp64 products and sums), one wave per router row and token.  With
@@ -245,7 +179,7 @@ __global__ void __launch_bounds__(kRouteThreads) k_router(QT W, const float* __r
       }
     }
     __syncthreads();
-    block_topk(keys, vals, rows, K, renorm, idx + (size_t)m * K, wout + (size_t)m * K);
+    block_topk<kRouteThreads>(keys, vals, rows, K, renorm, idx + (size_t)m * K, wout + (size_t)m * K);
   }
 }
 
@@ -264,7 +198,7 @@ __global__ void __launch_bounds__(kRouteThreads) k_topk_rows(const double* __res
     keys[e] = route_key(v, e);
   }
   __syncthreads();
-  block_topk(keys, vals, E, K, renorm, idx + (size_t)t * K, wout + (size_t)t * K);
+  block_topk<kRouteThreads>(keys, vals, E, K, renorm, idx + (size_t)t * K, wout + (size_t)t * K);
 }
 
 constexpr int kLastTopkMaxM = 4;

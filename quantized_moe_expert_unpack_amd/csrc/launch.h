@@ -24,14 +24,27 @@ struct DecodeLayer {
   int E, H, I, Is;
 };
 
-// Decode plan: unit counts and the workspace carve-up of the fused decode
-// expert kernel (counters are zero between calls).
+// Decode plan: unit counts and the workspace carve-up of the one-launch
+// decode kernel (counters and the routed-index copies are zero between calls).
 struct DecPlan {
   int M, K, S, P, Imax;
   int ng_routed, ng_shared, g_units, nc, d_units;
-  int* ctr;      // 128-byte lines: error word, then per token gdone, ready, ddone
-  float* h;      // [P][Imax] (pair p = token * S + slot)
-  float* sg;     // [M]
+  int r_units;     // router units in front of the expert units (routing in the launch), else 0
+  int* ctr;        // 128-byte lines: error word, then per token G and D arrival counters
+  int* ready;      // ready flags: copies [kRep] of M lines, rstride ints apart
+  int rstride;
+  float* h;        // [P][Imax] (pair p = token * S + slot)
+  float* sg;       // [M]
+  uint64_t* logits;  // [M][E] router logits as complemented fp64 bits, 0 = not written
+  int32_t* idx_c;  // route lines: copies [kRep] of M lines (64-bit expert + 1 | weight words)
+};
+
+// Router of a decode launch that routes in the same launch.
+struct RouteIn {
+  QT W;            // [E][H], 8-bit
+  int renorm;
+  int32_t* idx_out;  // [M][K] (caller's)
+  float* w_out;      // [M][K] (caller's)
 };
 
 // Workspace carve-up for the gather (prefill) path; every pointer is
@@ -62,9 +75,13 @@ int launch_route(const QT* router, const float* x_or_logits, int M, int E, int K
 // decode expert forward (one launch)
 int launch_decode_forward(const DecodeLayer& L, const float* x, const int32_t* idx, const float* w,
                           int M, int K, const float* residual, float* y, void* ws, hipStream_t s);
-size_t decode_ws_bytes(const DecodeLayer& L, int M, int K);
-size_t decode_lds_bytes(const DecodeLayer& L, int K);
+size_t decode_ws_bytes(const DecodeLayer& L, int M, int K, bool routed_in_launch = false);
 bool decode_supported(const DecodeLayer& L, int K);
+// router + experts in one launch (8-bit router, M <= kFusedMaxM)
+constexpr int kFusedMaxM = 4;
+bool fused_supported(const DecodeLayer& L, const QT& router, int M, int K);
+int launch_moe_forward(const DecodeLayer& L, const RouteIn& R, const float* x, int M, int K,
+                       const float* residual, float* y, void* ws, hipStream_t s);
 
 // gather path
 int launch_sort_pairs(const int32_t* idx, int n, int E, const GatherWs& ws, hipStream_t s);

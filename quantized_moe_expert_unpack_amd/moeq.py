@@ -20,7 +20,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libmoeq.so")
 
-PATH_ROUTE, PATH_DECODE, PATH_GATHER, PATH_GQMM = 0, 1, 2, 3
+PATH_ROUTE, PATH_DECODE, PATH_GATHER, PATH_GQMM, PATH_FORWARD = 0, 1, 2, 3, 4
 
 STATUS = {
     0: "MOEQ_OK", -1: "MOEQ_ERR_NULL_PTR", -2: "MOEQ_ERR_BAD_BITS", -3: "MOEQ_ERR_BAD_GROUP",
@@ -63,6 +63,8 @@ _SIGNATURES = {
                                  _P, _SZ, _P]),
     "moe_expert_forward": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _P, _P, _I, _I, _P, _P,
                                           _P, _SZ, _P]),
+    "moe_forward": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _I, _I, _I, _P, _P, _P, _P, _P,
+                                   _SZ, _P]),
     "moe_gather_qmm": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _P, _P, _I, _I, _P, _P, _SZ,
                                       _P]),
     "gather_qmm": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _P, _I, _I, _P, _P, _SZ, _P]),
@@ -263,6 +265,28 @@ def moe_expert_forward(layer: MoELayer, x: torch.Tensor, idx: torch.Tensor, w: t
                                     k, _ptr(residual), _ptr(y), _ptr(ws), ws.numel(),
                                     _stream(stream)), "moe_expert_forward")
     return y
+
+
+def moe_forward(layer: MoELayer, x: torch.Tensor, k: int, renorm: bool = True,
+                residual: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                y: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                w: Optional[torch.Tensor] = None, stream=None):
+    """Router + top-K + experts (one launch for an 8-bit router and M <= 4).
+    Returns (y, idx, w)."""
+    m = x.shape[0]
+    dev = x.device
+    if ws is None:
+        ws = workspace(layer, m, k, PATH_FORWARD, dev)
+    if y is None:
+        y = torch.empty((m, layer.hidden), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((m, k), dtype=torch.float32, device=dev)
+    _check(lib().moe_forward(ctypes.byref(layer.struct()), _ptr(x), m, k, int(bool(renorm)),
+                             _ptr(residual), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws), ws.numel(),
+                             _stream(stream)), "moe_forward")
+    return y, idx, w
 
 
 def moe_gather_qmm(layer: MoELayer, x_bf16: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,

@@ -139,6 +139,25 @@ def test_layer_validation():
     assert g(ctypes.byref(_layer(shared=True)), FAKE, FAKE, FAKE, 4, 2, FAKE, FAKE, 1 << 30, None) == -9
 
 
+def test_forward_validation():
+    f = moeq.lib().moe_forward
+
+    def call(L, M=1, K=2, ws=1 << 30, **kw):
+        a = dict(x=FAKE, res=None, y=FAKE, idx=FAKE, w=FAKE, wsp=FAKE)
+        a.update(kw)
+        return f(ctypes.byref(L), a["x"], M, K, 1, a["res"], a["y"], a["idx"], a["w"], a["wsp"], ws, None)
+
+    assert call(_layer(router=_qt(8, 1, 16, 256))) == -5       # router rows != E
+    assert call(_layer(router=_qt(8, 1, 8, 512))) == -5        # router cols != H
+    assert call(_layer(router=_qt(8, 1, 8, 256, q=0))) == -1
+    assert call(_layer(), K=9) == -5
+    assert call(_layer(), idx=0) == -1
+    assert call(_layer(), w=FAKE + 4) == -7
+    assert call(_layer(), ws=16) == -8
+    assert call(_layer(), M=0) == 0
+    assert moeq.lib().moe_workspace_size(ctypes.byref(_layer()), 1, 2, moeq.PATH_FORWARD) > 0
+
+
 def test_workspace_sizes():
     L = _layer()
     ws = moeq.lib().moe_workspace_size
