@@ -307,7 +307,11 @@ def run_decode(args, cfg):
                 evs[k][1].record(s_)
             k += 1
     torch.cuda.synchronize()
-    launch_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    eager_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    # one launch per layer: every node of the timed graphs is the kernel, so
+    # its average duration is the timed region over (steps x layers); else
+    # the eager, event-bracketed expert launches
+    launch_us = ms * 1e3 / n_layers if one_launch else eager_us
     lbytes = (layer_bytes(cfg, touched) + m * K * 8) if one_launch else expert_launch_bytes(cfg, touched)
     achieved = lbytes / (launch_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
@@ -315,7 +319,8 @@ def run_decode(args, cfg):
                 "traffic": traffic_for(args, "k_moe_decode"),
                 "kernel": "k_moe_decode (moe_forward: router + top-K + experts)" if one_launch
                           else "k_moe_decode (moe_expert_forward)",
-                "launch_us": round(launch_us, 2), "bytes_per_launch": int(lbytes)}
+                "launch_us": round(launch_us, 2), "eager_launch_us": round(eager_us, 2),
+                "bytes_per_launch": int(lbytes)}
 
     out = {
         "metric": METRIC, "value": round(m * 1e3 / ms, 2), "unit": "tokens/s", "n_gpus": 1,
@@ -403,7 +408,22 @@ def main():
     ap.add_argument("--cpu-layers", type=int, default=0)
     ap.add_argument("--traffic", type=float, default=None,
                     help="HBM bytes per launch from rocprofv3 counters, if taken")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 5 device copies of MIB MiB (the reference kernel that "
+                         "scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        import torch
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "copy_calibration_bytes_written": n * 4,
+                          "copies": 5}), flush=True)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:

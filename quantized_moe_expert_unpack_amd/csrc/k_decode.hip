@@ -381,28 +381,48 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
     rb[j] = bf16_to_f32(rsb[j] >> 16);
   }
   __syncthreads();
-  for (int m = 0; m < M; ++m) {
-    // the lane's chunks as independent fp64 chains, elements in order
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 1
-    for (int f = 0; f < 4; ++f) {     // rolled: keeps the fp64 operands out of registers
+  // per lane and token, its chunks as independent fp64 chains, elements in
+  // order; a weight is dequantized once for all tokens; one chunk at a time
+  // (the scheduling barrier keeps the compiler from hoisting every chunk's
+  // fp64 operands at once)
+  double acc[kFusedMaxM][4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int c = lane + kWave * j;
-        if (row_ok && c < nch) {
-          const float4 xv = xl[m * (H / 4) + f * nch + c];
-          acc[j] = fma((double)fmaf(rs[j], (float)chunk_code<8>(rv[j], 4 * f + 0), rb[j]), (double)xv.x, acc[j]);
-          acc[j] = fma((double)fmaf(rs[j], (float)chunk_code<8>(rv[j], 4 * f + 1), rb[j]), (double)xv.y, acc[j]);
-          acc[j] = fma((double)fmaf(rs[j], (float)chunk_code<8>(rv[j], 4 * f + 2), rb[j]), (double)xv.z, acc[j]);
-          acc[j] = fma((double)fmaf(rs[j], (float)chunk_code<8>(rv[j], 4 * f + 3), rb[j]), (double)xv.w, acc[j]);
+  for (int m = 0; m < kFusedMaxM; ++m)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[m][j] = 0.0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = lane + kWave * j;
+    if (row_ok && c < nch) {
+      const uint32_t wd[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        double w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) w[q] = (double)fmaf(rs[j], (float)((wd[f] >> (8 * q)) & 0xFFu), rb[j]);
+#pragma unroll
+        for (int m = 0; m < kFusedMaxM; ++m) {
+          if (m < M) {
+            const float4 xv = xl[m * (H / 4) + f * nch + c];
+            acc[m][j] = fma(w[0], (double)xv.x, acc[m][j]);
+            acc[m][j] = fma(w[1], (double)xv.y, acc[m][j]);
+            acc[m][j] = fma(w[2], (double)xv.z, acc[m][j]);
+            acc[m][j] = fma(w[3], (double)xv.w, acc[m][j]);
+          }
         }
       }
     }
-    const double tot = wave_sum_d((acc[0] + acc[1]) + (acc[2] + acc[3]));
-    // published as the complement of its bits: zero means "not written yet"
-    // (the complement of a finite double is never zero)
-    if (lane == 0 && row_ok)
-      st_coh_u64(P.logits + (size_t)m * E + e, ~(uint64_t)__double_as_longlong(tot));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int m = 0; m < kFusedMaxM; ++m) {
+    if (m < M) {
+      const double tot = wave_sum_d((acc[m][0] + acc[m][1]) + (acc[m][2] + acc[m][3]));
+      // published as the complement of its bits: zero means "not written yet"
+      // (the complement of a finite double is never zero)
+      if (lane == 0 && row_ok)
+        st_coh_u64(P.logits + (size_t)m * E + e, ~(uint64_t)__double_as_longlong(tot));
+    }
   }
   // the last R unit selects: it polls every logit (no counter round trips),
   // clears them for the next launch, and runs the top-K of each token
