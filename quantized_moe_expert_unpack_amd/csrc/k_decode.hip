@@ -53,7 +53,7 @@ constexpr int kThreads = 512;              // every unit is 8 waves
 constexpr int kWaves = kThreads / kWave;
 constexpr int kGRows = 16;                 // intermediate rows per G unit (two per wave)
 constexpr int kDRows = kWaves;             // output rows per D unit (one per wave)
-constexpr int kRRows = kWaves;             // router rows per R unit (one per wave)
+constexpr int kRRows = kWaves / 2;         // router rows per R unit (two waves per row)
 constexpr int kSpinLimit = 1 << 26;
 constexpr int kLine = kLineInts;
 constexpr int kRep = 64;      // copies of every flag that many units poll
@@ -272,19 +272,77 @@ __device__ __forceinline__ int tindex(int lane) {
 
 
 // ------------------------------------------------------------------ R unit
+// 64-bit maximum across the wave, left in every lane (exchange steps as in
+// wave_sum_d; the maximum is indifferent to the mirrors' lane order)
+template <int M>
+__device__ __forceinline__ uint64_t xmax_u64(uint64_t v) {
+  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  if constexpr (M >= 16) {
+    const auto rl = M == 32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
+                            : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
+    const auto rh = M == 32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
+                            : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
+    const uint64_t a = ((uint64_t)rh[0] << 32) | rl[0];
+    const uint64_t b = ((uint64_t)rh[1] << 32) | rl[1];
+    return a > b ? a : b;
+  } else {
+    constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : M == 4 ? 0x141 : 0x140;
+    lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, ctrl, 0xF, 0xF, false);
+    hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, ctrl, 0xF, 0xF, false);
+    const uint64_t w = ((uint64_t)hi << 32) | lo;
+    return v > w ? v : w;
+  }
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = xmax_u64<32>(v);
+  v = xmax_u64<16>(v);
+  v = xmax_u64<8>(v);
+  v = xmax_u64<4>(v);
+  v = xmax_u64<2>(v);
+  return xmax_u64<1>(v);
+}
+
+// top-K of at most 64*PER keys by one wave, keys held in registers: K rounds
+// of a wave maximum, the owner of each winner dropping it (keys are unique)
+template <int PER>
+__device__ __forceinline__ void wave_topk(const uint64_t* keys, int E, int K, int lane, int* sel) {
+  uint64_t kk[PER];
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int e = lane + kWave * i;
+    kk[i] = e < E ? keys[e] : 0ull;      // 0 is below every key
+  }
+  for (int r = 0; r < K; ++r) {
+    uint64_t mx = kk[0];
+#pragma unroll
+    for (int i = 1; i < PER; ++i) mx = kk[i] > mx ? kk[i] : mx;
+    mx = wave_max_u64(mx);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) kk[i] = kk[i] == mx ? 0ull : kk[i];
+    if (lane == 0) sel[r] = 1023 - (int)(mx & 0x3FFull);
+  }
+}
+
 // top-K of token m from keys/vals in LDS (E <= 1024), all threads of the
 // block: selection by rank as in topk.h, candidates ranked by four threads
 // each; publishes the weights into every route-line copy, drains, then the
 // indices, and writes the caller's outputs.
+// WIDE: allow the one-wave selection up to 512 experts (16 more registers)
+template <bool WIDE>
 __device__ __forceinline__ void route_select(const uint64_t* keys, const double* vals, int E,
                                              int K, int renorm, const DecPlan& P, const RouteIn& R,
-                                             int m) {
+                                             int m, int par) {
   __shared__ uint64_t cand[kWaves * kMaxTopK];
   __shared__ int sel[kMaxTopK];
   __shared__ double ex[kMaxTopK];
   __shared__ double red[kWaves];
   __shared__ double s_tot;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  if (E <= 2 * kWave) {                  // up to 128 experts: one wave, keys in registers
+    if (wid == 0) wave_topk<2>(keys, E, K, lane, sel);
+  } else if (WIDE && E <= 8 * kWave) {   // up to 512
+    if (wid == 0) wave_topk<8>(keys, E, K, lane, sel);
+  } else {
   const int nc = kWaves * K;             // candidate slots, K per wave
   if (tid < nc) cand[tid] = 0ull;        // 0 is below every key
   __syncthreads();
@@ -311,6 +369,7 @@ __device__ __forceinline__ void route_select(const uint64_t* keys, const double*
     rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, false);
     rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, false);
     if (part == 0 && c < nc && kc != 0ull && rank < K) sel[rank] = 1023 - (int)(kc & 0x3FFull);
+  }
   }
   __syncthreads();
   // 3) weights in fp64: p[idx] / sum p[idx] (renorm, summed in slot order) or
@@ -340,30 +399,37 @@ __device__ __forceinline__ void route_select(const uint64_t* keys, const double*
       R.idx_out[(size_t)m * K + k] = sel[k];
       R.w_out[(size_t)m * K + k] = w;
     }
-    st_coh_u64(route_line(P, rep, m) + k, ((uint64_t)(sel[k] + 1) << 32) | __float_as_uint(w));
+    const uint32_t hi = ((uint32_t)par << 31) | (uint32_t)(sel[k] + 1);
+    st_coh_u64(route_line(P, rep, m) + k, ((uint64_t)hi << 32) | __float_as_uint(w));
   }
 }
 
 // Router rows (8-bit) against x for all M tokens in fp64: the fp32
 // dequantized weight widened exactly, fp64 products and sums, as the oracle
 // defines the logits.  The R unit completing the arrivals selects.
+template <bool WIDE>
 __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P, const RouteIn R,
                                            const float* __restrict__ x, int u) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int E = L.E, H = L.H, M = P.M, K = P.K;
-  const int e = u * kRRows + wid;
+  // two waves per row: wave half h takes the row's chunks lane + 64 (2j + h)
+  const int e = u * kRRows + wid / 2, h = wid & 1;
   const int nch = H / 16;                 // 16 codes per chunk at 8 bits
   const int gpr = H / kGroup;
   const bool row_ok = e < E;
+  __shared__ double part[kFusedMaxM][kRRows];
   // Loads use clamped, always valid addresses and no branches, so they all
   // issue back to back; lanes past the row's end are never used.
   const int er = min(e, E - 1);
-  uint4 rv[4];
-  uint32_t rsb[4];
+  // the selector's epoch word (its parity picks the launch's h buffer), read
+  // now so the load overlaps the router rows
+  const int epoch = u == P.r_units - 1 ? ld_coh_i(P.epoch) : 0;
+  uint4 rv[2];
+  uint32_t rsb[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = min(lane + kWave * j, nch - 1);
+  for (int j = 0; j < 2; ++j) {
+    const int c = min(lane + kWave * (2 * j + h), nch - 1);
     rv[j] = reinterpret_cast<const uint4*>(R.W.q + (size_t)er * (H / 4))[c];
     rsb[j] = (uint32_t)R.W.scales[(size_t)er * gpr + c / 4] |
              ((uint32_t)R.W.biases[(size_t)er * gpr + c / 4] << 16);
@@ -374,9 +440,9 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
     const int m = i / (H / 4), ii = i - m * (H / 4);
     xl[m * (H / 4) + (ii % 4) * nch + ii / 4] = reinterpret_cast<const float4*>(x)[i];
   }
-  float rs[4], rb[4];
+  float rs[2], rb[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < 2; ++j) {
     rs[j] = bf16_to_f32(rsb[j] & 0xFFFFu);
     rb[j] = bf16_to_f32(rsb[j] >> 16);
   }
@@ -385,14 +451,14 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
   // order; a weight is dequantized once for all tokens; one chunk at a time
   // (the scheduling barrier keeps the compiler from hoisting every chunk's
   // fp64 operands at once)
-  double acc[kFusedMaxM][4];
+  double acc[kFusedMaxM][2];
 #pragma unroll
   for (int m = 0; m < kFusedMaxM; ++m)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[m][j] = 0.0;
+    for (int j = 0; j < 2; ++j) acc[m][j] = 0.0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = lane + kWave * j;
+  for (int j = 0; j < 2; ++j) {
+    const int c = lane + kWave * (2 * j + h);
     if (row_ok && c < nch) {
       const uint32_t wd[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
 #pragma unroll
@@ -414,14 +480,24 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
     }
     __builtin_amdgcn_sched_barrier(0);
   }
+  // the two halves of a row meet in LDS; the even wave publishes the logit
+  double wsum[kFusedMaxM];
 #pragma unroll
   for (int m = 0; m < kFusedMaxM; ++m) {
+    wsum[m] = 0.0;
     if (m < M) {
-      const double tot = wave_sum_d((acc[m][0] + acc[m][1]) + (acc[m][2] + acc[m][3]));
+      wsum[m] = wave_sum_d(acc[m][0] + acc[m][1]);
+      if (h == 1 && lane == 0) part[m][wid / 2] = wsum[m];
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int m = 0; m < kFusedMaxM; ++m) {
+    if (m < M && h == 0 && lane == 0 && row_ok) {
+      const double tot = wsum[m] + part[m][wid / 2];
       // published as the complement of its bits: zero means "not written yet"
       // (the complement of a finite double is never zero)
-      if (lane == 0 && row_ok)
-        st_coh_u64(P.logits + (size_t)m * E + e, ~(uint64_t)__double_as_longlong(tot));
+      st_coh_u64(P.logits + (size_t)m * E + e, ~(uint64_t)__double_as_longlong(tot));
     }
   }
   // the last R unit selects: it polls every logit (no counter round trips),
@@ -429,6 +505,7 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
   if (u != P.r_units - 1) return;
   uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
   double* vals = reinterpret_cast<double*>(keys + E);
+  // (the selector is the only reader and writer of the epoch word)
   __syncthreads();                       // x in LDS is no longer read
   for (int m = 0; m < M; ++m) {
     for (int ee = tid; ee < E; ee += kThreads) {
@@ -445,9 +522,10 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
       keys[ee] = route_key(lg, ee);
     }
     __syncthreads();
-    route_select(keys, vals, E, K, R.renorm, P, R, m);
+    route_select<WIDE>(keys, vals, E, K, R.renorm, P, R, m, epoch & 1);
     __syncthreads();
   }
+  if (tid == 0) st_coh_i(P.epoch, epoch + 1);
 }
 
 // ------------------------------------------------------------------ G unit
@@ -458,7 +536,7 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
                                              const float* __restrict__ x,
                                              const int32_t* __restrict__ idx, int u) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  __shared__ int s_e;
+  __shared__ int s_e, s_par, s_done;
   constexpr int kCpc = 128 / BITS;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int S = P.S, K = P.K, H = L.H;
@@ -503,7 +581,10 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
     chunk_sums<kCpc>(x4, xsum, nch);
     if (wid == 0 && !shared) {
       const uint64_t v = wave_wait_nonzero(route_line(P, u % kRep, t) + k, 1, lane, P.ctr);
-      if (lane == 0) s_e = (int)(v >> 32) - 1;
+      if (lane == 0) {
+        s_e = (int)((v >> 32) & 0x7FFFFFFFu) - 1;
+        s_par = (int)(v >> 63);
+      }
     }
     __syncthreads();
     if (!shared) erow = (size_t)min(max(s_e, 0), L.E - 1) * L.I;
@@ -539,6 +620,12 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
       wu[rr][j] = u4[c];
     }
   }
+  // done with the route words: count this reader (the last one clears
+  // them); the counter round trips overlap the loads just issued
+  bool last_reader = false;
+  if (FUSED && !shared && tid == 0)
+    last_reader = arrive(P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines) + (1 + kFan) * kLine, r,
+                         upt + P.nc);
   if constexpr (!FUSED) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -575,11 +662,32 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
   }
   const float gsum = treduce<2, 32>(pg, lane);
   const float usum = treduce<2, 32>(pu, lane);
+  if constexpr (FUSED) {
+    if (shared) {
+      // the shared expert does not wait for routing; it learns the launch's
+      // parity from the route words now, and counts itself as their reader
+      if (wid == 0) {
+        const uint64_t v = wave_wait_nonzero(route_line(P, u % kRep, t), 1, lane, P.ctr);
+        if (lane == 0) {
+          s_par = (int)(v >> 63);
+          s_done = arrive(P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines) + (1 + kFan) * kLine, r,
+                          upt + P.nc);
+        }
+      }
+      __syncthreads();
+    }
+  }
   if ((lane & 31) < kHCopies) {         // every lane of a half holds its row's sum
     const int i = wid * 2 + tindex<2, 32>(lane);
-    if (i < nrows)
-      st_coh(P.h + (size_t)(lane & 31) * P.P * P.Imax + (size_t)p * P.Imax + i_base + i,
-             valid ? silu(gsum) * usum : __builtin_nanf(""));
+    const float hv = valid ? silu(gsum) * usum : __builtin_nanf("");
+    if (i < nrows) {
+      const size_t at = (size_t)(lane & 31) * P.P * P.Imax + (size_t)p * P.Imax + i_base + i;
+      if constexpr (FUSED)   // complemented bits: 0 means "not written in this launch"
+        st_coh_i(reinterpret_cast<int*>(P.hb) + (size_t)s_par * kHCopies * P.P * P.Imax + at,
+                 (int)~__float_as_uint(hv));
+      else
+        st_coh(P.h + at, hv);
+    }
   }
   if (shared && g == 0 && wid == 0) {
     // the shared_expert_gate logit of token t (one row of H, its own bits)
@@ -602,14 +710,27 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
       a = fmaf(bf16_to_f32(L.sh_eg.scales[gg]), d, fmaf(bf16_to_f32(L.sh_eg.biases[gg]), xsm, a));
     }
     a = wave_sum(a);
-    if (lane == 0) st_coh(P.sg + t, a);
+    if (lane == 0) {
+      if constexpr (FUSED)
+        st_coh_i(reinterpret_cast<int*>(P.sgb) + s_par * P.M + t, (int)~__float_as_uint(a));
+      else
+        st_coh(P.sg + t, a);
+    }
   }
-  drain();
-  __syncthreads();
-  __shared__ int s_done;
-  if (tid == 0) s_done = arrive(P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines), r, upt);
-  __syncthreads();
-  if (s_done && tid < kRep) st_coh_i(ready_line(P, tid, t), 1);
+  if constexpr (FUSED) {
+    // h goes out with its own "written" marks, so there is nothing to
+    // announce; the last reader of the route words clears them
+    if (!shared && tid == 0) s_done = last_reader;
+    __syncthreads();
+    if (s_done)
+      for (int i = tid; i < kRep * K; i += kThreads) st_coh_u64(route_line(P, i / K, t) + i % K, 0);
+  } else {
+    drain();
+    __syncthreads();
+    if (tid == 0) s_done = arrive(P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines), r, upt);
+    __syncthreads();
+    if (s_done && tid < kRep) st_coh_i(ready_line(P, tid, t), 1);
+  }
 }
 
 // ------------------------------------------------------------------ D unit
@@ -624,7 +745,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float wk[kMaxTopK + 1];
   __shared__ int s_ex[kMaxTopK];
-  __shared__ int bad;
+  __shared__ int bad, s_par, s_done;
   constexpr int kCpc = 128 / BITS;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int K = P.K, H = L.H;
@@ -639,18 +760,18 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
   const int tot = K * cpr + cps;               // chunks per output row, all slots
   int* tl = P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines);
   // slot and chunk of every chunk position of the lane (q = lane + 64 j)
-  int kq[DCH], cq[DCH];
+  // (packed in one register: (slot + 1) << 16 | chunk; slot -1 = no chunk)
+  int kc[DCH];
 #pragma unroll
   for (int j = 0; j < DCH; ++j) {
     const int q = lane + kWave * j;
-    kq[j] = -1;
-    cq[j] = 0;
+    kc[j] = 0;
     if (q < tot) {
       const int k = q < K * cpr ? q / cpr : K;
-      kq[j] = k;
-      cq[j] = k < K ? q - k * cpr : q - K * cpr;
+      kc[j] = ((k + 1) << 16) | (k < K ? q - k * cpr : q - K * cpr);
     }
   }
+
   if (tid == 0) bad = 0;
   if constexpr (!FUSED) {
     __syncthreads();
@@ -666,12 +787,23 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     if (wid == 0) {
       const uint64_t v = wave_wait_nonzero(route_line(P, d % kRep, t), K, lane, P.ctr);
       if (lane < K) {
-        s_ex[lane] = min(max((int)(v >> 32) - 1, 0), L.E - 1);
+        s_ex[lane] = min(max((int)((v >> 32) & 0x7FFFFFFFu) - 1, 0), L.E - 1);
         wk[lane] = __uint_as_float((uint32_t)v);
       }
+      if (lane == 0) s_par = (int)(v >> 63);
     }
   }
   __syncthreads();
+  if constexpr (FUSED) {
+    // clear this unit's share of the other parity's h and shared-gate
+    // buffers: the previous launch used them, the next one fills them
+    const size_t nh4 = (size_t)kHCopies * P.P * P.Imax / 4;
+    const size_t per = (nh4 + (size_t)P.M * P.nc - 1) / ((size_t)P.M * P.nc);
+    uint4* hz = reinterpret_cast<uint4*>(P.hb + (size_t)(s_par ^ 1) * kHCopies * P.P * P.Imax);
+    for (size_t i = (size_t)d * per + tid; i < min(nh4, (size_t)(d + 1) * per); i += kThreads)
+      hz[i] = make_uint4(0, 0, 0, 0);
+    if (c == 0 && tid == 0) P.sgb[(s_par ^ 1) * P.M + t] = 0u;
+  }
   // scales and biases of every slot (per slot kDRows rows x groups bf16,
   // contiguous), then the routed chunks
   const int gr = I / kGroup, gs = L.has_shared ? Is / kGroup : 0;
@@ -696,12 +828,79 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
   const int rlc = min(rl, nrows - 1);
 #pragma unroll
   for (int j = 0; j < DCH; ++j) {
-    const bool sh = kq[j] == K;
+    const int kj = (kc[j] >> 16) - 1, cj = kc[j] & 0xFFFF;
+    const bool sh = kj == K;
     const uint32_t* base = sh ? L.sh_down.q
-                              : L.down.q + ((size_t)s_ex[max(kq[j], 0)] * H) * (I / (32 / BITS));
+                              : L.down.q + ((size_t)s_ex[max(kj, 0)] * H) * (I / (32 / BITS));
     const int wpr = (sh ? Is : I) / (32 / BITS);
-    wv[j] = reinterpret_cast<const uint4*>(base + (size_t)(r0 + rlc) * wpr)[cq[j]];
+    wv[j] = reinterpret_cast<const uint4*>(base + (size_t)(r0 + rlc) * wpr)[cj];
   }
+  // done with the route words: count this reader (the last one clears them);
+  // the last wave does it, after its loads are in flight
+  bool last_reader = false;
+  if (FUSED && tid == kThreads - kWave) {
+    const int upt = K * P.ng_routed + (L.has_shared ? P.ng_shared : 0);
+    last_reader = arrive(tl + (1 + kFan) * kLine, upt + c, upt + P.nc);
+  }
+  float* hs = smem;                            // [S][Imax]
+  float* hsum = hs + (size_t)P.S * P.Imax;     // [S][Imax/kCpc]
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(hsum + (size_t)P.S * P.Imax / 16);
+  if constexpr (FUSED) {
+    // h arrives element by element with its "written" marks: once this
+    // unit's own loads are in, poll the token's h (copy d % kHCopies of the
+    // launch's buffer) until every element of every slot is there
+    drain();
+    if (tid < n_sb) reinterpret_cast<uint4*>(sbl)[tid] = sbr;
+    if (wid == 0 && L.has_shared && lane == K) {
+      const uint32_t* sgp = P.sgb + s_par * P.M + t;
+      uint32_t v = 0;
+      for (int i = 0; i < kSpinLimit && v == 0; ++i) {
+        v = (uint32_t)ld_coh_i(reinterpret_cast<const int*>(sgp));
+        if (v == 0) __builtin_amdgcn_s_sleep(8);
+      }
+      if (v == 0) atomicOr(P.ctr, 8);
+      wk[K] = 1.0f / (1.0f + __expf(-__uint_as_float(~v)));
+    }
+    const uint64_t* h2 = reinterpret_cast<const uint64_t*>(P.hb) +
+                         ((size_t)s_par * kHCopies * P.P * P.Imax + (size_t)(d % kHCopies) * P.P * P.Imax +
+                          (size_t)t * P.S * P.Imax) / 2;
+    const int n2 = P.S * P.Imax / 2;
+    constexpr int kB = 6;
+    for (int b0 = 0; b0 < n2; b0 += kThreads * kB) {
+      uint32_t need = 0;                       // bit j: item j of this batch still missing
+#pragma unroll
+      for (int j = 0; j < kB; ++j) {
+        const int i = b0 + tid + kThreads * j;
+        if (i < n2) {
+          const int k = (2 * i) / P.Imax;
+          const int e = 2 * i - k * P.Imax;
+          if (e < (k == K ? Is : I)) need |= 1u << j;
+        }
+      }
+      for (int spin = 0; need && spin < kSpinLimit; ++spin) {
+        uint64_t rg[kB];
+#pragma unroll
+        for (int j = 0; j < kB; ++j)
+          rg[j] = (need >> j) & 1u ? ld_coh64(h2 + min(b0 + tid + kThreads * j, n2 - 1)) : 0ull;
+#pragma unroll
+        for (int j = 0; j < kB; ++j) {
+          const uint32_t lo = (uint32_t)rg[j], hi = (uint32_t)(rg[j] >> 32);
+          if (((need >> j) & 1u) && lo != 0u && hi != 0u) {
+            const int i = b0 + tid + kThreads * j;
+            const int k = (2 * i) / P.Imax;
+            const int e = 2 * i - k * P.Imax;
+            const int nk = (k == K ? Is : I) / kCpc;
+            float* dst = hs + (size_t)k * P.Imax + 4 * ilv<kCpc>(e / 4, nk) + e % 4;
+            dst[0] = __uint_as_float(~lo);
+            dst[1] = __uint_as_float(~hi);
+            need &= ~(1u << j);
+          }
+        }
+        if (need) __builtin_amdgcn_s_sleep(8);
+      }
+      if (need) atomicOr(P.ctr, 8);
+    }
+  } else {
   // wait for token t's h (and the routing weights, the shared gate)
   if (wid == 0) {
     if (lane == 0 && !wait_flag(ready_line(P, d % kRep, t))) atomicOr(P.ctr, 1);
@@ -709,13 +908,9 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     if (L.has_shared && lane == K) wk[K] = 1.0f / (1.0f + __expf(-ld_coh(P.sg + t)));
   }
   __syncthreads();
-  // this unit is done with the token's flags and route words: count it; the
-  // last unit of the token clears them for the next launch (below)
-  __shared__ int s_done;
+  // this unit is done with the token's flags: count it; the last unit of
+  // the token lowers them for the next launch (below)
   if (tid == 0) s_done = arrive(tl + (1 + kFan) * kLine, c, P.nc);
-  float* hs = smem;                            // [S][Imax]
-  float* hsum = hs + (size_t)P.S * P.Imax;     // [S][Imax/kCpc]
-  uint16_t* sbl = reinterpret_cast<uint16_t*>(hsum + (size_t)P.S * P.Imax / 16);
   if (tid < n_sb) reinterpret_cast<uint4*>(sbl)[tid] = sbr;
   {
     // all coherent loads of a batch in flight before any is consumed
@@ -745,11 +940,15 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
       }
     }
   }
+  }
+  if (FUSED && tid == kThreads - kWave) s_done = last_reader;
   __syncthreads();
   if (s_done) {
-    if (tid < kRep) st_coh_i(ready_line(P, tid, t), 0);
-    if constexpr (FUSED)
+    if constexpr (FUSED) {
       for (int i = tid; i < kRep * K; i += kThreads) st_coh_u64(route_line(P, i / K, t) + i % K, 0);
+    } else {
+      if (tid < kRep) st_coh_i(ready_line(P, tid, t), 0);
+    }
   }
   // chunk sums of every slot, one (slot, chunk) pair per thread
   for (int q = tid; q < tot; q += kThreads) {
@@ -772,17 +971,17 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < DCH; ++j) {
-      const int k = kq[j];
+      const int k = (kc[j] >> 16) - 1, cj = kc[j] & 0xFFFF;
       if (k >= 0 && rl < nrows) {
         const bool sh = k == K;
         const int Ik = sh ? Is : I;
         const int gpr = Ik / kGroup;
         const float4* hk = reinterpret_cast<const float4*>(hs + (size_t)k * P.Imax);
-        const float dd = chunk_dot<BITS>(wv[j], hk + cq[j], Ik / kCpc);
-        const int gi = (sh ? K * kDRows * gr : k * kDRows * gr) + rl * gpr + (cq[j] * kCpc) / kGroup;
+        const float dd = chunk_dot<BITS>(wv[j], hk + cj, Ik / kCpc);
+        const int gi = (sh ? K * kDRows * gr : k * kDRows * gr) + rl * gpr + (cj * kCpc) / kGroup;
         const int boff = K * kDRows * gr + kDRows * gs;    // biases follow all scales
         const float part = fmaf(bf16_to_f32(sbl[gi]), dd,
-                                bf16_to_f32(sbl[boff + gi]) * hsum[(size_t)k * (P.Imax / kCpc) + cq[j]]);
+                                bf16_to_f32(sbl[boff + gi]) * hsum[(size_t)k * (P.Imax / kCpc) + cj]);
         acc = fmaf(wk[k], part, acc);
       }
     }
@@ -809,7 +1008,7 @@ __global__ void __launch_bounds__(kThreads)
   int u = blockIdx.x;
   if constexpr (FUSED) {
     if (u < P.r_units) {
-      route_unit(L, P, R, x, u);
+      route_unit<!(BITS == 8 && CPL <= 2 && DCH <= 6)>(L, P, R, x, u);
       return;
     }
     u -= P.r_units;
@@ -842,6 +1041,9 @@ static DecPlan make_dec_plan(const DecodeLayer& L, int M, int K, bool routed, vo
   P.h = reinterpret_cast<float*>(take(sizeof(float) * kHCopies * (size_t)P.P * P.Imax));
   P.sg = reinterpret_cast<float*>(take(sizeof(float) * (size_t)M));
   if (routed) {
+    P.epoch = reinterpret_cast<int*>(take(sizeof(int)));
+    P.hb = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 2 * kHCopies * (size_t)P.P * P.Imax));
+    P.sgb = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 2 * (size_t)M));
     P.logits = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)M * L.E));
     P.idx_c = reinterpret_cast<int32_t*>(take(sizeof(int) * (size_t)kRep * P.rstride));
   }

@@ -36,6 +36,9 @@ struct DecPlan {
   float* h;        // [P][Imax] (pair p = token * S + slot)
   float* sg;       // [M]
   uint64_t* logits;  // [M][E] router logits as complemented fp64 bits, 0 = not written
+  int* epoch;        // launch counter (routing in the launch): its parity picks the h buffer
+  uint32_t* hb;      // [2][copies][P][Imax] h as complemented fp32 bits, 0 = not written
+  uint32_t* sgb;     // [2][M] shared-gate logits, the same way
   int32_t* idx_c;  // route lines: copies [kRep] of M lines (64-bit expert + 1 | weight words)
 };
 
