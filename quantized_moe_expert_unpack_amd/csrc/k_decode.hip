@@ -794,16 +794,6 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     }
   }
   __syncthreads();
-  if constexpr (FUSED) {
-    // clear this unit's share of the other parity's h and shared-gate
-    // buffers: the previous launch used them, the next one fills them
-    const size_t nh4 = (size_t)kHCopies * P.P * P.Imax / 4;
-    const size_t per = (nh4 + (size_t)P.M * P.nc - 1) / ((size_t)P.M * P.nc);
-    uint4* hz = reinterpret_cast<uint4*>(P.hb + (size_t)(s_par ^ 1) * kHCopies * P.P * P.Imax);
-    for (size_t i = (size_t)d * per + tid; i < min(nh4, (size_t)(d + 1) * per); i += kThreads)
-      hz[i] = make_uint4(0, 0, 0, 0);
-    if (c == 0 && tid == 0) P.sgb[(s_par ^ 1) * P.M + t] = 0u;
-  }
   // scales and biases of every slot (per slot kDRows rows x groups bf16,
   // contiguous), then the routed chunks
   const int gr = I / kGroup, gs = L.has_shared ? Is / kGroup : 0;
@@ -992,6 +982,17 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     float v = bad ? __builtin_nanf("") : tsum;
     if (residual) v += residual[(size_t)t * H + r0 + rl];
     y[(size_t)t * H + r0 + rl] = v;
+  }
+  if constexpr (FUSED) {
+    // clear this unit's share of the other parity's h and shared-gate
+    // buffers: the previous launch used them, the next one fills them (off the
+    // critical path, at the end)
+    const size_t nh4 = (size_t)kHCopies * P.P * P.Imax / 4;
+    const size_t per = (nh4 + (size_t)P.M * P.nc - 1) / ((size_t)P.M * P.nc);
+    uint4* hz = reinterpret_cast<uint4*>(P.hb + (size_t)(s_par ^ 1) * kHCopies * P.P * P.Imax);
+    for (size_t i = (size_t)d * per + tid; i < min(nh4, (size_t)(d + 1) * per); i += kThreads)
+      hz[i] = make_uint4(0, 0, 0, 0);
+    if (c == 0 && tid == 0) P.sgb[(s_par ^ 1) * P.M + t] = 0u;
   }
 }
 
