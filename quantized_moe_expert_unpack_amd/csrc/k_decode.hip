@@ -59,7 +59,7 @@ constexpr int kLine = kLineInts;
 constexpr int kRep = 64;      // copies of every flag that many units poll
 // per token: G arrival counter lines, D arrival counter lines
 constexpr int kCtrLines = 2 * (1 + kFan);
-constexpr int kHCopies = 8;   // copies of h (D unit d reads copy d % kHCopies): spreads the
+constexpr int kHCopies = 8;   // copies of h (one per XCD; the down units read their XCD's): spreads the
                               // reads of all D units of a token over more memory channels
 
 // ---- coherent (agent-scope) loads/stores for data crossing blocks ----------
@@ -338,8 +338,15 @@ __device__ __forceinline__ void route_select(const uint64_t* keys, const double*
   __shared__ double red[kWaves];
   __shared__ double s_tot;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  if (E <= 2 * kWave) {                  // up to 128 experts: one wave, keys in registers
-    if (wid == 0) wave_topk<2>(keys, E, K, lane, sel);
+  if (E <= kThreads / 4) {               // up to 128 experts: rank every key, one quad per key
+    const int a = tid >> 2, part = tid & 3;
+    const uint64_t ka = a < E ? keys[a] : 0ull;
+    int rank = 0;
+#pragma unroll 8
+    for (int j = part; j < E; j += 4) rank += keys[j] > ka;
+    rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, false);
+    rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, false);
+    if (part == 0 && a < E && rank < K) sel[rank] = a;
   } else if (WIDE && E <= 8 * kWave) {   // up to 512
     if (wid == 0) wave_topk<8>(keys, E, K, lane, sel);
   } else {
@@ -837,8 +844,9 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
   uint16_t* sbl = reinterpret_cast<uint16_t*>(hsum + (size_t)P.S * P.Imax / 16);
   if constexpr (FUSED) {
     // h arrives element by element with its "written" marks: once this
-    // unit's own loads are in, poll the token's h (copy d % kHCopies of the
-    // launch's buffer) until every element of every slot is there
+    // unit's own loads are in, poll the token's h (copy blockIdx % kHCopies
+    // of the launch's buffer, one copy per XCD) until every element of every
+    // slot is there
     drain();
     if (tid < n_sb) reinterpret_cast<uint4*>(sbl)[tid] = sbr;
     if (wid == 0 && L.has_shared && lane == K) {
@@ -851,9 +859,39 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
       if (v == 0) atomicOr(P.ctr, 8);
       wk[K] = 1.0f / (1.0f + __expf(-__uint_as_float(~v)));
     }
-    const uint64_t* h2 = reinterpret_cast<const uint64_t*>(P.hb) +
-                         ((size_t)s_par * kHCopies * P.P * P.Imax + (size_t)(d % kHCopies) * P.P * P.Imax +
-                          (size_t)t * P.S * P.Imax) / 2;
+    // first wait, cheaply, for one marker word per gate/up unit (the first
+    // of its rows; wave 0 alone), so that the whole of h is loaded once it is
+    // almost surely complete: polling all of it would put one copy of h per
+    // poll round and down unit on the memory system while the weights stream
+    const uint32_t* hw = P.hb + (size_t)s_par * kHCopies * P.P * P.Imax +
+                         (size_t)(blockIdx.x % kHCopies) * P.P * P.Imax + (size_t)t * P.S * P.Imax;
+    if (wid == 0) {
+      const int nmk = K * P.ng_routed + P.ng_shared;
+      constexpr int kMk = 8;
+      for (int b0 = 0; b0 < nmk; b0 += kWave * kMk) {
+        uint32_t need = 0;
+#pragma unroll
+        for (int j = 0; j < kMk; ++j)
+          if (b0 + lane + kWave * j < nmk) need |= 1u << j;
+        for (int spin = 0; spin < kSpinLimit; ++spin) {
+          uint32_t v[kMk];
+#pragma unroll
+          for (int j = 0; j < kMk; ++j) {
+            const int q = min(b0 + lane + kWave * j, nmk - 1);
+            const int k = q < K * P.ng_routed ? q / P.ng_routed : K;
+            const int g = k < K ? q - k * P.ng_routed : q - K * P.ng_routed;
+            v[j] = (need >> j) & 1u ? (uint32_t)ld_coh_i(reinterpret_cast<const int*>(hw) + k * P.Imax + g * kGRows) : 0u;
+          }
+#pragma unroll
+          for (int j = 0; j < kMk; ++j)
+            if (v[j] != 0u) need &= ~(1u << j);
+          if (__all(need == 0u)) break;
+          __builtin_amdgcn_s_sleep(4);
+        }
+      }
+    }
+    __syncthreads();
+    const uint64_t* h2 = reinterpret_cast<const uint64_t*>(hw);
     const int n2 = P.S * P.Imax / 2;
     constexpr int kB = 6;
     for (int b0 = 0; b0 < n2; b0 += kThreads * kB) {
@@ -868,10 +906,19 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
         }
       }
       for (int spin = 0; need && spin < kSpinLimit; ++spin) {
+        // The first pass reads through the XCD's L2: every down unit that
+        // reads this copy of h runs on the same XCD (workgroups are dealt to
+        // the 8 XCDs round robin and the copy is picked by block index), so
+        // one of them fetches a line from memory and the rest hit L2.  A line cached in L2 is never older than this launch (the L2s
+        // are invalidated at kernel start) and values are only trusted when
+        // their "written" mark is set; anything still missing is re-read
+        // with coherent loads, which always go to memory.
         uint64_t rg[kB];
 #pragma unroll
-        for (int j = 0; j < kB; ++j)
-          rg[j] = (need >> j) & 1u ? ld_coh64(h2 + min(b0 + tid + kThreads * j, n2 - 1)) : 0ull;
+        for (int j = 0; j < kB; ++j) {
+          const uint64_t* a = h2 + min(b0 + tid + kThreads * j, n2 - 1);
+          rg[j] = (need >> j) & 1u ? (spin == 0 ? *a : ld_coh64(a)) : 0ull;
+        }
 #pragma unroll
         for (int j = 0; j < kB; ++j) {
           const uint32_t lo = (uint32_t)rg[j], hi = (uint32_t)(rg[j] >> 32);
