@@ -39,6 +39,7 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill) 
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 TOKEN_SLOTS = 64
+BATCH_MIN_M = 16     # moe_expert_forward groups pairs by expert from this many tokens
 
 
 def log(*a):
@@ -80,7 +81,8 @@ def expert_launch_bytes(cfg, touched: float) -> float:
 # --------------------------------------------------------------------------
 
 KERNEL_SOURCES = {
-    "k_moe_decode": ["k_decode.hip", "common.h", "topk.h", "launch.h"],
+    "k_moe_decode": ["k_decode.hip", "decode_common.h", "common.h", "topk.h", "launch.h"],
+    "k_batch": ["k_batch.hip", "k_sort.hip", "decode_common.h", "common.h", "launch.h"],
     "k_gqmm": ["k_gemm.hip", "common.h", "launch.h"],
 }
 
@@ -316,9 +318,11 @@ def run_decode(args, cfg):
     achieved = lbytes / (launch_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_for(args, "k_moe_decode"),
+                "traffic": traffic_for(args, "k_batch" if not one_launch and m >= BATCH_MIN_M
+                                       else "k_moe_decode"),
                 "kernel": "k_moe_decode (moe_forward: router + top-K + experts)" if one_launch
-                          else "k_moe_decode (moe_expert_forward)",
+                          else ("moe_expert_forward batched by expert (sort, k_bgate, k_bdown, "
+                                "k_bcombine)" if m >= BATCH_MIN_M else "k_moe_decode (moe_expert_forward)"),
                 "launch_us": round(launch_us, 2), "eager_launch_us": round(eager_us, 2),
                 "bytes_per_launch": int(lbytes)}
 

@@ -131,11 +131,69 @@ size_t gather_ws(char* base, int E, int n, int I, int H, bool full, moeq::Gather
   return off;
 }
 
+// carve the batched-decode workspace (pairs sorted by expert in tiles of
+// kBTile rows); with base == nullptr only the size is computed
+size_t batch_ws(char* base, const moeq::DecodeLayer& dl, int M, int K, moeq::BatchWs* out) {
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    char* p = base ? base + off : nullptr;
+    off += align_up(bytes);
+    return p;
+  };
+  const int n = M * K, E = dl.E;
+  moeq::GatherWs w{};
+  // each expert's rows make ceil(rows / kBTile) tiles, each tile has a row
+  const int mt = (n + moeq::kBTile - 1) / moeq::kBTile + E;
+  w.max_tiles = mt < n ? mt : n;
+  w.counts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * E));
+  w.offsets = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
+  w.cursor = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * E));
+  w.tile_off = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
+  w.n_tiles = reinterpret_cast<int32_t*>(take(sizeof(int32_t)));
+  w.tiles = reinterpret_cast<int4*>(take(sizeof(int4) * (size_t)w.max_tiles));
+  w.sorted = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)n));
+  moeq::BatchWs b{};
+  b.sort = w;
+  b.max_tiles = w.max_tiles;
+  b.n_tiles = w.n_tiles;
+  b.tiles = w.tiles;
+  b.sorted = w.sorted;
+  b.h = reinterpret_cast<float*>(take(sizeof(float) * (size_t)n * dl.I));
+  b.hsh = reinterpret_cast<float*>(take(sizeof(float) * (size_t)M * (dl.Is > 0 ? dl.Is : 1)));
+  b.sg = reinterpret_cast<float*>(take(sizeof(float) * (size_t)M));
+  b.ypair = reinterpret_cast<float*>(take(sizeof(float) * (size_t)n * dl.H));
+  b.ysh = reinterpret_cast<float*>(take(sizeof(float) * (size_t)M * dl.H));
+  if (out) *out = b;
+  return off;
+}
+
+bool use_batch(const moeq::DecodeLayer& dl, int M) {
+  return M >= moeq::kBatchMinM && moeq::batch_supported(dl);
+}
+
+// moe_expert_forward's workspace: per-token decode launch or batched by expert
+size_t expert_ws_bytes(const moeq::DecodeLayer& dl, int M, int K) {
+  return use_batch(dl, M) ? batch_ws(nullptr, dl, M, K, nullptr) : moeq::decode_ws_bytes(dl, M, K);
+}
+
+// the expert part for given indices: batched by expert for many tokens, else
+// the per-token launch
+int run_expert_forward(const moeq::DecodeLayer& dl, const float* x, const int32_t* idx,
+                       const float* w, int M, int K, const float* residual, float* y, void* ws,
+                       hipStream_t s) {
+  if (use_batch(dl, M)) {
+    moeq::BatchWs b;
+    batch_ws(reinterpret_cast<char*>(ws), dl, M, K, &b);
+    return moeq::launch_batch_forward(dl, x, idx, w, M, K, residual, y, b, s);
+  }
+  return moeq::launch_decode_forward(dl, x, idx, w, M, K, residual, y, ws, s);
+}
+
 // moe_forward: one launch (routing in the launch) or moe_route's workspace
 // followed by moe_expert_forward's; room for either
 size_t forward_ws_bytes(const moeq::DecodeLayer& dl, int E, int M, int K) {
   const size_t one = moeq::decode_ws_bytes(dl, M, K, true);
-  const size_t two = align_up(moeq::route_ws_bytes(M, E)) + moeq::decode_ws_bytes(dl, M, K);
+  const size_t two = align_up(moeq::route_ws_bytes(M, E)) + expert_ws_bytes(dl, M, K);
   return one > two ? one : two;
 }
 
@@ -176,7 +234,7 @@ size_t moe_workspace_size(const moeq_moe* L, int32_t M, int32_t K, int32_t path)
   LayerDims d;
   if (check_experts(L, &d)) return 0;
   if (K < 1 || K > kMaxK || K > d.E) return 0;
-  if (path == MOEQ_PATH_DECODE) return moeq::decode_ws_bytes(to_decode_layer(L, d), M, K) + kAlign;
+  if (path == MOEQ_PATH_DECODE) return expert_ws_bytes(to_decode_layer(L, d), M, K) + kAlign;
   if (path == MOEQ_PATH_FORWARD) {
     if (!L->router.q || L->router.rows != d.E) return 0;
     return forward_ws_bytes(to_decode_layer(L, d), d.E, M, K) + kAlign;
@@ -255,10 +313,9 @@ int moe_expert_forward(const moeq_moe* L, const float* x, const int32_t* topk_id
     return MOEQ_ERR_ALIGN;
   const moeq::DecodeLayer dl = to_decode_layer(L, d);
   if (!moeq::decode_supported(dl, K)) return MOEQ_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < moeq::decode_ws_bytes(dl, M, K)) return MOEQ_ERR_WORKSPACE;
+  if (!ws || ws_bytes < expert_ws_bytes(dl, M, K)) return MOEQ_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOEQ_ERR_ALIGN;
-  st = moeq::launch_decode_forward(dl, x, topk_idx, topk_w, M, K, residual, y, ws,
-                                   (hipStream_t)stream);
+  st = run_expert_forward(dl, x, topk_idx, topk_w, M, K, residual, y, ws, (hipStream_t)stream);
   if (st) return MOEQ_ERR_UNSUPPORTED;
   return launch_status();
 }
@@ -292,7 +349,7 @@ int moe_forward(const moeq_moe* L, const float* x, int32_t M, int32_t K, int32_t
     char* wsr = reinterpret_cast<char*>(ws);
     char* wsd = wsr + align_up(moeq::route_ws_bytes(M, d.E));
     moeq::launch_route(&router, x, M, d.E, K, renorm, topk_idx, topk_w, nullptr, wsr, s);
-    st = moeq::launch_decode_forward(dl, x, topk_idx, topk_w, M, K, residual, y, wsd, s);
+    st = run_expert_forward(dl, x, topk_idx, topk_w, M, K, residual, y, wsd, s);
   }
   if (st) return MOEQ_ERR_UNSUPPORTED;
   return launch_status();

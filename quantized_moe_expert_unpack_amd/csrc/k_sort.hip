@@ -104,9 +104,13 @@ __global__ void __launch_bounds__(kSortThreads) k_scatter(const int32_t* __restr
 }
 
 int launch_sort_pairs(const int32_t* idx, int n, int E, const GatherWs& ws, hipStream_t s) {
+  return launch_sort_pairs_bm(idx, n, E, ws, kGemmBM, s);
+}
+
+int launch_sort_pairs_bm(const int32_t* idx, int n, int E, const GatherWs& ws, int bm, hipStream_t s) {
   const int blocks = (n + kSortChunk - 1) / kSortChunk;
   hipLaunchKernelGGL(k_hist, dim3(blocks), dim3(kSortThreads), 0, s, idx, n, E, ws.counts);
-  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, ws.counts, E, kGemmBM, ws.offsets,
+  hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, ws.counts, E, bm, ws.offsets,
                      ws.cursor, ws.tile_off, ws.n_tiles, ws.tiles);
   hipLaunchKernelGGL(k_scatter, dim3(blocks), dim3(kSortThreads), 0, s, idx, n, E, ws.cursor,
                      ws.sorted);

@@ -67,6 +67,24 @@ struct GatherWs {
 
 constexpr int kGemmBM = 256;  // rows per gather-GEMM tile
 
+// Batched decode (many fp32 tokens; k_batch.hip): pairs grouped by expert in
+// tiles of at most kBTile rows, applied kBTok tokens at a time.
+constexpr int kBTile = 16;
+constexpr int kBTok = 4;
+constexpr int kBatchMinM = 16;   // from this many tokens moe_expert_forward batches by expert
+struct BatchWs {
+  GatherWs sort;         // pair sort by expert (tiles of kBTile rows)
+  int max_tiles;
+  const int32_t* n_tiles;
+  const int4* tiles;
+  const int32_t* sorted;
+  float* h;              // [n][I]
+  float* hsh;            // [M][Is]
+  float* sg;             // [M]
+  float* ypair;          // [n][H]
+  float* ysh;            // [M][H]
+};
+
 int launch_qdequant(const QT& W, uint8_t* codes, float* deq, hipStream_t s);
 int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s);
 // routing: router projection (fp64) + softmax/top-K; ws holds the fp64 logits
@@ -86,8 +104,15 @@ bool fused_supported(const DecodeLayer& L, const QT& router, int M, int K);
 int launch_moe_forward(const DecodeLayer& L, const RouteIn& R, const float* x, int M, int K,
                        const float* residual, float* y, void* ws, hipStream_t s);
 
+// batched decode
+bool batch_supported(const DecodeLayer& L);
+int launch_batch_forward(const DecodeLayer& L, const float* x, const int32_t* idx, const float* w,
+                         int M, int K, const float* residual, float* y, const BatchWs& B,
+                         hipStream_t s);
+
 // gather path
 int launch_sort_pairs(const int32_t* idx, int n, int E, const GatherWs& ws, hipStream_t s);
+int launch_sort_pairs_bm(const int32_t* idx, int n, int E, const GatherWs& ws, int bm, hipStream_t s);
 int launch_gemm_gate_up(const QT& gate, const QT& up, const uint16_t* x, int K, const GatherWs& ws,
                         int n, hipStream_t s);
 int launch_gemm_down(const QT& down, const float* w, const GatherWs& ws, int n, hipStream_t s);
