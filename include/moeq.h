@@ -35,8 +35,12 @@
  *  - Outputs never alias inputs.
  *  - Workspaces: sized by moe_workspace_size().  A workspace must hold zeros
  *    before its first use (e.g. torch.zeros); every call leaves its counters
- *    at zero again.  Calls that share one workspace must be ordered on one
- *    stream; concurrent calls need separate workspaces.
+ *    at zero again.  The counters sit at offsets that do not depend on M, so
+ *    one workspace serves any sequence of calls of its path, for one layer
+ *    shape and one K, with any M up to the M it was sized for (the calls of
+ *    MOEQ_PATH_DECODE and MOEQ_PATH_FORWARD share one layout).  Calls that
+ *    share one workspace must be ordered on one stream; concurrent calls need
+ *    separate workspaces.
  */
 #ifndef MOEQ_H
 #define MOEQ_H

@@ -134,7 +134,9 @@ size_t gather_ws(char* base, int E, int n, int I, int H, bool full, moeq::Gather
 // carve the batched-decode workspace (pairs sorted by expert in tiles of
 // kBTile rows); with base == nullptr only the size is computed
 size_t batch_ws(char* base, const moeq::DecodeLayer& dl, int M, int K, moeq::BatchWs* out) {
-  size_t off = 0;
+  // the decode state block first (its per-expert counts serve the sort)
+  const moeq::DecState st = moeq::dec_state(dl, K, base);
+  size_t off = st.bytes;
   auto take = [&](size_t bytes) {
     char* p = base ? base + off : nullptr;
     off += align_up(bytes);
@@ -145,7 +147,7 @@ size_t batch_ws(char* base, const moeq::DecodeLayer& dl, int M, int K, moeq::Bat
   // each expert's rows make ceil(rows / kBTile) tiles, each tile has a row
   const int mt = (n + moeq::kBTile - 1) / moeq::kBTile + E;
   w.max_tiles = mt < n ? mt : n;
-  w.counts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * E));
+  w.counts = st.bcounts;
   w.offsets = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
   w.cursor = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * E));
   w.tile_off = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (E + 1)));
@@ -171,13 +173,16 @@ bool use_batch(const moeq::DecodeLayer& dl, int M) {
   return M >= moeq::kBatchMinM && moeq::batch_supported(dl);
 }
 
-// moe_expert_forward's workspace: per-token decode launch or batched by expert
+// moe_expert_forward's workspace: per-token decode launches (at most
+// kDecMaxM tokens each) or batched by expert; both start with the decode
+// state block
 size_t expert_ws_bytes(const moeq::DecodeLayer& dl, int M, int K) {
-  return use_batch(dl, M) ? batch_ws(nullptr, dl, M, K, nullptr) : moeq::decode_ws_bytes(dl, M, K);
+  return use_batch(dl, M) ? batch_ws(nullptr, dl, M, K, nullptr)
+                          : moeq::decode_ws_bytes(dl, M < moeq::kDecMaxM ? M : moeq::kDecMaxM, K);
 }
 
 // the expert part for given indices: batched by expert for many tokens, else
-// the per-token launch
+// per-token launches of at most kDecMaxM tokens, in order on the stream
 int run_expert_forward(const moeq::DecodeLayer& dl, const float* x, const int32_t* idx,
                        const float* w, int M, int K, const float* residual, float* y, void* ws,
                        hipStream_t s) {
@@ -186,14 +191,22 @@ int run_expert_forward(const moeq::DecodeLayer& dl, const float* x, const int32_
     batch_ws(reinterpret_cast<char*>(ws), dl, M, K, &b);
     return moeq::launch_batch_forward(dl, x, idx, w, M, K, residual, y, b, s);
   }
-  return moeq::launch_decode_forward(dl, x, idx, w, M, K, residual, y, ws, s);
+  for (int t0 = 0; t0 < M; t0 += moeq::kDecMaxM) {
+    const int m = M - t0 < moeq::kDecMaxM ? M - t0 : moeq::kDecMaxM;
+    const size_t xo = (size_t)t0 * dl.H, ko = (size_t)t0 * K;
+    const int st = moeq::launch_decode_forward(dl, x + xo, idx + ko, w + ko, m, K,
+                                               residual ? residual + xo : nullptr, y + xo, ws, s);
+    if (st) return st;
+  }
+  return 0;
 }
 
-// moe_forward: one launch (routing in the launch) or moe_route's workspace
-// followed by moe_expert_forward's; room for either
+// moe_forward: one launch (routing in the launch), or a routing launch and
+// moe_expert_forward: [decode state block | expert data | fp64 logits], the
+// routing counters inside the state block; room for either
 size_t forward_ws_bytes(const moeq::DecodeLayer& dl, int E, int M, int K) {
-  const size_t one = moeq::decode_ws_bytes(dl, M, K, true);
-  const size_t two = align_up(moeq::route_ws_bytes(M, E)) + expert_ws_bytes(dl, M, K);
+  const size_t one = moeq::decode_ws_bytes(dl, M < moeq::kFusedMaxM ? M : moeq::kFusedMaxM, K, true);
+  const size_t two = align_up(expert_ws_bytes(dl, M, K)) + align_up(sizeof(double) * (size_t)M * E);
   return one > two ? one : two;
 }
 
@@ -346,10 +359,12 @@ int moe_forward(const moeq_moe* L, const float* x, int32_t M, int32_t K, int32_t
     const moeq::RouteIn R{router, renorm, topk_idx, topk_w};
     st = moeq::launch_moe_forward(dl, R, x, M, K, residual, y, ws, s);
   } else {
-    char* wsr = reinterpret_cast<char*>(ws);
-    char* wsd = wsr + align_up(moeq::route_ws_bytes(M, d.E));
-    moeq::launch_route(&router, x, M, d.E, K, renorm, topk_idx, topk_w, nullptr, wsr, s);
-    st = run_expert_forward(dl, x, topk_idx, topk_w, M, K, residual, y, wsd, s);
+    char* base = reinterpret_cast<char*>(ws);
+    const moeq::DecState ds = moeq::dec_state(dl, K, base);
+    double* l64 = reinterpret_cast<double*>(base + align_up(expert_ws_bytes(dl, M, K)));
+    moeq::launch_route_parts(&router, x, M, d.E, K, renorm, topk_idx, topk_w, nullptr, l64,
+                             ds.route_ctr, s);
+    st = run_expert_forward(dl, x, topk_idx, topk_w, M, K, residual, y, base, s);
   }
   if (st) return MOEQ_ERR_UNSUPPORTED;
   return launch_status();

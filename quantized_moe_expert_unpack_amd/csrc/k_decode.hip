@@ -427,7 +427,12 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
     route_select<WIDE>(keys, vals, E, K, R.renorm, P, R, m, epoch & 1);
     __syncthreads();
   }
-  if (tid == 0) st_coh_i(P.epoch, epoch + 1);
+  if (tid == 0) {
+    st_coh_i(P.epoch, epoch + 1);
+    // how much of this launch's h buffer it fills (the launch after next
+    // clears that much of it)
+    st_coh_i(P.hext + (epoch & 1), (int)((size_t)kHCopies * P.P * P.Imax / 4));
+  }
 }
 
 // ------------------------------------------------------------------ G unit
@@ -585,7 +590,7 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
     if (i < nrows) {
       const size_t at = (size_t)(lane & 31) * P.P * P.Imax + (size_t)p * P.Imax + i_base + i;
       if constexpr (FUSED)   // complemented bits: 0 means "not written in this launch"
-        st_coh_i(reinterpret_cast<int*>(P.hb) + (size_t)s_par * kHCopies * P.P * P.Imax + at,
+        st_coh_i(reinterpret_cast<int*>(P.hb) + (size_t)s_par * P.hreg + at,
                  (int)~__float_as_uint(hv));
       else
         st_coh(P.h + at, hv);
@@ -614,7 +619,7 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
     a = wave_sum(a);
     if (lane == 0) {
       if constexpr (FUSED)
-        st_coh_i(reinterpret_cast<int*>(P.sgb) + s_par * P.M + t, (int)~__float_as_uint(a));
+        st_coh_i(reinterpret_cast<int*>(P.sgb) + s_par * kFusedMaxM + t, (int)~__float_as_uint(a));
       else
         st_coh(P.sg + t, a);
     }
@@ -647,7 +652,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float wk[kMaxTopK + 1];
   __shared__ int s_ex[kMaxTopK];
-  __shared__ int bad, s_par, s_done;
+  __shared__ int bad, s_par, s_done, s_zx;
   constexpr int kCpc = 128 / BITS;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int K = P.K, H = L.H;
@@ -727,6 +732,8 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     const int wpr = (sh ? Is : I) / (32 / BITS);
     wv[j] = reinterpret_cast<const uint4*>(base + (size_t)(r0 + rlc) * wpr)[cj];
   }
+  // the extent of the other h buffer's last use (cleared at the end)
+  const int zx = FUSED ? ld_coh_i(P.hext + (s_par ^ 1)) : 0;
   // done with the route words: count this reader (the last one clears them);
   // the last wave does it, after its loads are in flight
   bool last_reader = false;
@@ -744,8 +751,9 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     // slot is there
     drain();
     if (tid < n_sb) reinterpret_cast<uint4*>(sbl)[tid] = sbr;
+    if (tid == 0) s_zx = zx;
     if (wid == 0 && L.has_shared && lane == K) {
-      const uint32_t* sgp = P.sgb + s_par * P.M + t;
+      const uint32_t* sgp = P.sgb + s_par * kFusedMaxM + t;
       uint32_t v = 0;
       for (int i = 0; i < kSpinLimit && v == 0; ++i) {
         v = (uint32_t)ld_coh_i(reinterpret_cast<const int*>(sgp));
@@ -758,7 +766,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     // of its rows; wave 0 alone), so that the whole of h is loaded once it is
     // almost surely complete: polling all of it would put one copy of h per
     // poll round and down unit on the memory system while the weights stream
-    const uint32_t* hw = P.hb + (size_t)s_par * kHCopies * P.P * P.Imax +
+    const uint32_t* hw = P.hb + (size_t)s_par * P.hreg +
                          (size_t)(blockIdx.x % kHCopies) * P.P * P.Imax + (size_t)t * P.S * P.Imax;
     if (wid == 0) {
       const int nmk = K * P.ng_routed + P.ng_shared;
@@ -927,14 +935,15 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
   }
   if constexpr (FUSED) {
     // clear this unit's share of the other parity's h and shared-gate
-    // buffers: the previous launch used them, the next one fills them (off the
+    // buffers: the previous launch used them (as much of the h buffer as its
+    // extent word says, whatever its M), the next one fills them (off the
     // critical path, at the end)
-    const size_t nh4 = (size_t)kHCopies * P.P * P.Imax / 4;
+    const size_t nh4 = min((size_t)(unsigned)s_zx, P.hreg / 4);
     const size_t per = (nh4 + (size_t)P.M * P.nc - 1) / ((size_t)P.M * P.nc);
-    uint4* hz = reinterpret_cast<uint4*>(P.hb + (size_t)(s_par ^ 1) * kHCopies * P.P * P.Imax);
+    uint4* hz = reinterpret_cast<uint4*>(P.hb + (size_t)(s_par ^ 1) * P.hreg);
     for (size_t i = (size_t)d * per + tid; i < min(nh4, (size_t)(d + 1) * per); i += kThreads)
       hz[i] = make_uint4(0, 0, 0, 0);
-    if (c == 0 && tid == 0) P.sgb[(s_par ^ 1) * P.M + t] = 0u;
+    if (d == 0 && tid < kFusedMaxM) P.sgb[(s_par ^ 1) * kFusedMaxM + tid] = 0u;
   }
 }
 
@@ -960,6 +969,33 @@ __global__ void __launch_bounds__(kThreads)
   else down_unit<BITS, DCH, FUSED>(L, P, idx, wts, residual, y, u - P.g_units);
 }
 
+DecState dec_state(const DecodeLayer& L, int K, void* ws) {
+  auto al = [](size_t v) { return (v + 255) / 256 * 256; };
+  DecState D{};
+  size_t off = 0;
+  char* base = reinterpret_cast<char*>(ws);
+  auto take = [&](size_t n) { char* p = base ? base + off : nullptr; off += al(n); return p; };
+  const int S = K + (L.has_shared ? 1 : 0);
+  const int Imax = L.has_shared && L.Is > L.I ? L.Is : L.I;
+  D.ctr = reinterpret_cast<int*>(take(sizeof(int) * (size_t)kLine * (1 + (size_t)kCtrLines * kDecMaxM)));
+  // flag copies: kRep blocks of kDecMaxM lines, 4 KB + 256 B apart at least
+  D.rstride = (int)((((size_t)kDecMaxM * kLine * sizeof(int) + 4095) / 4096 * 4096 + 256) / sizeof(int));
+  D.ready = reinterpret_cast<int*>(take(sizeof(int) * (size_t)kRep * D.rstride));
+  D.epoch = reinterpret_cast<int*>(take(sizeof(int) * 4));
+  D.hext = D.epoch ? D.epoch + 1 : nullptr;
+  D.hreg = (size_t)kHCopies * kFusedMaxM * S * Imax;
+  D.hb = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 2 * D.hreg));
+  D.sgb = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 2 * kFusedMaxM));
+  D.logits = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)kFusedMaxM * L.E));
+  D.idx_c = reinterpret_cast<int32_t*>(take(sizeof(int) * (size_t)kRep * D.rstride));
+  D.route_ctr = reinterpret_cast<int*>(take(route_ctr_bytes()));
+  D.bcounts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)L.E));
+  D.bytes = off;
+  return D;
+}
+
+// the state block, then the launch's own data (h and the shared-gate logits
+// of the launch without routing); M <= kDecMaxM
 static DecPlan make_dec_plan(const DecodeLayer& L, int M, int K, bool routed, void* ws, size_t* bytes) {
   DecPlan P{};
   P.M = M;
@@ -973,22 +1009,24 @@ static DecPlan make_dec_plan(const DecodeLayer& L, int M, int K, bool routed, vo
   P.nc = (L.H + kDRows - 1) / kDRows;
   P.d_units = M * P.nc;
   P.r_units = routed ? (L.E + kRRows - 1) / kRRows : 0;
+  const DecState D = dec_state(L, K, ws);
+  P.ctr = D.ctr;
+  P.ready = D.ready;
+  P.rstride = D.rstride;
+  P.epoch = D.epoch;
+  P.hext = D.hext;
+  P.hb = D.hb;
+  P.hreg = D.hreg;
+  P.sgb = D.sgb;
+  P.logits = D.logits;
+  P.idx_c = D.idx_c;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
-  size_t off = 0;
+  size_t off = D.bytes;
   char* base = reinterpret_cast<char*>(ws);
   auto take = [&](size_t n) { char* p = base ? base + off : nullptr; off += al(n); return p; };
-  P.ctr = reinterpret_cast<int*>(take(sizeof(int) * (size_t)kLine * (1 + (size_t)kCtrLines * M)));
-  // flag copies: kRep blocks of M lines, 4 KB + 256 B apart at least
-  P.rstride = (int)((((size_t)M * kLine * sizeof(int) + 4095) / 4096 * 4096 + 256) / sizeof(int));
-  P.ready = reinterpret_cast<int*>(take(sizeof(int) * (size_t)kRep * P.rstride));
-  P.h = reinterpret_cast<float*>(take(sizeof(float) * kHCopies * (size_t)P.P * P.Imax));
-  P.sg = reinterpret_cast<float*>(take(sizeof(float) * (size_t)M));
-  if (routed) {
-    P.epoch = reinterpret_cast<int*>(take(sizeof(int)));
-    P.hb = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 2 * kHCopies * (size_t)P.P * P.Imax));
-    P.sgb = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 2 * (size_t)M));
-    P.logits = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)M * L.E));
-    P.idx_c = reinterpret_cast<int32_t*>(take(sizeof(int) * (size_t)kRep * P.rstride));
+  if (!routed) {
+    P.h = reinterpret_cast<float*>(take(sizeof(float) * kHCopies * (size_t)P.P * P.Imax));
+    P.sg = reinterpret_cast<float*>(take(sizeof(float) * (size_t)M));
   }
   if (bytes) *bytes = off;
   return P;
@@ -1093,6 +1131,7 @@ static int dispatch_dec(const DecodeLayer& L, const DecPlan& P, const RouteIn& R
 
 int launch_decode_forward(const DecodeLayer& L, const float* x, const int32_t* idx, const float* w,
                           int M, int K, const float* residual, float* y, void* ws, hipStream_t s) {
+  if (M > kDecMaxM) return -9;
   const DecPlan P = make_dec_plan(L, M, K, false, ws, nullptr);
   const RouteIn R{};
   return dispatch_dec<false>(L, P, R, x, idx, w, residual, y, s);
@@ -1100,6 +1139,7 @@ int launch_decode_forward(const DecodeLayer& L, const float* x, const int32_t* i
 
 int launch_moe_forward(const DecodeLayer& L, const RouteIn& R, const float* x, int M, int K,
                        const float* residual, float* y, void* ws, hipStream_t s) {
+  if (M > kFusedMaxM) return -9;
   const DecPlan P = make_dec_plan(L, M, K, true, ws, nullptr);
   return dispatch_dec<true>(L, P, R, x, nullptr, nullptr, residual, y, s);
 }

@@ -233,19 +233,29 @@ int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s) 
 
 constexpr size_t kRouteCtrBytes = sizeof(int) * kLineInts * (1 + kFan);
 
+size_t route_ctr_bytes() { return (kRouteCtrBytes + 255) / 256 * 256; }
+
+// [counters][fp64 logits]: the counters sit at the same place for every M
 size_t route_ws_bytes(int M, int E) {
-  return ((sizeof(double) * (size_t)M * E + 255) / 256) * 256 + kRouteCtrBytes;
+  return route_ctr_bytes() + ((sizeof(double) * (size_t)M * E + 255) / 256) * 256;
 }
 
 int launch_route(const QT* router, const float* x_or_logits, int M, int E, int K, int renorm,
                  int32_t* idx, float* w, float* logits32, void* ws, hipStream_t s) {
+  char* b = reinterpret_cast<char*>(ws);
+  return launch_route_parts(router, x_or_logits, M, E, K, renorm, idx, w, logits32,
+                            b ? reinterpret_cast<double*>(b + route_ctr_bytes()) : nullptr,
+                            reinterpret_cast<int*>(b), s);
+}
+
+int launch_route_parts(const QT* router, const float* x_or_logits, int M, int E, int K, int renorm,
+                       int32_t* idx, float* w, float* logits32, double* l64, int* ctr,
+                       hipStream_t s) {
   if (!router) {
     hipLaunchKernelGGL(k_topk_rows, dim3(M), dim3(kRouteThreads), 0, s, (const double*)nullptr,
                        x_or_logits, M, E, K, renorm, idx, w);
     return 0;
   }
-  double* l64 = reinterpret_cast<double*>(ws);
-  int* ctr = reinterpret_cast<int*>(reinterpret_cast<char*>(ws) + route_ws_bytes(M, E) - kRouteCtrBytes);
   const dim3 grid((E + 3) / 4);
   const QT& W = *router;
   const bool last = M <= kLastTopkMaxM;

@@ -24,22 +24,47 @@ struct DecodeLayer {
   int E, H, I, Is;
 };
 
-// Decode plan: unit counts and the workspace carve-up of the one-launch
-// decode kernel (counters and the routed-index copies are zero between calls).
+// Decode-family workspaces (moe_expert_forward, moe_forward) start with this
+// state block.  Its layout depends on the layer's shape and K only, never on
+// M, so one workspace serves calls of any M up to the size it was made for:
+// every word here holds zero between calls (the kernels clear what they set),
+// except the one-launch form's launch counter and its two extent words.
+constexpr int kDecMaxM = 16;   // tokens per per-token decode launch (more go in chunks)
+constexpr int kFusedMaxM = 4;  // tokens of the one-launch (routing inside) form
+struct DecState {
+  int* ctr;          // error word, then per-token arrival counters (kDecMaxM tokens)
+  int* ready;        // ready-flag copies
+  int rstride;       // ints between copies
+  int* epoch;        // one-launch counter; its parity picks the h buffer
+  int* hext;         // [2] 16-byte words of each h buffer the last launch using it wrote
+  uint32_t* hb;      // [2][hreg] complemented-bit h buffers of the one-launch form
+  size_t hreg;       // words per h buffer
+  uint32_t* sgb;     // [2][kFusedMaxM] shared-gate logits, the same way
+  uint64_t* logits;  // [kFusedMaxM][E] complemented fp64 logits, 0 = not written
+  int32_t* idx_c;    // route-line copies
+  int* route_ctr;    // counters of a separate routing launch
+  int32_t* bcounts;  // [E] per-expert pair counts of the batched form
+  size_t bytes;      // size of the block (256-byte multiple)
+};
+DecState dec_state(const DecodeLayer& L, int K, void* ws);
+
+// Decode plan: unit counts, the state block above and the launch's data.
 struct DecPlan {
   int M, K, S, P, Imax;
   int ng_routed, ng_shared, g_units, nc, d_units;
   int r_units;     // router units in front of the expert units (routing in the launch), else 0
   int* ctr;        // 128-byte lines: error word, then per token G and D arrival counters
-  int* ready;      // ready flags: copies [kRep] of M lines, rstride ints apart
+  int* ready;      // ready flags: copies [kRep] of token lines, rstride ints apart
   int rstride;
-  float* h;        // [P][Imax] (pair p = token * S + slot)
+  float* h;        // [copies][P][Imax] (pair p = token * S + slot)
   float* sg;       // [M]
-  uint64_t* logits;  // [M][E] router logits as complemented fp64 bits, 0 = not written
+  uint64_t* logits;  // [kFusedMaxM][E] router logits as complemented fp64 bits, 0 = not written
   int* epoch;        // launch counter (routing in the launch): its parity picks the h buffer
-  uint32_t* hb;      // [2][copies][P][Imax] h as complemented fp32 bits, 0 = not written
-  uint32_t* sgb;     // [2][M] shared-gate logits, the same way
-  int32_t* idx_c;  // route lines: copies [kRep] of M lines (64-bit expert + 1 | weight words)
+  int* hext;         // [2] extent (16-byte words) of each h buffer's last use
+  uint32_t* hb;      // [2][hreg]: [copies][P][Imax] h as complemented fp32 bits, 0 = not written
+  size_t hreg;
+  uint32_t* sgb;     // [2][kFusedMaxM] shared-gate logits, the same way
+  int32_t* idx_c;  // route lines: copies [kRep] of token lines (64-bit expert + 1 | weight words)
 };
 
 // Router of a decode launch that routes in the same launch.
@@ -87,19 +112,23 @@ struct BatchWs {
 
 int launch_qdequant(const QT& W, uint8_t* codes, float* deq, hipStream_t s);
 int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s);
-// routing: router projection (fp64) + softmax/top-K; ws holds the fp64 logits
-// and a counter (zero between calls)
+// routing: router projection (fp64) + softmax/top-K.  The standalone
+// workspace is [counters (zero between calls)][fp64 logits [M][E]].
+size_t route_ctr_bytes();
 size_t route_ws_bytes(int M, int E);
 int launch_route(const QT* router, const float* x_or_logits, int M, int E, int K, int renorm,
                  int32_t* idx, float* w, float* logits32, void* ws, hipStream_t s);
+int launch_route_parts(const QT* router, const float* x_or_logits, int M, int E, int K, int renorm,
+                       int32_t* idx, float* w, float* logits32, double* l64, int* ctr,
+                       hipStream_t s);
 
-// decode expert forward (one launch)
+// decode expert forward (one launch, M <= kDecMaxM); the workspace is the
+// state block followed by the launch's data
 int launch_decode_forward(const DecodeLayer& L, const float* x, const int32_t* idx, const float* w,
                           int M, int K, const float* residual, float* y, void* ws, hipStream_t s);
 size_t decode_ws_bytes(const DecodeLayer& L, int M, int K, bool routed_in_launch = false);
 bool decode_supported(const DecodeLayer& L, int K);
 // router + experts in one launch (8-bit router, M <= kFusedMaxM)
-constexpr int kFusedMaxM = 4;
 bool fused_supported(const DecodeLayer& L, const QT& router, int M, int K);
 int launch_moe_forward(const DecodeLayer& L, const RouteIn& R, const float* x, int M, int K,
                        const float* residual, float* y, void* ws, hipStream_t s);

@@ -94,3 +94,46 @@ def test_alternating_layers_share_one_workspace():
     for rep in range(3):
         for j, (_, host, L) in enumerate(layers):
             _check(cfg, host, L, xs[j][rep], ws)
+
+
+SHARED4 = synth.scaled(synth.CONFIGS["c1"], shared_inter=128, shared_bits=4, shared_gate_bits=8,
+                       seed=21)
+
+
+@pytest.mark.parametrize("name", ["c1", "c1_shared"])
+def test_one_workspace_serves_calls_of_any_m(name):
+    # a workspace sized for the largest M, then one-launch (M <= 4), per-token
+    # (M < 16) and batched (M >= 16) calls in a mixed order: the state words
+    # the kernels expect to be zero sit at the same place for every M
+    cfg = synth.CONFIGS["c1"] if name == "c1" else SHARED4
+    host = synth.host_layer(cfg, 0, threads=16)
+    L = moeq.MoELayer.from_host(host, dev())
+    ws = moeq.workspace(L, 40, cfg.top_k, moeq.PATH_FORWARD, dev())
+    for i, m in enumerate([4, 1, 8, 40, 3, 17, 2, 5, 1, 33, 4]):
+        say(f"{name} forward M={m}")
+        x = gapped_tokens(cfg, host, 0, i + 1, m=m)[i]      # a fresh draw per call
+        _check(cfg, host, L, x, ws)
+        if m <= 4:
+            assert int(ws[:4].view(torch.int32).item()) == 0
+    wsd = moeq.workspace(L, 40, cfg.top_k, moeq.PATH_DECODE, dev())
+    for i, m in enumerate([40, 1, 12, 16, 3, 33, 2]):
+        say(f"{name} expert_forward M={m}")
+        x = gapped_tokens(cfg, host, 0, i + 1, m=m)[i]
+        xd = to_dev(x)
+        idx, w = moeq.moe_route(L.router, xd, cfg.experts, cfg.top_k, renorm=cfg.renorm)
+        y = moeq.moe_expert_forward(L, xd, idx, w, ws=wsd)
+        ry, _, _, _ = oracle.moe_layer(host, x, cfg.top_k, cfg.renorm)
+        assert rel_l2_rows(y.cpu().numpy(), ry).max() <= TOL
+
+
+def test_route_workspace_serves_calls_of_any_m():
+    cfg, host, L = _layer("c2", 0)
+    ws = moeq.workspace(L, 64, cfg.top_k, moeq.PATH_ROUTE, dev())
+    for i, m in enumerate([64, 1, 10, 3, 5]):
+        say(f"route M={m}")
+        x = gapped_tokens(cfg, host, 0, i + 1, m=m)[i]
+        idx, w = moeq.moe_route(L.router, to_dev(x), cfg.experts, cfg.top_k, renorm=cfg.renorm,
+                                ws=ws)
+        _, ridx, rw, _ = oracle.moe_layer(host, x, cfg.top_k, cfg.renorm)
+        assert np.array_equal(idx.cpu().numpy(), ridx)
+        assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
