@@ -8,16 +8,15 @@
 // an expert serves r_e of the M*K (token, slot) pairs, so per token the
 // decode launch would stream each expert r_e times (and the shared expert M
 // times).  Here the pairs are grouped by expert first (the sort of the
-// gather path, tiles of at most kBTile rows), then
-//   k_bgate   one unit = (tile, 16 gate/up rows): the rows are loaded once,
-//             kept in registers and applied to the tile's tokens kBTok at a
-//             time (x staged in LDS), SwiGLU, h[pair]; the shared expert is one
-//             tile holding all M tokens, and its first row block also computes
-//             the shared_expert_gate logits;
-//   k_bdown   one unit = (tile, 8*64/LPR output rows): down rows loaded once,
-//             applied to the tile's h kBTok pairs at a time, scaled by the
-//             routing weight (or the sigmoid of the shared gate) into a per-pair
-//             output row;
+// gather path, tiles of at most kBTile pairs), then
+//   k_bgate   one unit = (tile, 64 gate/up rows): the tile's activations in
+//             LDS, each wave streams 16 rows of gate and of up with the next
+//             step's rows in flight, SwiGLU, h[pair]; the shared expert is
+//             cut into tiles of kBTok tokens, and the units of its first rows
+//             also compute the shared_expert_gate logits;
+//   k_bdown   one unit = (tile, a slab of output rows): the same streaming
+//             over down rows, scaled by the routing weight (or the sigmoid of
+//             the shared gate) into a per-pair output row;
 //   k_bcombine y[t] = sum over slots k in order of the pair outputs
 //             (+ the shared expert) (+ residual); NaN for a pair whose
 //             expert index is out of range.
@@ -28,146 +27,253 @@
 
 namespace moeq {
 
-constexpr int kBThreads = 512;
+constexpr int kBThreads = 256;               // four waves
 constexpr int kBWaves = kBThreads / kWave;
-constexpr int kBGRows = 16;   // gate/up rows per unit (two per wave)
+constexpr int kBSlab = 64;                   // gate/up rows of a unit (16 per wave)
+constexpr int kBDSteps = 8;                  // down: steps per wave
+constexpr int kBRpl = 2;                     // down: rows per lane and step
 
-// An empty asm that claims to modify v: the weights are reused for every
-// token, and without it the compiler hoists their unpacked codes out of the
-// token loop into (far too many) registers.
-__device__ __forceinline__ void opaque(uint4& v) {
-  asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+// ---- byte-wise unpacking ----------------------------------------------------
+// A 32-bit word of codes is split into passes whose four bytes each hold one
+// code, converted with one byte-to-float instruction apiece:
+//   2 bits: pass m = (w >> 2m) & 0x03030303, byte b = code 4b + m of the word
+//   4 bits: pass m = (w >> 4m) & 0x0F0F0F0F, byte b = code 2b + m
+//   8 bits: the word itself, byte b = code b
+// (the empty asm hides the mask from the compiler, which would otherwise
+// fold it into one bit-field extract per code)
+template <int BITS>
+__device__ __forceinline__ uint32_t upass(uint32_t w, int m) {
+  uint32_t t = w;
+  if constexpr (BITS == 2) t = (w >> (2 * m)) & 0x03030303u;
+  else if constexpr (BITS == 4) t = (w >> (4 * m)) & 0x0F0F0F0Fu;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+__device__ __forceinline__ float comp(const float4& v, int c) {
+  return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+
+// d[r][t] += (codes of the 16-byte chunk v[r]) . (activations of token t).
+// x4 points at float4 0 of the lane's chunk of token 0 in the chunk-interleaved
+// layout (float4 f at x4[f * stride], token t at + t * tstride).  Every code is
+// converted once and used for all T tokens.
+template <int BITS, int R, int T>
+__device__ __forceinline__ void chunk_dots(const uint4 (&v)[R], const float4* x4, int stride,
+                                           int tstride, float (&d)[R][T]) {
+  constexpr int kPasses = BITS == 2 ? 4 : BITS == 4 ? 2 : 1;
+  constexpr int kF = 8 / BITS;                 // float4s of activations per word
+#pragma unroll
+  for (int wi = 0; wi < 4; ++wi) {
+    float4 xv[T][kF];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int f = 0; f < kF; ++f) xv[t][f] = x4[t * tstride + (wi * kF + f) * stride];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const uint32_t w = wi == 0 ? v[r].x : wi == 1 ? v[r].y : wi == 2 ? v[r].z : v[r].w;
+#pragma unroll
+      for (int m = 0; m < kPasses; ++m) {
+        const uint32_t tb = upass<BITS>(w, m);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float c = (float)((tb >> (8 * b)) & 0xFFu);
+          // the code's place among the word's activations
+          const int f = BITS == 2 ? b : BITS == 4 ? b / 2 : 0;
+          const int cc = BITS == 2 ? m : BITS == 4 ? 2 * (b % 2) + m : b;
+#pragma unroll
+          for (int t = 0; t < T; ++t) d[r][t] = fmaf(c, comp(xv[t][f], cc), d[r][t]);
+        }
+      }
+      // one row of one word at a time: the compiler would otherwise convert
+      // (and fetch activations for) every word of every row at once and run
+      // out of registers
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// stage nt activation rows (H floats each, row t at src[t]) chunk-interleaved
+// into LDS with their chunk sums
+template <int CPC>
+__device__ __forceinline__ void stage_rows(float* xs, float* xsum, const float* const* src, int nt,
+                                           int H) {
+  const int nch = H / CPC, x16 = H / 4;
+  for (int i = threadIdx.x; i < nt * x16; i += kBThreads) {
+    const int j = i / x16, f = i - j * x16;
+    reinterpret_cast<float4*>(xs + j * H)[ilv<CPC>(f, nch)] = reinterpret_cast<const float4*>(src[j])[f];
+  }
+  __syncthreads();
+  for (int j = 0; j < nt; ++j)
+    chunk_sums<CPC>(reinterpret_cast<const float4*>(xs + j * H), xsum + j * (H / 16), nch);
+  __syncthreads();
 }
 
 // ---------------------------------------------------------------- gate / up
-// LDS: [kBTok tokens][x interleaved (H floats)][kBTok][chunk sums (H/16)]
-//      [bf16 scales/biases of the unit's gate and up rows]
-template <int BITS, int CPL>
-__global__ void __launch_bounds__(kBThreads) k_bgate(DecodeLayer L, BatchWs B, int M, int K,
-                                                    const float* __restrict__ x) {
+// One unit = (tile of at most kBTok pairs, or kBTok tokens of the shared
+// expert) x (kBSlab rows of gate and of up).  A wave streams its 16 rows RPS
+// at a time, the next step's rows (and their scales and biases) in flight
+// while the current ones are applied to the tile's tokens.
+// LDS: [kBTok][x interleaved (H floats)][kBTok][chunk sums (H/16)]
+template <int BITS, int CPL, int RPS>
+struct GateStep {
+  uint4 g[RPS][CPL], u[RPS][CPL];
+  uint32_t gs[RPS][CPL], gb[RPS][CPL], us[RPS][CPL], ub[RPS][CPL];
+};
+
+template <int BITS, int CPL, int RPS>
+__device__ __forceinline__ void gate_load(GateStep<BITS, CPL, RPS>& S, const QT& Gq, const QT& Uq,
+                                          size_t row, int lane, int nch, int wpr, int gpr) {
+  constexpr int kCpc = 128 / BITS;
+#pragma unroll
+  for (int rr = 0; rr < RPS; ++rr) {
+    const size_t rw = row + rr;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c = min(lane + kWave * j, nch - 1);
+      const int grp = (c * kCpc) / kGroup;
+      S.g[rr][j] = reinterpret_cast<const uint4*>(Gq.q + rw * wpr)[c];
+      S.u[rr][j] = reinterpret_cast<const uint4*>(Uq.q + rw * wpr)[c];
+      S.gs[rr][j] = Gq.scales[rw * gpr + grp];
+      S.gb[rr][j] = Gq.biases[rw * gpr + grp];
+      S.us[rr][j] = Uq.scales[rw * gpr + grp];
+      S.ub[rr][j] = Uq.biases[rw * gpr + grp];
+    }
+  }
+}
+
+template <int BITS, int CPL, int RPS, int T>
+__device__ __forceinline__ void gate_rows(const DecodeLayer& L, const BatchWs& B, const QT& Gq,
+                                          const QT& Uq, size_t erow, int i0, bool shared,
+                                          const float* xs, const float* xsum, const int* s_tok,
+                                          const int* s_pair, int nt, int lane) {
+  constexpr int kCpc = 128 / BITS;
+  constexpr int kSteps = kBSlab / kBWaves / RPS;
+  constexpr int kN = RPS * T;
+  const int H = L.H;
+  const int nch = H / kCpc, wpr = H / (32 / BITS), gpr = H / kGroup;
+  GateStep<BITS, CPL, RPS> cur, nxt;
+  gate_load<BITS, CPL, RPS>(cur, Gq, Uq, erow + i0, lane, nch, wpr, gpr);
+#pragma unroll 1
+  for (int s = 0; s < kSteps; ++s) {
+    if (s + 1 < kSteps) gate_load<BITS, CPL, RPS>(nxt, Gq, Uq, erow + i0 + (s + 1) * RPS, lane, nch, wpr, gpr);
+    float ag[RPS][T], au[RPS][T];
+#pragma unroll
+    for (int rr = 0; rr < RPS; ++rr)
+#pragma unroll
+      for (int t = 0; t < T; ++t) ag[rr][t] = au[rr][t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      const int c0 = lane + kWave * j;
+      const bool ok = c0 < nch;
+      const int c = min(c0, nch - 1);
+      uint4 v[2 * RPS];
+#pragma unroll
+      for (int rr = 0; rr < RPS; ++rr) {
+        v[rr] = cur.g[rr][j];
+        v[RPS + rr] = cur.u[rr][j];
+      }
+      float d[2 * RPS][T];
+#pragma unroll
+      for (int r = 0; r < 2 * RPS; ++r)
+#pragma unroll
+        for (int t = 0; t < T; ++t) d[r][t] = 0.f;
+      chunk_dots<BITS, 2 * RPS, T>(v, reinterpret_cast<const float4*>(xs) + c, nch, H / 4, d);
+#pragma unroll
+      for (int rr = 0; rr < RPS; ++rr) {
+        const float gsc = ok ? bf16_to_f32(cur.gs[rr][j]) : 0.f, gbi = ok ? bf16_to_f32(cur.gb[rr][j]) : 0.f;
+        const float usc = ok ? bf16_to_f32(cur.us[rr][j]) : 0.f, ubi = ok ? bf16_to_f32(cur.ub[rr][j]) : 0.f;
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+          const float sm = xsum[t * (H / 16) + c];
+          ag[rr][t] = fmaf(gsc, d[rr][t], fmaf(gbi, sm, ag[rr][t]));
+          au[rr][t] = fmaf(usc, d[RPS + rr][t], fmaf(ubi, sm, au[rr][t]));
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float pg[kN], pu[kN];
+#pragma unroll
+    for (int rr = 0; rr < RPS; ++rr)
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        pg[rr * T + t] = ag[rr][t];
+        pu[rr * T + t] = au[rr][t];
+      }
+    const float gsum = treduce<kN, 32>(pg, lane);
+    const float usum = treduce<kN, 32>(pu, lane);
+    const int vi = tindex<kN, 32>(lane);
+    const int rr = vi / T, t = vi - rr * T;
+    if ((lane & (kWave / kN - 1)) == 0 && t < nt) {
+      const int i = i0 + s * RPS + rr;
+      const float hv = silu(gsum) * usum;
+      if (shared) B.hsh[(size_t)s_tok[t] * L.Is + i] = hv;
+      else B.h[(size_t)s_pair[t] * L.I + i] = hv;
+    }
+    if (s + 1 < kSteps) cur = nxt;
+  }
+}
+
+template <int BITS, int CPL, int RPS>
+__global__ void __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(3)))
+k_bgate(DecodeLayer L, BatchWs B, int M, int K, const float* __restrict__ x) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   constexpr int kCpc = 128 / BITS;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: row addresses in SGPRs
   const int H = L.H;
-  const int ngr = L.I / kBGRows;
+  const int nsl = L.I / kBSlab;
   const int item = blockIdx.x;
-  const bool shared = item >= B.max_tiles * ngr;
-  int g, rows, e = 0, row0 = 0;
+  const bool shared = item >= B.max_tiles * nsl;
+  int sl, nt, e = 0, row0 = 0, tg = 0;
   if (!shared) {
-    const int tile = item / ngr;
-    g = item - tile * ngr;
+    const int tile = item / nsl;
+    sl = item - tile * nsl;
     if (tile >= B.n_tiles[0]) return;
     const int4 T = B.tiles[tile];
     e = T.x;
     row0 = T.y;
-    rows = T.z;
+    nt = T.z;
   } else {
-    g = item - B.max_tiles * ngr;
-    rows = M;
+    const int nss = L.Is / kBSlab;
+    const int it = item - B.max_tiles * nsl;
+    tg = it / nss;
+    sl = it - tg * nss;
+    nt = min(kBTok, M - tg * kBTok);
   }
   const QT Gq = shared ? L.sh_gate : L.gate;
   const QT Uq = shared ? L.sh_up : L.up;
   const int I = shared ? L.Is : L.I;
-  const int nch = H / kCpc, wpr = H / (32 / BITS), gpr = H / kGroup, x16 = H / 4;
-  const int i_base = g * kBGRows;
   const size_t erow = (size_t)e * I;
+  const int i0 = sl * kBSlab + wid * (kBSlab / kBWaves);
   __shared__ int s_tok[kBTok], s_pair[kBTok];
-  // weights and scales first (clamped addresses, no branches), then x
-  const int sb16 = kBGRows * gpr * 2 / 16;
-  uint4 sbr;
-  {
-    const int qq = min(tid, 4 * sb16 - 1);
-    const int q = qq / sb16, w = qq - q * sb16;
-    const uint16_t* src = q == 0 ? Gq.scales : q == 1 ? Gq.biases : q == 2 ? Uq.scales : Uq.biases;
-    sbr = reinterpret_cast<const uint4*>(src + (erow + i_base) * gpr)[w];
-  }
-  uint4 wg[2][CPL], wu[2][CPL];
-#pragma unroll
-  for (int rr = 0; rr < 2; ++rr) {
-    const size_t row = erow + i_base + wid * 2 + rr;
-    const uint4* g4 = reinterpret_cast<const uint4*>(Gq.q + row * wpr);
-    const uint4* u4 = reinterpret_cast<const uint4*>(Uq.q + row * wpr);
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-      const int c = min(lane + kWave * j, nch - 1);
-      wg[rr][j] = g4[c];
-      wu[rr][j] = u4[c];
-    }
-  }
-  float* xs = smem;                                    // [kBTok][H]
-  float* xsum = xs + kBTok * H;                        // [kBTok][H/16]
-  uint16_t* sbl = reinterpret_cast<uint16_t*>(xsum + kBTok * H / 16);
-  if (tid < 4 * sb16) reinterpret_cast<uint4*>(sbl)[tid] = sbr;
-  // the tile's tokens, kBTok at a time; the weights stay in registers
-  for (int j0 = 0; j0 < rows; j0 += kBTok) {
-  const int nj = min(kBTok, rows - j0);
-  __syncthreads();                                     // the previous group is done with LDS
+  __shared__ const float* s_src[kBTok];
   if (tid < kBTok) {
     int tk = 0, pr = 0;
-    if (tid < nj) {
+    if (tid < nt) {
       if (shared) {
-        tk = j0 + tid;
+        tk = tg * kBTok + tid;
       } else {
-        pr = B.sorted[row0 + j0 + tid];
+        pr = B.sorted[row0 + tid];
         tk = pr / K;
       }
     }
     s_tok[tid] = tk;
     s_pair[tid] = pr;
+    s_src[tid] = x + (size_t)tk * H;
   }
   __syncthreads();
-  for (int i = tid; i < nj * x16; i += kBThreads) {
-    const int j = i / x16, f = i - j * x16;
-    reinterpret_cast<float4*>(xs + j * H)[ilv<kCpc>(f, nch)] =
-        reinterpret_cast<const float4*>(x + (size_t)s_tok[j] * H)[f];
-  }
-  __syncthreads();
-  for (int j = 0; j < nj; ++j)
-    chunk_sums<kCpc>(reinterpret_cast<const float4*>(xs + j * H), xsum + j * (H / 16), nch);
-  __syncthreads();
-  for (int j = 0; j < nj; ++j) {
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr)
-#pragma unroll
-      for (int c8 = 0; c8 < CPL; ++c8) {
-        opaque(wg[rr][c8]);
-        opaque(wu[rr][c8]);
-      }
-    const float4* x4 = reinterpret_cast<const float4*>(xs + j * H);
-    const float* xsj = xsum + j * (H / 16);
-    float pg[2], pu[2];
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-      const int i = wid * 2 + rr;
-      float ag = 0.f, au = 0.f;
-#pragma unroll
-      for (int c8 = 0; c8 < CPL; ++c8) {
-        const int c = lane + kWave * c8;
-        if (c < nch) {
-          const int grp = i * gpr + (c * kCpc) / kGroup;
-          const float dg = chunk_dot<BITS>(wg[rr][c8], x4 + c, nch);
-          const float du = chunk_dot<BITS>(wu[rr][c8], x4 + c, nch);
-          ag = fmaf(bf16_to_f32(sbl[grp]), dg, fmaf(bf16_to_f32(sbl[kBGRows * gpr + grp]), xsj[c], ag));
-          au = fmaf(bf16_to_f32(sbl[2 * kBGRows * gpr + grp]), du,
-                    fmaf(bf16_to_f32(sbl[3 * kBGRows * gpr + grp]), xsj[c], au));
-        }
-      }
-      pg[rr] = ag;
-      pu[rr] = au;
-    }
-    const float gsum = treduce<2, 32>(pg, lane);
-    const float usum = treduce<2, 32>(pu, lane);
-    if ((lane & 31) == 0) {
-      const int i = i_base + wid * 2 + tindex<2, 32>(lane);
-      const float hv = silu(gsum) * usum;
-      if (shared) B.hsh[(size_t)s_tok[j] * L.Is + i] = hv;
-      else B.h[(size_t)s_pair[j] * L.I + i] = hv;
-    }
-  }
-  if (shared && g == 0 && wid < nj) {
+  float* xs = smem;                                    // [kBTok][H]
+  float* xsum = xs + kBTok * H;                        // [kBTok][H/16]
+  stage_rows<kCpc>(xs, xsum, s_src, nt, H);
+  if (nt == 1) gate_rows<BITS, CPL, RPS, 1>(L, B, Gq, Uq, erow, i0, shared, xs, xsum, s_tok, s_pair, nt, lane);
+  else gate_rows<BITS, CPL, RPS, kBTok>(L, B, Gq, Uq, erow, i0, shared, xs, xsum, s_tok, s_pair, nt, lane);
+  if (shared && sl == 0 && wid < nt) {
     // the shared_expert_gate logit of token s_tok[wid] (one row of H, its own bits)
     const int j = wid;
     const float* xsj = xs + j * H;
+    const int nch = H / kCpc;
     const int eb = L.sh_eg.bits;
     const int cpce = 128 / eb;
     const int nche = H / cpce;
@@ -189,25 +295,117 @@ __global__ void __launch_bounds__(kBThreads) k_bgate(DecodeLayer L, BatchWs B, i
     a = wave_sum(a);
     if (lane == 0) B.sg[s_tok[j]] = a;
   }
-  }
 }
 
 // ---------------------------------------------------------------------- down
-// A wave holds 64/LPR rows, LPR lanes per row, NCL 16-byte chunks per lane.
+// One unit = (tile or kBTok shared tokens) x (kBWaves * kBDSteps * kBRpl *
+// 64/LPR output rows).  LPR lanes share a row, NCL 16-byte chunks per lane;
+// a lane takes kBRpl rows per step, the next step's in flight.
 // LDS: [kBTok][h interleaved (Imax floats)][kBTok][chunk sums]
+template <int BITS, int NCL>
+struct DownStep {
+  uint4 w[kBRpl][NCL];
+  uint32_t sc[kBRpl][NCL], bi[kBRpl][NCL];
+};
+
 template <int BITS, int LPR, int NCL>
-__global__ void __launch_bounds__(kBThreads) k_bdown(DecodeLayer L, BatchWs B, int M, int K,
-                                                    const float* __restrict__ wts) {
+__device__ __forceinline__ void down_load(DownStep<BITS, NCL>& S, const QT& Dq, size_t erow, int r,
+                                          int H, int I, int ql) {
+  constexpr int kCpc = 128 / BITS;
+  constexpr int kGrp = kWave / LPR;
+  const int cpr = I / kCpc, gr = I / kGroup, wpr = I / (32 / BITS);
+#pragma unroll
+  for (int rr = 0; rr < kBRpl; ++rr) {
+    const size_t row = erow + min(r + rr * kGrp, H - 1);
+#pragma unroll
+    for (int j = 0; j < NCL; ++j) {
+      const int q = min(ql + LPR * j, cpr - 1);
+      const int grp = (q * kCpc) / kGroup;
+      S.w[rr][j] = reinterpret_cast<const uint4*>(Dq.q + row * wpr)[q];
+      S.sc[rr][j] = Dq.scales[row * gr + grp];
+      S.bi[rr][j] = Dq.biases[row * gr + grp];
+    }
+  }
+}
+
+template <int BITS, int LPR, int NCL, int T>
+__device__ __forceinline__ void down_rows(const DecodeLayer& L, const BatchWs& B, const QT& Dq,
+                                          size_t erow, int rbase, bool shared, const float* hs,
+                                          const float* hsum, const int* s_tok, const int* s_pair,
+                                          const float* s_w, int nt, int lane) {
+  constexpr int kCpc = 128 / BITS;
+  constexpr int kGrp = kWave / LPR;
+  constexpr int kRowsStep = kBRpl * kGrp;
+  constexpr int kN = kBRpl * T;
+  const int H = L.H;
+  const int I = shared ? L.Is : L.I;
+  const int cpr = I / kCpc;
+  const int ql = lane % LPR;
+  const int rl = lane / LPR;
+  DownStep<BITS, NCL> cur, nxt;
+  down_load<BITS, LPR, NCL>(cur, Dq, erow, rbase + rl, H, I, ql);
+#pragma unroll 1
+  for (int s = 0; s < kBDSteps; ++s) {
+    if (s + 1 < kBDSteps) down_load<BITS, LPR, NCL>(nxt, Dq, erow, rbase + (s + 1) * kRowsStep + rl, H, I, ql);
+    float acc[kBRpl][T];
+#pragma unroll
+    for (int rr = 0; rr < kBRpl; ++rr)
+#pragma unroll
+      for (int t = 0; t < T; ++t) acc[rr][t] = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCL; ++j) {
+      const int q0 = ql + LPR * j;
+      const bool ok = q0 < cpr;
+      const int q = min(q0, cpr - 1);
+      uint4 v[kBRpl];
+#pragma unroll
+      for (int rr = 0; rr < kBRpl; ++rr) v[rr] = cur.w[rr][j];
+      float d[kBRpl][T];
+#pragma unroll
+      for (int rr = 0; rr < kBRpl; ++rr)
+#pragma unroll
+        for (int t = 0; t < T; ++t) d[rr][t] = 0.f;
+      chunk_dots<BITS, kBRpl, T>(v, reinterpret_cast<const float4*>(hs) + q, cpr, I / 4, d);
+#pragma unroll
+      for (int rr = 0; rr < kBRpl; ++rr) {
+        const float sc = ok ? bf16_to_f32(cur.sc[rr][j]) : 0.f, bi = ok ? bf16_to_f32(cur.bi[rr][j]) : 0.f;
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          acc[rr][t] = fmaf(sc, d[rr][t], fmaf(bi, hsum[t * (I / 16) + q], acc[rr][t]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float pv[kN];
+#pragma unroll
+    for (int rr = 0; rr < kBRpl; ++rr)
+#pragma unroll
+      for (int t = 0; t < T; ++t) pv[rr * T + t] = acc[rr][t];
+    const float tot = treduce<kN, LPR / 2>(pv, lane);
+    const int vi = tindex<kN, LPR / 2>(lane);
+    const int rr = vi / T, t = vi - rr * T;
+    const int r = rbase + s * kRowsStep + rr * kGrp + rl;
+    if ((ql & (LPR / kN - 1)) == 0 && t < nt && r < H) {
+      if (shared) B.ysh[(size_t)s_tok[t] * H + r] = s_w[t] * tot;
+      else B.ypair[(size_t)s_pair[t] * H + r] = s_w[t] * tot;
+    }
+    if (s + 1 < kBDSteps) cur = nxt;
+  }
+}
+
+template <int BITS, int LPR, int NCL>
+__global__ void __launch_bounds__(kBThreads) __attribute__((amdgpu_waves_per_eu(3)))
+k_bdown(DecodeLayer L, BatchWs B, int M, int K, const float* __restrict__ wts) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   constexpr int kCpc = 128 / BITS;
-  constexpr int kRpw = kWave / LPR;                    // rows per wave
-  constexpr int kRows = kBWaves * kRpw;                // rows per unit
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
+  constexpr int kRowsStep = kBRpl * (kWave / LPR);
+  constexpr int kRowsUnit = kBWaves * kBDSteps * kRowsStep;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);   // uniform: row addresses in SGPRs
   const int H = L.H;
-  const int ndb = (H + kRows - 1) / kRows;
+  const int ndb = (H + kRowsUnit - 1) / kRowsUnit;
   const int item = blockIdx.x;
   const bool shared = item >= B.max_tiles * ndb;
-  int cb, rows, e = 0, row0 = 0;
+  int cb, nt, e = 0, row0 = 0, tg = 0;
   if (!shared) {
     const int tile = item / ndb;
     cb = item - tile * ndb;
@@ -215,48 +413,27 @@ __global__ void __launch_bounds__(kBThreads) k_bdown(DecodeLayer L, BatchWs B, i
     const int4 T = B.tiles[tile];
     e = T.x;
     row0 = T.y;
-    rows = T.z;
+    nt = T.z;
   } else {
-    cb = item - B.max_tiles * ndb;
-    rows = M;
+    const int it = item - B.max_tiles * ndb;
+    tg = it / ndb;
+    cb = it - tg * ndb;
+    nt = min(kBTok, M - tg * kBTok);
   }
   const QT Dq = shared ? L.sh_down : L.down;
   const int I = shared ? L.Is : L.I;
-  const int cpr = I / kCpc;                            // chunks per down row
-  const int gr = I / kGroup;
-  const int r = cb * kRows + wid * kRpw + lane / LPR;  // the lane's output row
-  const int rc = min(r, H - 1);
-  const int ql = lane % LPR;
-  const size_t drow = (size_t)e * H + rc;
   __shared__ int s_pair[kBTok], s_tok[kBTok];
   __shared__ float s_w[kBTok];
-  // the lane's chunks, their scales and biases (clamped addresses, no branches)
-  uint4 wv[NCL];
-  float sc[NCL], bi[NCL];
-#pragma unroll
-  for (int j = 0; j < NCL; ++j) {
-    const int q = min(ql + LPR * j, cpr - 1);
-    wv[j] = reinterpret_cast<const uint4*>(Dq.q + drow * (I / (32 / BITS)))[q];
-    const int grp = (q * kCpc) / kGroup;
-    sc[j] = bf16_to_f32(Dq.scales[drow * gr + grp]);
-    bi[j] = bf16_to_f32(Dq.biases[drow * gr + grp]);
-  }
-  float* hs = smem;                                    // [kBTok][I]
-  float* hsum = hs + kBTok * I;                        // [kBTok][I/16]
-  const int i4 = I / 4;
-  // the tile's pairs, kBTok at a time; the weights stay in registers
-  for (int j0 = 0; j0 < rows; j0 += kBTok) {
-  const int nj = min(kBTok, rows - j0);
-  __syncthreads();                                     // the previous group is done with LDS
+  __shared__ const float* s_src[kBTok];
   if (tid < kBTok) {
     int pr = 0, tk = 0;
     float wt = 0.f;
-    if (tid < nj) {
+    if (tid < nt) {
       if (shared) {
-        tk = j0 + tid;
+        tk = tg * kBTok + tid;
         wt = 1.0f / (1.0f + __expf(-B.sg[tk]));
       } else {
-        pr = B.sorted[row0 + j0 + tid];
+        pr = B.sorted[row0 + tid];
         tk = pr / K;
         wt = wts[pr];
       }
@@ -264,36 +441,16 @@ __global__ void __launch_bounds__(kBThreads) k_bdown(DecodeLayer L, BatchWs B, i
     s_pair[tid] = pr;
     s_tok[tid] = tk;
     s_w[tid] = wt;
+    s_src[tid] = shared ? B.hsh + (size_t)tk * L.Is : B.h + (size_t)pr * L.I;
   }
   __syncthreads();
-  for (int i = tid; i < nj * i4; i += kBThreads) {
-    const int j = i / i4, f = i - j * i4;
-    const float* src = shared ? B.hsh + (size_t)s_tok[j] * L.Is : B.h + (size_t)s_pair[j] * L.I;
-    reinterpret_cast<float4*>(hs + j * I)[ilv<kCpc>(f, cpr)] = reinterpret_cast<const float4*>(src)[f];
-  }
-  __syncthreads();
-  for (int j = 0; j < nj; ++j)
-    chunk_sums<kCpc>(reinterpret_cast<const float4*>(hs + j * I), hsum + j * (I / 16), cpr);
-  __syncthreads();
-  for (int j = 0; j < nj; ++j) {
-#pragma unroll
-    for (int c8 = 0; c8 < NCL; ++c8) opaque(wv[c8]);
-    const float4* h4 = reinterpret_cast<const float4*>(hs + j * I);
-    float acc = 0.f;
-#pragma unroll
-    for (int c8 = 0; c8 < NCL; ++c8) {
-      const int q = ql + LPR * c8;
-      if (q < cpr)
-        acc = fmaf(sc[c8], chunk_dot<BITS>(wv[c8], h4 + q, cpr), fmaf(bi[c8], hsum[j * (I / 16) + q], acc));
-    }
-    float v[1] = {acc};
-    const float tot = treduce<1, LPR / 2>(v, lane);
-    if (ql == 0 && r < H) {
-      if (shared) B.ysh[(size_t)s_tok[j] * H + r] = s_w[j] * tot;
-      else B.ypair[(size_t)s_pair[j] * H + r] = s_w[j] * tot;
-    }
-  }
-  }
+  float* hs = smem;                                    // [kBTok][I]
+  float* hsum = hs + kBTok * I;                        // [kBTok][I/16]
+  stage_rows<kCpc>(hs, hsum, s_src, nt, I);
+  const int rbase = cb * kRowsUnit + wid * kBDSteps * kRowsStep;
+  const size_t erow = (size_t)e * H;
+  if (nt == 1) down_rows<BITS, LPR, NCL, 1>(L, B, Dq, erow, rbase, shared, hs, hsum, s_tok, s_pair, s_w, nt, lane);
+  else down_rows<BITS, LPR, NCL, kBTok>(L, B, Dq, erow, rbase, shared, hs, hsum, s_tok, s_pair, s_w, nt, lane);
 }
 
 // y[t][c] = sum over slots k in order of ypair[t*K+k][c] (+ shared) (+ residual);
@@ -348,13 +505,12 @@ static void b_lpr(int I, int bits, int* lpr, int* ncl) {
 bool batch_supported(const DecodeLayer& L) {
   const int b = L.gate.bits;
   if (L.H > 4096 || !b_cpl(L.H, b)) return false;
-  if (4 * kBGRows * (L.H / kGroup) * 2 / 16 > kBThreads) return false;
-  if (L.I % kBGRows) return false;
+  if (L.I % kBSlab) return false;
   int lpr, ncl;
   b_lpr(L.I, b, &lpr, &ncl);
   if (!ncl) return false;
   if (L.has_shared) {
-    if (L.sh_gate.bits != b || L.Is % kBGRows) return false;
+    if (L.sh_gate.bits != b || L.Is % kBSlab) return false;
     int l2, n2;
     b_lpr(L.Is, b, &l2, &n2);
     if (l2 != lpr || n2 != ncl) return false;
@@ -364,7 +520,7 @@ bool batch_supported(const DecodeLayer& L) {
 }
 
 static size_t bgate_lds(const DecodeLayer& L) {
-  return sizeof(float) * (size_t)kBTok * (L.H + L.H / 16) + 2 * 4 * kBGRows * (L.H / kGroup);
+  return sizeof(float) * (size_t)kBTok * (L.H + L.H / 16);
 }
 static size_t bdown_lds(const DecodeLayer& L) {
   const int Im = L.has_shared && L.Is > L.I ? L.Is : L.I;
@@ -377,27 +533,25 @@ int launch_batch_forward(const DecodeLayer& L, const float* x, const int32_t* id
   const int b = L.gate.bits;
   const int n = M * K;
   launch_sort_pairs_bm(idx, n, L.E, B.sort, kBTile, s);
-  const int ngr = L.I / kBGRows;
-  const int nst = L.has_shared ? 1 : 0;                // the shared expert: one tile of all M tokens
-  const int ngs = L.has_shared ? L.Is / kBGRows : 0;
-  const dim3 gg((unsigned)(B.max_tiles * ngr + nst * ngs));
+  const int ntg = L.has_shared ? (M + kBTok - 1) / kBTok : 0;   // shared-expert token groups
+  const int nsl = L.I / kBSlab, nss = L.has_shared ? L.Is / kBSlab : 0;
+  const dim3 gg((unsigned)(B.max_tiles * nsl + ntg * nss));
   const size_t lg = bgate_lds(L);
   const int cpl = b_cpl(L.H, b);
-// (dynamic LDS above 64 KB needs the kernel's limit raised first)
-#define MOEQ_BG(B_, C_)                                                                     \
-  if (b == B_ && cpl == C_) {                                                              \
-    (void)hipFuncSetAttribute((const void*)k_bgate<B_, C_>,                                \
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lg);         \
-    hipLaunchKernelGGL((k_bgate<B_, C_>), gg, dim3(kBThreads), lg, s, L, B, M, K, x);      \
+#define MOEQ_BG(B_, C_, R_)                                                                   \
+  if (b == B_ && cpl == C_) {                                                                \
+    (void)hipFuncSetAttribute((const void*)k_bgate<B_, C_, R_>,                              \
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lg);           \
+    hipLaunchKernelGGL((k_bgate<B_, C_, R_>), gg, dim3(kBThreads), lg, s, L, B, M, K, x);    \
   }
-  MOEQ_BG(8, 1) MOEQ_BG(8, 2) MOEQ_BG(8, 4) MOEQ_BG(4, 1) MOEQ_BG(4, 2) MOEQ_BG(4, 4)
-  MOEQ_BG(2, 1) MOEQ_BG(2, 2) MOEQ_BG(2, 4)
+  MOEQ_BG(8, 1, 2) MOEQ_BG(8, 2, 1) MOEQ_BG(8, 4, 1) MOEQ_BG(4, 1, 2) MOEQ_BG(4, 2, 1)
+  MOEQ_BG(4, 4, 1) MOEQ_BG(2, 1, 2) MOEQ_BG(2, 2, 1) MOEQ_BG(2, 4, 1)
 #undef MOEQ_BG
   int lpr, ncl;
   b_lpr(L.I, b, &lpr, &ncl);
-  const int rows_unit = kBWaves * (kWave / lpr);
+  const int rows_unit = kBWaves * kBDSteps * kBRpl * (kWave / lpr);
   const int ndb = (L.H + rows_unit - 1) / rows_unit;
-  const dim3 gd((unsigned)(B.max_tiles * ndb + nst * ndb));
+  const dim3 gd((unsigned)(B.max_tiles * ndb + ntg * ndb));
   const size_t ld = bdown_lds(L);
 #define MOEQ_BD(B_, L_, N_)                                                                 \
   if (b == B_ && lpr == L_ && ncl == N_) {                                                 \

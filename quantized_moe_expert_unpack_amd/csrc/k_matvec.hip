@@ -183,6 +183,65 @@ __global__ void __launch_bounds__(kRouteThreads) k_router(QT W, const float* __r
   }
 }
 
+// Router projection for many tokens, the same fp64 arithmetic as k_router:
+// one wave per (router row, kRouteTM tokens).  Each weight is dequantized and
+// widened once and feeds kRouteTM independent fp64 chains; the grid spans
+// rows and token blocks so that it fills the chip.
+constexpr int kRouteTM = 8;
+template <int BITS>
+__global__ void __launch_bounds__(kRouteThreads) k_router_many(QT W, const float* __restrict__ x,
+                                                               int M, double* __restrict__ logits,
+                                                               float* __restrict__ logits32) {
+  constexpr int kCpc = 128 / BITS;
+  const int rows = W.rows, cols = W.cols;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = blockIdx.x * (kRouteThreads / kWave) + (threadIdx.x / kWave);
+  const int m0 = blockIdx.y * kRouteTM;
+  if (r >= rows) return;
+  const int nm = min(kRouteTM, M - m0);
+  const int chunks = cols / kCpc;
+  const int groups = cols / kGroup;
+  const uint4* rq = reinterpret_cast<const uint4*>(W.q + (size_t)r * (cols / (32 / BITS)));
+  const uint16_t* rs = W.scales + (size_t)r * groups;
+  const uint16_t* rb = W.biases + (size_t)r * groups;
+  double acc[kRouteTM];
+#pragma unroll
+  for (int t = 0; t < kRouteTM; ++t) acc[t] = 0.0;
+  for (int c = lane; c < chunks; c += kWave) {
+    const uint4 v = rq[c];
+    const int g = (c * kCpc) / kGroup;
+    const float s = bf16_to_f32(rs[g]);
+    const float b = bf16_to_f32(rb[g]);
+#pragma unroll
+    for (int j = 0; j < kCpc; j += 4) {
+      float4 xv[kRouteTM];
+#pragma unroll
+      for (int t = 0; t < kRouteTM; ++t)   // rows past the last token re-read token 0's x
+        xv[t] = *reinterpret_cast<const float4*>(x + (size_t)(m0 + (t < nm ? t : 0)) * cols +
+                                                 (size_t)c * kCpc + j);
+      double w[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) w[q] = (double)fmaf(s, (float)chunk_code<BITS>(v, j + q), b);
+#pragma unroll
+      for (int t = 0; t < kRouteTM; ++t) {
+        acc[t] = fma(w[0], (double)xv[t].x, acc[t]);
+        acc[t] = fma(w[1], (double)xv[t].y, acc[t]);
+        acc[t] = fma(w[2], (double)xv[t].z, acc[t]);
+        acc[t] = fma(w[3], (double)xv[t].w, acc[t]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kRouteTM; ++t) {
+    const double a = wave_sum(acc[t]);
+    if (lane == 0 && t < nm) {
+      logits[(size_t)(m0 + t) * rows + r] = a;
+      if (logits32) logits32[(size_t)(m0 + t) * rows + r] = (float)a;
+    }
+  }
+}
+
 // top-K for many tokens: one block per token, logits fp64 (router) or fp32 (given)
 __global__ void __launch_bounds__(kRouteThreads) k_topk_rows(const double* __restrict__ l64,
                                                              const float* __restrict__ l32, int M,
@@ -259,14 +318,15 @@ int launch_route_parts(const QT* router, const float* x_or_logits, int M, int E,
   const dim3 grid((E + 3) / 4);
   const QT& W = *router;
   const bool last = M <= kLastTopkMaxM;
+  const dim3 grid_many((E + 3) / 4, (M + kRouteTM - 1) / kRouteTM);
 #define MOEQ_ROUTER(B_)                                                                           \
   if (W.bits == B_) {                                                                             \
     if (last)                                                                                     \
       hipLaunchKernelGGL((k_router<B_, true>), grid, dim3(kRouteThreads), 0, s, W, x_or_logits, M, \
                          K, renorm, l64, ctr, logits32, idx, w);                                   \
     else                                                                                          \
-      hipLaunchKernelGGL((k_router<B_, false>), grid, dim3(kRouteThreads), 0, s, W, x_or_logits,  \
-                         M, K, renorm, l64, ctr, logits32, idx, w);                               \
+      hipLaunchKernelGGL((k_router_many<B_>), grid_many, dim3(kRouteThreads), 0, s, W,            \
+                         x_or_logits, M, l64, logits32);                                          \
   }
   MOEQ_ROUTER(8)
   MOEQ_ROUTER(4)

@@ -93,9 +93,9 @@ struct GatherWs {
 constexpr int kGemmBM = 256;  // rows per gather-GEMM tile
 
 // Batched decode (many fp32 tokens; k_batch.hip): pairs grouped by expert in
-// tiles of at most kBTile rows, applied kBTok tokens at a time.
-constexpr int kBTile = 16;
-constexpr int kBTok = 4;
+// tiles of at most kBTile pairs; a unit applies its rows to kBTok tokens.
+constexpr int kBTok = 2;
+constexpr int kBTile = kBTok;
 constexpr int kBatchMinM = 16;   // from this many tokens moe_expert_forward batches by expert
 struct BatchWs {
   GatherWs sort;         // pair sort by expert (tiles of kBTile rows)
