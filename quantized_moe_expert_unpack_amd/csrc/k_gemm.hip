@@ -5,13 +5,17 @@
 // here carries its exact row count in int32, rows past it are zero-filled on
 // load and never stored.
 //
-// A block computes a 256-row x 128-column tile of one expert: 256 rows
-// gathered through the sorted pair list, 128 weight rows ("B columns").  Per
-// 64-wide reduction step (one quantization group) it stages the A rows as bf16
-// in LDS and dequantizes the B codes to bf16 in LDS (w = scale*code + bias,
-// rounded to nearest even), while the next step's global loads are in flight;
-// four waves each own a 128x64 sub-tile (4x2 MFMA 32x32 tiles).  Dequantizing
-// once per 256 rows keeps the VALU work well under the MFMA time.
+// A block computes a 256-row x 256-column tile of one expert: 256 rows
+// gathered through the sorted pair list, 256 weight rows ("B columns").  Per
+// 64-wide reduction step (one quantization group) the A rows are staged as
+// bf16 in LDS and the B codes dequantized to bf16 in LDS (w = scale*code +
+// bias, rounded to nearest even).  LDS holds two stages: while the waves run
+// the MFMAs of one stage, the next steps' global loads land in registers (two
+// steps ahead) and are written to the other stage, one barrier per step.
+// Eight waves, two per SIMD, each own a 128x64 sub-tile (4x2 MFMA 32x32
+// tiles): the two waves of a SIMD hide each other's load, LDS and barrier
+// waits, and a 256-column block re-reads the gathered A rows half as often as
+// a 128-column one.
 //
 // Tile order is XCD-aware: workgroups are dealt round-robin to the 8 XCDs, so
 // block b works on item (b % 8) * ceil(T/8) + b / 8 of the T (m-tile, n-tile)
@@ -19,7 +23,9 @@
 // and the gathered A rows are re-read from that XCD's L2, not from HBM.
 //
 // Modes: 0 plain   out[pair][n] = x[pair] . W_e[n]                 (fp32)
-//        1 gate/up h[sorted row][i] = silu(x.G_e[i]) * (x.U_e[i])  (bf16)
+//        1 gate/up h[sorted row][i] = silu(x.G_e[i]) * (x.U_e[i])  (bf16);
+//                  a block's columns are 128 rows i of gate and the same
+//                  128 of up (per wave: 32 of each)
 //        2 down    ypair[pair][n] = w_pair * (h[sorted row] . D_e[n]) (bf16)
 #include "common.h"
 #include "launch.h"
@@ -29,72 +35,51 @@ namespace moeq {
 typedef short bf16x8 __attribute__((__vector_size__(8 * sizeof(short))));
 typedef float f32x16 __attribute__((__vector_size__(16 * sizeof(float))));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// staging registers as a native vector (HIP's uint4 is a struct with a union,
+// which keeps the compiler from promoting arrays of it to registers here)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kBM = kGemmBM;  // 256 rows
-constexpr int kBN = 128;      // B columns per block
+constexpr int kBN = 256;      // B columns per block
 constexpr int kBK = 64;       // one group per k-step
 constexpr int kLds = kBK + 8; // padded row stride (bf16 elements): 144 B, conflict-free b128 reads
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;   // eight waves, two per SIMD
 constexpr int kXcd = 8;
+constexpr int kStage = (kBM + kBN) * kLds;                      // bf16 elements per LDS stage
+constexpr size_t kGemmLds = 2 * (size_t)kStage * sizeof(uint16_t);
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   const bf16x2_t v = {(__bf16)a, (__bf16)b};   // v_cvt_pk_bf16_f32: round to nearest even
   return __builtin_bit_cast(uint32_t, v);
 }
 
-// dequantize 32 codes (this thread's half of a 64-code group) to 16 packed bf16 pairs
+// dequantize codes [32h, 32h + 32) of one group (its 16 / 8 / 4 words in v)
+// to 16 packed bf16 pairs
 template <int BITS>
-__device__ __forceinline__ void dequant32(const uint4* v, float s, float b, uint32_t* out) {
-  if constexpr (BITS == 8) {
+__device__ __forceinline__ void dequant32h(const u32x4* v, int h, float s, float b, uint32_t* out) {
+  constexpr int kPer = 32 / BITS;
+  constexpr uint32_t kMask = (1u << BITS) - 1u;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) {
-      const uint32_t x = w < 4 ? (&v[0].x)[w] : (&v[1].x)[w - 4];
-      out[2 * w] = pack_bf16(fmaf(s, (float)(x & 0xFFu), b), fmaf(s, (float)((x >> 8) & 0xFFu), b));
-      out[2 * w + 1] = pack_bf16(fmaf(s, (float)((x >> 16) & 0xFFu), b), fmaf(s, (float)(x >> 24), b));
-    }
-  } else if constexpr (BITS == 4) {
+  for (int w = 0; w < 32 / kPer; ++w) {
+    const int wi = h * (32 / kPer) + w;
+    const uint32_t x = v[wi / 4][wi % 4];
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      const uint32_t x = (&v[0].x)[w];
-#pragma unroll
-      for (int j = 0; j < 8; j += 2)
-        out[4 * w + j / 2] = pack_bf16(fmaf(s, (float)((x >> (4 * j)) & 0xFu), b),
-                                       fmaf(s, (float)((x >> (4 * j + 4)) & 0xFu), b));
-    }
-  } else {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const uint32_t x = (&v[0].x)[w];
-#pragma unroll
-      for (int j = 0; j < 16; j += 2)
-        out[8 * w + j / 2] = pack_bf16(fmaf(s, (float)((x >> (2 * j)) & 0x3u), b),
-                                       fmaf(s, (float)((x >> (2 * j + 2)) & 0x3u), b));
-    }
-  }
-}
-
-template <int BITS>
-__device__ __forceinline__ void load_codes(uint4* v, const uint32_t* p) {
-  if constexpr (BITS == 8) {
-    v[0] = reinterpret_cast<const uint4*>(p)[0];
-    v[1] = reinterpret_cast<const uint4*>(p)[1];
-  } else if constexpr (BITS == 4) {
-    v[0] = reinterpret_cast<const uint4*>(p)[0];
-  } else {
-    const uint2 t = reinterpret_cast<const uint2*>(p)[0];
-    v[0] = make_uint4(t.x, t.y, 0u, 0u);
+    for (int j = 0; j < kPer; j += 2)
+      out[(w * kPer + j) / 2] = pack_bf16(fmaf(s, (float)((x >> (BITS * j)) & kMask), b),
+                                          fmaf(s, (float)((x >> (BITS * j + BITS)) & kMask), b));
   }
 }
 
 template <int BITS, int MODE>
-__global__ void __launch_bounds__(kThreads, 2) k_gqmm(QT W, QT W2, int N, int Kd,
+__global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd,
                                                       const uint16_t* __restrict__ A, int a_div,
                                                       GatherWs ws, const float* __restrict__ wts,
                                                       void* __restrict__ out, int ntn) {
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * kLds];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[kBN * kLds];
+  extern __shared__ __attribute__((aligned(16))) uint16_t gsm[];
   __shared__ int s_pair[kBM];
   __shared__ float s_w[kBM];
+  constexpr int kWords = 64 * BITS / 32;     // code words per group and column
+  constexpr int kV = (kWords / 2 + 3) / 4;   // 16-byte words per thread (half a group)
 
   // ---- XCD-aware item: block b -> item (b % 8) * ceil(T/8) + b / 8
   const int T = ws.n_tiles[0] * ntn;
@@ -108,7 +93,7 @@ __global__ void __launch_bounds__(kThreads, 2) k_gqmm(QT W, QT W2, int N, int Kd
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wid = tid / kWave;
-  const int wm = wid & 1, wn = wid >> 1;
+  const int wm = wid & 1, wn = wid >> 1;      // 2 row halves x 4 column quarters
 
   for (int r = tid; r < kBM; r += kThreads) {
     const int pair = r < rows ? ws.sorted[row0 + r] : 0;
@@ -117,36 +102,41 @@ __global__ void __launch_bounds__(kThreads, 2) k_gqmm(QT W, QT W2, int N, int Kd
   }
   __syncthreads();
 
-  // ---- A source rows: rows (tid>>3) + 32u (u < 8), 16-byte segment tid&7
+  // ---- A source rows: rows (tid>>3) + 64u (u < 4), 16-byte segment tid&7
   const int aseg = tid & 7;
-  const uint16_t* asrc[8];
+  // (32-bit element offsets from A: the activations of one call stay below
+  // 2^31 elements).  Rows past the tile's count re-read its first row: an
+  // output row depends on its own A row only, and those rows are never stored,
+  // so the loads need no branches.
+  int aoff[4];
 #pragma unroll
-  for (int u = 0; u < 8; ++u) {
-    const int r = (tid >> 3) + 32 * u;
-    asrc[u] = nullptr;
-    if (r < rows) asrc[u] = MODE == 2 ? A + (size_t)(row0 + r) * Kd : A + (size_t)(s_pair[r] / a_div) * Kd;
+  for (int u = 0; u < 4; ++u) {
+    const int r = (tid >> 3) + 64 * u;
+    const int rc = r < rows ? r : 0;
+    aoff[u] = (MODE == 2 ? row0 + rc : s_pair[rc] / a_div) * Kd + aseg * 8;
   }
 
-  // ---- B column of this thread: column bc = tid>>1, codes [32*bh, 32*bh+32) of each group
+  // ---- B column of this thread: bc = tid >> 1, codes [32 bh, 32 bh + 32) of
+  // each group.  Columns past N read column N-1 (their outputs are never
+  // stored).
   const int bc = tid >> 1, bh = tid & 1;
-  const uint32_t* bq = nullptr;
-  const uint16_t *bs = nullptr, *bb = nullptr;
+  const uint32_t* bq;
+  const uint16_t *bs, *bb;
   {
     int n;
     const QT* M = &W;
     if (MODE == 1) {
-      const int cw = bc >> 6, hf = (bc >> 5) & 1, j = bc & 31;
-      n = nt * 64 + cw * 32 + j;
+      // wave column cw = bc >> 6 holds gate rows then up rows of i in [32 cw, 32 cw + 32)
+      const int cw = bc >> 6, hf = (bc >> 5) & 1;
+      n = nt * 128 + cw * 32 + (bc & 31);
       if (hf) M = &W2;
     } else {
       n = nt * kBN + bc;
     }
-    if (n < N) {
-      const size_t row = (size_t)e * N + n;
-      bq = M->q + row * (Kd / (32 / BITS)) + bh * BITS;  // 32 codes = BITS words
-      bs = M->scales + row * (Kd / kGroup);
-      bb = M->biases + row * (Kd / kGroup);
-    }
+    const size_t row = (size_t)e * N + min(n, N - 1);
+    bq = M->q + row * (Kd / (32 / BITS)) + bh * BITS;   // 32 codes = BITS words
+    bs = M->scales + row * (Kd / kGroup);
+    bb = M->biases + row * (Kd / kGroup);
   }
 
   f32x16 acc[4][2];
@@ -157,45 +147,43 @@ __global__ void __launch_bounds__(kThreads, 2) k_gqmm(QT W, QT W2, int N, int Kd
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 areg[8];
-  uint4 breg[2];
-  float bsv = 0.f, bbv = 0.f;
+  // two register stages of global loads: step k's data lands in stage k % 2
+  u32x4 a0[4], a1[4], b0[kV], b1[kV];
+  float s0 = 0.f, c0 = 0.f, s1 = 0.f, c1 = 0.f;   // scale, bias
   const int ksteps = Kd / kBK;
 
-  auto gload = [&](int kt) {
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      areg[u] = asrc[u] ? *reinterpret_cast<const uint4*>(asrc[u] + kt * kBK + aseg * 8)
-                        : make_uint4(0, 0, 0, 0);
-    if (bq) {
-      load_codes<BITS>(breg, bq + (size_t)kt * (kBK / (32 / BITS)));
-      bsv = bf16_to_f32(bs[kt]);
-      bbv = bf16_to_f32(bb[kt]);
-    }
-  };
+#define MOEQ_GLOAD(AR, BR, SV, CV, KT)                                                        \
+  do {                                                                                        \
+    const int k_ = (KT);                                                                      \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u)                                             \
+      AR[u] = *reinterpret_cast<const u32x4*>(A + aoff[u] + k_ * kBK);                        \
+    const uint32_t* p_ = bq + (size_t)k_ * kWords;                                            \
+    if constexpr (BITS == 2) {                                                                \
+      const uint2 t_ = *reinterpret_cast<const uint2*>(p_);                                   \
+      BR[0] = u32x4{t_.x, t_.y, 0u, 0u};                                                      \
+    } else {                                                                                  \
+      _Pragma("unroll") for (int q = 0; q < kV; ++q) BR[q] = reinterpret_cast<const u32x4*>(p_)[q]; \
+    }                                                                                         \
+    SV = bf16_to_f32(bs[k_]);                                                                 \
+    CV = bf16_to_f32(bb[k_]);                                                                 \
+  } while (0)
+#define MOEQ_LSTORE(AR, BR, SV, CV, BUF)                                                      \
+  do {                                                                                        \
+    uint16_t* As_ = gsm + (BUF) * kStage;                                                     \
+    uint16_t* Bs_ = As_ + kBM * kLds;                                                         \
+    _Pragma("unroll") for (int u = 0; u < 4; ++u)                                             \
+      *reinterpret_cast<u32x4*>(&As_[((tid >> 3) + 64 * u) * kLds + aseg * 8]) = AR[u];       \
+    u32x4* d_ = reinterpret_cast<u32x4*>(&Bs_[bc * kLds + bh * 32]);                          \
+    uint32_t pk_[16];                                                                         \
+    dequant32h<BITS>(BR, 0, SV, CV, pk_);                                                     \
+    _Pragma("unroll") for (int q = 0; q < 4; ++q)                                             \
+      d_[q] = u32x4{pk_[4 * q], pk_[4 * q + 1], pk_[4 * q + 2], pk_[4 * q + 3]};              \
+  } while (0)
 
-  gload(0);
-  for (int kt = 0; kt < ksteps; ++kt) {
-    // ---- registers -> LDS (B dequantized to bf16)
-#pragma unroll
-    for (int u = 0; u < 8; ++u)
-      *reinterpret_cast<uint4*>(&As[((tid >> 3) + 32 * u) * kLds + aseg * 8]) = areg[u];
-    {
-      uint32_t packed[16];
-      if (bq) {
-        dequant32<BITS>(breg, bsv, bbv, packed);
-      } else {
-#pragma unroll
-        for (int j = 0; j < 16; ++j) packed[j] = 0u;
-      }
-      uint4* dst = reinterpret_cast<uint4*>(&Bs[bc * kLds + bh * 32]);
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        dst[q] = make_uint4(packed[4 * q], packed[4 * q + 1], packed[4 * q + 2], packed[4 * q + 3]);
-    }
-    __syncthreads();
-    if (kt + 1 < ksteps) gload(kt + 1);
-    // ---- MFMA on the staged tile: 4 k16 steps x (4 x 2) tiles
+  auto mfma_step = [&](int buf) {
+    const uint16_t* As = gsm + buf * kStage;
+    const uint16_t* Bs = As + kBM * kLds;
+    // 4 k16 steps x (4 x 4) tiles
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int kof = kk * 16 + 8 * (lane >> 5);
@@ -212,8 +200,33 @@ __global__ void __launch_bounds__(kThreads, 2) k_gqmm(QT W, QT W2, int N, int Kd
         for (int ni = 0; ni < 2; ++ni)
           acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
     }
+  };
+
+  // a step: the loads of step kt+2 go out first (into the register stage step
+  // kt used), the MFMAs of step kt run on LDS stage kt % 2, then step kt+1
+  // (loaded one step earlier) is written to the other LDS stage.  The body
+  // has no branches (loads past the last step re-read it), so the compiler
+  // can interleave the loads, LDS traffic and dequantization with the MFMAs;
+  // both halves always run their MFMAs, and with an odd step count the last
+  // half's B stage is written with zero scale and bias so it adds nothing.
+  const int klast = ksteps - 1;
+  MOEQ_GLOAD(a0, b0, s0, c0, 0);
+  MOEQ_GLOAD(a1, b1, s1, c1, min(1, klast));
+  MOEQ_LSTORE(a0, b0, s0, c0, 0);
+  __syncthreads();
+  for (int kt = 0; kt < ksteps; kt += 2) {
+    const float on = kt + 1 < ksteps ? 1.f : 0.f;
+    MOEQ_GLOAD(a0, b0, s0, c0, min(kt + 2, klast));
+    mfma_step(0);
+    MOEQ_LSTORE(a1, b1, s1 * on, c1 * on, 1);
+    __syncthreads();
+    MOEQ_GLOAD(a1, b1, s1, c1, min(kt + 3, klast));
+    mfma_step(1);
+    MOEQ_LSTORE(a0, b0, s0, c0, 0);
     __syncthreads();
   }
+#undef MOEQ_GLOAD
+#undef MOEQ_LSTORE
 
   // ---- epilogue.  32x32 accumulator layout: register r of lane l holds
   // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
@@ -224,11 +237,15 @@ __global__ void __launch_bounds__(kThreads, 2) k_gqmm(QT W, QT W2, int N, int Kd
       const int rl = wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
       if (rl >= rows) continue;
       if (MODE == 1) {
-        const int i = nt * 64 + wn * 32 + (lane & 31);
-        const float h = silu(acc[mi][0][r]) * acc[mi][1][r];
-        const bf16x2_t hv = {(__bf16)h, (__bf16)0.f};
-        reinterpret_cast<uint16_t*>(out)[(size_t)(row0 + rl) * N + i] =
-            (uint16_t)(__builtin_bit_cast(uint32_t, hv) & 0xFFFFu);
+        {
+          const int i = nt * 128 + wn * 32 + (lane & 31);
+          if (i < N) {
+            const float h = silu(acc[mi][0][r]) * acc[mi][1][r];
+            const bf16x2_t hv = {(__bf16)h, (__bf16)0.f};
+            reinterpret_cast<uint16_t*>(out)[(size_t)(row0 + rl) * N + i] =
+                (uint16_t)(__builtin_bit_cast(uint32_t, hv) & 0xFFFFu);
+          }
+        }
       } else {
         const int pair = s_pair[rl];
 #pragma unroll
@@ -289,12 +306,25 @@ __global__ void __launch_bounds__(256) k_mark_invalid(const int32_t* __restrict_
   for (int c = threadIdx.x; c < N; c += blockDim.x) out[(size_t)row * N + c] = __builtin_nanf("");
 }
 
-#define MOEQ_GEMM_BITS(bits, MODE_, ...)                                                        \
-  do {                                                                                         \
-    if ((bits) == 8) hipLaunchKernelGGL((k_gqmm<8, MODE_>), __VA_ARGS__);                      \
-    else if ((bits) == 4) hipLaunchKernelGGL((k_gqmm<4, MODE_>), __VA_ARGS__);                 \
-    else hipLaunchKernelGGL((k_gqmm<2, MODE_>), __VA_ARGS__);                                  \
-  } while (0)
+template <int BITS, int MODE>
+static void gemm_launch(dim3 grid, hipStream_t s, const QT& W, const QT& W2, int N, int Kd,
+                        const uint16_t* A, int a_div, const GatherWs& ws, const float* wts,
+                        void* out, int ntn) {
+  // two LDS stages of 147,456 bytes: above the default dynamic limit
+  (void)hipFuncSetAttribute((const void*)k_gqmm<BITS, MODE>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+  hipLaunchKernelGGL((k_gqmm<BITS, MODE>), grid, dim3(kThreads), kGemmLds, s, W, W2, N, Kd, A,
+                     a_div, ws, wts, out, ntn);
+}
+
+template <int MODE>
+static void gemm_bits(int bits, dim3 grid, hipStream_t s, const QT& W, const QT& W2, int N, int Kd,
+                      const uint16_t* A, int a_div, const GatherWs& ws, const float* wts,
+                      void* out, int ntn) {
+  if (bits == 8) gemm_launch<8, MODE>(grid, s, W, W2, N, Kd, A, a_div, ws, wts, out, ntn);
+  else if (bits == 4) gemm_launch<4, MODE>(grid, s, W, W2, N, Kd, A, a_div, ws, wts, out, ntn);
+  else gemm_launch<2, MODE>(grid, s, W, W2, N, Kd, A, a_div, ws, wts, out, ntn);
+}
 
 static dim3 gemm_grid(const GatherWs& ws, int ntn) {
   const int items = ws.max_tiles * ntn;
@@ -305,9 +335,8 @@ int launch_gemm_gate_up(const QT& gate, const QT& up, const uint16_t* x, int K, 
                         int n, hipStream_t s) {
   (void)n;
   const int I = gate.rows, H = gate.cols;
-  const int ntn = I / 64;
-  MOEQ_GEMM_BITS(gate.bits, 1, gemm_grid(ws, ntn), dim3(kThreads), 0, s, gate, up, I, H, x, K, ws,
-                 (const float*)nullptr, (void*)ws.h, ntn);
+  const int ntn = (I + 127) / 128;
+  gemm_bits<1>(gate.bits, gemm_grid(ws, ntn), s, gate, up, I, H, x, K, ws, nullptr, (void*)ws.h, ntn);
   return 0;
 }
 
@@ -315,8 +344,8 @@ int launch_gemm_down(const QT& down, const float* w, const GatherWs& ws, int n, 
   (void)n;
   const int H = down.rows, I = down.cols;
   const int ntn = (H + kBN - 1) / kBN;
-  MOEQ_GEMM_BITS(down.bits, 2, gemm_grid(ws, ntn), dim3(kThreads), 0, s, down, down, H, I,
-                 (const uint16_t*)ws.h, 1, ws, w, (void*)ws.ypair, ntn);
+  gemm_bits<2>(down.bits, gemm_grid(ws, ntn), s, down, down, H, I, (const uint16_t*)ws.h, 1, ws, w,
+               (void*)ws.ypair, ntn);
   return 0;
 }
 
@@ -324,8 +353,7 @@ int launch_gemm_plain(const QT& W, const uint16_t* x, float* out, const GatherWs
                       hipStream_t s) {
   (void)n;
   const int ntn = (W.rows + kBN - 1) / kBN;
-  MOEQ_GEMM_BITS(W.bits, 0, gemm_grid(ws, ntn), dim3(kThreads), 0, s, W, W, W.rows, W.cols, x, 1, ws,
-                 (const float*)nullptr, (void*)out, ntn);
+  gemm_bits<0>(W.bits, gemm_grid(ws, ntn), s, W, W, W.rows, W.cols, x, 1, ws, nullptr, (void*)out, ntn);
   return 0;
 }
 

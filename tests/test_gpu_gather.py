@@ -60,6 +60,29 @@ def test_moe_gather_small_m_vs_oracle(m):
     assert err.max() <= TOL
 
 
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_moe_gather_widths_off_the_tile_grid(bits):
+    # H = 320 (not a multiple of the 256-column down tile) and I = 192 (not a
+    # multiple of the 128 gate/up rows of a tile): ragged column tiles in
+    # both GEMMs, and rows past the last expert's 256-row tile
+    cfg = synth.scaled(synth.CONFIGS["c4"], hidden=320, inter=192, experts=8, top_k=2,
+                       expert_bits=bits, router_bits=8, tokens=600, seed=40 + bits)
+    host = synth.host_layer(cfg, 0, threads=16)
+    L = moeq.MoELayer.from_host(host, dev())
+    m = 600
+    say(f"moe_gather_qmm H=320 I=192 bits={bits} M={m}")
+    xb = synth.prefill_x_bf16(cfg, m)
+    lg = synth.zipf_logits(cfg, m)
+    y, idx, w = _prefill(cfg, L, xb, lg, poison=POISON[0])
+    ridx, rw, _ = oracle.route(lg.astype(np.float64), cfg.top_k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    ref = oracle.moe_experts(host, bf16_bits_to_f32(xb), ridx, rw)
+    err = rel_l2_rows(y.cpu().numpy(), ref)
+    say(f"  max rel-L2 {err.max():.3e}")
+    assert np.isfinite(y.cpu().numpy()).all()
+    assert err.max() <= TOL
+
+
 @pytest.mark.parametrize("m", [16068, 16384])
 def test_c4_full_size_sampled_rows_chunks_poison(m):
     cfg, host, L = _c4_layer()
