@@ -247,6 +247,19 @@ k_bgate(DecodeLayer L, BatchWs B, int M, int K, const float* __restrict__ x) {
   const int I = shared ? L.Is : L.I;
   const size_t erow = (size_t)e * I;
   const int i0 = sl * kBSlab + wid * (kBSlab / kBWaves);
+  // the units of the shared expert's first rows also compute their tokens'
+  // shared_expert_gate logits (one row of H, its own bits): one 16-byte chunk
+  // per thread (H * bits / 128 <= kBThreads), loaded up front
+  const bool sgu = shared && sl == 0;               // uniform over the block
+  const int eb = L.sh_eg.bits, cpce = 128 / eb, nche = H / cpce;
+  uint4 egv = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t egsb = 0u;
+  if (sgu) {
+    const int c = min(tid, nche - 1);
+    const int gg = (c * cpce) / kGroup;
+    egv = reinterpret_cast<const uint4*>(L.sh_eg.q)[c];
+    egsb = (uint32_t)L.sh_eg.scales[gg] | ((uint32_t)L.sh_eg.biases[gg] << 16);
+  }
   __shared__ int s_tok[kBTok], s_pair[kBTok];
   __shared__ const float* s_src[kBTok];
   if (tid < kBTok) {
@@ -267,33 +280,48 @@ k_bgate(DecodeLayer L, BatchWs B, int M, int K, const float* __restrict__ x) {
   float* xs = smem;                                    // [kBTok][H]
   float* xsum = xs + kBTok * H;                        // [kBTok][H/16]
   stage_rows<kCpc>(xs, xsum, s_src, nt, H);
+  // (the gate row's chunk waits in LDS, not in registers, while the rows stream)
+  __shared__ uint4 s_egv[kBThreads];
+  __shared__ uint32_t s_egsb[kBThreads];
+  if (sgu) {
+    s_egv[tid] = egv;
+    s_egsb[tid] = egsb;
+  }
   if (nt == 1) gate_rows<BITS, CPL, RPS, 1>(L, B, Gq, Uq, erow, i0, shared, xs, xsum, s_tok, s_pair, nt, lane);
   else gate_rows<BITS, CPL, RPS, kBTok>(L, B, Gq, Uq, erow, i0, shared, xs, xsum, s_tok, s_pair, nt, lane);
-  if (shared && sl == 0 && wid < nt) {
-    // the shared_expert_gate logit of token s_tok[wid] (one row of H, its own bits)
-    const int j = wid;
-    const float* xsj = xs + j * H;
+  if (sgu) {
+    // each thread's chunk for every token of the tile, then the block's sums
+    // in wave order
+    __shared__ float sgp[kBWaves][kBTok];
     const int nch = H / kCpc;
-    const int eb = L.sh_eg.bits;
-    const int cpce = 128 / eb;
-    const int nche = H / cpce;
-    float a = 0.f;
-    for (int c = lane; c < nche; c += kWave) {
-      const uint4 v = reinterpret_cast<const uint4*>(L.sh_eg.q)[c];
-      const int gg = (c * cpce) / kGroup;
-      float d = 0.f, xsm = 0.f;
-      for (int q = 0; q < cpce; ++q) {
-        const int col = c * cpce + q;
-        const float xv = xsj[4 * ilv<kCpc>(col / 4, nch) + col % 4];
-        const uint32_t word = q / (32 / eb) == 0 ? v.x : q / (32 / eb) == 1 ? v.y : q / (32 / eb) == 2 ? v.z : v.w;
-        const uint32_t code = (word >> (eb * (q % (32 / eb)))) & ((1u << eb) - 1u);
-        d = fmaf((float)code, xv, d);
-        xsm += xv;
+    float a[kBTok];
+#pragma unroll
+    for (int j = 0; j < kBTok; ++j) {
+      a[j] = 0.f;
+      if (tid < nche && j < nt) {
+        const uint4 egv = s_egv[tid];
+        const uint32_t egsb = s_egsb[tid];
+        const float* xsj = xs + j * H;
+        float d = 0.f, xsm = 0.f;
+        for (int q = 0; q < cpce; ++q) {
+          const int col = tid * cpce + q;
+          const float xv = xsj[4 * ilv<kCpc>(col / 4, nch) + col % 4];
+          const uint32_t word = q / (32 / eb) == 0 ? egv.x : q / (32 / eb) == 1 ? egv.y : q / (32 / eb) == 2 ? egv.z : egv.w;
+          const uint32_t code = (word >> (eb * (q % (32 / eb)))) & ((1u << eb) - 1u);
+          d = fmaf((float)code, xv, d);
+          xsm += xv;
+        }
+        a[j] = fmaf(bf16_to_f32(egsb & 0xFFFFu), d, bf16_to_f32(egsb >> 16) * xsm);
       }
-      a = fmaf(bf16_to_f32(L.sh_eg.scales[gg]), d, fmaf(bf16_to_f32(L.sh_eg.biases[gg]), xsm, a));
+      a[j] = wave_sum(a[j]);
+      if (lane == 0) sgp[wid][j] = a[j];
     }
-    a = wave_sum(a);
-    if (lane == 0) B.sg[s_tok[j]] = a;
+    __syncthreads();
+    if (tid < nt) {
+      float tot = 0.f;
+      for (int w = 0; w < kBWaves; ++w) tot += sgp[w][tid];
+      B.sg[s_tok[tid]] = tot;
+    }
   }
 }
 

@@ -475,6 +475,19 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
     const int i = tid + j * kThreads;
     xr[j] = reinterpret_cast<const uint4*>(x + (size_t)t * H)[min(i, x16 - 1)];
   }
+  // the first shared-expert unit of a token also computes the token's
+  // shared_expert_gate logit (one row of H, its own bits): one 16-byte chunk
+  // per thread (H * bits / 128 <= kThreads), loaded now with the x loads
+  const bool sgu = shared && g == 0;                // uniform over the block
+  const int eb = L.sh_eg.bits, cpce = 128 / eb, nche = H / cpce;
+  uint4 egv = make_uint4(0u, 0u, 0u, 0u);
+  uint32_t egsb = 0u;
+  if (sgu) {
+    const int c = min(tid, nche - 1);
+    const int gg = (c * cpce) / kGroup;
+    egv = reinterpret_cast<const uint4*>(L.sh_eg.q)[c];
+    egsb = (uint32_t)L.sh_eg.scales[gg] | ((uint32_t)L.sh_eg.biases[gg] << 16);
+  }
   bool valid = true;
   size_t erow = 0;                                  // first row of the expert
   if constexpr (FUSED) {
@@ -596,32 +609,33 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
         st_coh(P.h + at, hv);
     }
   }
-  if (shared && g == 0 && wid == 0) {
-    // the shared_expert_gate logit of token t (one row of H, its own bits)
-    const int eb = L.sh_eg.bits;
-    const int cpce = 128 / eb;
-    const int nche = H / cpce;
+  if (sgu) {
+    // the shared_expert_gate logit: this thread's chunk, then the block's sum
+    // in wave order
+    __shared__ float sgp[kWaves];
     float a = 0.f;
-    for (int c = lane; c < nche; c += kWave) {
-      const uint4 v = reinterpret_cast<const uint4*>(L.sh_eg.q)[c];
-      const int gg = (c * cpce) / kGroup;
+    if (tid < nche) {
       float d = 0.f, xsm = 0.f;
       for (int q = 0; q < cpce; ++q) {
-        const int col = c * cpce + q;          // element of x in the interleaved layout
+        const int col = tid * cpce + q;        // element of x in the interleaved layout
         const float xv = xs[4 * ilv<kCpc>(col / 4, nch) + col % 4];
-        const uint32_t word = q / (32 / eb) == 0 ? v.x : q / (32 / eb) == 1 ? v.y : q / (32 / eb) == 2 ? v.z : v.w;
+        const uint32_t word = q / (32 / eb) == 0 ? egv.x : q / (32 / eb) == 1 ? egv.y : q / (32 / eb) == 2 ? egv.z : egv.w;
         const uint32_t code = (word >> (eb * (q % (32 / eb)))) & ((1u << eb) - 1u);
         d = fmaf((float)code, xv, d);
         xsm += xv;
       }
-      a = fmaf(bf16_to_f32(L.sh_eg.scales[gg]), d, fmaf(bf16_to_f32(L.sh_eg.biases[gg]), xsm, a));
+      a = fmaf(bf16_to_f32(egsb & 0xFFFFu), d, bf16_to_f32(egsb >> 16) * xsm);
     }
     a = wave_sum(a);
-    if (lane == 0) {
+    if (lane == 0) sgp[wid] = a;
+    __syncthreads();
+    if (tid == 0) {
+      float tot = 0.f;
+      for (int w = 0; w < kWaves; ++w) tot += sgp[w];
       if constexpr (FUSED)
-        st_coh_i(reinterpret_cast<int*>(P.sgb) + s_par * kFusedMaxM + t, (int)~__float_as_uint(a));
+        st_coh_i(reinterpret_cast<int*>(P.sgb) + s_par * kFusedMaxM + t, (int)~__float_as_uint(tot));
       else
-        st_coh(P.sg + t, a);
+        st_coh(P.sg + t, tot);
     }
   }
   if constexpr (FUSED) {
@@ -1043,7 +1057,7 @@ static int d_sb_words(const DecodeLayer& L, int K) {
   return 2 * kDRows * (K * (L.I / kGroup) + (L.has_shared ? L.Is / kGroup : 0)) * 2 / 16;
 }
 
-static size_t dec_lds_bytes(const DecodeLayer& L, int K, bool routed) {
+static size_t dec_lds_bytes(const DecodeLayer& L, int K, bool routed, int M) {
   // G: x (H floats) + chunk sums (<= H/16) + 4 x 16 rows x groups bf16;
   // D: h of all S slots (S x Imax floats) + their chunk sums (<= 1/16 of that)
   //    + the staged scale/bias words;
@@ -1052,8 +1066,8 @@ static size_t dec_lds_bytes(const DecodeLayer& L, int K, bool routed) {
   const int S = K + (L.has_shared ? 1 : 0);
   const int Im = L.has_shared && L.Is > L.I ? L.Is : L.I;
   const size_t d = sizeof(float) * ((size_t)S * Im + (size_t)S * Im / 16) + 16 * (size_t)d_sb_words(L, K);
-  const size_t r = routed ? 16 * (size_t)L.E : 0;        // + x of kFusedMaxM tokens below
-  const size_t rx = routed ? sizeof(float) * (size_t)kFusedMaxM * L.H : 0;
+  const size_t r = routed ? 16 * (size_t)L.E : 0;        // + x of the M tokens below
+  const size_t rx = routed ? sizeof(float) * (size_t)M * L.H : 0;
   size_t m = g > d ? g : d;
   m = m > r ? m : r;
   return m > rx ? m : rx;
@@ -1088,19 +1102,19 @@ bool decode_supported(const DecodeLayer& L, int K) {
   }
   if (!d_ch(L, K)) return false;
   if (d_sb_words(L, K) > kThreads) return false;
-  return dec_lds_bytes(L, K, false) <= 160 * 1024;
+  return dec_lds_bytes(L, K, false, 1) <= 160 * 1024;
 }
 
 bool fused_supported(const DecodeLayer& L, const QT& router, int M, int K) {
   return decode_supported(L, K) && router.bits == 8 && router.rows == L.E && router.cols == L.H &&
-         M >= 1 && M <= kFusedMaxM && L.E <= kMaxExperts && dec_lds_bytes(L, K, true) <= 160 * 1024;
+         M >= 1 && M <= kFusedMaxM && L.E <= kMaxExperts && dec_lds_bytes(L, K, true, M) <= 160 * 1024;
 }
 
 template <int B, int CPL, int DCH, bool FUSED>
 static void run_dec(const DecodeLayer& L, const DecPlan& P, const RouteIn& R, const float* x,
                     const int32_t* idx, const float* w, const float* residual, float* y,
                     hipStream_t s) {
-  const size_t lds = dec_lds_bytes(L, P.K, FUSED);
+  const size_t lds = dec_lds_bytes(L, P.K, FUSED, P.M);
   hipLaunchKernelGGL((k_moe_decode<B, CPL, DCH, FUSED>), dim3(P.r_units + P.g_units + P.d_units),
                      dim3(kThreads), lds, s, L, P, R, x, idx, w, residual, y);
 }
