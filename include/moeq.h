@@ -58,7 +58,7 @@ typedef enum moeq_status {
   MOEQ_OK = 0,
   MOEQ_ERR_NULL_PTR = -1,    /* a required pointer is NULL                      */
   MOEQ_ERR_BAD_BITS = -2,    /* bits not in {2, 4, 8}                           */
-  MOEQ_ERR_BAD_GROUP = -3,   /* group_size != 64                                 */
+  MOEQ_ERR_BAD_GROUP = -3,   /* group_size not 32, 64 or 128 (2 bits: 64 or 128) */
   MOEQ_ERR_K_TAIL = -4,      /* cols not a multiple of group_size               */
   MOEQ_ERR_SHAPE = -5,       /* inconsistent shapes (hidden/inter/experts, top-K) */
   MOEQ_ERR_OVERFLOW = -6,    /* a size or an index would not fit int32          */
@@ -73,10 +73,15 @@ typedef enum moeq_status {
  *   q      : uint32 [batch][rows][cols*bits/32], codes low bits first
  *   scales : bf16 bit patterns [batch][rows][cols/group_size]
  *   biases : bf16 bit patterns, same shape as scales
- * `group_size` is the number of input columns per group (64), not a group
- * count: the markbaseengine expert kernel hung when this parameter was missing
- * or garbage (MOE_FIX_SUCCESS_EXPERT_WORKS, "Bug Details"), so it is an
- * explicit, validated field here. */
+ * `group_size` is the number of input columns per group (32, 64 or 128; at
+ * 2 bits 64 or 128, so that the 64 codes of one 16-byte chunk share a group),
+ * not a group count.  cols must be a multiple of it; at group size 32 cols
+ * may end on half a 64-column step.  Every expert matrix of a layer (and the
+ * shared expert's gate/up/down) uses one group size (MOEQ_ERR_UNSUPPORTED
+ * otherwise); the router and the shared expert's gate row may use their own.
+ * The markbaseengine expert kernel hung when this parameter was missing or garbage
+ * (MOE_FIX_SUCCESS_EXPERT_WORKS, "Bug Details"), so it is an explicit,
+ * validated field here. */
 typedef struct moeq_qtensor {
   const uint32_t *q;
   const uint16_t *scales;

@@ -29,7 +29,10 @@ int check_qt(const moeq_qtensor* t, int batch, int rows, int cols) {
   if (!t) return MOEQ_ERR_NULL_PTR;
   if (!t->q || !t->scales || !t->biases) return MOEQ_ERR_NULL_PTR;
   if (t->bits != 2 && t->bits != 4 && t->bits != 8) return MOEQ_ERR_BAD_BITS;
-  if (t->group_size != 64) return MOEQ_ERR_BAD_GROUP;
+  // 32, 64 or 128 elements per group; at 2 bits 64 or 128 (a 16-byte chunk
+  // of 2-bit codes is 64 elements and must lie in one group)
+  if (t->group_size != 32 && t->group_size != 64 && t->group_size != 128) return MOEQ_ERR_BAD_GROUP;
+  if (t->bits == 2 && t->group_size == 32) return MOEQ_ERR_BAD_GROUP;
   if (t->batch <= 0 || t->rows <= 0 || t->cols <= 0) return MOEQ_ERR_SHAPE;
   if (t->cols % t->group_size) return MOEQ_ERR_K_TAIL;
   if (batch >= 0 && t->batch != batch) return MOEQ_ERR_SHAPE;
@@ -69,6 +72,10 @@ int check_experts(const moeq_moe* L, LayerDims* d) {
   if ((st = check_qt(&L->up, d->E, d->I, d->H))) return st;
   if ((st = check_qt(&L->down, d->E, d->H, d->I))) return st;
   if (L->up.bits != g.bits || L->down.bits != g.bits) return MOEQ_ERR_UNSUPPORTED;
+  // one group size for every expert matrix (the router and the shared
+  // expert's gate row may differ)
+  if (L->up.group_size != g.group_size || L->down.group_size != g.group_size)
+    return MOEQ_ERR_UNSUPPORTED;
   d->Is = 0;
   if (L->has_shared) {
     if ((st = check_qt(&L->sh_gate, 1, -1, d->H))) return st;
@@ -77,6 +84,9 @@ int check_experts(const moeq_moe* L, LayerDims* d) {
     if ((st = check_qt(&L->sh_down, 1, d->H, d->Is))) return st;
     if ((st = check_qt(&L->sh_expert_gate, 1, 1, d->H))) return st;
     if (L->sh_up.bits != L->sh_gate.bits || L->sh_down.bits != L->sh_gate.bits)
+      return MOEQ_ERR_UNSUPPORTED;
+    if (L->sh_gate.group_size != g.group_size || L->sh_up.group_size != g.group_size ||
+        L->sh_down.group_size != g.group_size)
       return MOEQ_ERR_UNSUPPORTED;
   }
   return MOEQ_OK;
@@ -219,7 +229,7 @@ const char* moeq_status_string(int status) {
     case MOEQ_OK: return "ok";
     case MOEQ_ERR_NULL_PTR: return "a required pointer is NULL";
     case MOEQ_ERR_BAD_BITS: return "bits must be 2, 4 or 8";
-    case MOEQ_ERR_BAD_GROUP: return "group_size must be 64";
+    case MOEQ_ERR_BAD_GROUP: return "group_size must be 32, 64 or 128 (64 or 128 at 2 bits)";
     case MOEQ_ERR_K_TAIL: return "cols must be a multiple of group_size";
     case MOEQ_ERR_SHAPE: return "inconsistent shapes";
     case MOEQ_ERR_OVERFLOW: return "a size or index does not fit int32";

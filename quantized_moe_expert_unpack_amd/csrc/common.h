@@ -8,7 +8,14 @@
 namespace moeq {
 
 constexpr int kWave = 64;
-constexpr int kGroup = 64;  // input columns per scale/bias group
+
+// index of the group holding column c for a power-of-two group size gs (32,
+// 64 or 128: validated on the host), without an integer division
+__device__ __forceinline__ int group_of(int c, int gs) { return c >> __builtin_ctz((unsigned)gs); }
+
+// n rounded up to a multiple of 4 (floats: to 16 bytes), for LDS regions
+// followed by 16-byte stores
+__host__ __device__ constexpr int pad4(int n) { return (n + 3) & ~3; }
 
 // bf16 bit pattern -> fp32 (exact: bf16 is the top half of an fp32)
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }

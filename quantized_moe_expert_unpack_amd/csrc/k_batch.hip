@@ -132,7 +132,7 @@ __device__ __forceinline__ void gate_load(GateStep<BITS, CPL, RPS>& S, const QT&
 #pragma unroll
     for (int j = 0; j < CPL; ++j) {
       const int c = min(lane + kWave * j, nch - 1);
-      const int grp = (c * kCpc) / kGroup;
+      const int grp = group_of(c * kCpc, Gq.group_size);
       S.g[rr][j] = reinterpret_cast<const uint4*>(Gq.q + rw * wpr)[c];
       S.u[rr][j] = reinterpret_cast<const uint4*>(Uq.q + rw * wpr)[c];
       S.gs[rr][j] = Gq.scales[rw * gpr + grp];
@@ -152,7 +152,7 @@ __device__ __forceinline__ void gate_rows(const DecodeLayer& L, const BatchWs& B
   constexpr int kSteps = kBSlab / kBWaves / RPS;
   constexpr int kN = RPS * T;
   const int H = L.H;
-  const int nch = H / kCpc, wpr = H / (32 / BITS), gpr = H / kGroup;
+  const int nch = H / kCpc, wpr = H / (32 / BITS), gpr = H >> __builtin_ctz((unsigned)Gq.group_size);
   GateStep<BITS, CPL, RPS> cur, nxt;
   gate_load<BITS, CPL, RPS>(cur, Gq, Uq, erow + i0, lane, nch, wpr, gpr);
 #pragma unroll 1
@@ -256,7 +256,7 @@ k_bgate(DecodeLayer L, BatchWs B, int M, int K, const float* __restrict__ x) {
   uint32_t egsb = 0u;
   if (sgu) {
     const int c = min(tid, nche - 1);
-    const int gg = (c * cpce) / kGroup;
+    const int gg = group_of(c * cpce, L.sh_eg.group_size);
     egv = reinterpret_cast<const uint4*>(L.sh_eg.q)[c];
     egsb = (uint32_t)L.sh_eg.scales[gg] | ((uint32_t)L.sh_eg.biases[gg] << 16);
   }
@@ -341,14 +341,14 @@ __device__ __forceinline__ void down_load(DownStep<BITS, NCL>& S, const QT& Dq, 
                                           int H, int I, int ql) {
   constexpr int kCpc = 128 / BITS;
   constexpr int kGrp = kWave / LPR;
-  const int cpr = I / kCpc, gr = I / kGroup, wpr = I / (32 / BITS);
+  const int cpr = I / kCpc, gr = I >> __builtin_ctz((unsigned)Dq.group_size), wpr = I / (32 / BITS);
 #pragma unroll
   for (int rr = 0; rr < kBRpl; ++rr) {
     const size_t row = erow + min(r + rr * kGrp, H - 1);
 #pragma unroll
     for (int j = 0; j < NCL; ++j) {
       const int q = min(ql + LPR * j, cpr - 1);
-      const int grp = (q * kCpc) / kGroup;
+      const int grp = group_of(q * kCpc, Dq.group_size);
       S.w[rr][j] = reinterpret_cast<const uint4*>(Dq.q + row * wpr)[q];
       S.sc[rr][j] = Dq.scales[row * gr + grp];
       S.bi[rr][j] = Dq.biases[row * gr + grp];

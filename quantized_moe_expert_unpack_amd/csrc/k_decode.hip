@@ -318,7 +318,8 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
   // two waves per row: wave half h takes the row's chunks lane + 64 (2j + h)
   const int e = u * kRRows + wid / 2, h = wid & 1;
   const int nch = H / 16;                 // 16 codes per chunk at 8 bits
-  const int gpr = H / kGroup;
+  const int rsh = __builtin_ctz((unsigned)R.W.group_size);   // log2 of the group size
+  const int gpr = H >> rsh;
   const bool row_ok = e < E;
   __shared__ double part[kFusedMaxM][kRRows];
   // Loads use clamped, always valid addresses and no branches, so they all
@@ -333,8 +334,8 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
   for (int j = 0; j < 2; ++j) {
     const int c = min(lane + kWave * (2 * j + h), nch - 1);
     rv[j] = reinterpret_cast<const uint4*>(R.W.q + (size_t)er * (H / 4))[c];
-    rsb[j] = (uint32_t)R.W.scales[(size_t)er * gpr + c / 4] |
-             ((uint32_t)R.W.biases[(size_t)er * gpr + c / 4] << 16);
+    rsb[j] = (uint32_t)R.W.scales[(size_t)er * gpr + ((c * 16) >> rsh)] |
+             ((uint32_t)R.W.biases[(size_t)er * gpr + ((c * 16) >> rsh)] << 16);
   }
   // x of every token in LDS, chunk-interleaved (float4 f of chunk c at f*nch+c)
   float4* xl = reinterpret_cast<float4*>(smem);
@@ -461,12 +462,14 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
   const int nrows = min(kGRows, I - i_base);
   const int nch = H / kCpc;                         // chunks per row
   const int wpr = H / (32 / BITS);                  // words per row
-  const int gpr = H / kGroup;                       // groups per row
+  const int esh = __builtin_ctz((unsigned)L.gate.group_size);  // log2 group size, every expert matrix
+  const int gpr = H >> esh;                         // groups per row
   const int x16 = H / 4;
   const int sb16 = kGRows * gpr * 2 / 16;           // 16-byte words per scale/bias tensor
   float* xs = smem;
   float* xsum = xs + H;
-  uint16_t* sbl = reinterpret_cast<uint16_t*>(xsum + H / 16);   // [4][kGRows * gpr]
+  // (the sums' region is padded to 16 bytes: the scale words are stored as uint4)
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(xsum + pad4(H / 16));   // [4][kGRows * gpr]
   float4* x4 = reinterpret_cast<float4*>(xs);
 
   uint4 xr[2];
@@ -484,7 +487,7 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
   uint32_t egsb = 0u;
   if (sgu) {
     const int c = min(tid, nche - 1);
-    const int gg = (c * cpce) / kGroup;
+    const int gg = group_of(c * cpce, L.sh_eg.group_size);
     egv = reinterpret_cast<const uint4*>(L.sh_eg.q)[c];
     egsb = (uint32_t)L.sh_eg.scales[gg] | ((uint32_t)L.sh_eg.biases[gg] << 16);
   }
@@ -569,7 +572,7 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
     for (int j = 0; j < CPL; ++j) {
       const int c = lane + kWave * j;
       if (c < nch) {
-        const int grp = i * gpr + (c * kCpc) / kGroup;
+        const int grp = i * gpr + ((c * kCpc) >> esh);
         const float dg = chunk_dot<BITS>(wg[rr][j], x4 + c, nch);
         const float du = chunk_dot<BITS>(wu[rr][j], x4 + c, nch);
         ag = fmaf(bf16_to_f32(sbl[grp]), dg, fmaf(bf16_to_f32(sbl[kGRows * gpr + grp]), xsum[c], ag));
@@ -717,7 +720,8 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
   __syncthreads();
   // scales and biases of every slot (per slot kDRows rows x groups bf16,
   // contiguous), then the routed chunks
-  const int gr = I / kGroup, gs = L.has_shared ? Is / kGroup : 0;
+  const int esh = __builtin_ctz((unsigned)L.gate.group_size);  // log2 group size, every expert matrix
+  const int gr = I >> esh, gs = L.has_shared ? Is >> esh : 0;
   const int sb_r = kDRows * gr * 2 / 16;       // 16-byte words per slot and tensor
   const int sb_s = kDRows * gs * 2 / 16;
   const int n_sb = 2 * (K * sb_r + sb_s);      // all slots, scales and biases
@@ -757,7 +761,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
   }
   float* hs = smem;                            // [S][Imax]
   float* hsum = hs + (size_t)P.S * P.Imax;     // [S][Imax/kCpc]
-  uint16_t* sbl = reinterpret_cast<uint16_t*>(hsum + (size_t)P.S * P.Imax / 16);
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(hsum + pad4(P.S * P.Imax / 16));   // 16-byte aligned
   if constexpr (FUSED) {
     // h arrives element by element with its "written" marks: once this
     // unit's own loads are in, poll the token's h (copy blockIdx % kHCopies
@@ -929,10 +933,10 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
       if (k >= 0 && rl < nrows) {
         const bool sh = k == K;
         const int Ik = sh ? Is : I;
-        const int gpr = Ik / kGroup;
+        const int gpr = Ik >> esh;
         const float4* hk = reinterpret_cast<const float4*>(hs + (size_t)k * P.Imax);
         const float dd = chunk_dot<BITS>(wv[j], hk + cj, Ik / kCpc);
-        const int gi = (sh ? K * kDRows * gr : k * kDRows * gr) + rl * gpr + (cj * kCpc) / kGroup;
+        const int gi = (sh ? K * kDRows * gr : k * kDRows * gr) + rl * gpr + ((cj * kCpc) >> esh);
         const int boff = K * kDRows * gr + kDRows * gs;    // biases follow all scales
         const float part = fmaf(bf16_to_f32(sbl[gi]), dd,
                                 bf16_to_f32(sbl[boff + gi]) * hsum[(size_t)k * (P.Imax / kCpc) + cj]);
@@ -1054,7 +1058,8 @@ size_t decode_ws_bytes(const DecodeLayer& L, int M, int K, bool routed) {
 
 // scale/bias words (16 bytes) a D unit stages: all slots, scales and biases
 static int d_sb_words(const DecodeLayer& L, int K) {
-  return 2 * kDRows * (K * (L.I / kGroup) + (L.has_shared ? L.Is / kGroup : 0)) * 2 / 16;
+  const int egs = L.gate.group_size;
+  return 2 * kDRows * (K * (L.I / egs) + (L.has_shared ? L.Is / egs : 0)) * 2 / 16;
 }
 
 static size_t dec_lds_bytes(const DecodeLayer& L, int K, bool routed, int M) {
@@ -1062,10 +1067,10 @@ static size_t dec_lds_bytes(const DecodeLayer& L, int K, bool routed, int M) {
   // D: h of all S slots (S x Imax floats) + their chunk sums (<= 1/16 of that)
   //    + the staged scale/bias words;
   // R (last unit only): E keys and E fp64 logits
-  const size_t g = sizeof(float) * (L.H + L.H / 16) + 2 * 4 * kGRows * (L.H / kGroup);
+  const size_t g = sizeof(float) * (L.H + pad4(L.H / 16)) + 2 * 4 * kGRows * (L.H / L.gate.group_size);
   const int S = K + (L.has_shared ? 1 : 0);
   const int Im = L.has_shared && L.Is > L.I ? L.Is : L.I;
-  const size_t d = sizeof(float) * ((size_t)S * Im + (size_t)S * Im / 16) + 16 * (size_t)d_sb_words(L, K);
+  const size_t d = sizeof(float) * ((size_t)S * Im + pad4(S * Im / 16)) + 16 * (size_t)d_sb_words(L, K);
   const size_t r = routed ? 16 * (size_t)L.E : 0;        // + x of the M tokens below
   const size_t rx = routed ? sizeof(float) * (size_t)M * L.H : 0;
   size_t m = g > d ? g : d;
@@ -1095,7 +1100,7 @@ static int g_cpl(int H, int bits) {
 bool decode_supported(const DecodeLayer& L, int K) {
   const int b = L.gate.bits;
   if (L.H > 4096 || !g_cpl(L.H, b)) return false;
-  if (4 * kGRows * (L.H / kGroup) * 2 / 16 > kThreads) return false;
+  if (4 * kGRows * (L.H / L.gate.group_size) * 2 / 16 > kThreads) return false;
   if (L.has_shared) {
     if (L.sh_gate.bits != b) return false;
     if (L.sh_eg.bits != 2 && L.sh_eg.bits != 4 && L.sh_eg.bits != 8) return false;

@@ -113,7 +113,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
   for (int u = 0; u < 4; ++u) {
     const int r = (tid >> 3) + 64 * u;
     const int rc = r < rows ? r : 0;
-    aoff[u] = (MODE == 2 ? row0 + rc : s_pair[rc] / a_div) * Kd + aseg * 8;
+    aoff[u] = (MODE == 2 ? row0 + rc : s_pair[rc] / a_div) * Kd;
   }
 
   // ---- B column of this thread: bc = tid >> 1, codes [32 bh, 32 bh + 32) of
@@ -122,6 +122,7 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
   const int bc = tid >> 1, bh = tid & 1;
   const uint32_t* bq;
   const uint16_t *bs, *bb;
+  int gsz;                                         // elements per group of this column's matrix
   {
     int n;
     const QT* M = &W;
@@ -134,9 +135,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
       n = nt * kBN + bc;
     }
     const size_t row = (size_t)e * N + min(n, N - 1);
-    bq = M->q + row * (Kd / (32 / BITS)) + bh * BITS;   // 32 codes = BITS words
-    bs = M->scales + row * (Kd / kGroup);
-    bb = M->biases + row * (Kd / kGroup);
+    bq = M->q + row * (Kd / (32 / BITS));
+    bs = M->scales + row * (Kd / M->group_size);
+    bb = M->biases + row * (Kd / M->group_size);
+    gsz = M->group_size;
   }
 
   f32x16 acc[4][2];
@@ -150,22 +152,30 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
   // two register stages of global loads: step k's data lands in stage k % 2
   u32x4 a0[4], a1[4], b0[kV], b1[kV];
   float s0 = 0.f, c0 = 0.f, s1 = 0.f, c1 = 0.f;   // scale, bias
-  const int ksteps = Kd / kBK;
+  // k-steps of 64 columns; Kd may end on half a step (group size 32, an odd
+  // number of groups): the missing half is read from valid columns and
+  // weighted by zero scale and bias
+  const int ksteps = (Kd + kBK - 1) / kBK;
 
 #define MOEQ_GLOAD(AR, BR, SV, CV, KT)                                                        \
   do {                                                                                        \
     const int k_ = (KT);                                                                      \
+    const int ac_ = min(k_ * kBK + aseg * 8, Kd - 8);                                         \
     _Pragma("unroll") for (int u = 0; u < 4; ++u)                                             \
-      AR[u] = *reinterpret_cast<const u32x4*>(A + aoff[u] + k_ * kBK);                        \
-    const uint32_t* p_ = bq + (size_t)k_ * kWords;                                            \
+      AR[u] = *reinterpret_cast<const u32x4*>(A + aoff[u] + ac_);                             \
+    const int cc_ = k_ * kBK + bh * 32;            /* this thread's 32 codes */                \
+    const bool ok_ = cc_ < Kd;                                                                \
+    const int cv_ = ok_ ? cc_ : cc_ - 32;                                                     \
+    const uint32_t* p_ = bq + (size_t)cv_ * BITS / 32;                                        \
     if constexpr (BITS == 2) {                                                                \
       const uint2 t_ = *reinterpret_cast<const uint2*>(p_);                                   \
       BR[0] = u32x4{t_.x, t_.y, 0u, 0u};                                                      \
     } else {                                                                                  \
       _Pragma("unroll") for (int q = 0; q < kV; ++q) BR[q] = reinterpret_cast<const u32x4*>(p_)[q]; \
     }                                                                                         \
-    SV = bf16_to_f32(bs[k_]);                                                                 \
-    CV = bf16_to_f32(bb[k_]);                                                                 \
+    const float m_ = ok_ ? 1.f : 0.f;              /* loads stay unconditional */              \
+    SV = bf16_to_f32(bs[group_of(cv_, gsz)]) * m_;                                            \
+    CV = bf16_to_f32(bb[group_of(cv_, gsz)]) * m_;                                            \
   } while (0)
 #define MOEQ_LSTORE(AR, BR, SV, CV, BUF)                                                      \
   do {                                                                                        \

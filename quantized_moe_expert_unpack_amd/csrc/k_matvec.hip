@@ -2,11 +2,12 @@
 // projection in fp64 + softmax/top-K) for libmoeq.
 //
 // Weight format: codes of BITS bits packed low-bits-first into uint32 words
-// along the input dimension, one bf16 scale and bias per 64 input columns,
-// w = scale*code + bias (flash-moe-inference skill page, matvec_4bit_fma;
-// danveloper/flash-moe issue thread, per-tensor bit widths).  Rows are
-// streamed in 16-byte chunks: a chunk holds 128/BITS codes and never straddles
-// a group because a group is 8*BITS bytes (a multiple of 16).
+// along the input dimension, one bf16 scale and bias per group of gs input
+// columns (gs = 32, 64 or 128; 64 or 128 at 2 bits), w = scale*code + bias
+// (flash-moe-inference skill page, matvec_4bit_fma; danveloper/flash-moe issue
+// thread, per-tensor bit widths; ml-explore/mlx issue #3856, the repros at
+// group_size 32).  Rows are streamed in 16-byte chunks: a chunk holds 128/BITS
+// codes and never straddles a group because gs is a multiple of 128/BITS.
 #include "common.h"
 #include "launch.h"
 #include "topk.h"
@@ -20,16 +21,16 @@ template <int BITS>
 __global__ void __launch_bounds__(256) k_qdequant(const uint32_t* __restrict__ q,
                                                   const uint16_t* __restrict__ sc,
                                                   const uint16_t* __restrict__ bi, int64_t words,
-                                                  int wpr, int cols, uint8_t* __restrict__ codes,
+                                                  int wpr, int cols, int gs, uint8_t* __restrict__ codes,
                                                   float* __restrict__ deq) {
   constexpr int kPer = 32 / BITS;
   constexpr uint32_t kMask = (1u << BITS) - 1u;
-  const int groups = cols / kGroup;
+  const int groups = cols / gs;
   for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < words;
        w += (int64_t)gridDim.x * blockDim.x) {
     const int64_t row = w / wpr;
     const int c0 = (int)(w - row * wpr) * kPer;
-    const int64_t gidx = row * groups + c0 / kGroup;
+    const int64_t gidx = row * groups + group_of(c0, gs);
     const float s = bf16_to_f32(sc[gidx]);
     const float b = bf16_to_f32(bi[gidx]);
     const uint32_t word = q[w];
@@ -52,14 +53,14 @@ template <int BITS>
 __global__ void __launch_bounds__(256) k_qmatvec(const uint32_t* __restrict__ q,
                                                  const uint16_t* __restrict__ sc,
                                                  const uint16_t* __restrict__ bi, int rows, int cols,
-                                                 const float* __restrict__ x, int M,
+                                                 int gs, const float* __restrict__ x, int M,
                                                  float* __restrict__ y) {
   constexpr int kCpc = 128 / BITS;  // codes per 16-byte chunk
   const int lane = threadIdx.x & (kWave - 1);
   const int r = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
   if (r >= rows) return;
   const int chunks = cols / kCpc;
-  const int groups = cols / kGroup;
+  const int groups = cols / gs;
   const uint4* rq = reinterpret_cast<const uint4*>(q + (size_t)r * (cols / (32 / BITS)));
   const uint16_t* rs = sc + (size_t)r * groups;
   const uint16_t* rb = bi + (size_t)r * groups;
@@ -68,7 +69,7 @@ __global__ void __launch_bounds__(256) k_qmatvec(const uint32_t* __restrict__ q,
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
     for (int c = lane; c < chunks; c += kWave) {
       const uint4 v = rq[c];
-      const int g = (c * kCpc) / kGroup;
+      const int g = group_of(c * kCpc, gs);
       const float s = bf16_to_f32(rs[g]);
       const float b = bf16_to_f32(rb[g]);
       const float* xc = x + (size_t)m0 * cols + (size_t)c * kCpc;
@@ -125,7 +126,7 @@ __global__ void __launch_bounds__(kRouteThreads) k_router(QT W, const float* __r
   const int r = blockIdx.x * (kRouteThreads / kWave) + (threadIdx.x / kWave);
   if (r < rows) {
     const int chunks = cols / kCpc;
-    const int groups = cols / kGroup;
+    const int groups = cols / W.group_size;
     const uint4* rq = reinterpret_cast<const uint4*>(W.q + (size_t)r * (cols / (32 / BITS)));
     const uint16_t* rs = W.scales + (size_t)r * groups;
     const uint16_t* rb = W.biases + (size_t)r * groups;
@@ -134,7 +135,7 @@ __global__ void __launch_bounds__(kRouteThreads) k_router(QT W, const float* __r
       const float* xm = x + (size_t)m * cols;
       for (int c = lane; c < chunks; c += kWave) {
         const uint4 v = rq[c];
-        const int g = (c * kCpc) / kGroup;
+        const int g = group_of(c * kCpc, W.group_size);
         const float s = bf16_to_f32(rs[g]);
         const float b = bf16_to_f32(rb[g]);
         const float* xc = xm + (size_t)c * kCpc;
@@ -200,7 +201,7 @@ __global__ void __launch_bounds__(kRouteThreads) k_router_many(QT W, const float
   if (r >= rows) return;
   const int nm = min(kRouteTM, M - m0);
   const int chunks = cols / kCpc;
-  const int groups = cols / kGroup;
+  const int groups = cols / W.group_size;
   const uint4* rq = reinterpret_cast<const uint4*>(W.q + (size_t)r * (cols / (32 / BITS)));
   const uint16_t* rs = W.scales + (size_t)r * groups;
   const uint16_t* rb = W.biases + (size_t)r * groups;
@@ -209,7 +210,7 @@ __global__ void __launch_bounds__(kRouteThreads) k_router_many(QT W, const float
   for (int t = 0; t < kRouteTM; ++t) acc[t] = 0.0;
   for (int c = lane; c < chunks; c += kWave) {
     const uint4 v = rq[c];
-    const int g = (c * kCpc) / kGroup;
+    const int g = group_of(c * kCpc, W.group_size);
     const float s = bf16_to_f32(rs[g]);
     const float b = bf16_to_f32(rb[g]);
 #pragma unroll
@@ -279,14 +280,14 @@ int launch_qdequant(const QT& W, uint8_t* codes, float* deq, hipStream_t s) {
   const int64_t want = (words + 255) / 256;
   const int blocks = (int)(want < 65536 ? want : 65536);
   MOEQ_BITS_LAUNCH(W.bits, k_qdequant, dim3(blocks), s, W.q, W.scales, W.biases, words, wpr,
-                   W.cols, codes, deq);
+                   W.cols, W.group_size, codes, deq);
   return 0;
 }
 
 int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s) {
   const int blocks = (W.rows + 3) / 4;
-  MOEQ_BITS_LAUNCH(W.bits, k_qmatvec, dim3(blocks), s, W.q, W.scales, W.biases, W.rows, W.cols, x,
-                   M, y);
+  MOEQ_BITS_LAUNCH(W.bits, k_qmatvec, dim3(blocks), s, W.q, W.scales, W.biases, W.rows, W.cols,
+                   W.group_size, x, M, y);
   return 0;
 }
 

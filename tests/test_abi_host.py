@@ -74,13 +74,18 @@ def test_bad_bits(bits, code):
     assert _qmatvec(_qt(bits=bits)) == code
 
 
-@pytest.mark.parametrize("gs,code", [(32, -3), (128, -3), (0, -3)])
-def test_bad_group(gs, code):
-    assert _qmatvec(_qt(gs=gs)) == code
+@pytest.mark.parametrize("bits,gs", [(4, 0), (4, 16), (4, 96), (4, 256), (8, 48), (2, 32), (2, 16)])
+def test_bad_group(bits, gs):
+    # group sizes 32, 64 and 128 are accepted (64 and 128 at 2 bits: a 16-byte
+    # chunk of 2-bit codes is 64 elements and must lie in one group)
+    assert _qmatvec(_qt(bits=bits, gs=gs)) == -3
 
 
 def test_k_tail_and_shapes():
     assert _qmatvec(_qt(cols=100)) == -4           # cols % 64 != 0 (reduction-dim tail)
+    assert _qmatvec(_qt(cols=96)) == -4            # not a multiple of the group size 64
+    assert _qmatvec(_qt(cols=160, gs=128)) == -4
+    assert _qmatvec(_qt(cols=80, gs=32)) == -4
     assert _qmatvec(_qt(rows=0)) == -5
     assert _qmatvec(_qt(batch=2)) == -5            # qmatvec takes one matrix
     assert _qmatvec(_qt(), M=-1) == -5
@@ -132,6 +137,7 @@ def test_layer_validation():
     assert call(_layer(up=_qt(4, 8, 128, 512))) == -5                   # up shape mismatch
     assert call(_layer(down=_qt(4, 8, 128, 256))) == -5                 # down not [E][H][I]
     assert call(_layer(down=_qt(8, 8, 256, 128))) == -9                 # mixed expert bits
+    assert call(_layer(down=_qt(4, 8, 256, 128, gs=32))) == -9          # mixed expert group sizes
     assert call(_layer(shared=True, sh_down=_qt(4, 1, 256, 128))) == -5 # shared down [H][Is]
     assert call(_layer(shared=True, sh_expert_gate=_qt(8, 1, 2, 256))) == -5
     assert call(_layer(), ws=16) == -8
