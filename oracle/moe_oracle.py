@@ -41,12 +41,18 @@ Sources, cited by page title and section:
   flash-moe quantization config.
 * gather_qmm: row i computes ``x_i @ dequant(W[rhs_indices[i]])^T``
   (``transpose=True``): ml-explore/mlx issue #3856, minimal repro.
+* Requantization of 4-bit experts to 2 bits: flash-moe-inference skill page,
+  the setup steps (the 4-bit to 2-bit conversion of the packed experts) and
+  the repository layout (``repack_experts_2bit.py``).  The page names the
+  tool but not its arithmetic; the reading used is below in
+  ``requant_2bit``.
 
 Readings where the pages are silent (each is listed with its reason in the
 design notes): codes sit low bits first inside a word; scales and biases are
 bf16; the group parameter is the number of elements per group; renormalized
 top-K weights ``p[idx] / sum(p[idx])``; ties go to the lower index; the
-combine adds the K experts in slot order.
+combine adds the K experts in slot order; the 2-bit requantization spans each
+group's exact minimum to maximum in three equal steps.
 
 Every function here is pinned by the CPU tests (``tests/test_oracle_*.py``)
 against hand-packed words, closed forms, invariants and brute force with
@@ -54,6 +60,8 @@ exactly rounded sums; none is "parity unpinned".
 """
 
 from __future__ import annotations
+
+from fractions import Fraction
 
 import numpy as np
 
@@ -71,6 +79,8 @@ __all__ = [
     "moe_experts",
     "moe_layer",
     "gather_qmm",
+    "bf16_round",
+    "requant_2bit",
     "expert_bytes",
 ]
 
@@ -301,6 +311,85 @@ def gather_qmm(qt_stack: dict, x, rhs_idx) -> np.ndarray:
         rows = np.nonzero(ridx == e)[0]
         out[rows] = x64[rows] @ _deq64(qt_stack, int(e)).T
     return out
+
+
+# --------------------------------------------------------------------------
+# Requantization to 2 bits
+# --------------------------------------------------------------------------
+
+def bf16_round(v) -> int:
+    """Bit pattern of the bf16 value nearest to the exact rational ``v``,
+    ties to the even significand (IEEE round to nearest even at 8 significant
+    bits).  Normal range only (ValueError outside it); zero maps to +0.
+    """
+    v = Fraction(v)
+    if v == 0:
+        return 0
+    sign = 0x8000 if v < 0 else 0
+    a = abs(v)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    if a < Fraction(2) ** e:          # now 2^e <= a < 2^(e+1)
+        e -= 1
+    m = round(a / Fraction(2) ** (e - 7))        # in [128, 256]; half to even
+    if m == 256:
+        m, e = 128, e + 1
+    if not -126 <= e <= 127:
+        raise ValueError(f"{float(v)!r} is outside bf16's normal range")
+    return sign | ((e + 127) << 7) | (m - 128)
+
+
+def _pack_2bit(codes) -> np.ndarray:
+    """Pack 2-bit codes along the last axis, low bits first (16 per word)."""
+    c = np.asarray(codes, dtype=np.uint32)
+    c = c.reshape(c.shape[:-1] + (c.shape[-1] // 16, 16))
+    words = np.zeros(c.shape[:-1], dtype=np.uint32)
+    for j in range(16):
+        words |= c[..., j] << np.uint32(2 * j)
+    return words
+
+
+def requant_2bit(qt: dict) -> dict:
+    """Requantize a 4- or 8-bit affine tensor to 2 bits, group by group, with
+    the group size kept (flash-moe-inference skill page: the 4-bit to 2-bit
+    conversion step and ``repack_experts_2bit.py``; the page gives no
+    arithmetic, so this is the plainest reading of "requantize to 2 bits").
+
+    For one group with scale ``s``, bias ``b`` and codes ``q_j`` the weights
+    are the exact values ``w_j = s*q_j + b``.  With ``lo = min w_j`` and
+    ``hi = max w_j`` the 2-bit grid is ``lo + k*step`` for k = 0..3 and
+    ``step = (hi - lo) / 3``.  Each weight takes the nearest grid point, ties
+    to the even k; a group with ``step == 0`` takes code 0.  The stored scale
+    and bias are ``step`` and ``lo`` rounded to bf16 (nearest, ties to even).
+    All of it is exact rational arithmetic; only the two stored values round.
+    """
+    bits, gs, cols = int(qt["bits"]), int(qt["group_size"]), int(qt["cols"])
+    if bits not in (4, 8):
+        raise ValueError("the source must be 4- or 8-bit")
+    if gs not in (64, 128):
+        raise ValueError("2-bit groups are 64 or 128 columns")
+    codes = unpack_codes(qt["q"], bits, cols)
+    lead = codes.shape[:-1]
+    ng = cols // gs
+    codes = codes.reshape(-1, ng, gs)
+    s_in = bf16_bits_to_f32(qt["scales"]).reshape(-1, ng)
+    b_in = bf16_bits_to_f32(qt["biases"]).reshape(-1, ng)
+    q2 = np.zeros(codes.shape, dtype=np.uint8)
+    s2 = np.zeros(s_in.shape, dtype=np.uint16)
+    b2 = np.zeros(b_in.shape, dtype=np.uint16)
+    for r in range(codes.shape[0]):
+        for g in range(ng):
+            s, b = Fraction(float(s_in[r, g])), Fraction(float(b_in[r, g]))
+            w = [s * int(c) + b for c in codes[r, g]]
+            lo, hi = min(w), max(w)
+            step = (hi - lo) / 3
+            s2[r, g] = bf16_round(step)
+            b2[r, g] = bf16_round(lo)
+            if step != 0:
+                q2[r, g] = [round((wj - lo) / step) for wj in w]
+    return {"q": _pack_2bit(q2.reshape(lead + (cols,))),
+            "scales": s2.reshape(lead + (ng,)), "biases": b2.reshape(lead + (ng,)),
+            "batch": qt.get("batch", 1), "rows": qt["rows"], "cols": cols, "bits": 2,
+            "group_size": gs}
 
 
 # --------------------------------------------------------------------------

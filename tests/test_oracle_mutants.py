@@ -12,6 +12,7 @@ import pytest
 import oracle
 import oracle.moe_oracle as mo
 from tests import test_oracle_format as tf
+from tests import test_oracle_requant as tq
 from tests import test_oracle_route_ffn as tr
 from tests.conftest import golden_rows
 
@@ -36,6 +37,8 @@ _route = mo.route
 _top_k = mo.top_k
 _silu = mo.silu
 _moe_experts = mo.moe_experts
+_bf16_round = mo.bf16_round
+_requant = mo.requant_2bit
 
 
 def _format_pins():
@@ -60,10 +63,24 @@ def _layer_pins():
     tr.test_silu_values()
 
 
+def _requant_pins():
+    for row in golden_rows("bf16_round.txt"):
+        tq.test_bf16_round_hand_worked(row)
+    tq.test_exact_grid_round_trips()
+    tq.test_negative_scale_reverses_the_codes()
+    tq.test_ties_go_to_the_even_code()
+    tq.test_rounded_step_and_nearest_codes()
+    tq.test_constant_groups_and_zero_scale()
+    tq.test_packing_low_bits_first()
+    tq.test_codes_are_the_nearest_grid_points_by_brute_force(4, 64)
+    tq.test_stored_grid_error_bound(4, 64)
+
+
 def test_pins_pass_on_the_real_oracle():
     _format_pins()
     _route_pins()
     _layer_pins()
+    _requant_pins()
 
 
 def test_high_bits_first_unpack_is_caught(monkeypatch):
@@ -164,6 +181,76 @@ def test_shared_expert_without_sigmoid_is_caught(monkeypatch):
     assert _fails(_layer_pins)
 
 
-@pytest.mark.parametrize("name", ["unpack_codes", "dequantize", "route", "moe_experts"])
+def test_bf16_truncation_instead_of_rounding_is_caught(monkeypatch):
+    def bad(v):
+        from fractions import Fraction
+        v = Fraction(v)
+        if v == 0:
+            return 0
+        a = abs(v)
+        e = a.numerator.bit_length() - a.denominator.bit_length()
+        if a < Fraction(2) ** e:
+            e -= 1
+        m = int(a / Fraction(2) ** (e - 7))          # truncates
+        return (0x8000 if v < 0 else 0) | ((e + 127) << 7) | (m - 128)
+    _patch(monkeypatch, "bf16_round", bad)
+    assert _fails(_requant_pins)
+
+
+def _requant_with(monkeypatch, rounding=None, lo_from_codes=False):
+    """The oracle's requantization with one step changed."""
+    from fractions import Fraction
+
+    def bad(qt):
+        r = _requant(qt)
+        if rounding is None and not lo_from_codes:
+            return r
+        bits, gs, cols = qt["bits"], qt["group_size"], qt["cols"]
+        codes = mo.unpack_codes(qt["q"], bits, cols).reshape(-1, cols // gs, gs)
+        s_in = mo.bf16_bits_to_f32(qt["scales"]).reshape(-1, cols // gs)
+        b_in = mo.bf16_bits_to_f32(qt["biases"]).reshape(-1, cols // gs)
+        q2 = np.zeros(codes.shape, np.uint8)
+        for i in range(codes.shape[0]):
+            for g in range(codes.shape[1]):
+                s, b = Fraction(float(s_in[i, g])), Fraction(float(b_in[i, g]))
+                q = [int(c) for c in codes[i, g]]
+                lo = s * min(q) + b if lo_from_codes else min(s * c + b for c in q)
+                hi = s * max(q) + b if lo_from_codes else max(s * c + b for c in q)
+                step = (hi - lo) / 3
+                if step != 0:
+                    q2[i, g] = [rounding((s * c + b - lo) / step) if rounding else
+                                min(3, max(0, round((s * c + b - lo) / step))) for c in q]
+        r["q"] = mo._pack_2bit(q2.reshape(np.asarray(r["q"]).shape[:-1] + (cols,)))
+        return r
+    _patch(monkeypatch, "requant_2bit", bad)
+
+
+def test_requant_ties_rounded_up_are_caught(monkeypatch):
+    import math
+    _requant_with(monkeypatch, rounding=lambda v: math.floor(v + 0.5))
+    assert _fails(_requant_pins)
+
+
+def test_requant_minimum_taken_at_the_smallest_code_is_caught(monkeypatch):
+    # right only for positive scales: a negative scale puts the minimum at
+    # the largest code
+    _requant_with(monkeypatch, lo_from_codes=True)
+    assert _fails(_requant_pins)
+
+
+def test_requant_high_bits_first_packing_is_caught(monkeypatch):
+    def bad(codes):
+        c = np.asarray(codes, dtype=np.uint32)
+        c = c.reshape(c.shape[:-1] + (c.shape[-1] // 16, 16))
+        words = np.zeros(c.shape[:-1], dtype=np.uint32)
+        for j in range(16):
+            words |= c[..., j] << np.uint32(30 - 2 * j)
+        return words
+    monkeypatch.setattr(mo, "_pack_2bit", bad)
+    assert _fails(_requant_pins)
+
+
+@pytest.mark.parametrize("name", ["unpack_codes", "dequantize", "route", "moe_experts",
+                                  "bf16_round", "requant_2bit"])
 def test_each_patch_target_exists(name):
     assert callable(getattr(mo, name))
