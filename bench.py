@@ -13,7 +13,9 @@ are resident in HBM before the timed region.
 
 Other workloads: ``c3`` (397B-A17B-shaped decode, 4-bit experts + shared
 expert, 8 layers), ``c5`` / ``c5_4bit`` (the same shapes at 2 / 4 bits, 64
-tokens per step), ``c4`` (prefill gather_qmm, M=16384 tokens, one layer).
+tokens per step), ``c4`` (prefill gather_qmm, M=16384 tokens, one layer),
+``requant`` (the 2-bit requantization of one 397B-A17B-shaped layer's three
+4-bit expert stacks, gate and up [512][1024][4096], down [512][4096][1024]).
 
 Prints one JSON line.  ``roofline`` rates the dominant launch against the HBM
 (decode) or bf16 MFMA (prefill) peak, timed live with HIP events on the stream
@@ -84,6 +86,7 @@ KERNEL_SOURCES = {
     "k_moe_decode": ["k_decode.hip", "decode_common.h", "common.h", "topk.h", "launch.h"],
     "k_batch": ["k_batch.hip", "k_sort.hip", "decode_common.h", "common.h", "launch.h"],
     "k_gqmm": ["k_gemm.hip", "common.h", "launch.h"],
+    "k_requant2": ["k_requant.hip", "common.h", "launch.h"],
 }
 
 
@@ -398,12 +401,100 @@ def run_prefill(args, cfg):
     return out
 
 
+# --------------------------------------------------------------------------
+# 2-bit requantization workload
+# --------------------------------------------------------------------------
+
+REQUANT_METRIC = "2-bit requantization throughput (algorithmic bytes read + written per s)"
+
+
+def requant_bytes(E, rows, cols, bits, gs):
+    """Algorithmic bytes of one requantization: the source codes and bf16
+    scale/bias, the 2-bit codes and their bf16 scale/bias."""
+    n = E * rows * cols
+    return n * bits // 8 + n // gs * 4 + n // 4 + n // gs * 4
+
+
+def cpu_baseline_requant(rows, cols, bits, gs):
+    import oracle
+    from quantized_moe_expert_unpack_amd import synth
+    host = synth.requant_source((7, rows), 1, rows, cols, bits, gs, narrow=0.0)
+    t0 = time.perf_counter()
+    oracle.requant_2bit(host)
+    dt = time.perf_counter() - t0
+    return {"value": round(requant_bytes(1, rows, cols, bits, gs) / dt / 1e9, 6), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{rows} rows x {cols} columns of a {bits}-bit expert matrix (exact rational "
+                      f"arithmetic, pure Python); {dt:.1f} s"}
+
+
+def run_requant(args):
+    import torch
+    from quantized_moe_expert_unpack_amd import moeq, synth
+
+    dev = torch.device("cuda:0")
+    E, I, H, bits, gs = 512, 1024, 4096, 4, 64
+    shapes = [(I, H), (I, H), (H, I)]                 # gate, up, down
+    srcs = []
+    for i, (r, c) in enumerate(shapes):
+        q, sc, bi = synth.requant_source_device(100 + i, E, r, c, bits, gs, dev)
+        srcs.append(moeq.QTensor(q, sc, bi, E, r, c, bits, gs))
+    outs = [moeq.requant_2bit(W) for W in srcs]      # allocates the outputs once
+    torch.cuda.synchronize()
+    lib, s_ = moeq.lib(), torch.cuda.current_stream()
+    import ctypes
+    args_ = [(ctypes.byref(W.struct()), o.q.data_ptr(), o.scales.data_ptr(), o.biases.data_ptr())
+             for W, o in zip(srcs, outs)]
+
+    def launch(i):
+        a = args_[i]
+        st = lib.requant_2bit(a[0], a[1], a[2], a[3], s_.cuda_stream)
+        if st:
+            raise RuntimeError(f"requant_2bit failed: {st}")
+
+    for _ in range(max(1, args.warmup)):
+        for i in range(3):
+            launch(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(3 * args.steps)]
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(s_)
+    for k in range(args.steps):
+        for i in range(3):
+            evs[3 * k + i][0].record(s_)
+            launch(i)
+            evs[3 * k + i][1].record(s_)
+    end.record(s_)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    launch_us = float(np.mean([a.elapsed_time(b) for a, b in evs])) * 1e3
+    per_launch = requant_bytes(E, I, H, bits, gs)     # the three stacks hold equal counts
+    step_bytes = 3 * per_launch
+    achieved = per_launch / (launch_us * 1e-6) / 1e9
+    log(f"[bench] requant: {ms * 1e3:.1f} us/step, {launch_us:.1f} us/launch")
+    return {
+        "metric": REQUANT_METRIC, "value": round(step_bytes / (ms * 1e-3) / 1e9, 1), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u32",
+        "data": "synthetic",
+        "config": {"workload": "requant-397b-a17b-layer-4to2bit", "experts": E, "hidden": H,
+                   "inter": I, "source_bits": bits, "group_size": gs,
+                   "matrices": "gate, up [E][I][H]; down [E][H][I]"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic_for(args, "k_requant2"), "kernel": "k_requant2<4>",
+                     "launch_us": round(launch_us, 2), "bytes_per_launch": int(per_launch)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c5_4bit"])
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c5_4bit", "requant"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (decode)")
     ap.add_argument("--tokens", type=int, default=0, help="override M (prefill)")
     ap.add_argument("--slots", type=int, default=TOKEN_SLOTS)
@@ -436,6 +527,12 @@ def main():
         sys.exit(2)
 
     from quantized_moe_expert_unpack_amd import synth
+    if args.config == "requant":
+        out = run_requant(args)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_requant(384, 4096, 4, 64)
+        print(json.dumps(out), flush=True)
+        return
     cfg = synth.CONFIGS[args.config]
     if args.config == "c4":
         out = run_prefill(args, cfg)

@@ -223,6 +223,27 @@ int gather_qmm(const moeq_qtensor *W, const uint16_t *x_bf16, const int32_t *rhs
                int32_t n, int32_t sorted, float *out, void *ws, size_t ws_bytes,
                moeq_stream_t stream);
 
+/* requant_2bit: requantize a 4- or 8-bit tensor (or stack) to 2 bits per
+ * group, keeping the group size (64 or 128).
+ *   W       : the source, bits 4 or 8 (2: MOEQ_ERR_UNSUPPORTED), group size
+ *             64 or 128 (32: MOEQ_ERR_BAD_GROUP)
+ *   q_out   : uint32 [batch][rows][cols/16], 2-bit codes low bits first
+ *   s_out, b_out : bf16 bit patterns [batch][rows][cols/group_size]
+ *   (all 16-byte aligned, caller-owned, not overlapping the source)
+ * Per group of the source, with w = scale*code + bias taken exactly: the
+ * 2-bit grid runs from the group's smallest weight lo to its largest hi in
+ * three equal steps; each weight gets the nearest grid point's code, ties to
+ * the even code, and every code is 0 when hi == lo; s_out = (hi - lo)/3 and
+ * b_out = lo, each rounded once to bf16 (nearest, ties to even).  Bit-exact:
+ * the codes are integer decisions and the two stored values are exactly
+ * rounded.
+ * Defines: the 4-bit to 2-bit conversion of the experts
+ * (flash-moe-inference skill page, setup steps and the repository layout's
+ * repack_experts_2bit.py; the page names the tool, the grid above is the
+ * reading taken). */
+int requant_2bit(const moeq_qtensor *W, uint32_t *q_out, uint16_t *s_out, uint16_t *b_out,
+                 moeq_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -278,6 +278,18 @@ int qdequant(const moeq_qtensor* W, uint8_t* codes, float* deq, moeq_stream_t st
   return launch_status();
 }
 
+int requant_2bit(const moeq_qtensor* W, uint32_t* q_out, uint16_t* s_out, uint16_t* b_out,
+                 moeq_stream_t stream) {
+  int st = check_qt(W, -1, -1, -1);
+  if (st) return st;
+  if (W->bits == 2) return MOEQ_ERR_UNSUPPORTED;     // already 2-bit
+  if (W->group_size == 32) return MOEQ_ERR_BAD_GROUP;   // no 2-bit groups of 32
+  if (!q_out || !s_out || !b_out) return MOEQ_ERR_NULL_PTR;
+  if (!aligned16(q_out) || !aligned16(s_out) || !aligned16(b_out)) return MOEQ_ERR_ALIGN;
+  moeq::launch_requant_2bit(to_qt(*W), q_out, s_out, b_out, (hipStream_t)stream);
+  return launch_status();
+}
+
 int qmatvec(const moeq_qtensor* W, const float* x, int32_t M, float* y, moeq_stream_t stream) {
   int st = check_qt(W, 1, -1, -1);
   if (st) return st;

@@ -112,6 +112,8 @@ struct BatchWs {
 
 int launch_qdequant(const QT& W, uint8_t* codes, float* deq, hipStream_t s);
 int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s);
+// 2-bit requantization of a 4- or 8-bit tensor (group size 64 or 128)
+int launch_requant_2bit(const QT& W, uint32_t* q2, uint16_t* s2, uint16_t* b2, hipStream_t s);
 // routing: router projection (fp64) + softmax/top-K.  The standalone
 // workspace is [counters (zero between calls)][fp64 logits [M][E]].
 size_t route_ctr_bytes();

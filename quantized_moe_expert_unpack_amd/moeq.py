@@ -59,6 +59,7 @@ _SIGNATURES = {
     "moe_workspace_size": (_SZ, [ctypes.POINTER(MoEStruct), _I, _I, _I]),
     "qdequant": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _P, _P]),
     "qmatvec": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _I, _P, _P]),
+    "requant_2bit": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _P, _P, _P]),
     "moe_route": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _I, _I, _I, _I, _P, _P, _P,
                                  _P, _SZ, _P]),
     "moe_expert_forward": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _P, _P, _I, _I, _P, _P,
@@ -223,6 +224,18 @@ def qdequant(W: QTensor, codes: bool = True, deq: bool = True, stream=None):
     d = torch.empty(shape, dtype=torch.float32, device=dev) if deq else None
     _check(lib().qdequant(ctypes.byref(W.struct()), _ptr(c), _ptr(d), _stream(stream)), "qdequant")
     return c, d
+
+
+def requant_2bit(W: QTensor, stream=None) -> QTensor:
+    """2-bit requantization of a 4- or 8-bit tensor (same shape and group size)."""
+    dev = W.q.device
+    ng = W.cols // W.group_size
+    q = torch.empty((W.batch, W.rows, W.cols // 16), dtype=torch.int32, device=dev)
+    s = torch.empty((W.batch, W.rows, ng), dtype=torch.int16, device=dev)
+    b = torch.empty((W.batch, W.rows, ng), dtype=torch.int16, device=dev)
+    _check(lib().requant_2bit(ctypes.byref(W.struct()), _ptr(q), _ptr(s), _ptr(b), _stream(stream)),
+           "requant_2bit")
+    return QTensor(q, s, b, W.batch, W.rows, W.cols, 2, W.group_size)
 
 
 def qmatvec(W: QTensor, x: torch.Tensor, y: Optional[torch.Tensor] = None, stream=None):

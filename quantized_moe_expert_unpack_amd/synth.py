@@ -15,7 +15,10 @@ The recipes follow the workloads named for the method: uniform codes (random
 words make every packed field uniform), scales ``U(0.005, 0.02)`` rounded to
 bf16, and biases at the code midpoint ``-2**(bits-1) * scale`` plus
 ``N(0, 0.001)`` noise, rounded to bf16 (for 4-bit codes this is
-``-8 * scale``).  Activations are fp32 ``N(0, 1)`` (decode) or bf16-rounded
+``-8 * scale``).  The 2-bit experts of the 397B-A17B-shaped batched decode
+are drawn with the statistics of a 4-bit draw requantized to 2 bits (code
+frequencies 3:5:5:3, scale 5s, bias -8s); the requantization itself is a
+library op and is not done here.  Activations are fp32 ``N(0, 1)`` (decode) or bf16-rounded
 ``N(0, 1)`` (prefill).  Prefill router logits are ``log p_rank(e) + Gumbel``
 with Zipf(1.1) rank probabilities over a seeded permutation of the experts.
 """
@@ -56,7 +59,7 @@ class MoEConfig:
     tokens: int = 1                 # M per call
     seed: int = 0
     renorm: bool = True
-    requant_from: int = 0           # 4 => 2-bit weights requantized from 4-bit draws
+    requant_from: int = 0           # 4 => 2-bit weights shaped like requantized 4-bit draws
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -81,7 +84,8 @@ CONFIGS = {
     "c4": MoEConfig("c4-30b-a3b-prefill", hidden=2048, experts=128, top_k=8,
                     inter=768, expert_bits=8, router_bits=8, layers=2,
                     tokens=16384, seed=4),
-    # 397B-A17B weights requantized to 2-bit, batched decode M=64
+    # 397B-A17B shapes with 2-bit experts shaped like a 4-bit model requantized
+    # to 2 bits, batched decode M=64
     "c5": MoEConfig("c5-397b-a17b-2bit-m64", hidden=4096, experts=512, top_k=4,
                     inter=1024, expert_bits=2, router_bits=8,
                     shared_inter=1024, shared_bits=2, shared_gate_bits=8,
@@ -160,57 +164,45 @@ def draw_matrix(key, rows: int, cols: int, bits: int, group_size: int = GROUP):
 
 
 def _draw_4bit_codes(key, rows, cols, group_size):
-    """4-bit draw kept as codes (for the 2-bit requantized variant): codes
-    uniform on 0..15 drawn one per column, then packed, with the usual
-    scale/bias recipe."""
+    """4-bit draw with codes uniform on 0..15 drawn one per column, then
+    packed, with the usual scale/bias recipe."""
     rng = _rng(*key)
     codes = np.frombuffer(rng.bytes(rows * cols), dtype=np.uint8).reshape(rows, cols) & np.uint8(15)
     s_bits, b_bits = _scales_biases(rng, rows, cols // group_size, 4)
-    return pack_codes(codes, 4), codes, s_bits, b_bits
+    return pack_codes(codes, 4), s_bits, b_bits
 
 
-def requant_2bit(codes4, s_bits, b_bits, group_size: int = GROUP):
-    """Requantize a 4-bit draw to 2 bits per group (data preparation, the
-    role of the pages' offline 2-bit repack tool).
+# inverse CDF of the 2-bit code frequencies 3:5:5:3 (of 16) over a uniform
+# 4-bit value: the frequencies with which requantizing a uniform 4-bit group
+# to 2 bits gives each code
+_CODE_OF_NIBBLE = np.repeat(np.arange(4, dtype=np.uint8), [3, 5, 5, 3])
 
-    Within a group every 4-bit weight is ``s*q + b`` with one ``s`` and one
-    ``b``, so the group's minimum and maximum sit at its smallest and largest
-    code.  The 2-bit grid spans them: ``scale2 = s*(qmax-qmin)/3``,
-    ``bias2 = s*qmin + b`` (both rounded to bf16) and
-    ``q2 = round_half_even(3*(q-qmin)/(qmax-qmin))`` taken in integers; a
-    constant group gets ``scale2 = 0`` and ``q2 = 0``.
-    """
-    rows, cols = codes4.shape
+
+def _draw_2bit_requant_like(key, rows, cols, group_size):
+    """2-bit draw with the statistics of a uniform 4-bit draw requantized to
+    2 bits: codes with the frequencies above, the 4-bit recipe's scale s
+    spread over the 2-bit grid (scale 5s, bias at the 4-bit code midpoint
+    -8s plus N(0, 0.001)), both rounded to bf16."""
+    rng = _rng(*key)
+    nib = np.frombuffer(rng.bytes(rows * cols), dtype=np.uint8).reshape(rows, cols) & np.uint8(15)
+    codes = _CODE_OF_NIBBLE[nib]
     g = cols // group_size
-    q = codes4.reshape(rows, g, group_size).astype(np.int16)
-    qmin = q.min(axis=2)
-    qmax = q.max(axis=2)
-    span = qmax - qmin
-    s = bf16_bits_as_f32(s_bits)
-    b = bf16_bits_as_f32(b_bits)
-    scale2 = (s * (span.astype(np.float32) / np.float32(3.0))).astype(np.float32)
-    bias2 = (s * qmin.astype(np.float32) + b).astype(np.float32)
-    # q2 for every (span, q - qmin) pair, rounding 3*(q-qmin)/span half to even
-    d = np.arange(16)[:, None]
-    t = 3 * np.arange(16)[None, :]
-    r = t // np.maximum(d, 1)
-    twice_rem = 2 * (t - r * np.maximum(d, 1))
-    r = r + (twice_rem > d) + ((twice_rem == d) & (r % 2 == 1))
-    table = np.where(d == 0, 0, np.clip(r, 0, 3)).astype(np.uint8).reshape(-1)
-    q2 = table[(span[..., None] * 16 + (q - qmin[..., None])).astype(np.intp)].reshape(rows, cols)
-    return pack_codes(q2, 2), f32_to_bf16_bits(scale2), f32_to_bf16_bits(bias2)
+    s = rng.uniform(0.005, 0.02, size=(rows, g)).astype(np.float32)
+    noise = rng.normal(0.0, 0.001, size=(rows, g)).astype(np.float32)
+    s_bits = f32_to_bf16_bits((np.float32(5.0) * s).astype(np.float32))
+    b_bits = f32_to_bf16_bits((np.float32(-8.0) * s + noise).astype(np.float32))
+    return pack_codes(codes, 2), s_bits, b_bits
 
 
 def draw_weight(cfg: MoEConfig, layer: int, expert: int, tensor: int, rows: int,
                 cols: int, bits: int):
     key = (cfg.seed, layer, expert, tensor)
     if cfg.requant_from and tensor in (T_GATE, T_UP, T_DOWN, T_SH_GATE, T_SH_UP, T_SH_DOWN):
-        words4, codes4, s4, b4 = _draw_4bit_codes(key, rows, cols, cfg.group_size)
         if bits == 4:
-            return words4, s4, b4
+            return _draw_4bit_codes(key, rows, cols, cfg.group_size)
         if bits == 2:
-            return requant_2bit(codes4, s4, b4, cfg.group_size)
-        raise ValueError("requantized draws are 4- or 2-bit")
+            return _draw_2bit_requant_like(key, rows, cols, cfg.group_size)
+        raise ValueError("requantization-shaped draws are 4- or 2-bit")
     return draw_matrix(key, rows, cols, bits, cfg.group_size)
 
 
@@ -303,6 +295,55 @@ def host_layer(cfg: MoEConfig, layer: int, threads: int = 8) -> dict:
             fill(j)
     out.update(_small_tensors(cfg, layer))
     return out
+
+
+# --------------------------------------------------------------------------
+# sources for the 2-bit requantization
+# --------------------------------------------------------------------------
+
+def requant_source(key, batch: int, rows: int, cols: int, bits: int, group_size: int,
+                   narrow: float = 0.25, negative: float = 0.3, zero: float = 0.03) -> dict:
+    """A 4- or 8-bit tensor (stack) to requantize, in host memory: uniform
+    codes, except that a ``narrow`` fraction of the groups draws its codes
+    from three or four neighbouring values (small spans, so grid ties occur
+    at 4 bits too); bf16 scales U(0.005, 0.02) with a ``negative`` fraction
+    negated and a ``zero`` fraction set to zero; bf16 biases N(0, 0.1)."""
+    rng = _rng(*key)
+    n, ng = batch * rows, cols // group_size
+    codes = rng.integers(0, 1 << bits, (n, ng, group_size))
+    pick = rng.random((n, ng)) < narrow
+    lo = rng.integers(0, (1 << bits) - 4, (n, ng))
+    width = rng.integers(3, 5, (n, ng))
+    near = lo[..., None] + rng.integers(0, 8, (n, ng, group_size)) % width[..., None]
+    codes = np.where(pick[..., None], near, codes).reshape(n, cols)
+    s = rng.uniform(0.005, 0.02, (n, ng)).astype(np.float32)
+    s = np.where(rng.random((n, ng)) < negative, -s, s)
+    s = np.where(rng.random((n, ng)) < zero, np.float32(0.0), s).astype(np.float32)
+    b = rng.normal(0.0, 0.1, (n, ng)).astype(np.float32)
+    return {"q": pack_codes(codes, bits).reshape(batch, rows, -1),
+            "scales": f32_to_bf16_bits(s).reshape(batch, rows, ng),
+            "biases": f32_to_bf16_bits(b).reshape(batch, rows, ng),
+            "batch": batch, "rows": rows, "cols": cols, "bits": bits, "group_size": group_size}
+
+
+def requant_source_device(seed: int, batch: int, rows: int, cols: int, bits: int,
+                          group_size: int, device):
+    """The same recipe without narrow groups, drawn on the device with torch's
+    generator (for sizes that host generation would make slow): returns int32
+    words and int16 bf16 bit patterns."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    n, ng = batch * rows, cols // group_size
+    q = torch.randint(-(2 ** 31), 2 ** 31, (batch, rows, cols * bits // 32), dtype=torch.int64,
+                      device=device, generator=g).to(torch.int32)
+    s = torch.empty((n, ng), device=device).uniform_(0.005, 0.02, generator=g)
+    sign = torch.where(torch.rand((n, ng), device=device, generator=g) < 0.3, -1.0, 1.0)
+    s = s * sign
+    b = torch.empty((n, ng), device=device).normal_(0.0, 0.1, generator=g)
+    to16 = lambda t: t.to(torch.bfloat16).view(torch.int16).reshape(batch, rows, ng).contiguous()
+    return q, to16(s), to16(b)
 
 
 # --------------------------------------------------------------------------

@@ -31,7 +31,8 @@ def declared_functions():
 def test_header_declares_the_four_calls_and_helpers():
     names = declared_functions()
     for n in ("qmatvec", "moe_route", "moe_expert_forward", "moe_gather_qmm", "qdequant",
-              "gather_qmm", "moe_workspace_size", "moeq_status_string", "moeq_version"):
+              "gather_qmm", "requant_2bit", "moe_workspace_size", "moeq_status_string",
+              "moeq_version"):
         assert n in names
 
 
@@ -89,6 +90,22 @@ def test_k_tail_and_shapes():
     assert _qmatvec(_qt(rows=0)) == -5
     assert _qmatvec(_qt(batch=2)) == -5            # qmatvec takes one matrix
     assert _qmatvec(_qt(), M=-1) == -5
+
+
+def test_requant_validation():
+    f = moeq.lib().requant_2bit
+
+    def call(W, q=FAKE, s=FAKE + 4096, b=FAKE + 8192):
+        return f(ctypes.byref(W), q, s, b, None)
+
+    assert call(_qt(bits=2)) == -9                  # already 2-bit
+    assert call(_qt(bits=4, gs=32)) == -3           # no 2-bit groups of 32
+    assert call(_qt(bits=3)) == -2
+    assert call(_qt(cols=96)) == -4
+    assert call(_qt(), q=0) == -1
+    assert call(_qt(), b=0) == -1
+    assert call(_qt(), s=FAKE + 2) == -7
+    assert call(_qt(q=0)) == -1
 
 
 def test_null_and_align():
