@@ -39,6 +39,13 @@ Sources, cited by page title and section:
   flash-moe-inference skill page, ``moe_combine_residual`` ("MoE combine +
   residual + sigmoid gate"), and the 8-bit ``shared_expert_gate`` of the
   flash-moe quantization config.
+* RMSNorm before the router, residual added in the combine:
+  flash-moe-inference skill page, the per-layer pipeline listing (CMD2:
+  o_proj, norm, routing; CMD3: expert forward, combine), the two-pass
+  ``rms_norm_pass1/2`` kernel sketches (sum of squares, then scale) and
+  ``moe_combine_residual``; danveloper/flash-moe issue thread, "Definitive
+  finding" (the CMD2 chain o_proj -> residual_add -> rms_norm -> routing
+  gate matvec).
 * gather_qmm: row i computes ``x_i @ dequant(W[rhs_indices[i]])^T``
   (``transpose=True``): ml-explore/mlx issue #3856, minimal repro.
 * Requantization of 4-bit experts to 2 bits: flash-moe-inference skill page,
@@ -78,6 +85,8 @@ __all__ = [
     "swiglu",
     "moe_experts",
     "moe_layer",
+    "rms_norm",
+    "moe_block",
     "gather_qmm",
     "bf16_round",
     "requant_2bit",
@@ -293,6 +302,37 @@ def moe_layer(layer: dict, x, k: int, renorm: bool = True, residual=None,
     y = moe_experts(layer, x64, idx, w, residual)
     return y, idx, w, np.asarray(logits, dtype=np.float64)
 
+
+def rms_norm(x, weight, eps: float) -> np.ndarray:
+    """``x / sqrt(mean(x^2) + eps) * weight`` per row, in fp64.
+
+    The two passes of the pages' ``rms_norm_pass1/2``: the mean of the
+    squares over the row's H elements, then every element scaled by the
+    reciprocal square root and by its own weight.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    g = np.asarray(weight, dtype=np.float64).reshape(-1)
+    if g.shape[0] != x64.shape[1]:
+        raise ValueError("norm weight length must equal the row length")
+    ms = np.mean(x64 * x64, axis=1, keepdims=True)
+    return x64 / np.sqrt(ms + float(eps)) * g[None, :]
+
+
+def moe_block(layer: dict, x, norm_weight, eps: float, k: int, renorm: bool = True):
+    """The MoE step with its neighbours fused: ``h = rms_norm(x)`` feeds the
+    router and the experts, and the residual stream ``x`` itself is added
+    in the combine: ``y = x + MoE(h)``.
+
+    Returns ``(y, idx, w, h)``.
+    """
+    x64 = np.asarray(x, dtype=np.float64)
+    if x64.ndim == 1:
+        x64 = x64[None, :]
+    h = rms_norm(x64, norm_weight, eps)
+    y, idx, w, _ = moe_layer(layer, h, k, renorm, residual=x64)
+    return y, idx, w, h
 
 # --------------------------------------------------------------------------
 # gather_qmm: one projection per row, weight matrix picked per row

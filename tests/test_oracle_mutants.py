@@ -12,6 +12,7 @@ import pytest
 import oracle
 import oracle.moe_oracle as mo
 from tests import test_oracle_format as tf
+from tests import test_oracle_norm as tn
 from tests import test_oracle_requant as tq
 from tests import test_oracle_route_ffn as tr
 from tests.conftest import golden_rows
@@ -38,6 +39,8 @@ _top_k = mo.top_k
 _silu = mo.silu
 _moe_experts = mo.moe_experts
 _bf16_round = mo.bf16_round
+_rms_norm = mo.rms_norm
+_moe_block = mo.moe_block
 _requant = mo.requant_2bit
 
 
@@ -76,11 +79,54 @@ def _requant_pins():
     tq.test_stored_grid_error_bound(4, 64)
 
 
+def _norm_pins():
+    tn.test_three_four_row()
+    for c, eps, want in [(2.0, 0.0, 1.0), (1e-3, 1e-6, 2 ** -0.5), (3.0, 7.0, 0.75)]:
+        tn.test_constant_rows(c, eps, want)
+    tn.test_invariants()
+    tn.test_block_brute_force(True)
+    tn.test_block_routes_and_runs_on_the_normalized_row()
+
+
 def test_pins_pass_on_the_real_oracle():
     _format_pins()
     _route_pins()
     _layer_pins()
     _requant_pins()
+    _norm_pins()
+
+
+def test_norm_without_eps_is_caught(monkeypatch):
+    _patch(monkeypatch, "rms_norm", lambda x, w, eps: _rms_norm(x, w, 0.0))
+    assert _fails(_norm_pins)
+
+
+def test_norm_by_sum_instead_of_mean_is_caught(monkeypatch):
+    def bad(x, w, eps):
+        x64 = np.atleast_2d(np.asarray(x, np.float64))
+        return x64 / np.sqrt(np.sum(x64 * x64, axis=1, keepdims=True) + eps) * np.asarray(w)[None, :]
+    _patch(monkeypatch, "rms_norm", bad)
+    assert _fails(_norm_pins)
+
+
+def test_block_with_the_normalized_row_as_residual_is_caught(monkeypatch):
+    def bad(layer, x, g, eps, k, renorm=True):
+        h = mo.rms_norm(x, g, eps)
+        y, idx, w, _ = mo.moe_layer(layer, h, k, renorm, residual=h)
+        return y, idx, w, h
+    _patch(monkeypatch, "moe_block", bad)
+    assert _fails(_norm_pins)
+
+
+def test_block_routing_on_the_raw_row_is_caught(monkeypatch):
+    def bad(layer, x, g, eps, k, renorm=True):
+        x64 = np.atleast_2d(np.asarray(x, np.float64))
+        h = mo.rms_norm(x64, g, eps)
+        lg = mo.qmatvec(layer["router"], x64)
+        y, idx, w, _ = mo.moe_layer(layer, h, k, renorm, residual=x64, logits=lg)
+        return y, idx, w, h
+    _patch(monkeypatch, "moe_block", bad)
+    assert _fails(_norm_pins)
 
 
 def test_high_bits_first_unpack_is_caught(monkeypatch):
@@ -251,6 +297,6 @@ def test_requant_high_bits_first_packing_is_caught(monkeypatch):
 
 
 @pytest.mark.parametrize("name", ["unpack_codes", "dequantize", "route", "moe_experts",
-                                  "bf16_round", "requant_2bit"])
+                                  "bf16_round", "requant_2bit", "rms_norm", "moe_block"])
 def test_each_patch_target_exists(name):
     assert callable(getattr(mo, name))
