@@ -42,6 +42,7 @@ HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2516.6
 TOKEN_SLOTS = 64
 BATCH_MIN_M = 16     # moe_expert_forward groups pairs by expert from this many tokens
+NORM_EPS = 1e-6
 
 
 def log(*a):
@@ -233,13 +234,19 @@ def run_decode(args, cfg):
     # one launch per layer (router + top-K + experts) when the library can
     # route inside the launch (8-bit router, M <= 4); else route, then experts
     one_launch = cfg.router_bits == 8 and m <= 4
-    ws_fwd = moeq.workspace(layers[0], m, K, moeq.PATH_FORWARD, dev)
+    ws_fwd = moeq.workspace(layers[0], m, K, moeq.PATH_FORWARD_NORM if args.norm else moeq.PATH_FORWARD,
+                            dev)
+    # --norm: RMSNorm in front of every layer's step, x added back in the combine
+    gam = [torch.from_numpy(synth.norm_weight(cfg, l)).to(dev) for l in range(n_layers)] if args.norm else None
     ws_route = torch.zeros(8 * m * cfg.experts + 4096, dtype=torch.uint8, device=dev)
     ws_dec = moeq.workspace(layers[0], m, K, moeq.PATH_DECODE, dev)
 
     def layer_call(l, t):
         L = layers[l]
-        if one_launch:
+        if args.norm:
+            moeq.moe_forward_norm(L, x[l, t], K, gam[l], NORM_EPS, cfg.renorm, ws=ws_fwd, y=y[l],
+                                  idx=idx[l], w=w[l])
+        elif one_launch:
             moeq.moe_forward(L, x[l, t], K, cfg.renorm, ws=ws_fwd, y=y[l], idx=idx[l], w=w[l])
         else:
             moeq.moe_route(L.router, x[l, t], cfg.experts, K, cfg.renorm, ws=ws_route,
@@ -300,7 +307,12 @@ def run_decode(args, cfg):
     for r in range(reps):
         t = r % slots
         for l, L in enumerate(layers):
-            if one_launch:
+            if args.norm:
+                evs[k][0].record(s_)
+                moeq.moe_forward_norm(L, x[l, t], K, gam[l], NORM_EPS, cfg.renorm, ws=ws_fwd, y=y[l],
+                                      idx=idx[l], w=w[l])
+                evs[k][1].record(s_)
+            elif one_launch:
                 evs[k][0].record(s_)
                 moeq.moe_forward(L, x[l, t], K, cfg.renorm, ws=ws_fwd, y=y[l], idx=idx[l], w=w[l])
                 evs[k][1].record(s_)
@@ -318,12 +330,19 @@ def run_decode(args, cfg):
     # the eager, event-bracketed expert launches
     launch_us = ms * 1e3 / n_layers if one_launch else eager_us
     lbytes = (layer_bytes(cfg, touched) + m * K * 8) if one_launch else expert_launch_bytes(cfg, touched)
+    if args.norm:
+        lbytes += cfg.hidden * 4                      # the norm weight
+        if not one_launch:                            # norm + route + experts, bracketed together
+            lbytes = layer_bytes(cfg, touched) + m * K * 8 + cfg.hidden * 4 + 2 * m * cfg.hidden * 4
     achieved = lbytes / (launch_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic_for(args, "k_batch" if not one_launch and m >= BATCH_MIN_M
-                                       else "k_moe_decode"),
-                "kernel": "k_moe_decode (moe_forward: router + top-K + experts)" if one_launch
+                "traffic": None if args.norm else traffic_for(
+                    args, "k_batch" if not one_launch and m >= BATCH_MIN_M else "k_moe_decode"),
+                "kernel": ("k_moe_decode (moe_forward_norm: RMSNorm + router + top-K + experts)"
+                           if args.norm and one_launch else
+                           "moe_forward_norm (norm, route, experts)" if args.norm else
+                           "k_moe_decode (moe_forward: router + top-K + experts)") if one_launch or args.norm
                           else ("moe_expert_forward batched by expert (sort, k_bgate, k_bdown, "
                                 "k_bcombine)" if m >= BATCH_MIN_M else "k_moe_decode (moe_expert_forward)"),
                 "launch_us": round(launch_us, 2), "eager_launch_us": round(eager_us, 2),
@@ -338,7 +357,7 @@ def run_decode(args, cfg):
                    "hidden": H, "experts": cfg.experts, "top_k": K, "inter": cfg.inter,
                    "expert_bits": cfg.expert_bits, "router_bits": cfg.router_bits,
                    "shared_expert": cfg.has_shared, "group_size": cfg.group_size,
-                   "token_slots": slots, "graph": True,
+                   "token_slots": slots, "graph": True, "rmsnorm_fused": bool(args.norm),
                    "launches_per_layer": 1 if one_launch else 2},
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "bytes_per_step": int(bytes_step), "touched_experts_per_layer": round(touched, 2),
@@ -500,6 +519,8 @@ def main():
     ap.add_argument("--slots", type=int, default=TOKEN_SLOTS)
     ap.add_argument("--launch-reps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--norm", action="store_true",
+                    help="decode: RMSNorm fused in front of the step (moe_forward_norm), x added back")
     ap.add_argument("--cpu-layers", type=int, default=0)
     ap.add_argument("--traffic", type=float, default=None,
                     help="HBM bytes per launch from rocprofv3 counters, if taken")

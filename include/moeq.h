@@ -116,6 +116,7 @@ typedef struct moeq_moe {
 #define MOEQ_PATH_GATHER 2  /* moe_gather_qmm                              */
 #define MOEQ_PATH_GQMM 3    /* gather_qmm (single projection; K is unused) */
 #define MOEQ_PATH_FORWARD 4 /* moe_forward                                 */
+#define MOEQ_PATH_FORWARD_NORM 5 /* moe_forward_norm                       */
 
 /* Human-readable text for a status code (static storage). */
 const char *moeq_status_string(int status);
@@ -197,6 +198,35 @@ int moe_expert_forward(const moeq_moe *L, const float *x, const int32_t *topk_id
 int moe_forward(const moeq_moe *L, const float *x, int32_t M, int32_t K, int32_t renorm,
                 const float *residual, float *y, int32_t *topk_idx, float *topk_w, void *ws,
                 size_t ws_bytes, moeq_stream_t stream);
+
+/* moe_rms_norm: h[m] = x[m] / sqrt(mean_k(x[m][k]^2) + eps) * norm_w, per row.
+ *   x : fp32 [M][H];  norm_w : fp32 [H];  h : fp32 [M][H] out;  H % 4 == 0;
+ *   eps >= 0 and finite (MOEQ_ERR_SHAPE otherwise)
+ * The mean square is reduced in fp32, its reciprocal square root taken in
+ * fp64.
+ * Defines: the two-pass RMSNorm before the router (flash-moe-inference skill
+ * page, rms_norm_pass1/2: sum of squares, then scale; the CMD2 chain o_proj ->
+ * residual_add -> rms_norm -> routing gate of the flash-moe issue thread). */
+int moe_rms_norm(const float *x, int32_t M, int32_t H, const float *norm_w, float eps, float *h,
+                 moeq_stream_t stream);
+
+/* moe_forward_norm: the step with its neighbours fused, for fp32 decode
+ * activations:  h = rms_norm(x), route and run the experts on h, and add the
+ * raw row back in the combine:  y = x + MoE(h).  Same results as moe_rms_norm
+ * followed by moe_forward(h, residual = x).
+ *   x : fp32 [M][H] (the residual stream);  norm_w, eps as in moe_rms_norm
+ *   y, topk_idx, topk_w out as in moe_forward
+ *   ws : workspace of moe_workspace_size(L, M, K, MOEQ_PATH_FORWARD_NORM)
+ * With an 8-bit router and M <= 4 this is ONE launch: every router and
+ * gate/up unit stages x * norm_w, reduces the row's mean square itself and
+ * scales its finished sums by the reciprocal root (both are linear in the
+ * row); otherwise the norm is a launch of its own in front of moe_forward's
+ * two launches, h kept in the workspace.
+ * Defines: the CMD2/CMD3 chain of the flash-moe-inference skill page (norm,
+ * routing, expert forward, combine + residual: moe_combine_residual). */
+int moe_forward_norm(const moeq_moe *L, const float *x, int32_t M, int32_t K, int32_t renorm,
+                     const float *norm_w, float eps, float *y, int32_t *topk_idx, float *topk_w,
+                     void *ws, size_t ws_bytes, moeq_stream_t stream);
 
 /* moe_gather_qmm: the expert part for many bf16 tokens (prefill).  Pairs
  * (token, slot) are sorted by expert on the device; per expert the gathered

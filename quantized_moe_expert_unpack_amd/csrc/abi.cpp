@@ -220,6 +220,14 @@ size_t forward_ws_bytes(const moeq::DecodeLayer& dl, int E, int M, int K) {
   return one > two ? one : two;
 }
 
+// moe_forward_norm: moe_forward's workspace, then the normalized rows [M][H]
+// (used when the step does not run as one launch)
+size_t forward_norm_ws_bytes(const moeq::DecodeLayer& dl, int E, int M, int K) {
+  return align_up(forward_ws_bytes(dl, E, M, K)) + align_up(sizeof(float) * (size_t)M * dl.H);
+}
+
+bool bad_eps(float eps) { return !(eps >= 0.0f) || eps > 3.0e38f; }
+
 }  // namespace
 
 extern "C" {
@@ -261,6 +269,10 @@ size_t moe_workspace_size(const moeq_moe* L, int32_t M, int32_t K, int32_t path)
   if (path == MOEQ_PATH_FORWARD) {
     if (!L->router.q || L->router.rows != d.E) return 0;
     return forward_ws_bytes(to_decode_layer(L, d), d.E, M, K) + kAlign;
+  }
+  if (path == MOEQ_PATH_FORWARD_NORM) {
+    if (!L->router.q || L->router.rows != d.E) return 0;
+    return forward_norm_ws_bytes(to_decode_layer(L, d), d.E, M, K) + kAlign;
   }
   if (path == MOEQ_PATH_GATHER) {
     if (!fits_i32((int64_t)M * K)) return 0;
@@ -387,6 +399,57 @@ int moe_forward(const moeq_moe* L, const float* x, int32_t M, int32_t K, int32_t
     moeq::launch_route_parts(&router, x, M, d.E, K, renorm, topk_idx, topk_w, nullptr, l64,
                              ds.route_ctr, s);
     st = run_expert_forward(dl, x, topk_idx, topk_w, M, K, residual, y, base, s);
+  }
+  if (st) return MOEQ_ERR_UNSUPPORTED;
+  return launch_status();
+}
+
+int moe_rms_norm(const float* x, int32_t M, int32_t H, const float* norm_w, float eps, float* h,
+                 moeq_stream_t stream) {
+  if (M < 0 || H <= 0 || H % 4 || bad_eps(eps)) return MOEQ_ERR_SHAPE;
+  if (M == 0) return MOEQ_OK;
+  if (!x || !norm_w || !h) return MOEQ_ERR_NULL_PTR;
+  if (!fits_i32((int64_t)M * H)) return MOEQ_ERR_OVERFLOW;
+  if (!aligned16(x) || !aligned16(norm_w) || !aligned16(h)) return MOEQ_ERR_ALIGN;
+  moeq::launch_rmsnorm(x, M, H, norm_w, eps, h, (hipStream_t)stream);
+  return launch_status();
+}
+
+int moe_forward_norm(const moeq_moe* L, const float* x, int32_t M, int32_t K, int32_t renorm,
+                     const float* norm_w, float eps, float* y, int32_t* topk_idx, float* topk_w,
+                     void* ws, size_t ws_bytes, moeq_stream_t stream) {
+  LayerDims d;
+  int st = check_experts(L, &d);
+  if (st) return st;
+  if ((st = check_qt(&L->router, 1, d.E, d.H))) return st;
+  if (M < 0 || K < 1 || K > kMaxK || K > d.E || bad_eps(eps)) return MOEQ_ERR_SHAPE;
+  if (M == 0) return MOEQ_OK;
+  if (!x || !norm_w || !y || !topk_idx || !topk_w) return MOEQ_ERR_NULL_PTR;
+  if (!fits_i32((int64_t)M * d.H) || !fits_i32((int64_t)M * d.E) ||
+      !fits_i32((int64_t)M * K * d.I + (int64_t)M * d.Is + M))
+    return MOEQ_ERR_OVERFLOW;
+  if (!aligned16(x) || !aligned16(norm_w) || !aligned16(y) || !aligned16(topk_idx) ||
+      !aligned16(topk_w))
+    return MOEQ_ERR_ALIGN;
+  const moeq::DecodeLayer dl = to_decode_layer(L, d);
+  if (!moeq::decode_supported(dl, K)) return MOEQ_ERR_UNSUPPORTED;
+  if (!ws || ws_bytes < forward_norm_ws_bytes(dl, d.E, M, K)) return MOEQ_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOEQ_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const QT router = to_qt(L->router);
+  if (moeq::fused_supported(dl, router, M, K)) {
+    const moeq::RouteIn R{router, renorm, topk_idx, topk_w};
+    st = moeq::launch_moe_forward_norm(dl, R, x, M, K, norm_w, eps, y, ws, s);
+  } else {
+    // normalize into the workspace, route and run the experts on h, add x back
+    char* base = reinterpret_cast<char*>(ws);
+    float* h = reinterpret_cast<float*>(base + align_up(forward_ws_bytes(dl, d.E, M, K)));
+    moeq::launch_rmsnorm(x, M, d.H, norm_w, eps, h, s);
+    const moeq::DecState ds = moeq::dec_state(dl, K, base);
+    double* l64 = reinterpret_cast<double*>(base + align_up(expert_ws_bytes(dl, M, K)));
+    moeq::launch_route_parts(&router, h, M, d.E, K, renorm, topk_idx, topk_w, nullptr, l64,
+                             ds.route_ctr, s);
+    st = run_expert_forward(dl, h, topk_idx, topk_w, M, K, x, y, base, s);
   }
   if (st) return MOEQ_ERR_UNSUPPORTED;
   return launch_status();

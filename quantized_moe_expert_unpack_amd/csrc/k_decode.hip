@@ -309,7 +309,10 @@ __device__ __forceinline__ void route_select(const uint64_t* keys, const double*
 // Router rows (8-bit) against x for all M tokens in fp64: the fp32
 // dequantized weight widened exactly, fp64 products and sums, as the oracle
 // defines the logits.  The R unit completing the arrivals selects.
-template <bool WIDE>
+// NORM: the rows see h = r * (x . g) with r = 1/sqrt(mean(x^2) + eps) per token
+// (RMSNorm): x . g is staged, each token's mean square reduced over the block,
+// and r applied to the finished logit.
+template <bool WIDE, bool NORM>
 __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P, const RouteIn R,
                                            const float* __restrict__ x, int u) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
@@ -339,9 +342,30 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
   }
   // x of every token in LDS, chunk-interleaved (float4 f of chunk c at f*nch+c)
   float4* xl = reinterpret_cast<float4*>(smem);
+  __shared__ float s_ss[NORM ? kWaves : 1][kFusedMaxM];
+  float ss[kFusedMaxM];
+#pragma unroll
+  for (int m = 0; m < kFusedMaxM; ++m) ss[m] = 0.f;
   for (int i = tid; i < M * (H / 4); i += kThreads) {
     const int m = i / (H / 4), ii = i - m * (H / 4);
-    xl[m * (H / 4) + (ii % 4) * nch + ii / 4] = reinterpret_cast<const float4*>(x)[i];
+    float4 v = reinterpret_cast<const float4*>(x)[i];
+    if constexpr (NORM) {
+      const float4 g = reinterpret_cast<const float4*>(P.norm_w)[ii];
+      const float q = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+#pragma unroll
+      for (int mm = 0; mm < kFusedMaxM; ++mm) ss[mm] += mm == m ? q : 0.f;
+      v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
+    }
+    xl[m * (H / 4) + (ii % 4) * nch + ii / 4] = v;
+  }
+  if constexpr (NORM) {
+#pragma unroll
+    for (int m = 0; m < kFusedMaxM; ++m) {
+      if (m < M) {
+        const float v = wave_sum(ss[m]);
+        if (lane == 0) s_ss[wid][m] = v;
+      }
+    }
   }
   float rs[2], rb[2];
 #pragma unroll
@@ -397,7 +421,12 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
 #pragma unroll
   for (int m = 0; m < kFusedMaxM; ++m) {
     if (m < M && h == 0 && lane == 0 && row_ok) {
-      const double tot = wsum[m] + part[m][wid / 2];
+      double tot = wsum[m] + part[m][wid / 2];
+      if constexpr (NORM) {
+        float sq = 0.f;
+        for (int w = 0; w < kWaves; ++w) sq += s_ss[w][m];
+        tot *= 1.0 / sqrt((double)sq / H + (double)P.norm_eps);
+      }
       // published as the complement of its bits: zero means "not written yet"
       // (the complement of a finite double is never zero)
       st_coh_u64(P.logits + (size_t)m * E + e, ~(uint64_t)__double_as_longlong(tot));
@@ -439,7 +468,7 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
 // ------------------------------------------------------------------ G unit
 // LDS: [x, chunk-interleaved][its chunk sums (<= H/16 floats)][bf16 scales and
 // biases of the unit's gate and up rows]
-template <int BITS, int CPL, bool FUSED>
+template <int BITS, int CPL, bool FUSED, bool NORM>
 __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan P,
                                              const float* __restrict__ x,
                                              const int32_t* __restrict__ idx, int u) {
@@ -472,12 +501,16 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
   uint16_t* sbl = reinterpret_cast<uint16_t*>(xsum + pad4(H / 16));   // [4][kGRows * gpr]
   float4* x4 = reinterpret_cast<float4*>(xs);
 
-  uint4 xr[2];
+  uint4 xr[2], gr[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int i = tid + j * kThreads;
     xr[j] = reinterpret_cast<const uint4*>(x + (size_t)t * H)[min(i, x16 - 1)];
+    if constexpr (NORM) gr[j] = reinterpret_cast<const uint4*>(P.norm_w)[min(i, x16 - 1)];
   }
+  // NORM: x . g is staged and the token's r = 1/sqrt(mean(x^2) + eps) scales
+  // the finished gate and up sums (both are linear in the row)
+  __shared__ float s_gss[NORM ? kWaves : 1];
   // the first shared-expert unit of a token also computes the token's
   // shared_expert_gate logit (one row of H, its own bits): one 16-byte chunk
   // per thread (H * bits / 128 <= kThreads), loaded now with the x loads
@@ -495,10 +528,23 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
   size_t erow = 0;                                  // first row of the expert
   if constexpr (FUSED) {
     // x and its chunk sums while the router runs, then the expert index
+    float ss = 0.f;
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int i = tid + j * kThreads;
-      if (i < x16) x4[ilv<kCpc>(i, nch)] = reinterpret_cast<const float4&>(xr[j]);
+      if (i < x16) {
+        float4 v = reinterpret_cast<const float4&>(xr[j]);
+        if constexpr (NORM) {
+          const float4 g = reinterpret_cast<const float4&>(gr[j]);
+          ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+          v = make_float4(v.x * g.x, v.y * g.y, v.z * g.z, v.w * g.w);
+        }
+        x4[ilv<kCpc>(i, nch)] = v;
+      }
+    }
+    if constexpr (NORM) {
+      ss = wave_sum(ss);
+      if (lane == 0) s_gss[wid] = ss;
     }
     __syncthreads();
     chunk_sums<kCpc>(x4, xsum, nch);
@@ -600,9 +646,15 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
       __syncthreads();
     }
   }
+  float rn = 1.f;
+  if constexpr (NORM) {
+    float sq = 0.f;
+    for (int w = 0; w < kWaves; ++w) sq += s_gss[w];
+    rn = (float)(1.0 / sqrt((double)sq / H + (double)P.norm_eps));
+  }
   if ((lane & 31) < kHCopies) {         // every lane of a half holds its row's sum
     const int i = wid * 2 + tindex<2, 32>(lane);
-    const float hv = valid ? silu(gsum) * usum : __builtin_nanf("");
+    const float hv = valid ? silu(rn * gsum) * (rn * usum) : __builtin_nanf("");
     if (i < nrows) {
       const size_t at = (size_t)(lane & 31) * P.P * P.Imax + (size_t)p * P.Imax + i_base + i;
       if constexpr (FUSED)   // complemented bits: 0 means "not written in this launch"
@@ -635,6 +687,7 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
     if (tid == 0) {
       float tot = 0.f;
       for (int w = 0; w < kWaves; ++w) tot += sgp[w];
+      tot *= rn;
       if constexpr (FUSED)
         st_coh_i(reinterpret_cast<int*>(P.sgb) + s_par * kFusedMaxM + t, (int)~__float_as_uint(tot));
       else
@@ -739,6 +792,12 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     const size_t base = k < K ? ((size_t)s_ex[k] * H + r0) * gr : (size_t)r0 * gs;
     sbr = reinterpret_cast<const uint4*>(src + base)[w];
   }
+  // the residual of the wave's row goes out with the unit's other loads, so
+  // the final sum does not wait for it (a wave-uniform address: a scalar
+  // load, held in a scalar register)
+  float resv = 0.f;
+  if (residual)
+    resv = residual[(size_t)t * H + r0 + __builtin_amdgcn_readfirstlane(min(rl, nrows - 1))];
   uint4 wv[DCH];
   const int rlc = min(rl, nrows - 1);
 #pragma unroll
@@ -948,7 +1007,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
   const float tsum = treduce<1, 32>(pv, lane);
   if (lane == 0 && rl < nrows) {
     float v = bad ? __builtin_nanf("") : tsum;
-    if (residual) v += residual[(size_t)t * H + r0 + rl];
+    if (residual) v += resv;
     y[(size_t)t * H + r0 + rl] = v;
   }
   if constexpr (FUSED) {
@@ -967,7 +1026,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
 
 // 8-bit layers of up to 2048 columns: at most 80 VGPRs, so three units fit per
 // CU (24 waves) and a 30B-A3B-shaped layer's units are all resident at once
-template <int BITS, int CPL, int DCH, bool FUSED>
+template <int BITS, int CPL, int DCH, bool FUSED, bool NORM>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(BITS == 8 && CPL <= 2 && DCH <= 6 ? 6 : 1))) k_moe_decode(DecodeLayer L, DecPlan P, RouteIn R,
                                                         const float* __restrict__ x,
@@ -978,12 +1037,12 @@ __global__ void __launch_bounds__(kThreads)
   int u = blockIdx.x;
   if constexpr (FUSED) {
     if (u < P.r_units) {
-      route_unit<!(BITS == 8 && CPL <= 2 && DCH <= 6)>(L, P, R, x, u);
+      route_unit<!(BITS == 8 && CPL <= 2 && DCH <= 6), NORM>(L, P, R, x, u);
       return;
     }
     u -= P.r_units;
   }
-  if (u < P.g_units) gate_up_unit<BITS, CPL, FUSED>(L, P, x, idx, u);
+  if (u < P.g_units) gate_up_unit<BITS, CPL, FUSED, NORM>(L, P, x, idx, u);
   else down_unit<BITS, DCH, FUSED>(L, P, idx, wts, residual, y, u - P.g_units);
 }
 
@@ -1115,16 +1174,16 @@ bool fused_supported(const DecodeLayer& L, const QT& router, int M, int K) {
          M >= 1 && M <= kFusedMaxM && L.E <= kMaxExperts && dec_lds_bytes(L, K, true, M) <= 160 * 1024;
 }
 
-template <int B, int CPL, int DCH, bool FUSED>
+template <int B, int CPL, int DCH, bool FUSED, bool NORM>
 static void run_dec(const DecodeLayer& L, const DecPlan& P, const RouteIn& R, const float* x,
                     const int32_t* idx, const float* w, const float* residual, float* y,
                     hipStream_t s) {
   const size_t lds = dec_lds_bytes(L, P.K, FUSED, P.M);
-  hipLaunchKernelGGL((k_moe_decode<B, CPL, DCH, FUSED>), dim3(P.r_units + P.g_units + P.d_units),
+  hipLaunchKernelGGL((k_moe_decode<B, CPL, DCH, FUSED, NORM>), dim3(P.r_units + P.g_units + P.d_units),
                      dim3(kThreads), lds, s, L, P, R, x, idx, w, residual, y);
 }
 
-template <bool FUSED>
+template <bool FUSED, bool NORM = false>
 static int dispatch_dec(const DecodeLayer& L, const DecPlan& P, const RouteIn& R, const float* x,
                         const int32_t* idx, const float* w, const float* residual, float* y,
                         hipStream_t s) {
@@ -1133,7 +1192,7 @@ static int dispatch_dec(const DecodeLayer& L, const DecPlan& P, const RouteIn& R
   const int dch = d_ch(L, P.K);
 #define MOEQ_DEC(B_, C_, D_)                                              \
   if (b == B_ && cpl == C_ && dch == D_) {                               \
-    run_dec<B_, C_, D_, FUSED>(L, P, R, x, idx, w, residual, y, s);      \
+    run_dec<B_, C_, D_, FUSED, NORM>(L, P, R, x, idx, w, residual, y, s); \
     return 0;                                                            \
   }
 #define MOEQ_DEC_PW(B_, C_) MOEQ_DEC(B_, C_, 1) MOEQ_DEC(B_, C_, 2) MOEQ_DEC(B_, C_, 3) \
@@ -1161,6 +1220,17 @@ int launch_moe_forward(const DecodeLayer& L, const RouteIn& R, const float* x, i
   if (M > kFusedMaxM) return -9;
   const DecPlan P = make_dec_plan(L, M, K, true, ws, nullptr);
   return dispatch_dec<true>(L, P, R, x, nullptr, nullptr, residual, y, s);
+}
+
+// the same launch with RMSNorm in front (router and experts see
+// x / sqrt(mean(x^2) + eps) * g) and x added back in the combine
+int launch_moe_forward_norm(const DecodeLayer& L, const RouteIn& R, const float* x, int M, int K,
+                            const float* norm_w, float eps, float* y, void* ws, hipStream_t s) {
+  if (M > kFusedMaxM) return -9;
+  DecPlan P = make_dec_plan(L, M, K, true, ws, nullptr);
+  P.norm_w = norm_w;
+  P.norm_eps = eps;
+  return dispatch_dec<true, true>(L, P, R, x, nullptr, nullptr, x, y, s);
 }
 
 }  // namespace moeq

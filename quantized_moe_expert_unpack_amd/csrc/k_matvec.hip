@@ -284,6 +284,45 @@ int launch_qdequant(const QT& W, uint8_t* codes, float* deq, hipStream_t s) {
   return 0;
 }
 
+// RMSNorm of one row per block (flash-moe-inference skill page, the two-pass
+// rms_norm_pass1/2: the row's sum of squares, then every element scaled):
+// h = x * r * g with r = 1/sqrt(mean(x^2) + eps), the mean square reduced in
+// fp32 over the block and r taken in fp64.  H % 4 == 0.
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ x, int H,
+                                                  const float* __restrict__ g, float eps,
+                                                  float* __restrict__ h) {
+  __shared__ float part[256 / kWave];
+  __shared__ float s_r;
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const float4* xr = reinterpret_cast<const float4*>(x + (size_t)t * H);
+  float ss = 0.f;
+  for (int i = tid; i < H / 4; i += 256) {
+    const float4 v = xr[i];
+    ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+  }
+  ss = wave_sum(ss);
+  if ((tid & (kWave - 1)) == 0) part[tid / kWave] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    float tot = 0.f;
+    for (int w = 0; w < 256 / kWave; ++w) tot += part[w];
+    s_r = (float)(1.0 / sqrt((double)tot / H + (double)eps));
+  }
+  __syncthreads();
+  const float r = s_r;
+  const float4* g4 = reinterpret_cast<const float4*>(g);
+  float4* hr = reinterpret_cast<float4*>(h + (size_t)t * H);
+  for (int i = tid; i < H / 4; i += 256) {
+    const float4 v = xr[i], w = g4[i];
+    hr[i] = make_float4(v.x * r * w.x, v.y * r * w.y, v.z * r * w.z, v.w * r * w.w);
+  }
+}
+
+int launch_rmsnorm(const float* x, int M, int H, const float* g, float eps, float* h, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(M), dim3(256), 0, s, x, H, g, eps, h);
+  return 0;
+}
+
 int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s) {
   const int blocks = (W.rows + 3) / 4;
   MOEQ_BITS_LAUNCH(W.bits, k_qmatvec, dim3(blocks), s, W.q, W.scales, W.biases, W.rows, W.cols,

@@ -65,6 +65,8 @@ struct DecPlan {
   size_t hreg;
   uint32_t* sgb;     // [2][kFusedMaxM] shared-gate logits, the same way
   int32_t* idx_c;  // route lines: copies [kRep] of token lines (64-bit expert + 1 | weight words)
+  const float* norm_w;  // RMSNorm weight [H] of a launch that normalizes x first, else null
+  float norm_eps;
 };
 
 // Router of a decode launch that routes in the same launch.
@@ -112,6 +114,8 @@ struct BatchWs {
 
 int launch_qdequant(const QT& W, uint8_t* codes, float* deq, hipStream_t s);
 int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s);
+// RMSNorm per row: h = x / sqrt(mean(x^2) + eps) * g, rows of H (H % 4 == 0)
+int launch_rmsnorm(const float* x, int M, int H, const float* g, float eps, float* h, hipStream_t s);
 // 2-bit requantization of a 4- or 8-bit tensor (group size 64 or 128)
 int launch_requant_2bit(const QT& W, uint32_t* q2, uint16_t* s2, uint16_t* b2, hipStream_t s);
 // routing: router projection (fp64) + softmax/top-K.  The standalone
@@ -134,6 +138,8 @@ bool decode_supported(const DecodeLayer& L, int K);
 bool fused_supported(const DecodeLayer& L, const QT& router, int M, int K);
 int launch_moe_forward(const DecodeLayer& L, const RouteIn& R, const float* x, int M, int K,
                        const float* residual, float* y, void* ws, hipStream_t s);
+int launch_moe_forward_norm(const DecodeLayer& L, const RouteIn& R, const float* x, int M, int K,
+                            const float* norm_w, float eps, float* y, void* ws, hipStream_t s);
 
 // batched decode
 bool batch_supported(const DecodeLayer& L);

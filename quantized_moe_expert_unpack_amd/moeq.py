@@ -20,7 +20,7 @@ import torch
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libmoeq.so")
 
-PATH_ROUTE, PATH_DECODE, PATH_GATHER, PATH_GQMM, PATH_FORWARD = 0, 1, 2, 3, 4
+PATH_ROUTE, PATH_DECODE, PATH_GATHER, PATH_GQMM, PATH_FORWARD, PATH_FORWARD_NORM = 0, 1, 2, 3, 4, 5
 
 STATUS = {
     0: "MOEQ_OK", -1: "MOEQ_ERR_NULL_PTR", -2: "MOEQ_ERR_BAD_BITS", -3: "MOEQ_ERR_BAD_GROUP",
@@ -68,6 +68,9 @@ _SIGNATURES = {
                                    _SZ, _P]),
     "moe_gather_qmm": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _P, _P, _I, _I, _P, _P, _SZ,
                                       _P]),
+    "moe_rms_norm": (ctypes.c_int, [_P, _I, _I, _P, ctypes.c_float, _P, _P]),
+    "moe_forward_norm": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _I, _I, _I, _P, ctypes.c_float,
+                                        _P, _P, _P, _P, _SZ, _P]),
     "gather_qmm": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _P, _I, _I, _P, _P, _SZ, _P]),
 }
 
@@ -299,6 +302,39 @@ def moe_forward(layer: MoELayer, x: torch.Tensor, k: int, renorm: bool = True,
     _check(lib().moe_forward(ctypes.byref(layer.struct()), _ptr(x), m, k, int(bool(renorm)),
                              _ptr(residual), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws), ws.numel(),
                              _stream(stream)), "moe_forward")
+    return y, idx, w
+
+
+def moe_rms_norm(x: torch.Tensor, norm_w: torch.Tensor, eps: float,
+                 h: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """h = x / sqrt(mean(x^2) + eps) * norm_w per row (fp32)."""
+    m, hdim = x.shape
+    if h is None:
+        h = torch.empty_like(x)
+    _check(lib().moe_rms_norm(_ptr(x), m, hdim, _ptr(norm_w), float(eps), _ptr(h), _stream(stream)),
+           "moe_rms_norm")
+    return h
+
+
+def moe_forward_norm(layer: MoELayer, x: torch.Tensor, k: int, norm_w: torch.Tensor, eps: float,
+                     renorm: bool = True, ws: Optional[torch.Tensor] = None,
+                     y: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                     w: Optional[torch.Tensor] = None, stream=None):
+    """y = x + MoE(rms_norm(x)) (one launch for an 8-bit router and M <= 4).
+    Returns (y, idx, w)."""
+    m = x.shape[0]
+    dev = x.device
+    if ws is None:
+        ws = workspace(layer, m, k, PATH_FORWARD_NORM, dev)
+    if y is None:
+        y = torch.empty((m, layer.hidden), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((m, k), dtype=torch.float32, device=dev)
+    _check(lib().moe_forward_norm(ctypes.byref(layer.struct()), _ptr(x), m, k, int(bool(renorm)),
+                                  _ptr(norm_w), float(eps), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws),
+                                  ws.numel(), _stream(stream)), "moe_forward_norm")
     return y, idx, w
 
 

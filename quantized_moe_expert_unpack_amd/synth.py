@@ -350,6 +350,12 @@ def requant_source_device(seed: int, batch: int, rows: int, cols: int, bits: int
 # activations and router logits
 # --------------------------------------------------------------------------
 
+def norm_weight(cfg: MoEConfig, layer: int) -> np.ndarray:
+    """The RMSNorm weight in front of a layer's MoE step: fp32 U(0.5, 1.5)."""
+    rng = _rng(cfg.seed, layer, 0x4E4F524D)
+    return rng.uniform(0.5, 1.5, cfg.hidden).astype(np.float32)
+
+
 def decode_x(cfg: MoEConfig, layer: int, token: int, sub: int = 0, m: int = 1) -> np.ndarray:
     """fp32 ``N(0,1)`` activations ``[m, hidden]`` for (layer, token slot);
     ``sub`` selects a redraw."""

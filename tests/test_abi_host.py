@@ -31,8 +31,8 @@ def declared_functions():
 def test_header_declares_the_four_calls_and_helpers():
     names = declared_functions()
     for n in ("qmatvec", "moe_route", "moe_expert_forward", "moe_gather_qmm", "qdequant",
-              "gather_qmm", "requant_2bit", "moe_workspace_size", "moeq_status_string",
-              "moeq_version"):
+              "gather_qmm", "requant_2bit", "moe_rms_norm", "moe_forward_norm",
+              "moe_workspace_size", "moeq_status_string", "moeq_version"):
         assert n in names
 
 
@@ -179,6 +179,38 @@ def test_forward_validation():
     assert call(_layer(), ws=16) == -8
     assert call(_layer(), M=0) == 0
     assert moeq.lib().moe_workspace_size(ctypes.byref(_layer()), 1, 2, moeq.PATH_FORWARD) > 0
+
+
+def test_norm_validation():
+    f = moeq.lib().moe_rms_norm
+    assert f(FAKE, -1, 256, FAKE, 1e-6, FAKE, None) == -5
+    assert f(FAKE, 2, 258, FAKE, 1e-6, FAKE, None) == -5            # H % 4 != 0
+    assert f(FAKE, 2, 256, FAKE, -1.0, FAKE, None) == -5            # eps < 0
+    assert f(FAKE, 2, 256, FAKE, float("nan"), FAKE, None) == -5
+    assert f(FAKE, 2, 256, FAKE, float("inf"), FAKE, None) == -5
+    assert f(FAKE, 0, 256, FAKE, 1e-6, FAKE, None) == 0             # empty: no launch
+    assert f(None, 2, 256, FAKE, 1e-6, FAKE, None) == -1
+    assert f(FAKE, 2, 256, None, 1e-6, FAKE, None) == -1
+    assert f(FAKE, 2, 256, FAKE + 4, 1e-6, FAKE, None) == -7
+    g = moeq.lib().moe_forward_norm
+
+    def call(L, M=1, K=2, eps=1e-6, ws=1 << 30, **kw):
+        a = dict(x=FAKE, nw=FAKE, y=FAKE, idx=FAKE, w=FAKE, wsp=FAKE)
+        a.update(kw)
+        return g(ctypes.byref(L), a["x"], M, K, 1, a["nw"], eps, a["y"], a["idx"], a["w"], a["wsp"], ws,
+                 None)
+
+    assert call(_layer(), nw=None) == -1
+    assert call(_layer(), nw=FAKE + 8) == -7
+    assert call(_layer(), eps=-1e-3) == -5
+    assert call(_layer(), K=9) == -5
+    assert call(_layer(router=_qt(8, 1, 16, 256))) == -5
+    assert call(_layer(), ws=16) == -8
+    assert call(_layer(), M=0) == 0
+    L = _layer()
+    n4 = moeq.lib().moe_workspace_size(ctypes.byref(L), 24, 2, moeq.PATH_FORWARD)
+    n5 = moeq.lib().moe_workspace_size(ctypes.byref(L), 24, 2, moeq.PATH_FORWARD_NORM)
+    assert n5 >= n4 + 24 * 256 * 4                                    # + the normalized rows
 
 
 def test_workspace_sizes():
