@@ -54,6 +54,13 @@ Sources, cited by page title and section:
   tool but not its arithmetic; the reading used is below in
   ``requant_2bit``.
 
+The mxfp4 expert mode that the mlx issue thread runs beside affine
+(``mode="mxfp4"``, group size 32, its repro table and the per-model list of
+mxfp4 experts) is the OCP Microscaling format that mode names: 4-bit E2M1
+elements (1 sign, 2 exponent, 1 mantissa bit, exponent bias 1) with one
+E8M0 scale byte (a power of two, ``2**(e - 127)``, 255 = NaN) per 32
+elements and no bias; the pages give no more than the mode's name.
+
 Readings where the pages are silent (each is listed with its reason in the
 design notes): codes sit low bits first inside a word; scales and biases are
 bf16; the group parameter is the number of elements per group; renormalized
@@ -75,6 +82,8 @@ import numpy as np
 __all__ = [
     "bf16_bits_to_f32",
     "unpack_codes",
+    "fp4_e2m1",
+    "e8m0_scale",
     "dequantize",
     "expert_slice",
     "qmatvec",
@@ -129,17 +138,50 @@ def unpack_codes(words, bits: int, cols: int) -> np.ndarray:
     return codes.reshape(w.shape[:-1] + (cols,)).astype(np.uint8)
 
 
+def fp4_e2m1(code) -> np.ndarray:
+    """Value of 4-bit E2M1 codes: bit 3 the sign, bits 2-1 the exponent e
+    (bias 1), bit 0 the mantissa m.  e = 0: m/2 (zero or one half);
+    otherwise (1 + m/2) * 2**(e - 1).  So the magnitudes of codes 0..7 are
+    0, 0.5, 1, 1.5, 2, 3, 4, 6."""
+    c = np.asarray(code, dtype=np.int64)
+    sign = np.where(c & 8, -1.0, 1.0)
+    e = (c >> 1) & 3
+    m = c & 1
+    mag = np.where(e == 0, 0.5 * m, (1.0 + 0.5 * m) * np.exp2(e - 1.0))
+    return sign * mag
+
+
+def e8m0_scale(byte) -> np.ndarray:
+    """Value of E8M0 scale bytes: ``2**(byte - 127)``, byte 255 is NaN."""
+    b = np.asarray(byte, dtype=np.int64)
+    return np.where(b == 255, np.nan, np.exp2(b - 127.0))
+
+
 def dequantize(qt: dict) -> np.ndarray:
     """Dequantize a quantized matrix (or a stack of them) to float32.
 
-    ``w = scale * code + bias`` per group of ``group_size`` consecutive input
-    columns.  The product of a bf16 scale (8 significant bits) and a code of at
-    most 8 bits is exact in float32, so the float32 result is the single
-    rounding of ``scale * code + bias``.
+    Affine: ``w = scale * code + bias`` per group of ``group_size``
+    consecutive input columns.  The product of a bf16 scale (8 significant
+    bits) and a code of at most 8 bits is exact in float32, so the float32
+    result is the single rounding of ``scale * code + bias``.
+
+    mxfp4 (``qt["mode"] == "mxfp4"``): ``w = fp4_e2m1(code) * 2**(e - 127)``
+    with the group's scale byte e, no bias; the product of a two-bit
+    significand and a power of two is exact in float32 (down to its
+    subnormals), so the float32 result is exact unless it overflows.
     """
     bits, gs, cols = int(qt["bits"]), int(qt["group_size"]), int(qt["cols"])
     if cols % gs:
         raise ValueError("cols must be a multiple of group_size")
+    if qt.get("mode", "affine") == "mxfp4":
+        if bits != 4 or gs != 32:
+            raise ValueError("mxfp4 is 4-bit with groups of 32")
+        codes = unpack_codes(qt["q"], 4, cols)
+        sc = np.repeat(e8m0_scale(qt["scales"]), gs, axis=-1)
+        if sc.shape != codes.shape:
+            raise ValueError(f"scales shape {sc.shape} does not match codes {codes.shape}")
+        with np.errstate(over="ignore", invalid="ignore"):
+            return (fp4_e2m1(codes) * sc).astype(np.float32)
     codes = unpack_codes(qt["q"], bits, cols).astype(np.float32)
     s = np.repeat(bf16_bits_to_f32(qt["scales"]), gs, axis=-1)
     b = np.repeat(bf16_bits_to_f32(qt["biases"]), gs, axis=-1)
@@ -155,7 +197,8 @@ def expert_slice(qt: dict, e: int) -> dict:
     out = dict(qt)
     out["q"] = qt["q"][e]
     out["scales"] = qt["scales"][e]
-    out["biases"] = qt["biases"][e]
+    if qt.get("biases") is not None:       # (mxfp4 tensors have none)
+        out["biases"] = qt["biases"][e]
     return out
 
 

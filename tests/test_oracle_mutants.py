@@ -12,6 +12,7 @@ import pytest
 import oracle
 import oracle.moe_oracle as mo
 from tests import test_oracle_format as tf
+from tests import test_oracle_mxfp4 as tm
 from tests import test_oracle_norm as tn
 from tests import test_oracle_requant as tq
 from tests import test_oracle_route_ffn as tr
@@ -40,6 +41,8 @@ _silu = mo.silu
 _moe_experts = mo.moe_experts
 _bf16_round = mo.bf16_round
 _rms_norm = mo.rms_norm
+_fp4 = mo.fp4_e2m1
+_e8m0 = mo.e8m0_scale
 _moe_block = mo.moe_block
 _requant = mo.requant_2bit
 
@@ -88,12 +91,37 @@ def _norm_pins():
     tn.test_block_routes_and_runs_on_the_normalized_row()
 
 
+def _mxfp4_pins():
+    for row in golden_rows("mxfp4_values.txt"):
+        tm.test_hand_worked_values(row)
+    tm.test_magnitudes_follow_the_e2m1_formula()
+    tm.test_scale_is_a_power_of_two_and_255_is_nan()
+    tm.test_groups_of_32_columns_take_their_own_scale()
+    tm.test_hand_packed_word_low_nibble_first()
+
+
 def test_pins_pass_on_the_real_oracle():
     _format_pins()
     _route_pins()
     _layer_pins()
     _requant_pins()
     _norm_pins()
+    _mxfp4_pins()
+
+
+def test_fp4_exponent_bias_zero_is_caught(monkeypatch):
+    _patch(monkeypatch, "fp4_e2m1", lambda c: 2.0 * _fp4(c))
+    assert _fails(_mxfp4_pins)
+
+
+def test_fp4_sign_ignored_is_caught(monkeypatch):
+    _patch(monkeypatch, "fp4_e2m1", lambda c: np.abs(_fp4(c)))
+    assert _fails(_mxfp4_pins)
+
+
+def test_e8m0_bias_off_by_one_is_caught(monkeypatch):
+    _patch(monkeypatch, "e8m0_scale", lambda b: _e8m0(b) / 2.0)
+    assert _fails(_mxfp4_pins)
 
 
 def test_norm_without_eps_is_caught(monkeypatch):
@@ -297,6 +325,7 @@ def test_requant_high_bits_first_packing_is_caught(monkeypatch):
 
 
 @pytest.mark.parametrize("name", ["unpack_codes", "dequantize", "route", "moe_experts",
-                                  "bf16_round", "requant_2bit", "rms_norm", "moe_block"])
+                                  "bf16_round", "requant_2bit", "rms_norm", "moe_block",
+                                  "fp4_e2m1", "e8m0_scale"])
 def test_each_patch_target_exists(name):
     assert callable(getattr(mo, name))
