@@ -14,7 +14,7 @@ are resident in HBM before the timed region.
 Other workloads: ``c3`` (397B-A17B-shaped decode, 4-bit experts + shared
 expert, 8 layers), ``c5`` / ``c5_4bit`` (the same shapes at 2 / 4 bits, 64
 tokens per step), ``c4`` (prefill gather_qmm, M=16384 tokens, one layer),
-``requant`` (the 2-bit requantization of one 397B-A17B-shaped layer's three
+``c4_mxfp4`` (the same prefill with mxfp4 experts), ``requant`` (the 2-bit requantization of one 397B-A17B-shaped layer's three
 4-bit expert stacks, gate and up [512][1024][4096], down [512][4096][1024]).
 
 Prints one JSON line.  ``roofline`` rates the dominant launch against the HBM
@@ -376,7 +376,8 @@ def run_prefill(args, cfg):
 
     dev = torch.device("cuda:0")
     m = args.tokens or cfg.tokens
-    host = synth.host_layer(cfg, 0, threads=16)
+    host = (synth.mxfp4_experts(cfg, 0) if cfg.expert_mode == "mxfp4"
+            else synth.host_layer(cfg, 0, threads=16))
     L = moeq.MoELayer.from_host(host, dev)
     xb = torch.from_numpy(synth.prefill_x_bf16(cfg, m).view(np.int16)).to(dev)
     lg = torch.from_numpy(synth.zipf_logits(cfg, m)).to(dev)
@@ -410,7 +411,8 @@ def run_prefill(args, cfg):
         "data": "synthetic",
         "config": {"workload": cfg.name, "tokens": m, "hidden": cfg.hidden,
                    "experts": cfg.experts, "top_k": K, "inter": cfg.inter,
-                   "expert_bits": cfg.expert_bits, "logits": "zipf(1.1)+gumbel"},
+                   "expert_bits": cfg.expert_bits, "expert_mode": cfg.expert_mode,
+                   "group_size": cfg.group_size, "logits": "zipf(1.1)+gumbel"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic_for(args, "k_gqmm"), "kernel": "moe_route + moe_gather_qmm",
@@ -513,7 +515,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5", "c5_4bit", "requant"])
+    ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c4_mxfp4", "c5", "c5_4bit", "requant"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (decode)")
     ap.add_argument("--tokens", type=int, default=0, help="override M (prefill)")
     ap.add_argument("--slots", type=int, default=TOKEN_SLOTS)
@@ -555,7 +557,7 @@ def main():
         print(json.dumps(out), flush=True)
         return
     cfg = synth.CONFIGS[args.config]
-    if args.config == "c4":
+    if args.config in ("c4", "c4_mxfp4"):
         out = run_prefill(args, cfg)
         host = out.pop("_host")
         if not args.no_cpu_baseline:

@@ -79,18 +79,31 @@ typedef enum moeq_status {
  * may end on half a 64-column step.  Every expert matrix of a layer (and the
  * shared expert's gate/up/down) uses one group size (MOEQ_ERR_UNSUPPORTED
  * otherwise); the router and the shared expert's gate row may use their own.
+ * mode MOEQ_MODE_MXFP4 (the mxfp4 mode the mlx issue runs beside affine; its
+ * format is the OCP Microscaling FP4 one): bits 4 and group_size 32
+ * (MOEQ_ERR_BAD_BITS / MOEQ_ERR_BAD_GROUP otherwise), 4-bit E2M1 codes
+ * packed like affine 4-bit codes (sign, two exponent bits with bias 1, one
+ * mantissa bit: magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6), one E8M0 scale byte per
+ * 32 columns (2^(e - 127); 255 is NaN and gives unspecified outputs), no bias.
+ * qdequant, qmatvec, gather_qmm and moe_gather_qmm take it; the decode entry
+ * points, moe_route and requant_2bit return MOEQ_ERR_UNSUPPORTED.  Any other
+ * mode value: MOEQ_ERR_UNSUPPORTED.
  * The markbaseengine expert kernel hung when this parameter was missing or garbage
  * (MOE_FIX_SUCCESS_EXPERT_WORKS, "Bug Details"), so it is an explicit,
  * validated field here. */
+#define MOEQ_MODE_AFFINE 0  /* w = scale * code + bias, bf16 scale and bias per group */
+#define MOEQ_MODE_MXFP4 1   /* w = e2m1(code) * 2^(e - 127), one E8M0 byte e per 32 cols */
+
 typedef struct moeq_qtensor {
   const uint32_t *q;
-  const uint16_t *scales;
-  const uint16_t *biases;
+  const uint16_t *scales;   /* MOEQ_MODE_MXFP4: uint8 E8M0 bytes [batch][rows][cols/32] */
+  const uint16_t *biases;   /* MOEQ_MODE_MXFP4: unused, may be NULL */
   int32_t batch;
   int32_t rows;
   int32_t cols;
   int32_t bits;
   int32_t group_size;
+  int32_t mode;             /* MOEQ_MODE_AFFINE (0) or MOEQ_MODE_MXFP4 (1) */
 } moeq_qtensor;
 
 /* One MoE layer.  router [1][E][H]; gate, up [E][I][H]; down [E][H][I].

@@ -27,7 +27,13 @@ inline bool fits_i32(int64_t v) { return v >= 0 && v <= INT32_MAX; }
 // Validate one quantized tensor; expected dims < 0 are not checked.
 int check_qt(const moeq_qtensor* t, int batch, int rows, int cols) {
   if (!t) return MOEQ_ERR_NULL_PTR;
-  if (!t->q || !t->scales || !t->biases) return MOEQ_ERR_NULL_PTR;
+  if (t->mode != MOEQ_MODE_AFFINE && t->mode != MOEQ_MODE_MXFP4) return MOEQ_ERR_UNSUPPORTED;
+  const bool mx = t->mode == MOEQ_MODE_MXFP4;
+  if (!t->q || !t->scales || (!mx && !t->biases)) return MOEQ_ERR_NULL_PTR;
+  if (mx) {
+    if (t->bits != 4) return MOEQ_ERR_BAD_BITS;
+    if (t->group_size != 32) return MOEQ_ERR_BAD_GROUP;
+  }
   if (t->bits != 2 && t->bits != 4 && t->bits != 8) return MOEQ_ERR_BAD_BITS;
   // 32, 64 or 128 elements per group; at 2 bits 64 or 128 (a 16-byte chunk
   // of 2-bit codes is 64 elements and must lie in one group)
@@ -42,12 +48,15 @@ int check_qt(const moeq_qtensor* t, int batch, int rows, int cols) {
       !fits_i32((int64_t)t->batch * t->rows * (t->cols / (32 / t->bits))) ||
       !fits_i32((int64_t)t->batch * t->rows * t->cols / 4))
     return MOEQ_ERR_OVERFLOW;
-  if (!aligned16(t->q) || !aligned16(t->scales) || !aligned16(t->biases)) return MOEQ_ERR_ALIGN;
+  if (!aligned16(t->q) || !aligned16(t->scales) || (!mx && !aligned16(t->biases))) return MOEQ_ERR_ALIGN;
   return MOEQ_OK;
 }
 
+bool is_mx(const moeq_qtensor& t) { return t.mode == MOEQ_MODE_MXFP4; }
+
 QT to_qt(const moeq_qtensor& t) {
-  return QT{t.q, t.scales, t.biases, t.batch, t.rows, t.cols, t.bits, t.group_size};
+  return QT{t.q, t.scales, is_mx(t) ? nullptr : t.biases, t.batch, t.rows, t.cols, t.bits,
+            t.group_size, t.mode};
 }
 
 int launch_status() {
@@ -72,6 +81,7 @@ int check_experts(const moeq_moe* L, LayerDims* d) {
   if ((st = check_qt(&L->up, d->E, d->I, d->H))) return st;
   if ((st = check_qt(&L->down, d->E, d->H, d->I))) return st;
   if (L->up.bits != g.bits || L->down.bits != g.bits) return MOEQ_ERR_UNSUPPORTED;
+  if (L->up.mode != g.mode || L->down.mode != g.mode) return MOEQ_ERR_UNSUPPORTED;
   // one group size for every expert matrix (the router and the shared
   // expert's gate row may differ)
   if (L->up.group_size != g.group_size || L->down.group_size != g.group_size)
@@ -85,6 +95,8 @@ int check_experts(const moeq_moe* L, LayerDims* d) {
     if ((st = check_qt(&L->sh_expert_gate, 1, 1, d->H))) return st;
     if (L->sh_up.bits != L->sh_gate.bits || L->sh_down.bits != L->sh_gate.bits)
       return MOEQ_ERR_UNSUPPORTED;
+    if (is_mx(L->sh_gate) || is_mx(L->sh_up) || is_mx(L->sh_down) || is_mx(L->sh_expert_gate))
+      return MOEQ_ERR_UNSUPPORTED;                    // the shared expert is affine
     if (L->sh_gate.group_size != g.group_size || L->sh_up.group_size != g.group_size ||
         L->sh_down.group_size != g.group_size)
       return MOEQ_ERR_UNSUPPORTED;
@@ -294,7 +306,7 @@ int requant_2bit(const moeq_qtensor* W, uint32_t* q_out, uint16_t* s_out, uint16
                  moeq_stream_t stream) {
   int st = check_qt(W, -1, -1, -1);
   if (st) return st;
-  if (W->bits == 2) return MOEQ_ERR_UNSUPPORTED;     // already 2-bit
+  if (W->bits == 2 || is_mx(*W)) return MOEQ_ERR_UNSUPPORTED;   // already 2-bit; not affine
   if (W->group_size == 32) return MOEQ_ERR_BAD_GROUP;   // no 2-bit groups of 32
   if (!q_out || !s_out || !b_out) return MOEQ_ERR_NULL_PTR;
   if (!aligned16(q_out) || !aligned16(s_out) || !aligned16(b_out)) return MOEQ_ERR_ALIGN;
@@ -321,6 +333,7 @@ int moe_route(const moeq_qtensor* gate, const float* x_or_logits, int32_t M, int
   if (gate) {
     int st = check_qt(gate, 1, E, -1);
     if (st) return st;
+    if (is_mx(*gate)) return MOEQ_ERR_UNSUPPORTED;   // routers are affine
   }
   if (M == 0) return MOEQ_OK;
   if (!x_or_logits || !topk_idx || !topk_w) return MOEQ_ERR_NULL_PTR;
@@ -350,6 +363,7 @@ int moe_expert_forward(const moeq_moe* L, const float* x, const int32_t* topk_id
   LayerDims d;
   int st = check_experts(L, &d);
   if (st) return st;
+  if (is_mx(L->gate)) return MOEQ_ERR_UNSUPPORTED;   // mxfp4 experts: gather paths only
   if (M < 0 || K < 1 || K > kMaxK || K > d.E) return MOEQ_ERR_SHAPE;
   if (M == 0) return MOEQ_OK;
   if (!x || !topk_idx || !topk_w || !y) return MOEQ_ERR_NULL_PTR;
@@ -373,7 +387,9 @@ int moe_forward(const moeq_moe* L, const float* x, int32_t M, int32_t K, int32_t
   LayerDims d;
   int st = check_experts(L, &d);
   if (st) return st;
+  if (is_mx(L->gate)) return MOEQ_ERR_UNSUPPORTED;   // mxfp4 experts: gather paths only
   if ((st = check_qt(&L->router, 1, d.E, d.H))) return st;
+  if (is_mx(L->router)) return MOEQ_ERR_UNSUPPORTED;
   if (M < 0 || K < 1 || K > kMaxK || K > d.E) return MOEQ_ERR_SHAPE;
   if (M == 0) return MOEQ_OK;
   if (!x || !y || !topk_idx || !topk_w) return MOEQ_ERR_NULL_PTR;
@@ -421,7 +437,9 @@ int moe_forward_norm(const moeq_moe* L, const float* x, int32_t M, int32_t K, in
   LayerDims d;
   int st = check_experts(L, &d);
   if (st) return st;
+  if (is_mx(L->gate)) return MOEQ_ERR_UNSUPPORTED;   // mxfp4 experts: gather paths only
   if ((st = check_qt(&L->router, 1, d.E, d.H))) return st;
+  if (is_mx(L->router)) return MOEQ_ERR_UNSUPPORTED;
   if (M < 0 || K < 1 || K > kMaxK || K > d.E || bad_eps(eps)) return MOEQ_ERR_SHAPE;
   if (M == 0) return MOEQ_OK;
   if (!x || !norm_w || !y || !topk_idx || !topk_w) return MOEQ_ERR_NULL_PTR;

@@ -70,7 +70,29 @@ __device__ __forceinline__ void dequant32h(const u32x4* v, int h, float s, float
   }
 }
 
-template <int BITS, int MODE>
+// mxfp4: the 32 E2M1 codes of one group (4 words) times the group's E8M0
+// scale, to 16 packed bf16 pairs, by the scaled conversion instruction (it
+// takes the exponent field of s: s = 2^(e-127) as fp32 bits, e = 0 as the
+// subnormal 2^-127).  s == 0 marks a masked half step: the codes are cleared
+// (the instruction does not scale by zero).
+__device__ __forceinline__ void dequant32_mx(const u32x4* v, float s, uint32_t* out) {
+  const uint32_t keep = s != 0.f ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t x = v[0][w] & keep;
+    out[4 * w + 0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, s, 0));
+    out[4 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, s, 1));
+    out[4 * w + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, s, 2));
+    out[4 * w + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, s, 3));
+  }
+}
+
+// E8M0 byte -> the fp32 whose exponent field the conversion reads
+__device__ __forceinline__ float e8m0_f32(uint32_t e) {
+  return __uint_as_float(e == 0 ? 0x00400000u : e << 23);
+}
+
+template <int BITS, int MODE, bool MX = false>
 __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd,
                                                       const uint16_t* __restrict__ A, int a_div,
                                                       GatherWs ws, const float* __restrict__ wts,
@@ -121,7 +143,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
   // stored).
   const int bc = tid >> 1, bh = tid & 1;
   const uint32_t* bq;
-  const uint16_t *bs, *bb;
+  const uint16_t *bs = nullptr, *bb = nullptr;
+  const uint8_t* bs8 = nullptr;                    // mxfp4: E8M0 scale bytes of the column
   int gsz;                                         // elements per group of this column's matrix
   {
     int n;
@@ -136,8 +159,12 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
     }
     const size_t row = (size_t)e * N + min(n, N - 1);
     bq = M->q + row * (Kd / (32 / BITS));
-    bs = M->scales + row * (Kd / M->group_size);
-    bb = M->biases + row * (Kd / M->group_size);
+    if constexpr (MX) {
+      bs8 = reinterpret_cast<const uint8_t*>(M->scales) + row * (Kd / 32);
+    } else {
+      bs = M->scales + row * (Kd / M->group_size);
+      bb = M->biases + row * (Kd / M->group_size);
+    }
     gsz = M->group_size;
   }
 
@@ -174,8 +201,13 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
       _Pragma("unroll") for (int q = 0; q < kV; ++q) BR[q] = reinterpret_cast<const u32x4*>(p_)[q]; \
     }                                                                                         \
     const float m_ = ok_ ? 1.f : 0.f;              /* loads stay unconditional */              \
-    SV = bf16_to_f32(bs[group_of(cv_, gsz)]) * m_;                                            \
-    CV = bf16_to_f32(bb[group_of(cv_, gsz)]) * m_;                                            \
+    if constexpr (MX) {                            /* one group of 32: scale byte cv_ / 32 */  \
+      SV = e8m0_f32(bs8[cv_ >> 5]) * m_;                                                      \
+      CV = 0.f;                                                                               \
+    } else {                                                                                  \
+      SV = bf16_to_f32(bs[group_of(cv_, gsz)]) * m_;                                          \
+      CV = bf16_to_f32(bb[group_of(cv_, gsz)]) * m_;                                          \
+    }                                                                                         \
   } while (0)
 #define MOEQ_LSTORE(AR, BR, SV, CV, BUF)                                                      \
   do {                                                                                        \
@@ -185,7 +217,8 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
       *reinterpret_cast<u32x4*>(&As_[((tid >> 3) + 64 * u) * kLds + aseg * 8]) = AR[u];       \
     u32x4* d_ = reinterpret_cast<u32x4*>(&Bs_[bc * kLds + bh * 32]);                          \
     uint32_t pk_[16];                                                                         \
-    dequant32h<BITS>(BR, 0, SV, CV, pk_);                                                     \
+    if constexpr (MX) dequant32_mx(BR, SV, pk_);                                              \
+    else dequant32h<BITS>(BR, 0, SV, CV, pk_);                                                \
     _Pragma("unroll") for (int q = 0; q < 4; ++q)                                             \
       d_[q] = u32x4{pk_[4 * q], pk_[4 * q + 1], pk_[4 * q + 2], pk_[4 * q + 3]};              \
   } while (0)
@@ -316,14 +349,14 @@ __global__ void __launch_bounds__(256) k_mark_invalid(const int32_t* __restrict_
   for (int c = threadIdx.x; c < N; c += blockDim.x) out[(size_t)row * N + c] = __builtin_nanf("");
 }
 
-template <int BITS, int MODE>
+template <int BITS, int MODE, bool MX = false>
 static void gemm_launch(dim3 grid, hipStream_t s, const QT& W, const QT& W2, int N, int Kd,
                         const uint16_t* A, int a_div, const GatherWs& ws, const float* wts,
                         void* out, int ntn) {
   // two LDS stages of 147,456 bytes: above the default dynamic limit
-  (void)hipFuncSetAttribute((const void*)k_gqmm<BITS, MODE>,
+  (void)hipFuncSetAttribute((const void*)k_gqmm<BITS, MODE, MX>,
                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
-  hipLaunchKernelGGL((k_gqmm<BITS, MODE>), grid, dim3(kThreads), kGemmLds, s, W, W2, N, Kd, A,
+  hipLaunchKernelGGL((k_gqmm<BITS, MODE, MX>), grid, dim3(kThreads), kGemmLds, s, W, W2, N, Kd, A,
                      a_div, ws, wts, out, ntn);
 }
 
@@ -331,7 +364,8 @@ template <int MODE>
 static void gemm_bits(int bits, dim3 grid, hipStream_t s, const QT& W, const QT& W2, int N, int Kd,
                       const uint16_t* A, int a_div, const GatherWs& ws, const float* wts,
                       void* out, int ntn) {
-  if (bits == 8) gemm_launch<8, MODE>(grid, s, W, W2, N, Kd, A, a_div, ws, wts, out, ntn);
+  if (W.mode == 1) gemm_launch<4, MODE, true>(grid, s, W, W2, N, Kd, A, a_div, ws, wts, out, ntn);
+  else if (bits == 8) gemm_launch<8, MODE>(grid, s, W, W2, N, Kd, A, a_div, ws, wts, out, ntn);
   else if (bits == 4) gemm_launch<4, MODE>(grid, s, W, W2, N, Kd, A, a_div, ws, wts, out, ntn);
   else gemm_launch<2, MODE>(grid, s, W, W2, N, Kd, A, a_div, ws, wts, out, ntn);
 }

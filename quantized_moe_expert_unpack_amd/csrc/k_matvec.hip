@@ -99,6 +99,86 @@ __global__ void __launch_bounds__(256) k_qmatvec(const uint32_t* __restrict__ q,
 }
 
 // ---------------------------------------------------------------------------
+// mxfp4 (E2M1 codes, one E8M0 scale byte per 32 columns, no bias)
+// ---------------------------------------------------------------------------
+// E2M1: bit 3 the sign, bits 2-1 the exponent (bias 1), bit 0 the mantissa
+__device__ __forceinline__ float e2m1(uint32_t c) {
+  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
+  const float mag = e == 0 ? 0.5f * (float)m : (1.0f + 0.5f * (float)m) * (float)(1u << (e - 1));
+  return (c & 8u) ? -mag : mag;
+}
+
+// one thread per packed word: codes, and value * 2^(e - 127) (exact: a
+// two-bit significand times a power of two, by ldexp, subnormals included)
+__global__ void __launch_bounds__(256) k_qdequant_mx(const uint32_t* __restrict__ q,
+                                                     const uint8_t* __restrict__ sc, int64_t words,
+                                                     int wpr, int cols, uint8_t* __restrict__ codes,
+                                                     float* __restrict__ deq) {
+  const int groups = cols / 32;
+  for (int64_t w = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; w < words;
+       w += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t row = w / wpr;
+    const int c0 = (int)(w - row * wpr) * 8;
+    const int e = (int)sc[row * groups + c0 / 32] - 127;
+    const uint32_t word = q[w];
+    const int64_t o = row * cols + c0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t code = (word >> (4 * j)) & 15u;
+      if (codes) codes[o + j] = (uint8_t)code;
+      if (deq) deq[o + j] = ldexpf(e2m1(code), e);
+    }
+  }
+}
+
+// one wave per output row, up to 4 tokens per pass; a 16-byte chunk is one
+// group of 32: the chunk's dot in fp32, then scaled by its power of two
+__global__ void __launch_bounds__(256) k_qmatvec_mx(const uint32_t* __restrict__ q,
+                                                    const uint8_t* __restrict__ sc, int rows,
+                                                    int cols, const float* __restrict__ x, int M,
+                                                    float* __restrict__ y) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int r = blockIdx.x * (blockDim.x / kWave) + (threadIdx.x / kWave);
+  if (r >= rows) return;
+  const int chunks = cols / 32;
+  const uint4* rq = reinterpret_cast<const uint4*>(q + (size_t)r * (cols / 8));
+  const uint8_t* rs = sc + (size_t)r * chunks;
+  for (int m0 = 0; m0 < M; m0 += 4) {
+    const int mn = min(4, M - m0);
+    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int c = lane; c < chunks; c += kWave) {
+      const uint4 v = rq[c];
+      const int e = (int)rs[c] - 127;
+      const float* xc = x + (size_t)m0 * cols + (size_t)c * 32;
+      float d[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 32; j += 4) {
+        float w[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) w[u] = e2m1(chunk_code<4>(v, j + u));
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          if (mm < mn) {
+            const float4 xv = *reinterpret_cast<const float4*>(xc + (size_t)mm * cols + j);
+            d[mm] = fmaf(w[0], xv.x, d[mm]);
+            d[mm] = fmaf(w[1], xv.y, d[mm]);
+            d[mm] = fmaf(w[2], xv.z, d[mm]);
+            d[mm] = fmaf(w[3], xv.w, d[mm]);
+          }
+        }
+      }
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) acc[mm] += ldexpf(d[mm], e);
+    }
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const float t = wave_sum(acc[mm]);
+      if (lane == 0 && mm < mn) y[(size_t)(m0 + mm) * rows + r] = t;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Routing (selection in topk.h)
 // ---------------------------------------------------------------------------
 constexpr int kRouteThreads = 256;
@@ -279,6 +359,11 @@ int launch_qdequant(const QT& W, uint8_t* codes, float* deq, hipStream_t s) {
   if (words == 0) return 0;
   const int64_t want = (words + 255) / 256;
   const int blocks = (int)(want < 65536 ? want : 65536);
+  if (W.mode == 1) {
+    hipLaunchKernelGGL(k_qdequant_mx, dim3(blocks), dim3(256), 0, s, W.q,
+                       reinterpret_cast<const uint8_t*>(W.scales), words, wpr, W.cols, codes, deq);
+    return 0;
+  }
   MOEQ_BITS_LAUNCH(W.bits, k_qdequant, dim3(blocks), s, W.q, W.scales, W.biases, words, wpr,
                    W.cols, W.group_size, codes, deq);
   return 0;
@@ -325,6 +410,11 @@ int launch_rmsnorm(const float* x, int M, int H, const float* g, float eps, floa
 
 int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s) {
   const int blocks = (W.rows + 3) / 4;
+  if (W.mode == 1) {
+    hipLaunchKernelGGL(k_qmatvec_mx, dim3(blocks), dim3(256), 0, s, W.q,
+                       reinterpret_cast<const uint8_t*>(W.scales), W.rows, W.cols, x, M, y);
+    return 0;
+  }
   MOEQ_BITS_LAUNCH(W.bits, k_qmatvec, dim3(blocks), s, W.q, W.scales, W.biases, W.rows, W.cols,
                    W.group_size, x, M, y);
   return 0;

@@ -14,6 +14,7 @@ struct QT {
   const uint16_t* scales;
   const uint16_t* biases;
   int batch, rows, cols, bits, group_size;
+  int mode;   // 0 affine; 1 mxfp4 (E2M1 codes, uint8 E8M0 scales in `scales`, no biases)
 };
 
 // Decode (fp32 activations) layer description.

@@ -21,6 +21,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "lib", "libmoeq.so")
 
 PATH_ROUTE, PATH_DECODE, PATH_GATHER, PATH_GQMM, PATH_FORWARD, PATH_FORWARD_NORM = 0, 1, 2, 3, 4, 5
+MODE_AFFINE, MODE_MXFP4 = 0, 1
 
 STATUS = {
     0: "MOEQ_OK", -1: "MOEQ_ERR_NULL_PTR", -2: "MOEQ_ERR_BAD_BITS", -3: "MOEQ_ERR_BAD_GROUP",
@@ -38,7 +39,7 @@ class MoeqError(RuntimeError):
 class QTensorStruct(ctypes.Structure):
     _fields_ = [("q", ctypes.c_void_p), ("scales", ctypes.c_void_p), ("biases", ctypes.c_void_p),
                 ("batch", ctypes.c_int32), ("rows", ctypes.c_int32), ("cols", ctypes.c_int32),
-                ("bits", ctypes.c_int32), ("group_size", ctypes.c_int32)]
+                ("bits", ctypes.c_int32), ("group_size", ctypes.c_int32), ("mode", ctypes.c_int32)]
 
 
 class MoEStruct(ctypes.Structure):
@@ -126,27 +127,35 @@ def _stream(stream=None) -> int:
 @dataclass
 class QTensor:
     """A quantized matrix (or stack) resident on the device.  ``q`` holds the
-    uint32 words as int32, ``scales``/``biases`` the bf16 bit patterns as int16."""
+    uint32 words as int32, ``scales``/``biases`` the bf16 bit patterns as int16
+    (affine), or ``scales`` the E8M0 bytes as uint8 and no biases (mxfp4)."""
     q: torch.Tensor
     scales: torch.Tensor
-    biases: torch.Tensor
+    biases: Optional[torch.Tensor]
     batch: int
     rows: int
     cols: int
     bits: int
     group_size: int = 64
+    mode: int = MODE_AFFINE
 
     def struct(self) -> QTensorStruct:
         return QTensorStruct(_ptr(self.q), _ptr(self.scales), _ptr(self.biases), self.batch,
-                             self.rows, self.cols, self.bits, self.group_size)
+                             self.rows, self.cols, self.bits, self.group_size, self.mode)
 
     @property
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in (self.q, self.scales, self.biases))
+        return sum(t.numel() * t.element_size() for t in (self.q, self.scales, self.biases)
+                   if t is not None)
 
     @staticmethod
     def from_host(d: dict, device="cuda") -> "QTensor":
         q = np.ascontiguousarray(d["q"]).view(np.int32)
+        if d.get("mode", "affine") == "mxfp4":
+            s = np.ascontiguousarray(d["scales"]).astype(np.uint8, copy=False)
+            return QTensor(torch.from_numpy(q).to(device), torch.from_numpy(s).to(device), None,
+                           int(d.get("batch", 1)), int(d["rows"]), int(d["cols"]), 4, 32,
+                           MODE_MXFP4)
         s = np.ascontiguousarray(d["scales"]).view(np.int16)
         b = np.ascontiguousarray(d["biases"]).view(np.int16)
         return QTensor(torch.from_numpy(q).to(device), torch.from_numpy(s).to(device),

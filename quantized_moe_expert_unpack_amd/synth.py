@@ -60,6 +60,7 @@ class MoEConfig:
     seed: int = 0
     renorm: bool = True
     requant_from: int = 0           # 4 => 2-bit weights shaped like requantized 4-bit draws
+    expert_mode: str = "affine"     # "mxfp4": E2M1 experts, E8M0 scale per 32 columns
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
     @property
@@ -84,6 +85,10 @@ CONFIGS = {
     "c4": MoEConfig("c4-30b-a3b-prefill", hidden=2048, experts=128, top_k=8,
                     inter=768, expert_bits=8, router_bits=8, layers=2,
                     tokens=16384, seed=4),
+    # the prefill on the same shapes with mxfp4 experts (group size 32)
+    "c4_mxfp4": MoEConfig("c4-30b-a3b-prefill-mxfp4", hidden=2048, experts=128, top_k=8,
+                          inter=768, expert_bits=4, router_bits=8, group_size=32, layers=2,
+                          tokens=16384, seed=4, expert_mode="mxfp4"),
     # 397B-A17B shapes with 2-bit experts shaped like a 4-bit model requantized
     # to 2 bits, batched decode M=64
     "c5": MoEConfig("c5-397b-a17b-2bit-m64", hidden=4096, experts=512, top_k=4,
@@ -295,6 +300,32 @@ def host_layer(cfg: MoEConfig, layer: int, threads: int = 8) -> dict:
             fill(j)
     out.update(_small_tensors(cfg, layer))
     return out
+
+
+# --------------------------------------------------------------------------
+# mxfp4 experts
+# --------------------------------------------------------------------------
+
+def draw_mxfp4(key, batch: int, rows: int, cols: int, e_lo: int = 118, e_hi: int = 124) -> dict:
+    """An mxfp4 tensor (stack) in host memory: uniform random words (every
+    4-bit E2M1 field uniform) and E8M0 scale bytes uniform on [e_lo, e_hi]
+    (2^-9 .. 2^-3 by default: weights up to 0.75 in magnitude), no biases."""
+    rng = _rng(*key)
+    q = rng.integers(0, 2 ** 32, size=(batch, rows, cols // 8), dtype=np.uint32)
+    sc = rng.integers(e_lo, e_hi + 1, size=(batch, rows, cols // 32)).astype(np.uint8)
+    return {"q": q, "scales": sc, "biases": None, "batch": batch, "rows": rows, "cols": cols,
+            "bits": 4, "group_size": 32, "mode": "mxfp4"}
+
+
+def mxfp4_experts(cfg: MoEConfig, layer: int) -> dict:
+    """The expert stacks of a layer of ``cfg``'s shapes in mxfp4 (gate, up
+    ``[E][I][H]``, down ``[E][H][I]``); no router and no shared expert (the
+    prefill path takes routing logits)."""
+    E, H, I = cfg.experts, cfg.hidden, cfg.inter
+    return {"gate": draw_mxfp4((cfg.seed, layer, 0x4D58, T_GATE), E, I, H),
+            "up": draw_mxfp4((cfg.seed, layer, 0x4D58, T_UP), E, I, H),
+            "down": draw_mxfp4((cfg.seed, layer, 0x4D58, T_DOWN), E, H, I),
+            "router": None, "shared": None}
 
 
 # --------------------------------------------------------------------------

@@ -108,6 +108,30 @@ def test_requant_validation():
     assert call(_qt(q=0)) == -1
 
 
+def _mx(batch=1, rows=64, cols=256, bits=4, gs=32, mode=1, b=0):
+    return moeq.QTensorStruct(FAKE, FAKE + 4096, b, batch, rows, cols, bits, gs, mode)
+
+
+def test_mxfp4_validation():
+    assert _qmatvec(_mx(bits=8)) == -2               # mxfp4 is 4-bit
+    assert _qmatvec(_mx(gs=64)) == -3                # with groups of 32
+    assert _qmatvec(_mx(mode=7)) == -9               # unknown mode
+    assert _qmatvec(_mx(cols=80)) == -4
+    assert _qmatvec(_mx(), M=0) == 0                 # biases may be NULL
+    f = moeq.lib().requant_2bit
+    assert f(ctypes.byref(_mx()), FAKE, FAKE, FAKE, None) == -9
+    r = moeq.lib().moe_route
+    assert r(ctypes.byref(_mx(rows=8)), FAKE, 1, 8, 2, 1, FAKE, FAKE, None, FAKE, 1 << 20, None) == -9
+    # mxfp4 experts: gather paths only
+    L = _layer(gate=_mx(8, 128, 256), up=_mx(8, 128, 256), down=_mx(8, 256, 128))
+    fwd = moeq.lib().moe_expert_forward
+    assert fwd(ctypes.byref(L), FAKE, FAKE, FAKE, 1, 2, None, FAKE, FAKE, 1 << 30, None) == -9
+    mixed = _layer(down=_mx(8, 256, 128))
+    assert fwd(ctypes.byref(mixed), FAKE, FAKE, FAKE, 1, 2, None, FAKE, FAKE, 1 << 30, None) == -9
+    g = moeq.lib().moe_gather_qmm
+    assert g(ctypes.byref(L), FAKE, FAKE, FAKE, 4, 2, FAKE, FAKE, 16, None) == -8   # validated, ws short
+
+
 def test_null_and_align():
     assert _qmatvec(_qt(q=0)) == -1
     assert _qmatvec(_qt(s=0)) == -1
