@@ -423,6 +423,83 @@ def run_prefill(args, cfg):
 
 
 # --------------------------------------------------------------------------
+# host-resident experts streamed into HBM slots
+# --------------------------------------------------------------------------
+
+PCIE_PEAK_GBPS = 64.0     # PCIe 5.0 x16, one direction
+
+
+def run_stream(args, cfg):
+    """Decode with the experts in pinned host memory only: per layer, route on
+    the device, bring the selected experts into the layer's HBM slots
+    (moe_stream_experts: LRU, async copies on the stream), run the expert
+    forward on the slots.  The router and the shared expert stay resident."""
+    import torch
+    from quantized_moe_expert_unpack_amd import moeq, synth
+
+    dev = torch.device("cuda:0")
+    n_layers = args.layers or cfg.layers
+    K = cfg.top_k
+    caches, routers = [], []
+    t0 = time.time()
+    for l in range(n_layers):
+        host = synth.host_layer(cfg, l, threads=16)
+        sh = None
+        if host.get("shared") is not None:
+            sh = {k: moeq.QTensor.from_host(v, dev) for k, v in host["shared"].items()}
+        resident = moeq.MoELayer(moeq.QTensor.from_host(host["router"], dev), None, None, None, sh)
+        caches.append(moeq.ExpertCache(host, args.stream_slots, resident, dev))
+        routers.append(resident.router)
+        del host
+    log(f"[bench] {n_layers} layers in pinned host memory, {args.stream_slots} HBM slots each "
+        f"({time.time() - t0:.0f}s)")
+    slots_n = args.slots
+    x = torch.stack([torch.stack([torch.from_numpy(synth.decode_x(cfg, l, t)[0]) for t in range(slots_n)])
+                     for l in range(n_layers)]).to(dev)
+    y = torch.empty((1, cfg.hidden), dtype=torch.float32, device=dev)
+    ws_dec = moeq.workspace(caches[0].layer, 1, K, moeq.PATH_DECODE, dev)
+    ws_route = torch.zeros(8 * cfg.experts + 4096, dtype=torch.uint8, device=dev)
+    copied = [0]
+
+    def step(t):
+        for l in range(n_layers):
+            xt = x[l, t % slots_n][None, :]
+            idx, w = moeq.moe_route(routers[l], xt, cfg.experts, K, cfg.renorm, ws=ws_route)
+            slot_idx, n = caches[l].stream(idx.cpu().numpy())
+            copied[0] += n
+            moeq.moe_expert_forward(caches[l].layer, xt, torch.from_numpy(slot_idx).to(dev), w,
+                                    ws=ws_dec, y=y)
+
+    for s_ in range(max(1, args.warmup)):
+        step(s_)
+    torch.cuda.synchronize()
+    copied[0] = 0
+    t1 = time.perf_counter()
+    for s_ in range(args.steps):
+        step(args.warmup + s_)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t1
+    ms = dt * 1e3 / args.steps
+    per_expert = 3 * cfg.hidden * cfg.inter * cfg.expert_bits // 8 + 3 * cfg.hidden * cfg.inter // cfg.group_size * 4
+    gbps = copied[0] * per_expert / dt / 1e9
+    log(f"[bench] stream: {ms:.3f} ms/token, {copied[0] / (args.steps * n_layers):.2f} experts copied per layer")
+    return {
+        "metric": "MoE-layer tokens/s with experts streamed from host memory (PCIe GB/s vs peak)",
+        "value": round(1e3 / ms, 2), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": cfg.name + "-streamed", "layers": n_layers, "tokens_per_step": 1,
+                   "hidden": cfg.hidden, "experts": cfg.experts, "top_k": K, "inter": cfg.inter,
+                   "expert_bits": cfg.expert_bits, "hbm_slots_per_layer": args.stream_slots,
+                   "expert_bytes": per_expert},
+        "experts_copied_per_layer": round(copied[0] / (args.steps * n_layers), 3),
+        "roofline": {"bound": "pcie", "achieved": round(gbps, 2), "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / PCIE_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "moe_stream_experts host->device copies (route, copy, expert forward per layer)"},
+    }
+
+
+# --------------------------------------------------------------------------
 # 2-bit requantization workload
 # --------------------------------------------------------------------------
 
@@ -521,6 +598,8 @@ def main():
     ap.add_argument("--slots", type=int, default=TOKEN_SLOTS)
     ap.add_argument("--launch-reps", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--stream-slots", type=int, default=0, metavar="S",
+                    help="decode with the experts in pinned host memory, S HBM slots per layer")
     ap.add_argument("--norm", action="store_true",
                     help="decode: RMSNorm fused in front of the step (moe_forward_norm), x added back")
     ap.add_argument("--cpu-layers", type=int, default=0)
@@ -562,6 +641,10 @@ def main():
         host = out.pop("_host")
         if not args.no_cpu_baseline:
             out["cpu_baseline"] = cpu_baseline_prefill(cfg, host, 1024)
+    elif args.stream_slots:
+        out = run_stream(args, cfg)
+        if not args.no_cpu_baseline:
+            out["cpu_baseline"] = cpu_baseline_decode(cfg, 2, args.cpu_layers or min(8, cfg.layers))
     else:
         out = run_decode(args, cfg)
         if not args.no_cpu_baseline:

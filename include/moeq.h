@@ -123,6 +123,28 @@ typedef struct moeq_moe {
   moeq_qtensor sh_expert_gate;
 } moeq_moe;
 
+/* Experts held in host memory and streamed into device slots (the models
+ * larger than HBM case): caller-owned memory, contents managed by
+ * moe_stream_experts.
+ *   host  : gate, up, down stacks [E][...] in PINNED host memory
+ *           (hipHostMalloc; pageable memory works but the copies then
+ *           serialize with the host); the other fields are unused
+ *   slots : gate, up, down stacks [S][...] in device memory, the same
+ *           per-expert shapes, bits, group size and mode as host
+ *   slot_expert : host int32 [S], the expert each slot holds, -1 = empty
+ *                 (the caller sets every entry to -1 before the first call)
+ *   slot_stamp  : host int64 [S], the last call that used each slot
+ *   clock       : host counter of calls (start at 0)
+ *   n_slots     : S */
+typedef struct moeq_slot_cache {
+  moeq_moe host;
+  moeq_moe slots;
+  int32_t *slot_expert;
+  int64_t *slot_stamp;
+  int64_t clock;
+  int32_t n_slots;
+} moeq_slot_cache;
+
 /* Workspace paths for moe_workspace_size(). */
 #define MOEQ_PATH_ROUTE 0   /* moe_route                                   */
 #define MOEQ_PATH_DECODE 1  /* moe_expert_forward                          */
@@ -286,6 +308,30 @@ int gather_qmm(const moeq_qtensor *W, const uint16_t *x_bf16, const int32_t *rhs
  * reading taken). */
 int requant_2bit(const moeq_qtensor *W, uint32_t *q_out, uint16_t *s_out, uint16_t *b_out,
                  moeq_stream_t stream);
+
+/* moe_stream_experts: bring the experts a routing result selects into device
+ * slots and rewrite the indices to slot numbers, so that moe_expert_forward
+ * on a layer whose gate/up/down are C->slots (and whose shared expert, if
+ * any, is resident) computes the step for experts that live in host memory.
+ *   topk_idx_host : host int32 [M][K] (e.g. moe_route's output copied back)
+ *   slot_idx_host : host int32 [M][K] out: the slot of each pair; an index
+ *                   outside [0, E) maps to slot S (its row then comes out NaN,
+ *                   as with any out-of-range index)
+ *   n_copied      : nullable host int32 out: experts copied by this call
+ * The distinct experts of the call stay in their slots if already there
+ * (least recently used slots are refilled first); each missing expert's
+ * codes, scales and biases go out as hipMemcpyAsync host->device copies on
+ * `stream`, in order with the caller's other work there: a slot is only
+ * refilled after the work queued before it on that stream (the previous
+ * forward that read it).  More distinct experts than slots:
+ * MOEQ_ERR_WORKSPACE, nothing copied.  Runs on the host; returns once the
+ * copies are queued.
+ * Defines: the K parallel expert reads per layer into expert buffers, the OS
+ * page cache acting as the LRU (flash-moe-inference skill page, parallel
+ * expert loading; the per-layer pipeline's I/O phase), with host memory in
+ * place of the SSD and HBM slots in place of the buffers. */
+int moe_stream_experts(moeq_slot_cache *C, const int32_t *topk_idx_host, int32_t M, int32_t K,
+                       int32_t *slot_idx_host, int32_t *n_copied, moeq_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <climits>
+#include <vector>
 #include <cstdint>
 
 #include "launch.h"
@@ -471,6 +472,87 @@ int moe_forward_norm(const moeq_moe* L, const float* x, int32_t M, int32_t K, in
   }
   if (st) return MOEQ_ERR_UNSUPPORTED;
   return launch_status();
+}
+
+int moe_stream_experts(moeq_slot_cache* C, const int32_t* topk_idx_host, int32_t M, int32_t K,
+                       int32_t* slot_idx_host, int32_t* n_copied, moeq_stream_t stream) {
+  if (!C) return MOEQ_ERR_NULL_PTR;
+  LayerDims dh, ds;
+  int st = check_experts(&C->host, &dh);
+  if (st) return st;
+  if ((st = check_experts(&C->slots, &ds))) return st;
+  const int E = dh.E, S = C->n_slots;
+  if (S < 1 || ds.E != S || ds.H != dh.H || ds.I != dh.I) return MOEQ_ERR_SHAPE;
+  const moeq_qtensor* hq[3] = {&C->host.gate, &C->host.up, &C->host.down};
+  const moeq_qtensor* sq[3] = {&C->slots.gate, &C->slots.up, &C->slots.down};
+  for (int i = 0; i < 3; ++i)
+    if (hq[i]->bits != sq[i]->bits || hq[i]->group_size != sq[i]->group_size ||
+        hq[i]->mode != sq[i]->mode)
+      return MOEQ_ERR_SHAPE;
+  if (M < 0 || K < 1 || K > kMaxK) return MOEQ_ERR_SHAPE;
+  if (n_copied) *n_copied = 0;
+  if (M == 0) return MOEQ_OK;
+  if (!topk_idx_host || !slot_idx_host || !C->slot_expert || !C->slot_stamp) return MOEQ_ERR_NULL_PTR;
+  // the call's distinct experts, in order of first appearance
+  std::vector<int> need;
+  std::vector<int> where(E, -1);            // expert -> its slot for this call
+  for (int64_t i = 0; i < (int64_t)M * K; ++i) {
+    const int e = topk_idx_host[i];
+    if (e < 0 || e >= E || where[e] == -2) continue;
+    where[e] = -2;
+    need.push_back(e);
+  }
+  if ((int)need.size() > S) return MOEQ_ERR_WORKSPACE;
+  const int64_t now = ++C->clock;
+  // hits keep their slots (and are stamped first, so no miss evicts them)
+  for (int s = 0; s < S; ++s) {
+    const int e = C->slot_expert[s];
+    if (e >= 0 && e < E && where[e] == -2) {
+      where[e] = s;
+      C->slot_stamp[s] = now;
+    }
+  }
+  int copied = 0;
+  for (int e : need) {
+    if (where[e] >= 0) continue;
+    // an empty slot, else the least recently used one not used by this call
+    int v = -1;
+    for (int s = 0; s < S; ++s) {
+      if (C->slot_stamp[s] == now) continue;
+      if (C->slot_expert[s] < 0) { v = s; break; }
+      if (v < 0 || C->slot_stamp[s] < C->slot_stamp[v]) v = s;
+    }
+    if (v < 0) return MOEQ_ERR_WORKSPACE;   // (cannot happen: need.size() <= S)
+    for (int i = 0; i < 3; ++i) {
+      const moeq_qtensor& h = *hq[i];
+      const moeq_qtensor& d = *sq[i];
+      const size_t qb = (size_t)h.rows * h.cols / (32 / h.bits) * sizeof(uint32_t);
+      const size_t sbytes = (size_t)h.rows * (h.cols / h.group_size) * (is_mx(h) ? 1 : 2);
+      hipStream_t st_ = (hipStream_t)stream;
+      const char* hqp = reinterpret_cast<const char*>(h.q) + (size_t)e * qb;
+      char* dqp = reinterpret_cast<char*>(const_cast<uint32_t*>(d.q)) + (size_t)v * qb;
+      if (hipMemcpyAsync(dqp, hqp, qb, hipMemcpyHostToDevice, st_) != hipSuccess) return MOEQ_ERR_LAUNCH;
+      const char* hs = reinterpret_cast<const char*>(h.scales) + (size_t)e * sbytes;
+      char* ds_ = reinterpret_cast<char*>(const_cast<uint16_t*>(d.scales)) + (size_t)v * sbytes;
+      if (hipMemcpyAsync(ds_, hs, sbytes, hipMemcpyHostToDevice, st_) != hipSuccess) return MOEQ_ERR_LAUNCH;
+      if (!is_mx(h)) {
+        const char* hb = reinterpret_cast<const char*>(h.biases) + (size_t)e * sbytes;
+        char* db = reinterpret_cast<char*>(const_cast<uint16_t*>(d.biases)) + (size_t)v * sbytes;
+        if (hipMemcpyAsync(db, hb, sbytes, hipMemcpyHostToDevice, st_) != hipSuccess)
+          return MOEQ_ERR_LAUNCH;
+      }
+    }
+    C->slot_expert[v] = e;
+    C->slot_stamp[v] = now;
+    where[e] = v;
+    ++copied;
+  }
+  for (int64_t i = 0; i < (int64_t)M * K; ++i) {
+    const int e = topk_idx_host[i];
+    slot_idx_host[i] = (e < 0 || e >= E) ? S : where[e];
+  }
+  if (n_copied) *n_copied = copied;
+  return MOEQ_OK;
 }
 
 int moe_gather_qmm(const moeq_moe* L, const uint16_t* x_bf16, const int32_t* topk_idx,

@@ -49,6 +49,11 @@ class MoEStruct(ctypes.Structure):
                 ("sh_expert_gate", QTensorStruct)]
 
 
+class SlotCacheStruct(ctypes.Structure):
+    _fields_ = [("host", MoEStruct), ("slots", MoEStruct), ("slot_expert", ctypes.c_void_p),
+                ("slot_stamp", ctypes.c_void_p), ("clock", ctypes.c_int64), ("n_slots", ctypes.c_int32)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -70,6 +75,7 @@ _SIGNATURES = {
     "moe_gather_qmm": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _P, _P, _I, _I, _P, _P, _SZ,
                                       _P]),
     "moe_rms_norm": (ctypes.c_int, [_P, _I, _I, _P, ctypes.c_float, _P, _P]),
+    "moe_stream_experts": (ctypes.c_int, [ctypes.POINTER(SlotCacheStruct), _P, _I, _I, _P, _P, _P]),
     "moe_forward_norm": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _I, _I, _I, _P, ctypes.c_float,
                                         _P, _P, _P, _P, _SZ, _P]),
     "gather_qmm": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _P, _I, _I, _P, _P, _SZ, _P]),
@@ -345,6 +351,75 @@ def moe_forward_norm(layer: MoELayer, x: torch.Tensor, k: int, norm_w: torch.Ten
                                   _ptr(norm_w), float(eps), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws),
                                   ws.numel(), _stream(stream)), "moe_forward_norm")
     return y, idx, w
+
+
+class ExpertCache:
+    """Experts of one layer held in pinned host memory and S device slots
+    (the buffers moe_stream_experts manages; allocated here with torch).
+    ``layer`` is the device layer to run moe_expert_forward on: the slot
+    stacks as its experts, the resident router and shared expert of
+    ``resident``."""
+
+    def __init__(self, host_layer: dict, n_slots: int, resident: "MoELayer", device="cuda"):
+        def pinned(a):
+            a = np.ascontiguousarray(a)
+            t = torch.empty(a.shape, dtype=_TORCH_OF[a.dtype.str[1:]], pin_memory=True)
+            t.copy_(torch.from_numpy(a.view(_VIEW_OF[a.dtype.str[1:]])))
+            return t
+
+        self.host = {}
+        self.slots = {}
+        for name in ("gate", "up", "down"):
+            d = host_layer[name]
+            q, sc = np.asarray(d["q"]), np.asarray(d["scales"])
+            b = None if d.get("biases") is None else np.asarray(d["biases"])
+            mode = MODE_MXFP4 if d.get("mode", "affine") == "mxfp4" else MODE_AFFINE
+            E, rows, cols = int(d["batch"]), int(d["rows"]), int(d["cols"])
+            self.host[name] = QTensor(pinned(q), pinned(sc), None if b is None else pinned(b), E, rows,
+                                      cols, int(d["bits"]), int(d["group_size"]), mode)
+            h = self.host[name]
+            self.slots[name] = QTensor(
+                torch.empty((n_slots,) + tuple(h.q.shape[1:]), dtype=h.q.dtype, device=device),
+                torch.empty((n_slots,) + tuple(h.scales.shape[1:]), dtype=h.scales.dtype, device=device),
+                None if h.biases is None else
+                torch.empty((n_slots,) + tuple(h.biases.shape[1:]), dtype=h.biases.dtype, device=device),
+                n_slots, rows, cols, h.bits, h.group_size, mode)
+        self.n_slots = n_slots
+        self.slot_expert = np.full(n_slots, -1, np.int32)
+        self.slot_stamp = np.zeros(n_slots, np.int64)
+        self.layer = MoELayer(resident.router, self.slots["gate"], self.slots["up"], self.slots["down"],
+                              resident.shared)
+        self._host_layer = MoELayer(None, self.host["gate"], self.host["up"], self.host["down"])
+        self._cs = SlotCacheStruct(_host_struct(self._host_layer), _host_struct(
+            MoELayer(None, self.slots["gate"], self.slots["up"], self.slots["down"])),
+            self.slot_expert.ctypes.data, self.slot_stamp.ctypes.data, 0, n_slots)
+
+    def stream(self, topk_idx_host: np.ndarray, stream=None):
+        """Copy the experts ``topk_idx_host`` selects into slots (async on the
+        stream); returns (slot indices [M][K] int32 host array, experts copied)."""
+        idx = np.ascontiguousarray(topk_idx_host, dtype=np.int32)
+        m, k = idx.shape
+        out = np.empty_like(idx)
+        n = ctypes.c_int32(0)
+        _check(lib().moe_stream_experts(ctypes.byref(self._cs), idx.ctypes.data, m, k,
+                                        out.ctypes.data, ctypes.byref(n), _stream(stream)),
+               "moe_stream_experts")
+        return out, n.value
+
+
+_TORCH_OF = {"u4": torch.int32, "u2": torch.int16, "u1": torch.uint8, "i4": torch.int32,
+             "i2": torch.int16}
+_VIEW_OF = {"u4": np.int32, "u2": np.int16, "u1": np.uint8, "i4": np.int32, "i2": np.int16}
+
+
+def _host_struct(layer: "MoELayer") -> MoEStruct:
+    """MoEStruct of expert stacks whose tensors may live in pinned host memory."""
+    def qs(t: QTensor) -> QTensorStruct:
+        ptr = lambda a: None if a is None else a.data_ptr()
+        return QTensorStruct(ptr(t.q), ptr(t.scales), ptr(t.biases), t.batch, t.rows, t.cols,
+                             t.bits, t.group_size, t.mode)
+    return MoEStruct(_empty_qt(), qs(layer.gate), qs(layer.up), qs(layer.down), 0,
+                     _empty_qt(), _empty_qt(), _empty_qt(), _empty_qt())
 
 
 def moe_gather_qmm(layer: MoELayer, x_bf16: torch.Tensor, idx: torch.Tensor, w: torch.Tensor,

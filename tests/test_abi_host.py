@@ -31,7 +31,7 @@ def declared_functions():
 def test_header_declares_the_four_calls_and_helpers():
     names = declared_functions()
     for n in ("qmatvec", "moe_route", "moe_expert_forward", "moe_gather_qmm", "qdequant",
-              "gather_qmm", "requant_2bit", "moe_rms_norm", "moe_forward_norm",
+              "gather_qmm", "requant_2bit", "moe_rms_norm", "moe_forward_norm", "moe_stream_experts",
               "moe_workspace_size", "moeq_status_string", "moeq_version"):
         assert n in names
 
@@ -235,6 +235,41 @@ def test_norm_validation():
     n4 = moeq.lib().moe_workspace_size(ctypes.byref(L), 24, 2, moeq.PATH_FORWARD)
     n5 = moeq.lib().moe_workspace_size(ctypes.byref(L), 24, 2, moeq.PATH_FORWARD_NORM)
     assert n5 >= n4 + 24 * 256 * 4                                    # + the normalized rows
+
+
+def test_stream_experts_slot_logic_without_copies():
+    import numpy as np
+    f = moeq.lib().moe_stream_experts
+    S = 3
+    host = _layer()                                                    # E = 8
+    slots = _layer(gate=_qt(4, S, 128, 256), up=_qt(4, S, 128, 256), down=_qt(4, S, 256, 128))
+    se = np.array([5, 2, 7], np.int32)                                 # experts already in slots
+    ss = np.zeros(S, np.int64)
+    C = moeq.SlotCacheStruct(host, slots, se.ctypes.data, ss.ctypes.data, 0, S)
+    n = ctypes.c_int32(-1)
+
+    def call(idx):
+        idx = np.asarray(idx, np.int32)
+        out = np.full_like(idx, -7)
+        st = f(ctypes.byref(C), idx.ctypes.data, idx.shape[0], idx.shape[1], out.ctypes.data,
+               ctypes.byref(n), None)
+        return st, out
+
+    st, out = call([[2, 5], [7, 2]])                   # all hits: no copy, slots kept
+    assert st == 0 and out.tolist() == [[1, 0], [2, 1]] and n.value == 0
+    assert C.clock == 1 and ss.tolist() == [1, 1, 1]
+    st, out = call([[9, 5], [-1, 5]])                  # out-of-range indices map to slot S
+    assert st == 0 and out.tolist() == [[3, 0], [3, 0]] and ss.tolist() == [2, 1, 1]
+    st, out = call([[0, 1], [3, 4]])                   # 4 distinct experts > 3 slots
+    assert st == -8 and out.tolist() == [[-7, -7], [-7, -7]]
+    assert se.tolist() == [5, 2, 7]                    # nothing evicted
+    assert call(np.zeros((0, 2)))[0] == 0
+    bad = moeq.SlotCacheStruct(host, slots, se.ctypes.data, ss.ctypes.data, 0, 4)
+    idx = np.array([[2, 5]], np.int32)
+    assert f(ctypes.byref(bad), idx.ctypes.data, 1, 2, idx.ctypes.data, None, None) == -5   # S != batch
+    wrong = _layer(gate=_qt(8, S, 128, 256), up=_qt(8, S, 128, 256), down=_qt(8, S, 256, 128))
+    C2 = moeq.SlotCacheStruct(host, wrong, se.ctypes.data, ss.ctypes.data, 0, S)
+    assert f(ctypes.byref(C2), idx.ctypes.data, 1, 2, idx.ctypes.data, None, None) == -5   # bits differ
 
 
 def test_workspace_sizes():
