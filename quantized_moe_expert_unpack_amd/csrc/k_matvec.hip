@@ -437,6 +437,111 @@ int launch_route(const QT* router, const float* x_or_logits, int M, int E, int K
                             reinterpret_cast<int*>(b), s);
 }
 
+// Router projection for many tokens with the tokens' x staged in LDS: a block
+// takes kRtTok tokens and kRtRows router rows (kRtRows / 4 per wave), so one
+// LDS read of x feeds every row of the wave and a block reads its tokens' x
+// from memory once (one wave per row re-reads x from L2 for every row).  The
+// arithmetic is k_router's: each fp32 dequantized weight widened exactly,
+// fp64 products and sums (per lane over its chunks in order, then the wave).
+// H <= 4096 (x of kRtTok tokens within 64 KB).
+constexpr int kRtTok = 4;
+constexpr int kRtRows = 16;
+template <int BITS>
+__global__ void __launch_bounds__(kRouteThreads) k_router_tile(QT W, const float* __restrict__ x,
+                                                               int M, double* __restrict__ logits,
+                                                               float* __restrict__ logits32) {
+  extern __shared__ __attribute__((aligned(16))) float xs[];   // [kRtTok][H], chunk-interleaved
+  constexpr int kCpc = 128 / BITS;
+  constexpr int kRpw = kRtRows / (kRouteThreads / kWave);     // rows per wave
+  constexpr int kCpl = 4096 / kCpc / kWave;                   // chunks per lane at most (H <= 4096)
+  const int rows = W.rows, H = W.cols;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wid = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int r0 = blockIdx.x * kRtRows + wid * kRpw;
+  const int m0 = blockIdx.y * kRtTok;
+  const int nm = min(kRtTok, M - m0);
+  const int nch = H / kCpc;
+  const int groups = H / W.group_size;
+  const int gsh = __builtin_ctz((unsigned)W.group_size);
+  // every weight load of the lane first (clamped, always valid addresses;
+  // rows past the last re-read row 0 and are never stored), so they are in
+  // flight while x is staged
+  uint4 wv[kCpl][kRpw];
+  uint32_t wsb[kCpl][kRpw];                   // bf16 scale | bias << 16
+#pragma unroll
+  for (int j = 0; j < kCpl; ++j) {
+    const int c = min(lane + kWave * j, nch - 1);
+    const int g = (c * kCpc) >> gsh;
+#pragma unroll
+    for (int rr = 0; rr < kRpw; ++rr) {
+      const int r = r0 + rr < rows ? r0 + rr : 0;
+      wv[j][rr] = reinterpret_cast<const uint4*>(W.q + (size_t)r * (H / (32 / BITS)))[c];
+      wsb[j][rr] = (uint32_t)W.scales[(size_t)r * groups + g] |
+                   ((uint32_t)W.biases[(size_t)r * groups + g] << 16);
+    }
+  }
+  // x of the block's tokens (tokens past the last re-read the first): float4
+  // f of chunk c of token t at t * H / 4 + f * nch + c
+  float4* x4 = reinterpret_cast<float4*>(xs);
+  for (int i = tid; i < kRtTok * (H / 4); i += kRouteThreads) {
+    const int t = i / (H / 4), ii = i - t * (H / 4);
+    const int m = m0 + (t < nm ? t : 0);
+    x4[t * (H / 4) + (ii % (kCpc / 4)) * nch + ii / (kCpc / 4)] =
+        reinterpret_cast<const float4*>(x + (size_t)m * H)[ii];
+  }
+  __syncthreads();
+  double acc[kRpw][kRtTok];
+#pragma unroll
+  for (int rr = 0; rr < kRpw; ++rr)
+#pragma unroll
+    for (int t = 0; t < kRtTok; ++t) acc[rr][t] = 0.0;
+#pragma unroll
+  for (int j = 0; j < kCpl; ++j) {
+    const int c = lane + kWave * j;
+    if (c < nch) {
+#pragma unroll
+      for (int f = 0; f < kCpc / 4; ++f) {
+        double xd[kRtTok][4];                // widened once, used by every row of the wave
+#pragma unroll
+        for (int t = 0; t < kRtTok; ++t) {
+          const float4 xv = x4[t * (H / 4) + f * nch + c];
+          xd[t][0] = (double)xv.x;
+          xd[t][1] = (double)xv.y;
+          xd[t][2] = (double)xv.z;
+          xd[t][3] = (double)xv.w;
+        }
+#pragma unroll
+        for (int rr = 0; rr < kRpw; ++rr) {
+          const float sc = bf16_to_f32(wsb[j][rr] & 0xFFFFu), bi = bf16_to_f32(wsb[j][rr] >> 16);
+          double w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            w[q] = (double)fmaf(sc, (float)chunk_code<BITS>(wv[j][rr], 4 * f + q), bi);
+#pragma unroll
+          for (int t = 0; t < kRtTok; ++t) {
+            acc[rr][t] = fma(w[0], xd[t][0], acc[rr][t]);
+            acc[rr][t] = fma(w[1], xd[t][1], acc[rr][t]);
+            acc[rr][t] = fma(w[2], xd[t][2], acc[rr][t]);
+            acc[rr][t] = fma(w[3], xd[t][3], acc[rr][t]);
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int rr = 0; rr < kRpw; ++rr) {
+#pragma unroll
+    for (int t = 0; t < kRtTok; ++t) {
+      const double a = wave_sum(acc[rr][t]);
+      const int r = r0 + rr;
+      if (lane == 0 && t < nm && r < rows) {
+        logits[(size_t)(m0 + t) * rows + r] = a;
+        if (logits32) logits32[(size_t)(m0 + t) * rows + r] = (float)a;
+      }
+    }
+  }
+}
+
 int launch_route_parts(const QT* router, const float* x_or_logits, int M, int E, int K, int renorm,
                        int32_t* idx, float* w, float* logits32, double* l64, int* ctr,
                        hipStream_t s) {
@@ -449,11 +554,18 @@ int launch_route_parts(const QT* router, const float* x_or_logits, int M, int E,
   const QT& W = *router;
   const bool last = M <= kLastTopkMaxM;
   const dim3 grid_many((E + 3) / 4, (M + kRouteTM - 1) / kRouteTM);
+  // many tokens: the LDS-staged tile kernel when the tokens' x fits (64 KB)
+  const bool tile = W.cols <= 4096;
+  const size_t tile_lds = sizeof(float) * kRtTok * (size_t)W.cols;
+  const dim3 grid_tile((E + kRtRows - 1) / kRtRows, (M + kRtTok - 1) / kRtTok);
 #define MOEQ_ROUTER(B_)                                                                           \
   if (W.bits == B_) {                                                                             \
     if (last)                                                                                     \
       hipLaunchKernelGGL((k_router<B_, true>), grid, dim3(kRouteThreads), 0, s, W, x_or_logits, M, \
                          K, renorm, l64, ctr, logits32, idx, w);                                   \
+    else if (tile)                                                                                \
+      hipLaunchKernelGGL((k_router_tile<B_>), grid_tile, dim3(kRouteThreads), tile_lds, s, W,     \
+                         x_or_logits, M, l64, logits32);                                          \
     else                                                                                          \
       hipLaunchKernelGGL((k_router_many<B_>), grid_many, dim3(kRouteThreads), 0, s, W,            \
                          x_or_logits, M, l64, logits32);                                          \
