@@ -648,9 +648,9 @@ def main():
     else:
         out = run_decode(args, cfg)
         if not args.no_cpu_baseline:
-            # bounded samples of ~10-30 s of oracle time: one whole token of the
+            # bounded samples of ~10-30 s of oracle time: two tokens of the
             # 48-layer stack, two tokens of the 8-layer stack, one 64-token layer
-            n, tok = {"c2": (48, 1), "c3": (8, 2), "c5": (1, 64), "c5_4bit": (1, 64)}[args.config]
+            n, tok = {"c2": (48, 2), "c3": (8, 2), "c5": (1, 64), "c5_4bit": (1, 64)}[args.config]
             out["cpu_baseline"] = cpu_baseline_decode(cfg, tok, args.cpu_layers or n)
     print(json.dumps(out), flush=True)
 
