@@ -42,6 +42,23 @@ def test_route_batched_m64_and_logits_out():
     assert np.abs(lo.cpu().numpy() - lg).max() <= 1e-5 * np.abs(lg).max()
 
 
+@pytest.mark.parametrize("bits,hidden,m", [(8, 4608, 20), (4, 4608, 9), (2, 4096, 37), (8, 160, 13)])
+def test_route_many_tokens_all_router_kernels(bits, hidden, m):
+    # hidden > 4096 takes the one-row-per-wave kernel, the rest the LDS-staged
+    # tile kernel (ragged token and row blocks, hidden off the 64-column grid)
+    cfg = synth.scaled(synth.CONFIGS["c1"], hidden=hidden, experts=40, top_k=4, router_bits=bits,
+                       group_size=32 if hidden % 64 else 64, seed=95 + bits)
+    small = synth._small_tensors(cfg, 0)
+    say(f"route {bits}-bit router H={hidden} M={m}")
+    x = gapped_tokens(cfg, small, 0, m)[:, 0]
+    idx, w = moeq.moe_route(moeq.QTensor.from_host(small["router"], dev()), to_dev(x), cfg.experts,
+                            cfg.top_k)
+    lg = oracle.qmatvec(small["router"], x)
+    ridx, rw, _ = oracle.route(lg, cfg.top_k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+
+
 @pytest.mark.parametrize("m", [1, 5, 16068])
 def test_route_logits_mode_zipf(m):
     cfg = synth.CONFIGS["c4"]
