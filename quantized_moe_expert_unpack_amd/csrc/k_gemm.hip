@@ -241,7 +241,9 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[mi], bfr[ni], acc[mi][ni], 0, 0, 0);
+          // the transposed product (weights x activations): the accumulator's
+          // lanes run over tokens and its registers over output columns
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
     }
   };
 
@@ -271,36 +273,59 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
 #undef MOEQ_GLOAD
 #undef MOEQ_LSTORE
 
-  // ---- epilogue.  32x32 accumulator layout: register r of lane l holds
-  // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+  // ---- epilogue.  The transposed 32x32 accumulator: register r of lane l
+  // holds output column 8*(r/4) + 4*(l/32) + r%4 of the tile's 32 and token
+  // row l%32, so registers 4q..4q+3 are four consecutive columns of one row
+  // and go out as one 8-byte (bf16) or 16-byte (fp32) store.
+  auto pk4 = [](float a, float b, float c, float d) {
+    return make_uint2(pack_bf16(a, b), pack_bf16(c, d));
+  };
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
+    const int rl = wm * 128 + mi * 32 + (lane & 31);       // the lane's token row
+    if (rl >= rows) continue;
+    const int pair = s_pair[rl];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rl = wm * 128 + mi * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-      if (rl >= rows) continue;
+    for (int q = 0; q < 4; ++q) {
+      const int cofs = 8 * q + 4 * (lane >> 5);             // first of the four columns
       if (MODE == 1) {
-        {
-          const int i = nt * 128 + wn * 32 + (lane & 31);
-          if (i < N) {
-            const float h = silu(acc[mi][0][r]) * acc[mi][1][r];
-            const bf16x2_t hv = {(__bf16)h, (__bf16)0.f};
-            reinterpret_cast<uint16_t*>(out)[(size_t)(row0 + rl) * N + i] =
-                (uint16_t)(__builtin_bit_cast(uint32_t, hv) & 0xFFFFu);
+        const int i = nt * 128 + wn * 32 + cofs;
+        if (i < N) {
+          float hv[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) hv[u] = silu(acc[mi][0][4 * q + u]) * acc[mi][1][4 * q + u];
+          uint16_t* o = reinterpret_cast<uint16_t*>(out) + (size_t)(row0 + rl) * N + i;
+          if (i + 3 < N && (N & 3) == 0) {
+            *reinterpret_cast<uint2*>(o) = pk4(hv[0], hv[1], hv[2], hv[3]);
+          } else {
+            for (int u = 0; u < 4 && i + u < N; ++u)
+              o[u] = (uint16_t)(pack_bf16(hv[u], 0.f) & 0xFFFFu);
           }
         }
       } else {
-        const int pair = s_pair[rl];
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni) {
-          const int n = nt * kBN + wn * 64 + ni * 32 + (lane & 31);
-          if (n < N) {
-            if (MODE == 2) {
-              const bf16x2_t v = {(__bf16)(acc[mi][ni][r] * s_w[rl]), (__bf16)0.f};
-              reinterpret_cast<uint16_t*>(out)[(size_t)pair * N + n] =
-                  (uint16_t)(__builtin_bit_cast(uint32_t, v) & 0xFFFFu);
+          const int n = nt * kBN + wn * 64 + ni * 32 + cofs;
+          if (n >= N) continue;
+          if (MODE == 2) {
+            const float sw = s_w[rl];
+            const float v0 = acc[mi][ni][4 * q] * sw, v1 = acc[mi][ni][4 * q + 1] * sw;
+            const float v2 = acc[mi][ni][4 * q + 2] * sw, v3 = acc[mi][ni][4 * q + 3] * sw;
+            uint16_t* o = reinterpret_cast<uint16_t*>(out) + (size_t)pair * N + n;
+            if (n + 3 < N && (N & 3) == 0) {
+              *reinterpret_cast<uint2*>(o) = pk4(v0, v1, v2, v3);
             } else {
-              reinterpret_cast<float*>(out)[(size_t)pair * N + n] = acc[mi][ni][r];
+              const float vv[4] = {v0, v1, v2, v3};
+              for (int u = 0; u < 4 && n + u < N; ++u)
+                o[u] = (uint16_t)(pack_bf16(vv[u], 0.f) & 0xFFFFu);
+            }
+          } else {
+            float* o = reinterpret_cast<float*>(out) + (size_t)pair * N + n;
+            if (n + 3 < N && (N & 3) == 0) {
+              *reinterpret_cast<float4*>(o) = make_float4(acc[mi][ni][4 * q], acc[mi][ni][4 * q + 1],
+                                                          acc[mi][ni][4 * q + 2], acc[mi][ni][4 * q + 3]);
+            } else {
+              for (int u = 0; u < 4 && n + u < N; ++u) o[u] = acc[mi][ni][4 * q + u];
             }
           }
         }
