@@ -21,9 +21,11 @@
  *   experts are 4-bit).
  *
  * Conventions for every entry point:
- *  - All array pointers are DEVICE pointers owned by the caller; the library
- *    allocates nothing, keeps no global mutable state besides what lives in the
- *    caller's workspace, and only enqueues work on `stream` (no host sync).
+ *  - All array pointers are DEVICE pointers owned by the caller (except the
+ *    host arrays and pinned host stacks of moe_stream_experts, documented
+ *    there); the library allocates nothing, keeps no global mutable state
+ *    besides what lives in the caller's workspace (and slot cache), and only
+ *    enqueues work on `stream` (no host sync).
  *  - Every argument is validated on the host BEFORE anything is launched; on
  *    a bad argument the call returns a negative moeq_status and launches
  *    nothing.  A kernel launch failure returns MOEQ_ERR_LAUNCH.
