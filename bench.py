@@ -238,6 +238,10 @@ def run_decode(args, cfg):
                             dev)
     # --norm: RMSNorm in front of every layer's step, x added back in the combine
     gam = [torch.from_numpy(synth.norm_weight(cfg, l)).to(dev) for l in range(n_layers)] if args.norm else None
+    # --post-norm: also the norm after the combine (the next layer's weight)
+    gam2 = ([torch.from_numpy(synth.norm_weight(cfg, l + 1)).to(dev) for l in range(n_layers)]
+            if args.post_norm else [None] * n_layers)
+    yn = torch.zeros((n_layers, m, H), dtype=torch.float32, device=dev) if args.post_norm else None
     ws_route = torch.zeros(8 * m * cfg.experts + 4096, dtype=torch.uint8, device=dev)
     ws_dec = moeq.workspace(layers[0], m, K, moeq.PATH_DECODE, dev)
 
@@ -245,7 +249,8 @@ def run_decode(args, cfg):
         L = layers[l]
         if args.norm:
             moeq.moe_forward_norm(L, x[l, t], K, gam[l], NORM_EPS, cfg.renorm, ws=ws_fwd, y=y[l],
-                                  idx=idx[l], w=w[l])
+                                  idx=idx[l], w=w[l], post_norm_w=gam2[l],
+                                  y_norm=yn[l] if args.post_norm else None)
         elif one_launch:
             moeq.moe_forward(L, x[l, t], K, cfg.renorm, ws=ws_fwd, y=y[l], idx=idx[l], w=w[l])
         else:
@@ -310,7 +315,8 @@ def run_decode(args, cfg):
             if args.norm:
                 evs[k][0].record(s_)
                 moeq.moe_forward_norm(L, x[l, t], K, gam[l], NORM_EPS, cfg.renorm, ws=ws_fwd, y=y[l],
-                                      idx=idx[l], w=w[l])
+                                      idx=idx[l], w=w[l], post_norm_w=gam2[l],
+                                      y_norm=yn[l] if args.post_norm else None)
                 evs[k][1].record(s_)
             elif one_launch:
                 evs[k][0].record(s_)
@@ -334,12 +340,16 @@ def run_decode(args, cfg):
         lbytes += cfg.hidden * 4                      # the norm weight
         if not one_launch:                            # norm + route + experts, bracketed together
             lbytes = layer_bytes(cfg, touched) + m * K * 8 + cfg.hidden * 4 + 2 * m * cfg.hidden * 4
+    if args.post_norm:                                # its weight, y read, y_norm written
+        lbytes += cfg.hidden * 4 + 2 * m * cfg.hidden * 4
     achieved = lbytes / (launch_us * 1e-6) / 1e9
     roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": None if args.norm else traffic_for(
                     args, "k_batch" if not one_launch and m >= BATCH_MIN_M else "k_moe_decode"),
-                "kernel": ("k_moe_decode (moe_forward_norm: RMSNorm + router + top-K + experts)"
+                "kernel": ("k_moe_decode + k_rmsnorm (moe_forward_norm with the norm after the "
+                           "combine: two launches per layer)" if args.post_norm and one_launch else
+                           "k_moe_decode (moe_forward_norm: RMSNorm + router + top-K + experts)"
                            if args.norm and one_launch else
                            "moe_forward_norm (norm, route, experts)" if args.norm else
                            "k_moe_decode (moe_forward: router + top-K + experts)") if one_launch or args.norm
@@ -358,7 +368,8 @@ def run_decode(args, cfg):
                    "expert_bits": cfg.expert_bits, "router_bits": cfg.router_bits,
                    "shared_expert": cfg.has_shared, "group_size": cfg.group_size,
                    "token_slots": slots, "graph": True, "rmsnorm_fused": bool(args.norm),
-                   "launches_per_layer": 1 if one_launch else 2},
+                   "post_norm": bool(args.post_norm),
+                   "launches_per_layer": (1 if one_launch else 2) + int(args.post_norm)},
         "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
         "bytes_per_step": int(bytes_step), "touched_experts_per_layer": round(touched, 2),
         "roofline": roofline,
@@ -602,6 +613,8 @@ def main():
                     help="decode with the experts in pinned host memory, S HBM slots per layer")
     ap.add_argument("--norm", action="store_true",
                     help="decode: RMSNorm fused in front of the step (moe_forward_norm), x added back")
+    ap.add_argument("--post-norm", action="store_true",
+                    help="decode: --norm plus the norm after the combine (the next layer's input)")
     ap.add_argument("--cpu-layers", type=int, default=0)
     ap.add_argument("--traffic", type=float, default=None,
                     help="HBM bytes per launch from rocprofv3 counters, if taken")
@@ -609,6 +622,8 @@ def main():
                     help="only run 5 device copies of MIB MiB (the reference kernel that "
                          "scales rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes) and exit")
     args = ap.parse_args()
+    if args.post_norm:
+        args.norm = True
 
     if args.copy_calibration:
         import torch

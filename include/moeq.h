@@ -253,6 +253,11 @@ int moe_rms_norm(const float *x, int32_t M, int32_t H, const float *norm_w, floa
  * followed by moe_forward(h, residual = x).
  *   x : fp32 [M][H] (the residual stream);  norm_w, eps as in moe_rms_norm
  *   y, topk_idx, topk_w out as in moe_forward
+ *   post_norm_w, y_norm : both NULL, or fp32 [H] and fp32 [M][H] out (not
+ *               overlapping y): the norm after the combine, y_norm =
+ *               rms_norm(y) * post_norm_w with the same eps (the next block's
+ *               input), one more launch after the step; NULL for only one of
+ *               them is MOEQ_ERR_NULL_PTR
  *   ws : workspace of moe_workspace_size(L, M, K, MOEQ_PATH_FORWARD_NORM)
  * With an 8-bit router and M <= 4 this is ONE launch: every router and
  * gate/up unit stages x * norm_w, reduces the row's mean square itself and
@@ -260,10 +265,12 @@ int moe_rms_norm(const float *x, int32_t M, int32_t H, const float *norm_w, floa
  * row); otherwise the norm is a launch of its own in front of moe_forward's
  * two launches, h kept in the workspace.
  * Defines: the CMD2/CMD3 chain of the flash-moe-inference skill page (norm,
- * routing, expert forward, combine + residual: moe_combine_residual). */
+ * routing, expert forward, combine + residual: moe_combine_residual, then
+ * the norm that closes CMD3). */
 int moe_forward_norm(const moeq_moe *L, const float *x, int32_t M, int32_t K, int32_t renorm,
                      const float *norm_w, float eps, float *y, int32_t *topk_idx, float *topk_w,
-                     void *ws, size_t ws_bytes, moeq_stream_t stream);
+                     const float *post_norm_w, float *y_norm, void *ws, size_t ws_bytes,
+                     moeq_stream_t stream);
 
 /* moe_gather_qmm: the expert part for many bf16 tokens (prefill).  Pairs
  * (token, slot) are sorted by expert on the device; per expert the gathered

@@ -434,7 +434,8 @@ int moe_rms_norm(const float* x, int32_t M, int32_t H, const float* norm_w, floa
 
 int moe_forward_norm(const moeq_moe* L, const float* x, int32_t M, int32_t K, int32_t renorm,
                      const float* norm_w, float eps, float* y, int32_t* topk_idx, float* topk_w,
-                     void* ws, size_t ws_bytes, moeq_stream_t stream) {
+                     const float* post_norm_w, float* y_norm, void* ws, size_t ws_bytes,
+                     moeq_stream_t stream) {
   LayerDims d;
   int st = check_experts(L, &d);
   if (st) return st;
@@ -444,6 +445,9 @@ int moe_forward_norm(const moeq_moe* L, const float* x, int32_t M, int32_t K, in
   if (M < 0 || K < 1 || K > kMaxK || K > d.E || bad_eps(eps)) return MOEQ_ERR_SHAPE;
   if (M == 0) return MOEQ_OK;
   if (!x || !norm_w || !y || !topk_idx || !topk_w) return MOEQ_ERR_NULL_PTR;
+  if (!post_norm_w != !y_norm) return MOEQ_ERR_NULL_PTR;   // both or neither
+  if (y_norm && !aligned16(post_norm_w)) return MOEQ_ERR_ALIGN;
+  if (y_norm && !aligned16(y_norm)) return MOEQ_ERR_ALIGN;
   if (!fits_i32((int64_t)M * d.H) || !fits_i32((int64_t)M * d.E) ||
       !fits_i32((int64_t)M * K * d.I + (int64_t)M * d.Is + M))
     return MOEQ_ERR_OVERFLOW;
@@ -471,6 +475,8 @@ int moe_forward_norm(const moeq_moe* L, const float* x, int32_t M, int32_t K, in
     st = run_expert_forward(dl, h, topk_idx, topk_w, M, K, x, y, base, s);
   }
   if (st) return MOEQ_ERR_UNSUPPORTED;
+  // the norm after the combine: the next block's input, from the finished y
+  if (y_norm) moeq::launch_rmsnorm(y, M, d.H, post_norm_w, eps, y_norm, s);
   return launch_status();
 }
 

@@ -77,7 +77,7 @@ _SIGNATURES = {
     "moe_rms_norm": (ctypes.c_int, [_P, _I, _I, _P, ctypes.c_float, _P, _P]),
     "moe_stream_experts": (ctypes.c_int, [ctypes.POINTER(SlotCacheStruct), _P, _I, _I, _P, _P, _P]),
     "moe_forward_norm": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _I, _I, _I, _P, ctypes.c_float,
-                                        _P, _P, _P, _P, _SZ, _P]),
+                                        _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "gather_qmm": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _P, _I, _I, _P, _P, _SZ, _P]),
 }
 
@@ -334,11 +334,16 @@ def moe_rms_norm(x: torch.Tensor, norm_w: torch.Tensor, eps: float,
 def moe_forward_norm(layer: MoELayer, x: torch.Tensor, k: int, norm_w: torch.Tensor, eps: float,
                      renorm: bool = True, ws: Optional[torch.Tensor] = None,
                      y: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
-                     w: Optional[torch.Tensor] = None, stream=None):
+                     w: Optional[torch.Tensor] = None, stream=None,
+                     post_norm_w: Optional[torch.Tensor] = None,
+                     y_norm: Optional[torch.Tensor] = None):
     """y = x + MoE(rms_norm(x)) (one launch for an 8-bit router and M <= 4).
-    Returns (y, idx, w)."""
+    Returns (y, idx, w); with ``post_norm_w`` also the norm after the combine,
+    rms_norm(y) * post_norm_w: (y, idx, w, y_norm)."""
     m = x.shape[0]
     dev = x.device
+    if post_norm_w is not None and y_norm is None:
+        y_norm = torch.empty((m, layer.hidden), dtype=torch.float32, device=dev)
     if ws is None:
         ws = workspace(layer, m, k, PATH_FORWARD_NORM, dev)
     if y is None:
@@ -348,9 +353,10 @@ def moe_forward_norm(layer: MoELayer, x: torch.Tensor, k: int, norm_w: torch.Ten
     if w is None:
         w = torch.empty((m, k), dtype=torch.float32, device=dev)
     _check(lib().moe_forward_norm(ctypes.byref(layer.struct()), _ptr(x), m, k, int(bool(renorm)),
-                                  _ptr(norm_w), float(eps), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws),
-                                  ws.numel(), _stream(stream)), "moe_forward_norm")
-    return y, idx, w
+                                  _ptr(norm_w), float(eps), _ptr(y), _ptr(idx), _ptr(w),
+                                  _ptr(post_norm_w), _ptr(y_norm), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "moe_forward_norm")
+    return (y, idx, w) if post_norm_w is None else (y, idx, w, y_norm)
 
 
 class ExpertCache:

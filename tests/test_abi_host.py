@@ -219,13 +219,17 @@ def test_norm_validation():
     g = moeq.lib().moe_forward_norm
 
     def call(L, M=1, K=2, eps=1e-6, ws=1 << 30, **kw):
-        a = dict(x=FAKE, nw=FAKE, y=FAKE, idx=FAKE, w=FAKE, wsp=FAKE)
+        a = dict(x=FAKE, nw=FAKE, y=FAKE, idx=FAKE, w=FAKE, pw=None, yn=None, wsp=FAKE)
         a.update(kw)
-        return g(ctypes.byref(L), a["x"], M, K, 1, a["nw"], eps, a["y"], a["idx"], a["w"], a["wsp"], ws,
-                 None)
+        return g(ctypes.byref(L), a["x"], M, K, 1, a["nw"], eps, a["y"], a["idx"], a["w"], a["pw"],
+                 a["yn"], a["wsp"], ws, None)
 
     assert call(_layer(), nw=None) == -1
     assert call(_layer(), nw=FAKE + 8) == -7
+    assert call(_layer(), pw=FAKE) == -1                             # post norm: both or neither
+    assert call(_layer(), yn=FAKE) == -1
+    assert call(_layer(), pw=FAKE + 4, yn=FAKE) == -7
+    assert call(_layer(), pw=FAKE, yn=FAKE + 8) == -7
     assert call(_layer(), eps=-1e-3) == -5
     assert call(_layer(), K=9) == -5
     assert call(_layer(router=_qt(8, 1, 16, 256))) == -5

@@ -6,7 +6,10 @@ the oracle's ``rms_norm`` and ``moe_block``).
 Acceptance: moe_rms_norm per-row relative L2 <= 1e-6 (fp32 arithmetic);
 moe_forward_norm top-K indices bit-exact and per-row relative L2 <= 1e-4, in
 the one-launch form (8-bit router, M <= 4), the per-token form and the
-batched form, with and without a shared expert; reruns bitwise equal.
+batched form, with and without a shared expert; reruns bitwise equal.  The
+norm after the combine (rms_norm(y) * w2, the norm closing the page's CMD3):
+y unchanged bit for bit, y_norm within 1e-6 of the oracle's norm of the
+library's own y and within 1e-4 of the oracle's whole block.
 """
 
 import functools
@@ -127,3 +130,24 @@ def test_norm_equals_rms_norm_then_moe_forward_with_residual():
     torch.cuda.synchronize()
     assert torch.equal(idx, idx2)
     assert rel_l2_rows(y.cpu().numpy(), y2.cpu().numpy().astype(np.float64)).max() <= 1e-5
+
+
+@pytest.mark.parametrize("name,m", [("c1", 2), ("c1_shared", 7), ("c1_4bit_router", 3), ("c2", 1)])
+def test_norm_after_the_combine(name, m):
+    # one-launch form (c1, c2), per-token form (7 tokens), separate-norm form
+    cfg, host, L, g = _layer(name)
+    say(f"moe_forward_norm + post norm {name} M={m}")
+    x = _gapped_norm_tokens(cfg, host, g, 0, 6, m)
+    g2 = np.random.default_rng(m).uniform(0.5, 1.5, cfg.hidden).astype(np.float32)
+    xd, gd = to_dev(x), to_dev(g)
+    y, idx, _ = moeq.moe_forward_norm(L, xd, cfg.top_k, gd, EPS, cfg.renorm)
+    y2, idx2, _, yn = moeq.moe_forward_norm(L, xd, cfg.top_k, gd, EPS, cfg.renorm,
+                                            post_norm_w=to_dev(g2))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y2) and torch.equal(idx, idx2)
+    yh = y2.cpu().numpy()
+    assert rel_l2_rows(yn.cpu().numpy(), oracle.rms_norm(yh, g2, EPS)).max() <= 1e-6
+    ry, _, _, _ = oracle.moe_block(host, x, g, EPS, cfg.top_k, cfg.renorm)
+    err = rel_l2_rows(yn.cpu().numpy(), oracle.rms_norm(ry, g2, EPS)).max()
+    say(f"  y_norm max rel-L2 against the oracle's block {err:.3e}")
+    assert err <= 1e-4
