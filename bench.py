@@ -459,7 +459,8 @@ def run_stream(args, cfg):
         if host.get("shared") is not None:
             sh = {k: moeq.QTensor.from_host(v, dev) for k, v in host["shared"].items()}
         resident = moeq.MoELayer(moeq.QTensor.from_host(host["router"], dev), None, None, None, sh)
-        caches.append(moeq.ExpertCache(host, args.stream_slots, resident, dev))
+        caches.append(moeq.ExpertCache(host, args.stream_slots, resident, dev,
+                                       device_lru=args.stream_device))
         routers.append(resident.router)
         del host
     log(f"[bench] {n_layers} layers in pinned host memory, {args.stream_slots} HBM slots each "
@@ -471,25 +472,38 @@ def run_stream(args, cfg):
     ws_dec = moeq.workspace(caches[0].layer, 1, K, moeq.PATH_DECODE, dev)
     ws_route = torch.zeros(8 * cfg.experts + 4096, dtype=torch.uint8, device=dev)
     copied = [0]
+    n_warm = max(1, args.warmup)
+    # device form: one copy counter per (step, layer), summed after the run
+    ncp = (torch.zeros((n_warm + args.steps, n_layers, 4), dtype=torch.int32, device=dev)
+           if args.stream_device else None)
+    idx_b = torch.empty((1, K), dtype=torch.int32, device=dev)
+    w_b = torch.empty((1, K), dtype=torch.float32, device=dev)
+    sidx_b = torch.empty((1, K), dtype=torch.int32, device=dev)
 
     def step(t):
         for l in range(n_layers):
             xt = x[l, t % slots_n][None, :]
-            idx, w = moeq.moe_route(routers[l], xt, cfg.experts, K, cfg.renorm, ws=ws_route)
-            slot_idx, n = caches[l].stream(idx.cpu().numpy())
-            copied[0] += n
-            moeq.moe_expert_forward(caches[l].layer, xt, torch.from_numpy(slot_idx).to(dev), w,
-                                    ws=ws_dec, y=y)
+            moeq.moe_route(routers[l], xt, cfg.experts, K, cfg.renorm, ws=ws_route, idx=idx_b, w=w_b)
+            if args.stream_device:
+                caches[l].stream_device(idx_b, slot_idx=sidx_b, n_copied=ncp[t, l])
+                moeq.moe_expert_forward(caches[l].layer, xt, sidx_b, w_b, ws=ws_dec, y=y)
+            else:
+                slot_idx, n = caches[l].stream(idx_b.cpu().numpy())
+                copied[0] += n
+                moeq.moe_expert_forward(caches[l].layer, xt, torch.from_numpy(slot_idx).to(dev), w_b,
+                                        ws=ws_dec, y=y)
 
-    for s_ in range(max(1, args.warmup)):
+    for s_ in range(n_warm):
         step(s_)
     torch.cuda.synchronize()
     copied[0] = 0
     t1 = time.perf_counter()
     for s_ in range(args.steps):
-        step(args.warmup + s_)
+        step(n_warm + s_)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t1
+    if args.stream_device:
+        copied[0] = int(ncp[n_warm:, :, 0].sum().item())
     ms = dt * 1e3 / args.steps
     per_expert = 3 * cfg.hidden * cfg.inter * cfg.expert_bits // 8 + 3 * cfg.hidden * cfg.inter // cfg.group_size * 4
     gbps = copied[0] * per_expert / dt / 1e9
@@ -502,11 +516,15 @@ def run_stream(args, cfg):
         "config": {"workload": cfg.name + "-streamed", "layers": n_layers, "tokens_per_step": 1,
                    "hidden": cfg.hidden, "experts": cfg.experts, "top_k": K, "inter": cfg.inter,
                    "expert_bits": cfg.expert_bits, "hbm_slots_per_layer": args.stream_slots,
-                   "expert_bytes": per_expert},
+                   "expert_bytes": per_expert,
+                   "slot_choice": "device" if args.stream_device else "host"},
         "experts_copied_per_layer": round(copied[0] / (args.steps * n_layers), 3),
         "roofline": {"bound": "pcie", "achieved": round(gbps, 2), "peak": PCIE_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / PCIE_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": "moe_stream_experts host->device copies (route, copy, expert forward per layer)"},
+                     "kernel": ("moe_stream_experts_device: k_slot_lru + k_slot_copy reading pinned host "
+                                "memory (route, slot choice, copy, expert forward per layer, no host sync)"
+                                if args.stream_device else
+                                "moe_stream_experts host->device copies (route, copy, expert forward per layer)")},
     }
 
 
@@ -611,6 +629,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--stream-slots", type=int, default=0, metavar="S",
                     help="decode with the experts in pinned host memory, S HBM slots per layer")
+    ap.add_argument("--stream-device", action="store_true",
+                    help="with --stream-slots: slot choice and copies on the device (no host sync)")
     ap.add_argument("--norm", action="store_true",
                     help="decode: RMSNorm fused in front of the step (moe_forward_norm), x added back")
     ap.add_argument("--post-norm", action="store_true",

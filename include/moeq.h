@@ -67,7 +67,8 @@ typedef enum moeq_status {
   MOEQ_ERR_ALIGN = -7,       /* a device pointer is not 16-byte aligned         */
   MOEQ_ERR_WORKSPACE = -8,   /* workspace missing or smaller than required      */
   MOEQ_ERR_UNSUPPORTED = -9, /* valid request outside what this build computes  */
-  MOEQ_ERR_LAUNCH = -10      /* the HIP runtime rejected a kernel launch        */
+  MOEQ_ERR_LAUNCH = -10,     /* the HIP runtime rejected a kernel launch        */
+  MOEQ_ERR_HOST_MEMORY = -11 /* host memory not pinned and mapped for the device */
 } moeq_status;
 
 /* One quantized matrix [rows][cols], or a stack of `batch` such matrices laid
@@ -146,6 +147,27 @@ typedef struct moeq_slot_cache {
   int64_t clock;
   int32_t n_slots;
 } moeq_slot_cache;
+
+/* The device-side form of the slot cache (moe_stream_experts_device): the
+ * same host and slot stacks, the LRU state in device memory.
+ *   host        : expert stacks [E] in pinned host memory that the device can
+ *                 read (hipHostMalloc, torch pin_memory); biases NULL for mxfp4
+ *   slots       : the same stacks with S experts, in device memory
+ *   slot_expert : DEVICE int32 [S], the expert each slot holds, -1 = empty
+ *                 (the caller fills it with -1 once)
+ *   slot_stamp  : DEVICE int64 [S + 1], the call that last used each slot;
+ *                 element S counts the calls (the caller zeroes it once)
+ *   copy_list   : DEVICE int32 [2 S + 1], scratch of one call (the copies)
+ *   n_slots     : S, 1 <= S <= 1024
+ * The state arrays belong to the library between calls. */
+typedef struct moeq_slot_cache_dev {
+  moeq_moe host;
+  moeq_moe slots;
+  int32_t *slot_expert;
+  int64_t *slot_stamp;
+  int32_t *copy_list;
+  int32_t n_slots;
+} moeq_slot_cache_dev;
 
 /* Workspace paths for moe_workspace_size(). */
 #define MOEQ_PATH_ROUTE 0   /* moe_route                                   */
@@ -341,6 +363,29 @@ int requant_2bit(const moeq_qtensor *W, uint32_t *q_out, uint16_t *s_out, uint16
  * place of the SSD and HBM slots in place of the buffers. */
 int moe_stream_experts(moeq_slot_cache *C, const int32_t *topk_idx_host, int32_t M, int32_t K,
                        int32_t *slot_idx_host, int32_t *n_copied, moeq_stream_t stream);
+
+/* moe_stream_experts_device: moe_stream_experts with the routing result, the
+ * slot choice and the copies all on the device: no host round trip between
+ * moe_route and moe_expert_forward, so a layer's route -> stream -> forward
+ * chain queues without a synchronization (and can be captured in a graph).
+ *   topk_idx : device int32 [M][K] (moe_route's output)
+ *   slot_idx : device int32 [M][K] out, the slot of each pair (S for an index
+ *              outside [0, E), whose row then comes out NaN)
+ *   n_copied : nullable device int32 out, experts copied by this call
+ * Two launches on `stream`: one wave takes the LRU decisions of
+ * moe_stream_experts (same order, same slots for the same call sequence) and
+ * writes the copy list; then one kernel copies every listed expert's codes,
+ * scales and biases, its waves reading the pinned host stacks over PCIe.
+ * A slot is refilled only after the work queued before it on the stream.
+ * M*K must not exceed S (MOEQ_ERR_WORKSPACE), so every call has slots enough
+ * whatever it selects; E <= 1024.  Each host stack must be pinned and mapped
+ * for the device over its whole extent (checked at its first and last byte:
+ * MOEQ_ERR_HOST_MEMORY otherwise).  All other pointers are device pointers,
+ * 16-byte aligned.
+ * Defines: as moe_stream_experts (flash-moe-inference skill page, parallel
+ * expert loading), with the I/O phase issued by the device itself. */
+int moe_stream_experts_device(moeq_slot_cache_dev *C, const int32_t *topk_idx, int32_t M, int32_t K,
+                              int32_t *slot_idx, int32_t *n_copied, moeq_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -22,7 +22,8 @@ LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libmoeq.so")
 
 ARCH = "gfx950"
-SOURCES = ["abi.cpp", "k_matvec.hip", "k_decode.hip", "k_sort.hip", "k_gemm.hip", "k_batch.hip", "k_requant.hip"]
+SOURCES = ["abi.cpp", "k_matvec.hip", "k_decode.hip", "k_sort.hip", "k_gemm.hip", "k_batch.hip", "k_requant.hip",
+           "k_stream.hip"]
 # packed fp32 instructions are turned off for all device code
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-I", INCLUDE, "-I", CSRC,
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -5,6 +5,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <vector>
 #include <cstdint>
@@ -258,6 +259,7 @@ const char* moeq_status_string(int status) {
     case MOEQ_ERR_WORKSPACE: return "workspace missing or too small";
     case MOEQ_ERR_UNSUPPORTED: return "unsupported combination";
     case MOEQ_ERR_LAUNCH: return "kernel launch failed";
+    case MOEQ_ERR_HOST_MEMORY: return "host memory is not pinned and mapped for the device";
     default: return "unknown status";
   }
 }
@@ -480,21 +482,54 @@ int moe_forward_norm(const moeq_moe* L, const float* x, int32_t M, int32_t K, in
   return launch_status();
 }
 
-int moe_stream_experts(moeq_slot_cache* C, const int32_t* topk_idx_host, int32_t M, int32_t K,
-                       int32_t* slot_idx_host, int32_t* n_copied, moeq_stream_t stream) {
-  if (!C) return MOEQ_ERR_NULL_PTR;
-  LayerDims dh, ds;
-  int st = check_experts(&C->host, &dh);
+namespace {
+
+// The device-mapped address of pinned host memory [p, p + n), or nullptr when
+// either end is not host memory the device can read or the mapping of the
+// range is not contiguous.
+const char* mapped_host_range(const void* p, uint64_t n) {
+  if (!p || n == 0) return nullptr;
+  hipPointerAttribute_t a{}, b{};
+  const char* last = static_cast<const char*>(p) + (n - 1);
+  if (hipPointerGetAttributes(&a, p) != hipSuccess || hipPointerGetAttributes(&b, last) != hipSuccess) {
+    (void)hipGetLastError();   // not a registered pointer: leave no error behind
+    return nullptr;
+  }
+  if (a.type != hipMemoryTypeHost || b.type != hipMemoryTypeHost || !a.devicePointer ||
+      !b.devicePointer)
+    return nullptr;
+  const char* da = static_cast<const char*>(a.devicePointer);
+  if (static_cast<const char*>(b.devicePointer) - da != (ptrdiff_t)(n - 1)) return nullptr;
+  return da;
+}
+
+// Host and slot stacks of a slot cache: same shapes except the expert count.
+int check_slot_stacks(const moeq_moe* host, const moeq_moe* slots, int S, LayerDims* dh) {
+  LayerDims ds;
+  int st = check_experts(host, dh);
   if (st) return st;
-  if ((st = check_experts(&C->slots, &ds))) return st;
-  const int E = dh.E, S = C->n_slots;
-  if (S < 1 || ds.E != S || ds.H != dh.H || ds.I != dh.I) return MOEQ_ERR_SHAPE;
-  const moeq_qtensor* hq[3] = {&C->host.gate, &C->host.up, &C->host.down};
-  const moeq_qtensor* sq[3] = {&C->slots.gate, &C->slots.up, &C->slots.down};
+  if ((st = check_experts(slots, &ds))) return st;
+  if (S < 1 || ds.E != S || ds.H != dh->H || ds.I != dh->I) return MOEQ_ERR_SHAPE;
+  const moeq_qtensor* hq[3] = {&host->gate, &host->up, &host->down};
+  const moeq_qtensor* sq[3] = {&slots->gate, &slots->up, &slots->down};
   for (int i = 0; i < 3; ++i)
     if (hq[i]->bits != sq[i]->bits || hq[i]->group_size != sq[i]->group_size ||
         hq[i]->mode != sq[i]->mode)
       return MOEQ_ERR_SHAPE;
+  return MOEQ_OK;
+}
+
+}  // namespace
+
+int moe_stream_experts(moeq_slot_cache* C, const int32_t* topk_idx_host, int32_t M, int32_t K,
+                       int32_t* slot_idx_host, int32_t* n_copied, moeq_stream_t stream) {
+  if (!C) return MOEQ_ERR_NULL_PTR;
+  LayerDims dh;
+  int st = check_slot_stacks(&C->host, &C->slots, C->n_slots, &dh);
+  if (st) return st;
+  const int E = dh.E, S = C->n_slots;
+  const moeq_qtensor* hq[3] = {&C->host.gate, &C->host.up, &C->host.down};
+  const moeq_qtensor* sq[3] = {&C->slots.gate, &C->slots.up, &C->slots.down};
   if (M < 0 || K < 1 || K > kMaxK) return MOEQ_ERR_SHAPE;
   if (n_copied) *n_copied = 0;
   if (M == 0) return MOEQ_OK;
@@ -559,6 +594,55 @@ int moe_stream_experts(moeq_slot_cache* C, const int32_t* topk_idx_host, int32_t
   }
   if (n_copied) *n_copied = copied;
   return MOEQ_OK;
+}
+
+int moe_stream_experts_device(moeq_slot_cache_dev* C, const int32_t* topk_idx, int32_t M, int32_t K,
+                              int32_t* slot_idx, int32_t* n_copied, moeq_stream_t stream) {
+  if (!C) return MOEQ_ERR_NULL_PTR;
+  LayerDims dh;
+  const int S = C->n_slots;
+  int st = check_slot_stacks(&C->host, &C->slots, S, &dh);
+  if (st) return st;
+  const int E = dh.E;
+  if (M < 0 || K < 1 || K > kMaxK || S > moeq::kMaxStreamSlots || E > moeq::kMaxStreamExperts)
+    return MOEQ_ERR_SHAPE;
+  if ((int64_t)M * K > S) return MOEQ_ERR_WORKSPACE;
+  if (M == 0) return MOEQ_OK;
+  if (!topk_idx || !slot_idx || !C->slot_expert || !C->slot_stamp || !C->copy_list)
+    return MOEQ_ERR_NULL_PTR;
+  if (!aligned16(topk_idx) || !aligned16(slot_idx) || !aligned16(C->slot_expert) ||
+      !aligned16(C->slot_stamp) || !aligned16(C->copy_list) || (n_copied && !aligned16(n_copied)))
+    return MOEQ_ERR_ALIGN;
+  moeq::StreamCopy P{};
+  const moeq_qtensor* hq[3] = {&C->host.gate, &C->host.up, &C->host.down};
+  const moeq_qtensor* sq[3] = {&C->slots.gate, &C->slots.up, &C->slots.down};
+  uint64_t per_expert = 0;
+  for (int i = 0; i < 3; ++i) {
+    const moeq_qtensor& h = *hq[i];
+    const uint64_t qb = (uint64_t)h.rows * h.cols / (32 / h.bits) * sizeof(uint32_t);
+    const uint64_t sb = (uint64_t)h.rows * (h.cols / h.group_size) * (is_mx(h) ? 1 : 2);
+    const void* hp[3] = {h.q, h.scales, is_mx(h) ? nullptr : h.biases};
+    const void* dp[3] = {sq[i]->q, sq[i]->scales, is_mx(h) ? nullptr : sq[i]->biases};
+    const uint64_t nb[3] = {qb, sb, sb};
+    for (int j = 0; j < 3; ++j) {
+      if (!hp[j]) continue;
+      const char* src = mapped_host_range(hp[j], nb[j] * E);
+      if (!src) return MOEQ_ERR_HOST_MEMORY;
+      if (!aligned16(src)) return MOEQ_ERR_ALIGN;
+      P.src[P.nseg] = src;
+      P.dst[P.nseg] = static_cast<char*>(const_cast<void*>(dp[j]));
+      P.bytes[P.nseg] = nb[j];
+      ++P.nseg;
+      per_expert += nb[j];
+    }
+  }
+  // about 96 KB per block, so a few experts spread over a few hundred blocks
+  P.parts = (int)std::min<uint64_t>(256, std::max<uint64_t>(1, per_expert / (96u << 10)));
+  if (!fits_i32((int64_t)M * K * P.parts)) return MOEQ_ERR_OVERFLOW;
+  if (moeq::launch_stream_experts(P, topk_idx, M * K, E, S, C->slot_expert, C->slot_stamp, slot_idx,
+                                  C->copy_list, n_copied, (hipStream_t)stream))
+    return MOEQ_ERR_UNSUPPORTED;
+  return launch_status();
 }
 
 int moe_gather_qmm(const moeq_moe* L, const uint16_t* x_bf16, const int32_t* topk_idx,

@@ -27,6 +27,7 @@ STATUS = {
     0: "MOEQ_OK", -1: "MOEQ_ERR_NULL_PTR", -2: "MOEQ_ERR_BAD_BITS", -3: "MOEQ_ERR_BAD_GROUP",
     -4: "MOEQ_ERR_K_TAIL", -5: "MOEQ_ERR_SHAPE", -6: "MOEQ_ERR_OVERFLOW", -7: "MOEQ_ERR_ALIGN",
     -8: "MOEQ_ERR_WORKSPACE", -9: "MOEQ_ERR_UNSUPPORTED", -10: "MOEQ_ERR_LAUNCH",
+    -11: "MOEQ_ERR_HOST_MEMORY",
 }
 
 
@@ -54,6 +55,12 @@ class SlotCacheStruct(ctypes.Structure):
                 ("slot_stamp", ctypes.c_void_p), ("clock", ctypes.c_int64), ("n_slots", ctypes.c_int32)]
 
 
+class SlotCacheDevStruct(ctypes.Structure):
+    _fields_ = [("host", MoEStruct), ("slots", MoEStruct), ("slot_expert", ctypes.c_void_p),
+                ("slot_stamp", ctypes.c_void_p), ("copy_list", ctypes.c_void_p),
+                ("n_slots", ctypes.c_int32)]
+
+
 _lib = None
 _P = ctypes.c_void_p
 _I = ctypes.c_int32
@@ -76,6 +83,8 @@ _SIGNATURES = {
                                       _P]),
     "moe_rms_norm": (ctypes.c_int, [_P, _I, _I, _P, ctypes.c_float, _P, _P]),
     "moe_stream_experts": (ctypes.c_int, [ctypes.POINTER(SlotCacheStruct), _P, _I, _I, _P, _P, _P]),
+    "moe_stream_experts_device": (ctypes.c_int, [ctypes.POINTER(SlotCacheDevStruct), _P, _I, _I, _P,
+                                                 _P, _P]),
     "moe_forward_norm": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _I, _I, _I, _P, ctypes.c_float,
                                         _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "gather_qmm": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _P, _I, _I, _P, _P, _SZ, _P]),
@@ -364,9 +373,12 @@ class ExpertCache:
     (the buffers moe_stream_experts manages; allocated here with torch).
     ``layer`` is the device layer to run moe_expert_forward on: the slot
     stacks as its experts, the resident router and shared expert of
-    ``resident``."""
+    ``resident``.  With ``device_lru`` the slot choice and the copies run on
+    the device (``stream_device``, moe_stream_experts_device), else on the
+    host (``stream``); one cache uses one of the two."""
 
-    def __init__(self, host_layer: dict, n_slots: int, resident: "MoELayer", device="cuda"):
+    def __init__(self, host_layer: dict, n_slots: int, resident: "MoELayer", device="cuda",
+                 device_lru: bool = False):
         def pinned(a):
             a = np.ascontiguousarray(a)
             t = torch.empty(a.shape, dtype=_TORCH_OF[a.dtype.str[1:]], pin_memory=True)
@@ -399,10 +411,20 @@ class ExpertCache:
         self._cs = SlotCacheStruct(_host_struct(self._host_layer), _host_struct(
             MoELayer(None, self.slots["gate"], self.slots["up"], self.slots["down"])),
             self.slot_expert.ctypes.data, self.slot_stamp.ctypes.data, 0, n_slots)
+        self.device_lru = bool(device_lru)
+        if self.device_lru:
+            self.slot_expert_dev = torch.full((n_slots,), -1, dtype=torch.int32, device=device)
+            self.slot_stamp_dev = torch.zeros(n_slots + 1, dtype=torch.int64, device=device)
+            self.copy_list = torch.zeros(2 * n_slots + 4, dtype=torch.int32, device=device)
+            self._csd = SlotCacheDevStruct(
+                self._cs.host, self._cs.slots, self.slot_expert_dev.data_ptr(),
+                self.slot_stamp_dev.data_ptr(), self.copy_list.data_ptr(), n_slots)
 
     def stream(self, topk_idx_host: np.ndarray, stream=None):
         """Copy the experts ``topk_idx_host`` selects into slots (async on the
         stream); returns (slot indices [M][K] int32 host array, experts copied)."""
+        if self.device_lru:
+            raise ValueError("this cache keeps its LRU on the device: use stream_device")
         idx = np.ascontiguousarray(topk_idx_host, dtype=np.int32)
         m, k = idx.shape
         out = np.empty_like(idx)
@@ -411,6 +433,24 @@ class ExpertCache:
                                         out.ctypes.data, ctypes.byref(n), _stream(stream)),
                "moe_stream_experts")
         return out, n.value
+
+    def stream_device(self, topk_idx: torch.Tensor, slot_idx: Optional[torch.Tensor] = None,
+                      n_copied: Optional[torch.Tensor] = None, stream=None):
+        """Device-side form: ``topk_idx`` is moe_route's device output; the
+        slot choice and the copies are queued on the stream with no host
+        synchronization.  Returns (slot indices [M][K] int32, experts copied
+        as a device int32 [1]), both device tensors."""
+        if not self.device_lru:
+            raise ValueError("this cache keeps its LRU on the host: use stream")
+        m, k = topk_idx.shape
+        if slot_idx is None:
+            slot_idx = torch.empty((m, k), dtype=torch.int32, device=topk_idx.device)
+        if n_copied is None:
+            n_copied = torch.zeros(4, dtype=torch.int32, device=topk_idx.device)
+        _check(lib().moe_stream_experts_device(ctypes.byref(self._csd), _ptr(topk_idx), m, k,
+                                               _ptr(slot_idx), _ptr(n_copied), _stream(stream)),
+               "moe_stream_experts_device")
+        return slot_idx, n_copied[:1]
 
 
 _TORCH_OF = {"u4": torch.int32, "u2": torch.int16, "u1": torch.uint8, "i4": torch.int32,

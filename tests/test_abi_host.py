@@ -32,7 +32,7 @@ def test_header_declares_the_four_calls_and_helpers():
     names = declared_functions()
     for n in ("qmatvec", "moe_route", "moe_expert_forward", "moe_gather_qmm", "qdequant",
               "gather_qmm", "requant_2bit", "moe_rms_norm", "moe_forward_norm", "moe_stream_experts",
-              "moe_workspace_size", "moeq_status_string", "moeq_version"):
+              "moe_stream_experts_device", "moe_workspace_size", "moeq_status_string", "moeq_version"):
         assert n in names
 
 
@@ -274,6 +274,37 @@ def test_stream_experts_slot_logic_without_copies():
     wrong = _layer(gate=_qt(8, S, 128, 256), up=_qt(8, S, 128, 256), down=_qt(8, S, 256, 128))
     C2 = moeq.SlotCacheStruct(host, wrong, se.ctypes.data, ss.ctypes.data, 0, S)
     assert f(ctypes.byref(C2), idx.ctypes.data, 1, 2, idx.ctypes.data, None, None) == -5   # bits differ
+
+
+def test_stream_experts_device_validation():
+    # every check before the pinned-memory test and the launches; host
+    # pointers that are not pinned (none can be without a device) are refused
+    f = moeq.lib().moe_stream_experts_device
+    S = 4
+    host = _layer()                                                    # E = 8, K up to 16
+    slots = _layer(gate=_qt(4, S, 128, 256), up=_qt(4, S, 128, 256), down=_qt(4, S, 256, 128))
+
+    def C(**kw):
+        a = dict(host=host, slots=slots, se=FAKE, ss=FAKE, cl=FAKE, S=S)
+        a.update(kw)
+        return moeq.SlotCacheDevStruct(a["host"], a["slots"], a["se"], a["ss"], a["cl"], a["S"])
+
+    def call(c, M=1, K=2, idx=FAKE, out=FAKE, n=None):
+        return f(ctypes.byref(c), idx, M, K, out, n, None)
+
+    assert f(None, FAKE, 1, 2, FAKE, None, None) == -1
+    assert call(C(S=3)) == -5                                          # S != slot stack batch
+    wrong = _layer(gate=_qt(8, S, 128, 256), up=_qt(8, S, 128, 256), down=_qt(8, S, 256, 128))
+    assert call(C(slots=wrong)) == -5                                  # bits differ
+    assert call(C(), K=0) == -5 and call(C(), K=17) == -5 and call(C(), M=-1) == -5
+    assert call(C(), M=3, K=2) == -8                                   # 6 pairs > 4 slots
+    assert call(C(), M=0) == 0                                         # empty: nothing queued
+    assert call(C(), idx=None) == -1 and call(C(), out=None) == -1
+    assert call(C(se=None)) == -1 and call(C(ss=None)) == -1 and call(C(cl=None)) == -1
+    assert call(C(ss=FAKE + 8)) == -7 and call(C(), out=FAKE + 4) == -7
+    assert call(C(), n=FAKE + 4) == -7
+    assert call(C()) == -11                                            # host stacks not pinned
+    assert moeq.lib().moeq_status_string(-11) == b"host memory is not pinned and mapped for the device"
 
 
 def test_workspace_sizes():
