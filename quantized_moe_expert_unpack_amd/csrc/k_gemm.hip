@@ -177,14 +177,17 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   // two register stages of global loads: step k's data lands in stage k % 2
+  // (scale and bias stay raw bits until the stage is written to LDS, so the
+  // first use of every loaded register is two steps after its load)
   u32x4 a0[4], a1[4], b0[kV], b1[kV];
-  float s0 = 0.f, c0 = 0.f, s1 = 0.f, c1 = 0.f;   // scale, bias
+  uint32_t s0 = 0u, c0 = 0u, s1 = 0u, c1 = 0u;   // raw scale, bias bits
+  float m0 = 0.f, m1 = 0.f;                      // 1, or 0 for a masked half step
   // k-steps of 64 columns; Kd may end on half a step (group size 32, an odd
   // number of groups): the missing half is read from valid columns and
   // weighted by zero scale and bias
   const int ksteps = (Kd + kBK - 1) / kBK;
 
-#define MOEQ_GLOAD(AR, BR, SV, CV, KT)                                                        \
+#define MOEQ_GLOAD(AR, BR, SV, CV, MV, KT)                                                    \
   do {                                                                                        \
     const int k_ = (KT);                                                                      \
     const int ac_ = min(k_ * kBK + aseg * 8, Kd - 8);                                         \
@@ -200,17 +203,21 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
     } else {                                                                                  \
       _Pragma("unroll") for (int q = 0; q < kV; ++q) BR[q] = reinterpret_cast<const u32x4*>(p_)[q]; \
     }                                                                                         \
-    const float m_ = ok_ ? 1.f : 0.f;              /* loads stay unconditional */              \
+    MV = ok_ ? 1.f : 0.f;                          /* loads stay unconditional */              \
     if constexpr (MX) {                            /* one group of 32: scale byte cv_ / 32 */  \
-      SV = e8m0_f32(bs8[cv_ >> 5]) * m_;                                                      \
-      CV = 0.f;                                                                               \
+      SV = bs8[cv_ >> 5];                                                                     \
+      CV = 0u;                                                                                \
     } else {                                                                                  \
-      SV = bf16_to_f32(bs[group_of(cv_, gsz)]) * m_;                                          \
-      CV = bf16_to_f32(bb[group_of(cv_, gsz)]) * m_;                                          \
+      SV = bs[group_of(cv_, gsz)];                                                            \
+      CV = bb[group_of(cv_, gsz)];                                                            \
     }                                                                                         \
   } while (0)
-#define MOEQ_LSTORE(AR, BR, SV, CV, BUF)                                                      \
+  // MV: the stage's mask (the half-step tail and, for the unused half of the
+  // last pair of steps, zero)
+#define MOEQ_LSTORE(AR, BR, SRAW, CRAW, MV, BUF)                                              \
   do {                                                                                        \
+    const float SV = (MX ? e8m0_f32(SRAW) : bf16_to_f32(SRAW)) * (MV);                        \
+    const float CV = (MX ? 0.f : bf16_to_f32(CRAW)) * (MV);                                   \
     uint16_t* As_ = gsm + (BUF) * kStage;                                                     \
     uint16_t* Bs_ = As_ + kBM * kLds;                                                         \
     _Pragma("unroll") for (int u = 0; u < 4; ++u)                                             \
@@ -255,19 +262,23 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
   // both halves always run their MFMAs, and with an odd step count the last
   // half's B stage is written with zero scale and bias so it adds nothing.
   const int klast = ksteps - 1;
-  MOEQ_GLOAD(a0, b0, s0, c0, 0);
-  MOEQ_GLOAD(a1, b1, s1, c1, min(1, klast));
-  MOEQ_LSTORE(a0, b0, s0, c0, 0);
+  MOEQ_GLOAD(a0, b0, s0, c0, m0, 0);
+  MOEQ_GLOAD(a1, b1, s1, c1, m1, min(1, klast));
+  MOEQ_LSTORE(a0, b0, s0, c0, m0, 0);
   __syncthreads();
   for (int kt = 0; kt < ksteps; kt += 2) {
     const float on = kt + 1 < ksteps ? 1.f : 0.f;
-    MOEQ_GLOAD(a0, b0, s0, c0, min(kt + 2, klast));
+    MOEQ_GLOAD(a0, b0, s0, c0, m0, min(kt + 2, klast));
+    // affine: the loads go out before this step's MFMAs (the scheduler
+    // would sink them; measured faster on 8-bit codes, slower on mxfp4)
+    if constexpr (!MX) __builtin_amdgcn_sched_barrier(0);
     mfma_step(0);
-    MOEQ_LSTORE(a1, b1, s1 * on, c1 * on, 1);
+    MOEQ_LSTORE(a1, b1, s1, c1, m1 * on, 1);
     __syncthreads();
-    MOEQ_GLOAD(a1, b1, s1, c1, min(kt + 3, klast));
+    MOEQ_GLOAD(a1, b1, s1, c1, m1, min(kt + 3, klast));
+    if constexpr (!MX) __builtin_amdgcn_sched_barrier(0);
     mfma_step(1);
-    MOEQ_LSTORE(a0, b0, s0, c0, 0);
+    MOEQ_LSTORE(a0, b0, s0, c0, m0, 0);
     __syncthreads();
   }
 #undef MOEQ_GLOAD
