@@ -11,6 +11,7 @@
 #include <cstdint>
 
 #include "launch.h"
+#include "stream.h"
 
 using moeq::QT;
 

@@ -21,6 +21,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "stream.h"
 
 namespace moeq {
 namespace {

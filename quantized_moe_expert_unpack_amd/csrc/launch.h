@@ -119,21 +119,6 @@ int launch_qmatvec(const QT& W, const float* x, int M, float* y, hipStream_t s);
 int launch_rmsnorm(const float* x, int M, int H, const float* g, float eps, float* h, hipStream_t s);
 // 2-bit requantization of a 4- or 8-bit tensor (group size 64 or 128)
 int launch_requant_2bit(const QT& W, uint32_t* q2, uint16_t* s2, uint16_t* b2, hipStream_t s);
-
-// device-side expert streaming: per expert up to 9 segments (codes, scales,
-// biases of gate, up, down), each a stack of per-expert blocks of `bytes`
-constexpr int kMaxStreamExperts = 1024;
-constexpr int kMaxStreamSlots = 1024;
-struct StreamCopy {
-  const char* src[9];   // device-mapped addresses of the pinned host stacks
-  char* dst[9];         // the slot stacks
-  uint64_t bytes[9];    // per-expert bytes of each segment
-  int nseg;
-  int parts;            // blocks per copied expert
-};
-int launch_stream_experts(const StreamCopy& P, const int32_t* idx, int MK, int E, int S,
-                          int32_t* slot_expert, int64_t* slot_stamp, int32_t* slot_idx,
-                          int32_t* list, int32_t* n_copied, hipStream_t s);
 // routing: router projection (fp64) + softmax/top-K.  The standalone
 // workspace is [counters (zero between calls)][fp64 logits [M][E]].
 size_t route_ctr_bytes();
