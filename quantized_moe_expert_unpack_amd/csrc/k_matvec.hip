@@ -188,7 +188,7 @@ constexpr int kMaxE = kMaxExperts;
 // fp64 products and sums), one wave per router row and token.  With
 // LAST_TOPK the block that finishes last (arrival counter) runs top-K for all
 // M tokens and resets the counter; otherwise logits stay in the workspace for
-// k_topk_rows.
+// k_topk_wave.
 template <int BITS, bool LAST_TOPK>
 __global__ void __launch_bounds__(kRouteThreads) k_router(QT W, const float* __restrict__ x, int M,
                                                           int K, int renorm,
@@ -323,22 +323,74 @@ __global__ void __launch_bounds__(kRouteThreads) k_router_many(QT W, const float
   }
 }
 
-// top-K for many tokens: one block per token, logits fp64 (router) or fp32 (given)
-__global__ void __launch_bounds__(kRouteThreads) k_topk_rows(const double* __restrict__ l64,
+// top-K for many tokens, one wave per token (four per block): the same
+// unique keys and rank order as block_topk, the selection by K rounds of a
+// wave-wide maximum, with the weights from the same fp64 expressions
+// (renormalized: the K exponentials summed in slot order; otherwise the
+// partial sums of 64 experts each, added in expert order).  PER keys per
+// lane: E <= 64 * PER.
+template <int PER>
+__global__ void __launch_bounds__(kRouteThreads) k_topk_wave(const double* __restrict__ l64,
                                                              const float* __restrict__ l32, int M,
                                                              int E, int K, int renorm,
                                                              int32_t* __restrict__ idx,
                                                              float* __restrict__ wout) {
-  __shared__ uint64_t keys[kMaxE];
-  __shared__ double vals[kMaxE];
-  const int t = blockIdx.x;
-  for (int e = threadIdx.x; e < E; e += kRouteThreads) {
-    const double v = l64 ? l64[(size_t)t * E + e] : (double)l32[(size_t)t * E + e];
-    vals[e] = v;
-    keys[e] = route_key(v, e);
+  constexpr int kPer = PER;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int t = blockIdx.x * (kRouteThreads / kWave) + threadIdx.x / kWave;
+  if (t >= M) return;                            // whole waves leave together
+  const size_t row = (size_t)t * E;
+  uint64_t key[kPer];
+  double val[kPer];
+  uint32_t live = 0u;                            // bit j: slot j holds an unselected key
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int e = lane + kWave * j;
+    val[j] = 0.0;
+    key[j] = 0ull;
+    if (e < E) {
+      val[j] = l64 ? l64[row + e] : (double)l32[row + e];
+      key[j] = route_key(val[j], e);
+      live |= 1u << j;
+    }
   }
-  __syncthreads();
-  block_topk<kRouteThreads>(keys, vals, E, K, renorm, idx + (size_t)t * K, wout + (size_t)t * K);
+  int my_e = 0;                                  // lane k < K: the expert of slot k
+  for (int k = 0; k < K; ++k) {
+    uint64_t local = 0ull;
+    int lj = -1;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j)
+      if (((live >> j) & 1u) && (lj < 0 || key[j] > local)) {
+        local = key[j];
+        lj = j;
+      }
+    uint64_t best = local;
+#pragma unroll
+    for (int o = kWave / 2; o >= 1; o >>= 1) {
+      const uint64_t other = __shfl_xor(best, o, kWave);
+      best = other > best ? other : best;
+    }
+    if (lj >= 0 && local == best) live &= ~(1u << lj);   // keys are unique: one lane
+    if (lane == k) my_e = 1023 - (int)(best & 0x3FFull);
+  }
+  const double v = lane < K ? (l64 ? l64[row + my_e] : (double)l32[row + my_e]) : 0.0;
+  const double mx = __shfl(v, 0, kWave);
+  double total = 0.0;
+  if (renorm) {
+    const double ex = lane < K ? exp(v - mx) : 0.0;
+    for (int k = 0; k < K; ++k) total += __shfl(ex, k, kWave);   // slot order
+  } else {
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      if (kWave * j >= E) break;
+      const double part = lane + kWave * j < E ? exp(val[j] - mx) : 0.0;
+      total += wave_sum(part);
+    }
+  }
+  if (lane < K) {
+    idx[(size_t)t * K + lane] = my_e;
+    wout[(size_t)t * K + lane] = (float)(exp(v - mx) / total);
+  }
 }
 
 constexpr int kLastTopkMaxM = 4;
@@ -545,9 +597,22 @@ __global__ void __launch_bounds__(kRouteThreads) k_router_tile(QT W, const float
 int launch_route_parts(const QT* router, const float* x_or_logits, int M, int E, int K, int renorm,
                        int32_t* idx, float* w, float* logits32, double* l64, int* ctr,
                        hipStream_t s) {
+  const dim3 grid_topk((M + kRouteThreads / kWave - 1) / (kRouteThreads / kWave));
+  // the many-token top-K with the fewest key slots per lane that hold E
+  auto topk = [&](const double* l64_, const float* l32_) {
+#define MOEQ_TOPK(P_)                                                                             \
+  hipLaunchKernelGGL(k_topk_wave<P_>, grid_topk, dim3(kRouteThreads), 0, s, l64_, l32_, M, E, K,  \
+                     renorm, idx, w)
+    if (E <= 64) MOEQ_TOPK(1);
+    else if (E <= 128) MOEQ_TOPK(2);
+    else if (E <= 256) MOEQ_TOPK(4);
+    else if (E <= 512) MOEQ_TOPK(8);
+    else MOEQ_TOPK(16);
+#undef MOEQ_TOPK
+  };
+  static_assert(kMaxE <= 16 * kWave, "k_topk_wave holds at most 16 keys per lane");
   if (!router) {
-    hipLaunchKernelGGL(k_topk_rows, dim3(M), dim3(kRouteThreads), 0, s, (const double*)nullptr,
-                       x_or_logits, M, E, K, renorm, idx, w);
+    topk(nullptr, x_or_logits);
     return 0;
   }
   const dim3 grid((E + 3) / 4);
@@ -574,9 +639,7 @@ int launch_route_parts(const QT* router, const float* x_or_logits, int M, int E,
   MOEQ_ROUTER(4)
   MOEQ_ROUTER(2)
 #undef MOEQ_ROUTER
-  if (!last)
-    hipLaunchKernelGGL(k_topk_rows, dim3(M), dim3(kRouteThreads), 0, s, l64, (const float*)nullptr,
-                       M, E, K, renorm, idx, w);
+  if (!last) topk(l64, nullptr);
   return 0;
 }
 
