@@ -356,20 +356,30 @@ __global__ void __launch_bounds__(256) k_combine(const uint16_t* __restrict__ yp
   const int64_t t = (i * 8) / H;
   const int64_t c = i * 8 - t * H;
   float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < K; ++k) {
-    const int64_t p = t * K + k;
-    const int e = idx[p];
-    if (e >= 0 && e < E) {
-      const uint4 v = *reinterpret_cast<const uint4*>(ypair + p * H + c);
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  // the K rows' loads go out together (every pair row exists in the
+  // workspace; an invalid pair's row is read and discarded), then the sums
+  // in slot order
+  constexpr int kB = 8;
+  for (int k0 = 0; k0 < K; k0 += kB) {
+    uint4 v[kB];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s[2 * j] += bf16_to_f32(w[j] & 0xFFFFu);
-        s[2 * j + 1] += bf16_to_f32(w[j] >> 16);
+    for (int j = 0; j < kB; ++j)
+      if (k0 + j < K) v[j] = *reinterpret_cast<const uint4*>(ypair + (t * K + k0 + j) * H + c);
+#pragma unroll
+    for (int j = 0; j < kB; ++j) {
+      if (k0 + j >= K) break;
+      const int e = idx[t * K + k0 + j];
+      if (e >= 0 && e < E) {
+        const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          s[2 * q] += bf16_to_f32(w[q] & 0xFFFFu);
+          s[2 * q + 1] += bf16_to_f32(w[q] >> 16);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 8; ++q) s[q] = __builtin_nanf("");
       }
-    } else {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) s[j] = __builtin_nanf("");
     }
   }
   float4* yo = reinterpret_cast<float4*>(y + t * H + c);
