@@ -102,3 +102,17 @@ def test_gap_filter_is_satisfied_by_generated_tokens():
     small = synth._small_tensors(cfg, 3)
     x = gapped_tokens(cfg, small, 3, 4)[:, 0]
     assert topk_gaps_ok(oracle.qmatvec(small["router"], x), cfg.top_k).all()
+
+
+@pytest.mark.parametrize("E,K,m,renorm", [(200, 16, 300, True), (256, 8, 7, False), (1000, 16, 33, True),
+                                          (1024, 10, 5, False), (513, 1, 64, True), (64, 16, 9, False)])
+def test_route_logits_mode_every_key_width(E, K, m, renorm):
+    # the many-token top-K holds 1, 2, 4, 8 or 16 keys per lane by E; widths,
+    # K up to 16 and the unrenormalized sum over several parts of 64 experts
+    say(f"route logits E={E} K={K} M={m} renorm={renorm}")
+    rng = np.random.default_rng(E * 31 + K)
+    lg = (rng.standard_normal((m, E)) * 2.5).astype(np.float32)
+    idx, w = moeq.moe_route(None, to_dev(lg), E, K, renorm=renorm)
+    ridx, rw, _ = oracle.route(lg.astype(np.float64), K, renorm=renorm)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
