@@ -183,6 +183,7 @@ __global__ void __launch_bounds__(256) k_qmatvec_mx(const uint32_t* __restrict__
 // ---------------------------------------------------------------------------
 constexpr int kRouteThreads = 256;
 constexpr int kMaxE = kMaxExperts;
+constexpr int kLastTopkMaxM = 4;   // tokens of the one-launch router form (k_router)
 
 // Router projection in fp64 (the fp32 dequantized weight widened exactly,
 // fp64 products and sums), one wave per router row and token.  With
@@ -210,28 +211,54 @@ __global__ void __launch_bounds__(kRouteThreads) k_router(QT W, const float* __r
     const uint4* rq = reinterpret_cast<const uint4*>(W.q + (size_t)r * (cols / (32 / BITS)));
     const uint16_t* rs = W.scales + (size_t)r * groups;
     const uint16_t* rb = W.biases + (size_t)r * groups;
-    for (int m = 0; m < M; ++m) {
-      double acc = 0.0;
-      const float* xm = x + (size_t)m * cols;
-      for (int c = lane; c < chunks; c += kWave) {
-        const uint4 v = rq[c];
+    // per lane its chunks lane, lane + 64, ... in order, one fp64 chain per
+    // token (M <= 4); four chunks' loads go out together, and a weight is
+    // dequantized once for all tokens
+    constexpr int kB = 4;
+    double acc[kLastTopkMaxM];
+#pragma unroll
+    for (int m = 0; m < kLastTopkMaxM; ++m) acc[m] = 0.0;
+    for (int c0 = lane; c0 < chunks; c0 += kB * kWave) {
+      uint4 v[kB];
+      float s[kB], b[kB];
+#pragma unroll
+      for (int q = 0; q < kB; ++q) {
+        const int c = min(c0 + q * kWave, chunks - 1);      // clamped: always a valid address
         const int g = group_of(c * kCpc, W.group_size);
-        const float s = bf16_to_f32(rs[g]);
-        const float b = bf16_to_f32(rb[g]);
-        const float* xc = xm + (size_t)c * kCpc;
+        v[q] = rq[c];
+        s[q] = bf16_to_f32(rs[g]);
+        b[q] = bf16_to_f32(rb[g]);
+      }
+#pragma unroll
+      for (int q = 0; q < kB; ++q) {
+        const int c = c0 + q * kWave;
+        if (c >= chunks) break;
 #pragma unroll
         for (int j = 0; j < kCpc; j += 4) {
-          const float4 xv = *reinterpret_cast<const float4*>(xc + j);
-          acc = fma((double)fmaf(s, (float)chunk_code<BITS>(v, j + 0), b), (double)xv.x, acc);
-          acc = fma((double)fmaf(s, (float)chunk_code<BITS>(v, j + 1), b), (double)xv.y, acc);
-          acc = fma((double)fmaf(s, (float)chunk_code<BITS>(v, j + 2), b), (double)xv.z, acc);
-          acc = fma((double)fmaf(s, (float)chunk_code<BITS>(v, j + 3), b), (double)xv.w, acc);
+          double w[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) w[i] = (double)fmaf(s[q], (float)chunk_code<BITS>(v[q], j + i), b[q]);
+#pragma unroll
+          for (int m = 0; m < kLastTopkMaxM; ++m) {
+            if (m < M) {
+              const float4 xv = *reinterpret_cast<const float4*>(x + (size_t)m * cols + (size_t)c * kCpc + j);
+              acc[m] = fma(w[0], (double)xv.x, acc[m]);
+              acc[m] = fma(w[1], (double)xv.y, acc[m]);
+              acc[m] = fma(w[2], (double)xv.z, acc[m]);
+              acc[m] = fma(w[3], (double)xv.w, acc[m]);
+            }
+          }
         }
       }
-      acc = wave_sum(acc);
-      if (lane == 0) {
-        __hip_atomic_store(logits + (size_t)m * rows + r, acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (logits32) logits32[(size_t)m * rows + r] = (float)acc;
+    }
+#pragma unroll
+    for (int m = 0; m < kLastTopkMaxM; ++m) {
+      if (m < M) {
+        const double a = wave_sum(acc[m]);
+        if (lane == 0) {
+          __hip_atomic_store(logits + (size_t)m * rows + r, a, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (logits32) logits32[(size_t)m * rows + r] = (float)a;
+        }
       }
     }
   }
@@ -393,7 +420,6 @@ __global__ void __launch_bounds__(kRouteThreads) k_topk_wave(const double* __res
   }
 }
 
-constexpr int kLastTopkMaxM = 4;
 
 // ---------------------------------------------------------------------------
 // host launchers
