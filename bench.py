@@ -106,6 +106,8 @@ def traffic_for(args, kernel):
     those counters were taken on a different version of the kernel's sources."""
     if args.traffic is not None:
         return args.traffic
+    if getattr(args, "group_size", 0):
+        return None                 # the stored counters are for the workload's own group size
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{args.config}.md")
     if not os.path.exists(path):
         return None
@@ -623,6 +625,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c4_mxfp4", "c5", "c5_4bit", "requant"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (decode)")
+    ap.add_argument("--group-size", type=int, default=0, choices=[0, 32, 64, 128],
+                    help="override the quantization group size of every matrix")
     ap.add_argument("--tokens", type=int, default=0, help="override M (prefill)")
     ap.add_argument("--slots", type=int, default=TOKEN_SLOTS)
     ap.add_argument("--launch-reps", type=int, default=8)
@@ -671,6 +675,10 @@ def main():
         print(json.dumps(out), flush=True)
         return
     cfg = synth.CONFIGS[args.config]
+    if args.group_size:
+        if args.config == "c4_mxfp4":
+            raise SystemExit("--group-size: mxfp4 groups are 32 columns by definition")
+        cfg = synth.scaled(cfg, group_size=args.group_size, name=f"{cfg.name}-gs{args.group_size}")
     if args.config in ("c4", "c4_mxfp4"):
         out = run_prefill(args, cfg)
         host = out.pop("_host")
