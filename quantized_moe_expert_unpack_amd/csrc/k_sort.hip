@@ -7,7 +7,8 @@
 // records its exact row count, so ragged tails of any length are covered (the
 // issue's defect came from narrowing a remaining-row count to 16 bits).
 //
-// Three launches: a histogram (LDS counts per block, one global add per
+// Up to 4096 pairs, one block does it all (k_sort_small); more take three
+// launches: a histogram (LDS counts per block, one global add per
 // (block, expert)), a one-block scan (expert offsets, tile offsets, the tile
 // list, and per-expert cursors initialised to the offsets; it also clears the
 // counts for the next call) and a scatter (LDS ranks per block, one global
@@ -103,11 +104,70 @@ __global__ void __launch_bounds__(kSortThreads) k_scatter(const int32_t* __restr
   }
 }
 
+// Up to kSortChunk pairs: the three phases in one block of 1024 threads (LDS
+// counts with each pair's rank, the scan and tile list, the scatter).  The
+// outputs are those of the three launches; the global counts are not used
+// (they stay zero), nor the cursors.
+__global__ void __launch_bounds__(1024) k_sort_small(const int32_t* __restrict__ idx, int n, int E,
+                                                     int bm, int32_t* __restrict__ offsets,
+                                                     int32_t* __restrict__ tile_off,
+                                                     int32_t* __restrict__ n_tiles,
+                                                     int4* __restrict__ tiles,
+                                                     int32_t* __restrict__ sorted) {
+  __shared__ int sc[1024];
+  __shared__ int st[1024];
+  constexpr int kPer = kSortChunk / 1024;
+  const int tid = threadIdx.x;
+  sc[tid] = 0;
+  __syncthreads();
+  int rank[kPer], ev[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const int p = tid + j * 1024;
+    ev[j] = p < n ? idx[p] : -1;
+    rank[j] = (ev[j] >= 0 && ev[j] < E) ? atomicAdd(&sc[ev[j]], 1) : -1;
+  }
+  __syncthreads();
+  const int c = tid < E ? sc[tid] : 0;
+  st[tid] = (c + bm - 1) / bm;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
+    const int a = tid >= o ? sc[tid - o] : 0;
+    const int b = tid >= o ? st[tid - o] : 0;
+    __syncthreads();
+    sc[tid] += a;
+    st[tid] += b;
+    __syncthreads();
+  }
+  if (tid < E) {
+    const int off = sc[tid] - c;
+    const int toff = st[tid] - (c + bm - 1) / bm;
+    offsets[tid] = off;
+    offsets[tid + 1] = sc[tid];
+    tile_off[tid] = toff;
+    tile_off[tid + 1] = st[tid];
+    for (int j = 0; j * bm < c; ++j) tiles[toff + j] = make_int4(tid, off + j * bm, min(bm, c - j * bm), 0);
+  }
+  if (tid == 0) n_tiles[0] = st[E - 1];
+  // a pair's place: its expert's first row (the exclusive prefix) + its rank
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    if (rank[j] < 0) continue;
+    const int e = ev[j];
+    sorted[(e > 0 ? sc[e - 1] : 0) + rank[j]] = tid + j * 1024;
+  }
+}
+
 int launch_sort_pairs(const int32_t* idx, int n, int E, const GatherWs& ws, hipStream_t s) {
   return launch_sort_pairs_bm(idx, n, E, ws, kGemmBM, s);
 }
 
 int launch_sort_pairs_bm(const int32_t* idx, int n, int E, const GatherWs& ws, int bm, hipStream_t s) {
+  if (n <= kSortChunk) {
+    hipLaunchKernelGGL(k_sort_small, dim3(1), dim3(1024), 0, s, idx, n, E, bm, ws.offsets,
+                       ws.tile_off, ws.n_tiles, ws.tiles, ws.sorted);
+    return 0;
+  }
   const int blocks = (n + kSortChunk - 1) / kSortChunk;
   hipLaunchKernelGGL(k_hist, dim3(blocks), dim3(kSortThreads), 0, s, idx, n, E, ws.counts);
   hipLaunchKernelGGL(k_scan, dim3(1), dim3(1024), 0, s, ws.counts, E, bm, ws.offsets,
