@@ -244,7 +244,7 @@ def run_decode(args, cfg):
     gam2 = ([torch.from_numpy(synth.norm_weight(cfg, l + 1)).to(dev) for l in range(n_layers)]
             if args.post_norm else [None] * n_layers)
     yn = torch.zeros((n_layers, m, H), dtype=torch.float32, device=dev) if args.post_norm else None
-    ws_route = torch.zeros(8 * m * cfg.experts + 4096, dtype=torch.uint8, device=dev)
+    ws_route = moeq.workspace(layers[0], m, K, moeq.PATH_ROUTE, dev)
     ws_dec = moeq.workspace(layers[0], m, K, moeq.PATH_DECODE, dev)
 
     def layer_call(l, t):
@@ -472,7 +472,7 @@ def run_stream(args, cfg):
                      for l in range(n_layers)]).to(dev)
     y = torch.empty((1, cfg.hidden), dtype=torch.float32, device=dev)
     ws_dec = moeq.workspace(caches[0].layer, 1, K, moeq.PATH_DECODE, dev)
-    ws_route = torch.zeros(8 * cfg.experts + 4096, dtype=torch.uint8, device=dev)
+    ws_route = moeq.workspace(caches[0].layer, 1, K, moeq.PATH_ROUTE, dev)
     copied = [0]
     n_warm = max(1, args.warmup)
     # device form: one copy counter per (step, layer), summed after the run

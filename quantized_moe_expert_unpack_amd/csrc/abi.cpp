@@ -231,7 +231,7 @@ int run_expert_forward(const moeq::DecodeLayer& dl, const float* x, const int32_
 // routing counters inside the state block; room for either
 size_t forward_ws_bytes(const moeq::DecodeLayer& dl, int E, int M, int K) {
   const size_t one = moeq::decode_ws_bytes(dl, M < moeq::kFusedMaxM ? M : moeq::kFusedMaxM, K, true);
-  const size_t two = align_up(expert_ws_bytes(dl, M, K)) + align_up(sizeof(double) * (size_t)M * E);
+  const size_t two = align_up(expert_ws_bytes(dl, M, K)) + align_up(moeq::route_ws_bytes(M, E));
   return one > two ? one : two;
 }
 

@@ -185,6 +185,16 @@ constexpr int kRouteThreads = 256;
 constexpr int kMaxE = kMaxExperts;
 constexpr int kLastTopkMaxM = 4;   // tokens of the one-launch router form (k_router)
 
+// splits of the hidden dimension for k_router_mma: enough blocks to fill
+// the chip (16 tokens x 64 rows per block), at most 8
+constexpr int kMaxParts = 8;
+int router_splits(int M, int E) {
+  const int blocks = ((M + 15) / 16) * ((E + 63) / 64);
+  return blocks >= 512 ? 1 : (512 / blocks < kMaxParts ? 512 / blocks : kMaxParts);
+}
+constexpr int kMmaMinM = 16;   // the MFMA router from this many tokens
+
+
 // Router projection in fp64 (the fp32 dequantized weight widened exactly,
 // fp64 products and sums), one wave per router row and token.  With
 // LAST_TOPK the block that finishes last (arrival counter) runs top-K for all
@@ -356,12 +366,16 @@ __global__ void __launch_bounds__(kRouteThreads) k_router_many(QT W, const float
 // (renormalized: the K exponentials summed in slot order; otherwise the
 // partial sums of 64 experts each, added in expert order).  PER keys per
 // lane: E <= 64 * PER.
+// With nparts > 1 the fp64 logits arrive as nparts partial sums (a split
+// reduction dimension, part p at p * M * E) and are added here in part order;
+// l32_out, if given, receives them rounded to fp32.
 template <int PER>
 __global__ void __launch_bounds__(kRouteThreads) k_topk_wave(const double* __restrict__ l64,
                                                              const float* __restrict__ l32, int M,
                                                              int E, int K, int renorm,
                                                              int32_t* __restrict__ idx,
-                                                             float* __restrict__ wout) {
+                                                             float* __restrict__ wout, int nparts,
+                                                             float* __restrict__ l32_out) {
   constexpr int kPer = PER;
   const int lane = threadIdx.x & (kWave - 1);
   const int t = blockIdx.x * (kRouteThreads / kWave) + threadIdx.x / kWave;
@@ -376,7 +390,21 @@ __global__ void __launch_bounds__(kRouteThreads) k_topk_wave(const double* __res
     val[j] = 0.0;
     key[j] = 0ull;
     if (e < E) {
-      val[j] = l64 ? l64[row + e] : (double)l32[row + e];
+      if (l64) {
+        // every part's load first (at most kMaxParts), then the sum in part order
+        double pv[kMaxParts];
+#pragma unroll
+        for (int p = 0; p < kMaxParts; ++p)
+          pv[p] = p < nparts ? l64[(size_t)p * M * E + row + e] : 0.0;
+        double v = pv[0];
+#pragma unroll
+        for (int p = 1; p < kMaxParts; ++p)
+          if (p < nparts) v += pv[p];
+        val[j] = v;
+        if (l32_out) l32_out[row + e] = (float)v;
+      } else {
+        val[j] = (double)l32[row + e];
+      }
       key[j] = route_key(val[j], e);
       live |= 1u << j;
     }
@@ -400,7 +428,14 @@ __global__ void __launch_bounds__(kRouteThreads) k_topk_wave(const double* __res
     if (lj >= 0 && local == best) live &= ~(1u << lj);   // keys are unique: one lane
     if (lane == k) my_e = 1023 - (int)(best & 0x3FFull);
   }
-  const double v = lane < K ? (l64 ? l64[row + my_e] : (double)l32[row + my_e]) : 0.0;
+  // the selected experts' logits from the lanes holding them
+  double v = 0.0;
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) {
+    const double vj = __shfl(val[j], my_e & (kWave - 1), kWave);
+    if ((my_e >> 6) == j) v = vj;
+  }
+  if (lane >= K) v = 0.0;
   const double mx = __shfl(v, 0, kWave);
   double total = 0.0;
   if (renorm) {
@@ -504,7 +539,8 @@ size_t route_ctr_bytes() { return (kRouteCtrBytes + 255) / 256 * 256; }
 
 // [counters][fp64 logits]: the counters sit at the same place for every M
 size_t route_ws_bytes(int M, int E) {
-  return route_ctr_bytes() + ((sizeof(double) * (size_t)M * E + 255) / 256) * 256;
+  const size_t parts = M >= kMmaMinM ? (size_t)router_splits(M, E) : 1;
+  return route_ctr_bytes() + ((sizeof(double) * parts * (size_t)M * E + 255) / 256) * 256;
 }
 
 int launch_route(const QT* router, const float* x_or_logits, int M, int E, int K, int renorm,
@@ -522,6 +558,78 @@ int launch_route(const QT* router, const float* x_or_logits, int M, int E, int K
 // arithmetic is k_router's: each fp32 dequantized weight widened exactly,
 // fp64 products and sums (per lane over its chunks in order, then the wave).
 // H <= 4096 (x of kRtTok tokens within 64 KB).
+// Router projection for many tokens on the fp64 matrix cores
+// (v_mfma_f64_16x16x4f64): a wave takes 16 tokens x 16 router rows over one
+// split of the hidden dimension, in 64-column chunks.  Lane (i, q), i = lane
+// % 16, q = lane / 16, feeds token i's x and row i's weights for columns
+// 64c + 16q + s, s = 0..15, one column per instruction, the weight the fp32
+// scale * code + bias widened exactly (as in the other router kernels); the
+// products are exact in fp64 and summed in fp64.  Each split's sums go to
+// part[split][token][row]; the top-K kernel adds the splits in order.
+// H % 64 == 0.
+template <int BITS>
+__global__ void __launch_bounds__(kRouteThreads) k_router_mma(QT W, const float* __restrict__ x,
+                                                              int M, int nsplit,
+                                                              double* __restrict__ part) {
+  typedef double f64x4 __attribute__((ext_vector_type(4)));
+  const int lane = threadIdx.x & (kWave - 1), wid = threadIdx.x / kWave;
+  const int rows = W.rows, H = W.cols;
+  const int n0 = (blockIdx.x * (kRouteThreads / kWave) + wid) * 16;   // the wave's router rows
+  const int m0 = blockIdx.y * 16;                                     // its tokens
+  const int sp = blockIdx.z;
+  const int nchunk = H / 64;
+  const int c0 = sp * nchunk / nsplit, c1 = (sp + 1) * nchunk / nsplit;
+  const int i = lane & 15, q = lane >> 4;
+  // rows and tokens past the ends re-read the last valid one (never stored)
+  const int r = min(n0 + i, rows - 1);
+  const int t = min(m0 + i, M - 1);
+  const float* xt = x + (size_t)t * H;
+  const uint32_t* wq = W.q + (size_t)r * (H / (32 / BITS));
+  const uint16_t* ws = W.scales + (size_t)r * (H / W.group_size);
+  const uint16_t* wb = W.biases + (size_t)r * (H / W.group_size);
+  const int gsh = __builtin_ctz((unsigned)W.group_size);
+  f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+  // a chunk's operands: the lane's 16 columns (one group) of codes, its
+  // scale and bias, and the token's 16 x values; the next chunk's are loaded
+  // while this one's products run
+  struct Chunk {
+    uint32_t cw[BITS / 2];
+    uint32_t sb;
+    float4 xv[4];
+  };
+  auto load = [&](int c, Chunk& C) {
+    const int k0 = min(c, c1 - 1) * 64 + 16 * q;   // clamped: always a valid address
+#pragma unroll
+    for (int u = 0; u < BITS / 2; ++u) C.cw[u] = wq[k0 / (32 / BITS) + u];
+    C.sb = (uint32_t)ws[k0 >> gsh] | ((uint32_t)wb[k0 >> gsh] << 16);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) C.xv[u] = reinterpret_cast<const float4*>(xt + k0)[u];
+  };
+  Chunk cur, nxt;
+  if (c0 < c1) load(c0, cur);
+  for (int c = c0; c < c1; ++c) {
+    load(c + 1, nxt);
+    const float sc = bf16_to_f32(cur.sb & 0xFFFFu), bi = bf16_to_f32(cur.sb >> 16);
+#pragma unroll
+    for (int s2 = 0; s2 < 16; ++s2) {
+      constexpr int kPer = 32 / BITS;
+      const uint32_t code = (cur.cw[s2 / kPer] >> (BITS * (s2 % kPer))) & ((1u << BITS) - 1u);
+      const double w = (double)fmaf(sc, (float)code, bi);
+      const float4 x4v = cur.xv[s2 / 4];
+      const float xs = (s2 & 3) == 0 ? x4v.x : (s2 & 3) == 1 ? x4v.y : (s2 & 3) == 2 ? x4v.z : x4v.w;
+      acc = __builtin_amdgcn_mfma_f64_16x16x4f64((double)xs, w, acc, 0, 0, 0);
+    }
+    cur = nxt;
+  }
+  // accumulator: register v of lane (i, q) holds token 4v + q of row i (the
+  // instruction's output rows interleave over the four lane groups)
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int tok = m0 + 4 * v + q, row = n0 + i;
+    if (tok < M && row < rows) part[((size_t)sp * M + tok) * rows + row] = acc[v];
+  }
+}
+
 constexpr int kRtTok = 4;
 constexpr int kRtRows = 16;
 template <int BITS>
@@ -625,10 +733,10 @@ int launch_route_parts(const QT* router, const float* x_or_logits, int M, int E,
                        hipStream_t s) {
   const dim3 grid_topk((M + kRouteThreads / kWave - 1) / (kRouteThreads / kWave));
   // the many-token top-K with the fewest key slots per lane that hold E
-  auto topk = [&](const double* l64_, const float* l32_) {
+  auto topk = [&](const double* l64_, const float* l32_, int nparts, float* l32_out) {
 #define MOEQ_TOPK(P_)                                                                             \
   hipLaunchKernelGGL(k_topk_wave<P_>, grid_topk, dim3(kRouteThreads), 0, s, l64_, l32_, M, E, K,  \
-                     renorm, idx, w)
+                     renorm, idx, w, nparts, l32_out)
     if (E <= 64) MOEQ_TOPK(1);
     else if (E <= 128) MOEQ_TOPK(2);
     else if (E <= 256) MOEQ_TOPK(4);
@@ -638,7 +746,7 @@ int launch_route_parts(const QT* router, const float* x_or_logits, int M, int E,
   };
   static_assert(kMaxE <= 16 * kWave, "k_topk_wave holds at most 16 keys per lane");
   if (!router) {
-    topk(nullptr, x_or_logits);
+    topk(nullptr, x_or_logits, 1, nullptr);
     return 0;
   }
   const dim3 grid((E + 3) / 4);
@@ -649,11 +757,18 @@ int launch_route_parts(const QT* router, const float* x_or_logits, int M, int E,
   const bool tile = W.cols <= 4096;
   const size_t tile_lds = sizeof(float) * kRtTok * (size_t)W.cols;
   const dim3 grid_tile((E + kRtRows - 1) / kRtRows, (M + kRtTok - 1) / kRtTok);
+  // the fp64 matrix cores from 16 tokens (hidden a multiple of 64)
+  const bool mma = !last && M >= kMmaMinM && W.cols % 64 == 0;
+  const int nsplit = mma ? min(router_splits(M, E), W.cols / 64) : 1;
+  const dim3 grid_mma((E + 63) / 64, (M + 15) / 16, nsplit);
 #define MOEQ_ROUTER(B_)                                                                           \
   if (W.bits == B_) {                                                                             \
     if (last)                                                                                     \
       hipLaunchKernelGGL((k_router<B_, true>), grid, dim3(kRouteThreads), 0, s, W, x_or_logits, M, \
                          K, renorm, l64, ctr, logits32, idx, w);                                   \
+    else if (mma)                                                                                 \
+      hipLaunchKernelGGL((k_router_mma<B_>), grid_mma, dim3(kRouteThreads), 0, s, W, x_or_logits, \
+                         M, nsplit, l64);                                                          \
     else if (tile)                                                                                \
       hipLaunchKernelGGL((k_router_tile<B_>), grid_tile, dim3(kRouteThreads), tile_lds, s, W,     \
                          x_or_logits, M, l64, logits32);                                          \
@@ -665,7 +780,7 @@ int launch_route_parts(const QT* router, const float* x_or_logits, int M, int E,
   MOEQ_ROUTER(4)
   MOEQ_ROUTER(2)
 #undef MOEQ_ROUTER
-  if (!last) topk(l64, nullptr);
+  if (!last) topk(l64, nullptr, mma ? nsplit : 1, mma ? logits32 : nullptr);
   return 0;
 }
 

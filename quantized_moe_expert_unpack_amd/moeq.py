@@ -284,7 +284,12 @@ def moe_route(gate: Optional[QTensor], x_or_logits: torch.Tensor, experts: int, 
     if w is None:
         w = torch.empty((m, k), dtype=torch.float32, device=dev)
     if gate is not None and ws is None:
-        n = 8 * m * experts + 4096
+        # the size the library asks for (a layer struct holding only the router)
+        only = MoEStruct(gate.struct(), _empty_qt(), _empty_qt(), _empty_qt(), 0,
+                         _empty_qt(), _empty_qt(), _empty_qt(), _empty_qt())
+        n = int(lib().moe_workspace_size(ctypes.byref(only), m, k, PATH_ROUTE))
+        if n == 0:
+            raise MoeqError(-5, "moe_workspace_size")
         ws = torch.zeros(n, dtype=torch.uint8, device=dev)
     gs = ctypes.byref(gate.struct()) if gate is not None else None
     _check(lib().moe_route(gs, _ptr(x_or_logits), m, experts, k, 1 if renorm else 0, _ptr(idx),
