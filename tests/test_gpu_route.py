@@ -42,10 +42,13 @@ def test_route_batched_m64_and_logits_out():
     assert np.abs(lo.cpu().numpy() - lg).max() <= 1e-5 * np.abs(lg).max()
 
 
-@pytest.mark.parametrize("bits,hidden,m", [(8, 4608, 20), (4, 4608, 9), (2, 4096, 37), (8, 160, 13)])
+@pytest.mark.parametrize("bits,hidden,m", [(8, 4608, 20), (4, 4608, 9), (2, 4096, 37), (8, 160, 13),
+                                           (4, 2048, 24), (8, 256, 8200)])
 def test_route_many_tokens_all_router_kernels(bits, hidden, m):
-    # hidden > 4096 takes the one-row-per-wave kernel, the rest the LDS-staged
-    # tile kernel (ragged token and row blocks, hidden off the 64-column grid)
+    # 16 tokens or more with hidden % 64 == 0 take the fp64 MFMA kernel (split
+    # hidden dimension; 8200 tokens fill the chip unsplit); otherwise the
+    # LDS-staged tile kernel (hidden <= 4096: 160 columns, off the 64-column
+    # grid) or the one-row-per-wave kernel (wider); ragged token and row blocks
     cfg = synth.scaled(synth.CONFIGS["c1"], hidden=hidden, experts=40, top_k=4, router_bits=bits,
                        group_size=32 if hidden % 64 else 64, seed=95 + bits)
     small = synth._small_tensors(cfg, 0)
