@@ -322,3 +322,21 @@ def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(moeq, "LIB_PATH", "/nonexistent/libmoeq.so")
     with pytest.raises(RuntimeError, match="no fallback"):
         moeq.lib()
+
+
+def test_route_workspace_covers_the_split_router_partials():
+    # from 16 tokens the router may split the hidden dimension into up to 8
+    # parts, each an fp64 [M][E] block in the workspace; few row/token blocks
+    # mean the full 8 parts, a chip-filling grid means one
+    ws = moeq.lib().moe_workspace_size
+
+    def route_bytes(M, E):
+        only = moeq.MoEStruct(_qt(8, 1, E, 4096), moeq._empty_qt(), moeq._empty_qt(), moeq._empty_qt(), 0,
+                              moeq._empty_qt(), moeq._empty_qt(), moeq._empty_qt(), moeq._empty_qt())
+        return ws(ctypes.byref(only), M, 4, moeq.PATH_ROUTE)
+
+    assert route_bytes(64, 512) >= 8 * 64 * 512 * 8        # 32 blocks: 8 parts
+    assert route_bytes(15, 512) >= 15 * 512 * 8             # below 16 tokens: one part
+    assert route_bytes(15, 512) < 2 * 15 * 512 * 8
+    assert route_bytes(8200, 40) >= 8200 * 40 * 8           # 513 blocks: one part
+    assert route_bytes(8200, 40) < 2 * 8200 * 40 * 8
