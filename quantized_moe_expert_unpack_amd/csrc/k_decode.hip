@@ -167,36 +167,6 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 
 
 // ------------------------------------------------------------------ R unit
-// 64-bit maximum across the wave, left in every lane (exchange steps as in
-// wave_sum_d; the maximum is indifferent to the mirrors' lane order)
-template <int M>
-__device__ __forceinline__ uint64_t xmax_u64(uint64_t v) {
-  uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
-  if constexpr (M >= 16) {
-    const auto rl = M == 32 ? __builtin_amdgcn_permlane32_swap(lo, lo, false, false)
-                            : __builtin_amdgcn_permlane16_swap(lo, lo, false, false);
-    const auto rh = M == 32 ? __builtin_amdgcn_permlane32_swap(hi, hi, false, false)
-                            : __builtin_amdgcn_permlane16_swap(hi, hi, false, false);
-    const uint64_t a = ((uint64_t)rh[0] << 32) | rl[0];
-    const uint64_t b = ((uint64_t)rh[1] << 32) | rl[1];
-    return a > b ? a : b;
-  } else {
-    constexpr int ctrl = M == 1 ? 0xB1 : M == 2 ? 0x4E : M == 4 ? 0x141 : 0x140;
-    lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)lo, ctrl, 0xF, 0xF, false);
-    hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)hi, ctrl, 0xF, 0xF, false);
-    const uint64_t w = ((uint64_t)hi << 32) | lo;
-    return v > w ? v : w;
-  }
-}
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-  v = xmax_u64<32>(v);
-  v = xmax_u64<16>(v);
-  v = xmax_u64<8>(v);
-  v = xmax_u64<4>(v);
-  v = xmax_u64<2>(v);
-  return xmax_u64<1>(v);
-}
-
 // top-K of at most 64*PER keys by one wave, keys held in registers: K rounds
 // of a wave maximum, the owner of each winner dropping it (keys are unique)
 template <int PER>

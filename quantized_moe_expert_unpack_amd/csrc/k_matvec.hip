@@ -419,12 +419,7 @@ __global__ void __launch_bounds__(kRouteThreads) k_topk_wave(const double* __res
         local = key[j];
         lj = j;
       }
-    uint64_t best = local;
-#pragma unroll
-    for (int o = kWave / 2; o >= 1; o >>= 1) {
-      const uint64_t other = __shfl_xor(best, o, kWave);
-      best = other > best ? other : best;
-    }
+    const uint64_t best = wave_max_u64(local);
     if (lj >= 0 && local == best) live &= ~(1u << lj);   // keys are unique: one lane
     if (lane == k) my_e = 1023 - (int)(best & 0x3FFull);
   }
