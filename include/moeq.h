@@ -68,7 +68,9 @@ typedef enum moeq_status {
   MOEQ_ERR_WORKSPACE = -8,   /* workspace missing or smaller than required      */
   MOEQ_ERR_UNSUPPORTED = -9, /* valid request outside what this build computes  */
   MOEQ_ERR_LAUNCH = -10,     /* the HIP runtime rejected a kernel launch        */
-  MOEQ_ERR_HOST_MEMORY = -11 /* host memory not pinned and mapped for the device */
+  MOEQ_ERR_HOST_MEMORY = -11, /* host memory not pinned and mapped for the device */
+  MOEQ_ERR_TIMEOUT = -12     /* a bounded wait inside a decode launch gave up
+                                (reported by moe_workspace_status)              */
 } moeq_status;
 
 /* One quantized matrix [rows][cols], or a stack of `batch` such matrices laid
@@ -294,6 +296,29 @@ int moe_forward_norm(const moeq_moe *L, const float *x, int32_t M, int32_t K, in
                      const float *post_norm_w, float *y_norm, void *ws, size_t ws_bytes,
                      moeq_stream_t stream);
 
+/* moe_workspace_status: report, then clear, the error word of a decode-family
+ * workspace (one sized for MOEQ_PATH_DECODE, MOEQ_PATH_FORWARD or
+ * MOEQ_PATH_FORWARD_NORM).
+ * The decode launches of moe_expert_forward, moe_forward and moe_forward_norm
+ * hand data from one workgroup of the grid to another (routing result, h,
+ * the shared gate); every such wait is bounded, and one that runs out of spins
+ * gives up instead of hanging the GPU and sets a bit in this word.  The calls
+ * whose waits gave up have wrong outputs, and the word stays set until this
+ * call clears it.
+ *   ws         : the workspace (device, 256-byte aligned)
+ *   status_out : device int32 [2], 16-byte aligned: [0] = MOEQ_OK or
+ *                MOEQ_ERR_TIMEOUT, [1] = the raw bits (1 ready flag, 2 routing
+ *                result, 4 router logits, 8 h or shared gate)
+ * One small kernel on `stream`, ordered after the work queued before it (no
+ * memset node: the call can be captured in a graph).  The host return value
+ * only says whether that kernel was queued; the status itself is in
+ * status_out once the stream reaches it.  Workspaces of the other paths hold
+ * no error word: do not pass them.
+ * Defines: no passage of the pages; it reports the bounded cross-workgroup
+ * waits this library uses in place of the pages' one-command-buffer-per-stage
+ * pipeline (flash-moe-inference skill page, per-layer pipeline). */
+int moe_workspace_status(void *ws, int32_t *status_out, moeq_stream_t stream);
+
 /* moe_gather_qmm: the expert part for many bf16 tokens (prefill).  Pairs
  * (token, slot) are sorted by expert on the device; per expert the gathered
  * rows run through a bf16 MFMA gate/up GEMM with a SwiGLU epilogue (h kept in
@@ -310,9 +335,12 @@ int moe_gather_qmm(const moeq_moe *L, const uint16_t *x_bf16, const int32_t *top
 /* gather_qmm: one projection per row, the weight picked per row:
  *   out[i] = x[i] @ deq(W[rhs_idx[i]])^T       (transpose=True)
  *   W : stacked [E][N][Kd];  x_bf16 : bf16 [n][Kd];  rhs_idx : int32 [n] in [0, E)
- *   sorted : nonzero if rhs_idx is non-decreasing (rows are then used in
- *            place); otherwise rows are grouped by expert on the device
- *   out : fp32 [n][N]
+ *   sorted : nonzero if rhs_idx is non-decreasing: the rows are then used in
+ *            place with no sort, expert e taking the run of rows that holds
+ *            index e; a row outside the run of its own index (indices that
+ *            were not in fact non-decreasing) comes out NaN.  0: the rows are
+ *            grouped by expert on the device first.
+ *   out : fp32 [n][N]; rows whose index is outside [0, E) come out NaN
  * Defines: mx.gather_qmm(x, w, scales, biases, rhs_indices, transpose=True,
  * sorted_indices) of the ml-explore/mlx issue #3856 minimal repro. */
 int gather_qmm(const moeq_qtensor *W, const uint16_t *x_bf16, const int32_t *rhs_idx,

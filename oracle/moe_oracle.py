@@ -99,6 +99,7 @@ __all__ = [
     "gather_qmm",
     "bf16_round",
     "requant_2bit",
+    "requant_2bit_fast",
     "expert_bytes",
 ]
 
@@ -470,6 +471,80 @@ def requant_2bit(qt: dict) -> dict:
             if step != 0:
                 q2[r, g] = [round((wj - lo) / step) for wj in w]
     return {"q": _pack_2bit(q2.reshape(lead + (cols,))),
+            "scales": s2.reshape(lead + (ng,)), "biases": b2.reshape(lead + (ng,)),
+            "batch": qt.get("batch", 1), "rows": qt["rows"], "cols": cols, "bits": 2,
+            "group_size": gs}
+
+
+def _bf16_bits_of_exact_f64(v) -> np.ndarray:
+    """bf16 bit patterns of fp64 values that hold exact results, each rounded
+    once to 8 significant bits (nearest, ties to even) from its full fp64
+    significand; zero maps to +0 and anything that would leave bf16's normal
+    range raises, as in ``bf16_round``."""
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    u = v.view(np.uint64)
+    lsb = (u >> np.uint64(45)) & np.uint64(1)
+    r = ((u + np.uint64((1 << 44) - 1) + lsb) >> np.uint64(45)) << np.uint64(45)
+    rv = r.view(np.float64)
+    ra = np.abs(rv)
+    nz = v != 0
+    if np.any(nz & ((ra < 2.0 ** -126) | (ra > float(np.float32(3.3895314e38))))):
+        raise ValueError("a value is outside bf16's normal range")
+    bits = (rv.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return np.where(nz, bits, np.uint16(0))
+
+
+def requant_2bit_fast(qt: dict) -> dict:
+    """``requant_2bit`` with the same results, reached by integer arithmetic
+    on the codes so it can run over whole expert stacks.
+
+    In one group the weights are ``w_j = s*q_j + b``.  For ``s > 0`` the
+    smallest weight belongs to the smallest code and for ``s < 0`` to the
+    largest; call that code ``q_lo`` and ``D = q_max - q_min``.  Then
+    ``lo = s*q_lo + b``, ``step = |s|*D/3`` and the position of ``w_j`` on the
+    grid is ``(w_j - lo)/step = 3*|q_j - q_lo|/D``: a ratio of small integers,
+    rounded to the nearest integer with ties to even.  A group with ``s == 0``
+    or ``D == 0`` has no spread and takes code 0.  The stored scale is
+    ``|s|*D/3`` and the stored bias ``lo``, each rounded once to bf16: ``|s|*D``
+    and ``s*q_lo`` are exact in fp64 (at most 16 significant bits), the
+    division by three is rounded once in fp64 and its binary expansion never
+    falls on a bf16 tie; the sum ``s*q_lo + b`` is checked to be exact in fp64
+    and any group where it is not is rounded from the exact rational with
+    ``bf16_round``.
+    """
+    bits, gs, cols = int(qt["bits"]), int(qt["group_size"]), int(qt["cols"])
+    if bits not in (4, 8):
+        raise ValueError("the source must be 4- or 8-bit")
+    if gs not in (64, 128):
+        raise ValueError("2-bit groups are 64 or 128 columns")
+    codes = unpack_codes(qt["q"], bits, cols)
+    lead = codes.shape[:-1]
+    ng = cols // gs
+    codes = codes.reshape(-1, ng, gs).astype(np.int32)
+    s_in = bf16_bits_to_f32(qt["scales"]).reshape(-1, ng).astype(np.float64)
+    b_in = bf16_bits_to_f32(qt["biases"]).reshape(-1, ng).astype(np.float64)
+    qmin = codes.min(axis=-1)
+    qmax = codes.max(axis=-1)
+    D = qmax - qmin
+    q_lo = np.where(s_in < 0, qmax, qmin)
+    flat = (s_in == 0) | (D == 0)
+    Dd = np.where(D == 0, 1, D)[..., None]
+    twice = 6 * np.abs(codes - q_lo[..., None]) + Dd    # 2 * (3 d / D + 1/2) * D
+    k = twice // (2 * Dd)                                # round half up ...
+    tie = twice % (2 * Dd) == 0
+    k = np.where(tie & (k % 2 == 1), k - 1, k)          # ... then ties to even
+    k = np.where(flat[..., None], 0, k).astype(np.uint8)
+    step = np.abs(s_in) * D / 3.0
+    prod = s_in * q_lo
+    lo = prod + b_in
+    bp = lo - prod                                       # two-sum: lo is exact iff err == 0
+    err = (prod - (lo - bp)) + (b_in - bp)
+    lo = lo + 0.0                                        # -0 -> +0, as the exact rational
+    s2 = _bf16_bits_of_exact_f64(step)
+    b2 = _bf16_bits_of_exact_f64(np.where(err == 0, lo, 0.0))
+    for r, g in zip(*np.nonzero(err != 0)):
+        b2[r, g] = bf16_round(Fraction(float(s_in[r, g])) * int(q_lo[r, g]) + Fraction(float(b_in[r, g])))
+    return {"q": _pack_2bit(k.reshape(lead + (cols,))),
             "scales": s2.reshape(lead + (ng,)), "biases": b2.reshape(lead + (ng,)),
             "batch": qt.get("batch", 1), "rows": qt["rows"], "cols": cols, "bits": 2,
             "group_size": gs}

@@ -261,6 +261,7 @@ const char* moeq_status_string(int status) {
     case MOEQ_ERR_UNSUPPORTED: return "unsupported combination";
     case MOEQ_ERR_LAUNCH: return "kernel launch failed";
     case MOEQ_ERR_HOST_MEMORY: return "host memory is not pinned and mapped for the device";
+    case MOEQ_ERR_TIMEOUT: return "a bounded wait inside a decode launch gave up (outputs wrong)";
     default: return "unknown status";
   }
 }
@@ -646,6 +647,14 @@ int moe_stream_experts_device(moeq_slot_cache_dev* C, const int32_t* topk_idx, i
   return launch_status();
 }
 
+int moe_workspace_status(void* ws, int32_t* status_out, moeq_stream_t stream) {
+  if (!ws || !status_out) return MOEQ_ERR_NULL_PTR;
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOEQ_ERR_ALIGN;
+  if (!aligned16(status_out)) return MOEQ_ERR_ALIGN;
+  moeq::launch_ws_status(ws, status_out, MOEQ_ERR_TIMEOUT, (hipStream_t)stream);
+  return launch_status();
+}
+
 int moe_gather_qmm(const moeq_moe* L, const uint16_t* x_bf16, const int32_t* topk_idx,
                    const float* topk_w, int32_t M, int32_t K, float* y, void* ws, size_t ws_bytes,
                    moeq_stream_t stream) {
@@ -677,7 +686,6 @@ int moe_gather_qmm(const moeq_moe* L, const uint16_t* x_bf16, const int32_t* top
 
 int gather_qmm(const moeq_qtensor* W, const uint16_t* x_bf16, const int32_t* rhs_idx, int32_t n,
                int32_t sorted, float* out, void* ws, size_t ws_bytes, moeq_stream_t stream) {
-  (void)sorted;  // both cases group rows on the device; sorted input keeps its order
   int st = check_qt(W, -1, -1, -1);
   if (st) return st;
   if (W->batch > kMaxE) return MOEQ_ERR_SHAPE;
@@ -694,9 +702,12 @@ int gather_qmm(const moeq_qtensor* W, const uint16_t* x_bf16, const int32_t* rhs
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOEQ_ERR_ALIGN;
   gather_ws(reinterpret_cast<char*>(ws), W->batch, n, 0, 0, false, &g);
   hipStream_t s = (hipStream_t)stream;
-  moeq::launch_sort_pairs(rhs_idx, n, W->batch, g, s);
+  if (sorted)   // rows in place, each expert's run of rows is its tiles
+    moeq::launch_runs(rhs_idx, n, W->batch, g, s);
+  else
+    moeq::launch_sort_pairs(rhs_idx, n, W->batch, g, s);
   moeq::launch_gemm_plain(to_qt(*W), x_bf16, out, g, n, s);
-  moeq::launch_mark_invalid_rows(rhs_idx, n, W->batch, W->rows, out, s);
+  moeq::launch_mark_invalid_rows(rhs_idx, n, W->batch, W->rows, sorted ? g.offsets : nullptr, out, s);
   return launch_status();
 }
 

@@ -568,8 +568,7 @@ int launch_batch_forward(const DecodeLayer& L, const float* x, const int32_t* id
   const int cpl = b_cpl(L.H, b);
 #define MOEQ_BG(B_, C_, R_)                                                                   \
   if (b == B_ && cpl == C_) {                                                                \
-    (void)hipFuncSetAttribute((const void*)k_bgate<B_, C_, R_>,                              \
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lg);           \
+    MOEQ_ALLOW_FULL_LDS((k_bgate<B_, C_, R_>), lg);                                            \
     hipLaunchKernelGGL((k_bgate<B_, C_, R_>), gg, dim3(kBThreads), lg, s, L, B, M, K, x);    \
   }
   MOEQ_BG(8, 1, 2) MOEQ_BG(8, 2, 1) MOEQ_BG(8, 4, 1) MOEQ_BG(4, 1, 2) MOEQ_BG(4, 2, 1)
@@ -583,8 +582,7 @@ int launch_batch_forward(const DecodeLayer& L, const float* x, const int32_t* id
   const size_t ld = bdown_lds(L);
 #define MOEQ_BD(B_, L_, N_)                                                                 \
   if (b == B_ && lpr == L_ && ncl == N_) {                                                 \
-    (void)hipFuncSetAttribute((const void*)k_bdown<B_, L_, N_>,                            \
-                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)ld);         \
+    MOEQ_ALLOW_FULL_LDS((k_bdown<B_, L_, N_>), ld);                                            \
     hipLaunchKernelGGL((k_bdown<B_, L_, N_>), gd, dim3(kBThreads), ld, s, L, B, M, K, w);  \
   }
 #define MOEQ_BD_B(B_) MOEQ_BD(B_, 8, 1) MOEQ_BD(B_, 16, 1) MOEQ_BD(B_, 32, 1) MOEQ_BD(B_, 64, 1) \

@@ -1016,6 +1016,21 @@ __global__ void __launch_bounds__(kThreads)
   else down_unit<BITS, DCH, FUSED>(L, P, idx, wts, residual, y, u - P.g_units);
 }
 
+// The error word (the state block's first int, where every bounded wait of
+// the decode launches records a timeout) out to the caller, then cleared.
+__global__ void k_ws_status(int* word, int32_t* out, int timeout_status) {
+  const int v = ld_coh_i(word);
+  out[0] = v ? timeout_status : 0;
+  out[1] = v;
+  st_coh_i(word, 0);
+}
+
+int launch_ws_status(void* ws, int32_t* out, int timeout_status, hipStream_t s) {
+  hipLaunchKernelGGL(k_ws_status, dim3(1), dim3(1), 0, s, reinterpret_cast<int*>(ws), out,
+                     timeout_status);
+  return 0;
+}
+
 DecState dec_state(const DecodeLayer& L, int K, void* ws) {
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   DecState D{};

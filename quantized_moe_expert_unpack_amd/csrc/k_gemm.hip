@@ -387,11 +387,14 @@ __global__ void __launch_bounds__(256) k_combine(const uint16_t* __restrict__ yp
   yo[1] = make_float4(s[4], s[5], s[6], s[7]);
 }
 
+// rows whose expert index is out of range, and with `runs` (rows used in
+// place: sorted indices) rows outside their expert's run, come out NaN
 __global__ void __launch_bounds__(256) k_mark_invalid(const int32_t* __restrict__ idx, int n, int E,
-                                                      int N, float* __restrict__ out) {
+                                                      int N, const int32_t* __restrict__ runs,
+                                                      float* __restrict__ out) {
   const int row = blockIdx.x;
   const int e = idx[row];
-  if (e >= 0 && e < E) return;
+  if (e >= 0 && e < E && (!runs || (runs[e] <= row && row < runs[e + 1]))) return;
   for (int c = threadIdx.x; c < N; c += blockDim.x) out[(size_t)row * N + c] = __builtin_nanf("");
 }
 
@@ -400,8 +403,7 @@ static void gemm_launch(dim3 grid, hipStream_t s, const QT& W, const QT& W2, int
                         const uint16_t* A, int a_div, const GatherWs& ws, const float* wts,
                         void* out, int ntn) {
   // two LDS stages of 147,456 bytes: above the default dynamic limit
-  (void)hipFuncSetAttribute((const void*)k_gqmm<BITS, MODE, MX>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds);
+  MOEQ_ALLOW_FULL_LDS((k_gqmm<BITS, MODE, MX>), kGemmLds);
   hipLaunchKernelGGL((k_gqmm<BITS, MODE, MX>), grid, dim3(kThreads), kGemmLds, s, W, W2, N, Kd, A,
                      a_div, ws, wts, out, ntn);
 }
@@ -447,8 +449,9 @@ int launch_gemm_plain(const QT& W, const uint16_t* x, float* out, const GatherWs
   return 0;
 }
 
-int launch_mark_invalid_rows(const int32_t* idx, int n, int E, int N, float* out, hipStream_t s) {
-  hipLaunchKernelGGL(k_mark_invalid, dim3(n), dim3(256), 0, s, idx, n, E, N, out);
+int launch_mark_invalid_rows(const int32_t* idx, int n, int E, int N, const int32_t* runs, float* out,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(k_mark_invalid, dim3(n), dim3(256), 0, s, idx, n, E, N, runs, out);
   return 0;
 }
 

@@ -158,6 +158,78 @@ __global__ void __launch_bounds__(1024) k_sort_small(const int32_t* __restrict__
   }
 }
 
+// Indices already non-decreasing (gather_qmm with sorted indices): the rows
+// stay where they are (sorted[i] = i) and expert e owns the run of rows
+// [offsets[e], offsets[e+1]).  Thread i in [0, n] looks at the step from index
+// i-1 to index i (an index below 0 reads as -1, one at or above E as E, and
+// the two ends as -1 and E): each expert that the step passes starts its run
+// at row i.  For non-decreasing indices every offset is written exactly once;
+// otherwise some are written by several threads, which k_scan_runs and the
+// run check of k_mark_invalid make harmless.
+__global__ void __launch_bounds__(kSortThreads) k_runs(const int32_t* __restrict__ idx, int n, int E,
+                                                       int32_t* __restrict__ offsets,
+                                                       int32_t* __restrict__ sorted) {
+  const int i = blockIdx.x * kSortThreads + threadIdx.x;
+  if (i > n) return;
+  auto clamp_e = [E](int v) { return v < 0 ? -1 : (v >= E ? E : v); };
+  const int prev = i > 0 ? clamp_e(idx[i - 1]) : -1;
+  const int cur = i < n ? clamp_e(idx[i]) : E;
+  for (int e = prev + 1; e <= cur; ++e) offsets[e] = i;
+  if (i < n) sorted[i] = i;
+}
+
+// one block of 1024 threads, E <= 1024: the run starts made non-decreasing (a
+// running maximum: with non-decreasing indices they already are), then the
+// tile list of k_scan from the run lengths
+__global__ void __launch_bounds__(1024) k_scan_runs(int32_t* __restrict__ offsets, int E, int bm,
+                                                    int32_t* __restrict__ tile_off,
+                                                    int32_t* __restrict__ n_tiles,
+                                                    int4* __restrict__ tiles) {
+  __shared__ int so[1024];
+  __shared__ int st[1024];
+  __shared__ int s_end;
+  const int e = threadIdx.x;
+  so[e] = e < E ? offsets[e] : 0;
+  if (e == 0) s_end = offsets[E];
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // inclusive running maximum
+    const int a = e >= o ? so[e - o] : 0;
+    __syncthreads();
+    so[e] = max(so[e], a);
+    __syncthreads();
+  }
+  const int last = max(s_end, so[E - 1]);
+  const int start = so[e];
+  const int c = e < E ? (e + 1 < E ? so[e + 1] : last) - start : 0;
+  st[e] = (c + bm - 1) / bm;
+  __syncthreads();
+  for (int o = 1; o < 1024; o <<= 1) {  // Hillis-Steele inclusive scan
+    const int b = e >= o ? st[e - o] : 0;
+    __syncthreads();
+    st[e] += b;
+    __syncthreads();
+  }
+  if (e < E) {
+    const int toff = st[e] - (c + bm - 1) / bm;
+    offsets[e] = start;
+    tile_off[e] = toff;
+    tile_off[e + 1] = st[e];
+    for (int j = 0; j * bm < c; ++j) tiles[toff + j] = make_int4(e, start + j * bm, min(bm, c - j * bm), 0);
+  }
+  if (e == 0) {
+    offsets[E] = last;
+    n_tiles[0] = st[E - 1];
+  }
+}
+
+int launch_runs(const int32_t* idx, int n, int E, const GatherWs& ws, hipStream_t s) {
+  const int blocks = (n + 1 + kSortThreads - 1) / kSortThreads;
+  hipLaunchKernelGGL(k_runs, dim3(blocks), dim3(kSortThreads), 0, s, idx, n, E, ws.offsets, ws.sorted);
+  hipLaunchKernelGGL(k_scan_runs, dim3(1), dim3(1024), 0, s, ws.offsets, E, kGemmBM, ws.tile_off,
+                     ws.n_tiles, ws.tiles);
+  return 0;
+}
+
 int launch_sort_pairs(const int32_t* idx, int n, int E, const GatherWs& ws, hipStream_t s) {
   return launch_sort_pairs_bm(idx, n, E, ws, kGemmBM, s);
 }

@@ -6,7 +6,39 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace moeq {
+
+constexpr int kMaxLdsBytes = 160 * 1024;   // LDS of one gfx950 CU
+
+// Allow a kernel all the LDS its static shared arrays leave free as dynamic
+// shared memory, once per device: the limit is an attribute of the kernel, so
+// setting it on every launch would only add host work.  `done` is the call
+// site's own static bit set.
+// `need` is the launch's own dynamic LDS: if the runtime refuses the larger
+// limit, its error is taken back and the launch's size is set instead (then
+// on every launch, as the limit does not cover other sizes).
+inline void allow_full_lds(const void* kernel, int need, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  const uint64_t bit = 1ull << (dev & 63);
+  if (done.load(std::memory_order_acquire) & bit) return;
+  hipFuncAttributes a{};
+  if (hipFuncGetAttributes(&a, kernel) == hipSuccess &&
+      hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                          kMaxLdsBytes - (int)a.sharedSizeBytes) == hipSuccess) {
+    done.fetch_or(bit, std::memory_order_acq_rel);
+    return;
+  }
+  (void)hipGetLastError();   // the refusal above, not a launch failure
+  (void)hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, need);
+}
+#define MOEQ_ALLOW_FULL_LDS(kernel, need)                \
+  do {                                                   \
+    static std::atomic<uint64_t> moeq_lds_once_{0};      \
+    ::moeq::allow_full_lds((const void*)(kernel), (int)(need), moeq_lds_once_); \
+  } while (0)
 
 // A validated quantized tensor (see moeq_qtensor in include/moeq.h).
 struct QT {
@@ -142,6 +174,10 @@ int launch_moe_forward(const DecodeLayer& L, const RouteIn& R, const float* x, i
 int launch_moe_forward_norm(const DecodeLayer& L, const RouteIn& R, const float* x, int M, int K,
                             const float* norm_w, float eps, float* y, void* ws, hipStream_t s);
 
+// the error word of a decode-family workspace: out[0] = 0 or `timeout_status`,
+// out[1] = its bits; then the word is cleared (one thread, stream-ordered)
+int launch_ws_status(void* ws, int32_t* out, int timeout_status, hipStream_t s);
+
 // batched decode
 bool batch_supported(const DecodeLayer& L);
 int launch_batch_forward(const DecodeLayer& L, const float* x, const int32_t* idx, const float* w,
@@ -156,8 +192,13 @@ int launch_gemm_gate_up(const QT& gate, const QT& up, const uint16_t* x, int K, 
 int launch_gemm_down(const QT& down, const float* w, const GatherWs& ws, int n, hipStream_t s);
 int launch_gemm_plain(const QT& W, const uint16_t* x, float* out, const GatherWs& ws, int n,
                       hipStream_t s);
-// rows whose expert index is outside [0, E) become NaN (gather_qmm output)
-int launch_mark_invalid_rows(const int32_t* idx, int n, int E, int N, float* out, hipStream_t s);
+// indices already non-decreasing: rows used in place, each expert's run of
+// rows as its tiles (no sort)
+int launch_runs(const int32_t* idx, int n, int E, const GatherWs& ws, hipStream_t s);
+// rows whose expert index is outside [0, E) become NaN (gather_qmm output);
+// with runs (the offsets of launch_runs) also rows outside their expert's run
+int launch_mark_invalid_rows(const int32_t* idx, int n, int E, int N, const int32_t* runs, float* out,
+                             hipStream_t s);
 int launch_combine(const uint16_t* ypair, const int32_t* idx, int M, int K, int H, int E, float* y,
                    hipStream_t s);
 

@@ -27,8 +27,9 @@ STATUS = {
     0: "MOEQ_OK", -1: "MOEQ_ERR_NULL_PTR", -2: "MOEQ_ERR_BAD_BITS", -3: "MOEQ_ERR_BAD_GROUP",
     -4: "MOEQ_ERR_K_TAIL", -5: "MOEQ_ERR_SHAPE", -6: "MOEQ_ERR_OVERFLOW", -7: "MOEQ_ERR_ALIGN",
     -8: "MOEQ_ERR_WORKSPACE", -9: "MOEQ_ERR_UNSUPPORTED", -10: "MOEQ_ERR_LAUNCH",
-    -11: "MOEQ_ERR_HOST_MEMORY",
+    -11: "MOEQ_ERR_HOST_MEMORY", -12: "MOEQ_ERR_TIMEOUT",
 }
+MOEQ_ERR_TIMEOUT = -12
 
 
 class MoeqError(RuntimeError):
@@ -88,6 +89,7 @@ _SIGNATURES = {
     "moe_forward_norm": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _I, _I, _I, _P, ctypes.c_float,
                                         _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "gather_qmm": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _P, _I, _I, _P, _P, _SZ, _P]),
+    "moe_workspace_status": (ctypes.c_int, [_P, _P, _P]),
 }
 
 
@@ -212,6 +214,17 @@ class MoELayer:
     def hidden(self) -> int:
         return self.gate.cols
 
+    def requantized_2bit(self, stream=None) -> "MoELayer":
+        """The layer with its routed and shared experts requantized to 2 bits
+        on the device (requant_2bit, one launch per stack); the router and
+        the shared expert gate are kept as they are."""
+        sh = None
+        if self.shared is not None:
+            sh = {k: requant_2bit(v, stream) for k, v in self.shared.items() if k != "expert_gate"}
+            sh["expert_gate"] = self.shared["expert_gate"]
+        return MoELayer(self.router, requant_2bit(self.gate, stream), requant_2bit(self.up, stream),
+                        requant_2bit(self.down, stream), sh)
+
     @staticmethod
     def from_host(layer: dict, device="cuda") -> "MoELayer":
         sh = None
@@ -235,13 +248,46 @@ def workspace_size(layer: MoELayer, m: int, k: int, path: int) -> int:
     return int(lib().moe_workspace_size(ctypes.byref(layer.struct()), m, k, path))
 
 
+_DECODE_PATHS = (PATH_DECODE, PATH_FORWARD, PATH_FORWARD_NORM)
+_tracked: Optional[list] = None
+
+
 def workspace(layer: MoELayer, m: int, k: int, path: int, device="cuda") -> torch.Tensor:
     """A zeroed workspace of the size the library asks for (256-byte aligned:
     torch's caching allocator returns 512-byte aligned blocks)."""
     n = workspace_size(layer, m, k, path)
     if n == 0:
         raise MoeqError(-5, "moe_workspace_size")
-    return torch.zeros(n, dtype=torch.uint8, device=device)
+    ws = torch.zeros(n, dtype=torch.uint8, device=device)
+    if _tracked is not None and path in _DECODE_PATHS:
+        _tracked.append(ws)
+    return ws
+
+
+def workspace_status(ws: torch.Tensor, stream=None) -> tuple:
+    """(status, bits) of a decode-family workspace's error word, which is
+    cleared (moe_workspace_status; synchronizes the host with the stream)."""
+    out = torch.zeros(4, dtype=torch.int32, device=ws.device)
+    _check(lib().moe_workspace_status(_ptr(ws), _ptr(out), _stream(stream)), "moe_workspace_status")
+    st, bits = out[:2].tolist()
+    return int(st), int(bits)
+
+
+def track_workspaces(on: bool) -> None:
+    """Start (and empty) or stop the record of the decode-family workspaces
+    that workspace() makes, explicit ones and those the calls below make for
+    themselves; check_workspaces() reads their error words."""
+    global _tracked
+    _tracked = [] if on else None
+
+
+def check_workspaces() -> None:
+    """Raise MoeqError(MOEQ_ERR_TIMEOUT) if a bounded wait gave up in any call
+    on a recorded workspace (each error word is read and cleared)."""
+    for ws in list(_tracked or []):
+        st, bits = workspace_status(ws)
+        if st != 0:
+            raise MoeqError(st, f"decode workspace error word 0x{bits:x}")
 
 
 def qdequant(W: QTensor, codes: bool = True, deq: bool = True, stream=None):

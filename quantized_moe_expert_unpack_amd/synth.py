@@ -16,11 +16,12 @@ words make every packed field uniform), scales ``U(0.005, 0.02)`` rounded to
 bf16, and biases at the code midpoint ``-2**(bits-1) * scale`` plus
 ``N(0, 0.001)`` noise, rounded to bf16 (for 4-bit codes this is
 ``-8 * scale``).  The 2-bit experts of the 397B-A17B-shaped batched decode
-are drawn with the statistics of a 4-bit draw requantized to 2 bits (code
-frequencies 3:5:5:3, scale 5s, bias -8s); the requantization itself is a
-library op and is not done here.  Activations are fp32 ``N(0, 1)`` (decode) or bf16-rounded
-``N(0, 1)`` (prefill).  Prefill router logits are ``log p_rank(e) + Gumbel``
-with Zipf(1.1) rank probabilities over a seeded permutation of the experts.
+are the 397B-A17B-shaped decode's own 4-bit layers requantized to 2 bits;
+the requantization is a library op (and an oracle function) and is not done
+here: this module draws the 4-bit source (``source_config``).  Activations
+are fp32 ``N(0, 1)`` (decode) or bf16-rounded ``N(0, 1)`` (prefill).  Prefill
+router logits are ``log p_rank(e) + Gumbel`` with Zipf(1.1) rank
+probabilities over a seeded permutation of the experts.
 """
 
 from __future__ import annotations
@@ -59,7 +60,7 @@ class MoEConfig:
     tokens: int = 1                 # M per call
     seed: int = 0
     renorm: bool = True
-    requant_from: int = 0           # 4 => 2-bit weights shaped like requantized 4-bit draws
+    requant_from: int = 0           # 4: the experts are this config's 4-bit draws requantized to 2 bits
     expert_mode: str = "affine"     # "mxfp4": E2M1 experts, E8M0 scale per 32 columns
     extra: dict = field(default_factory=dict, compare=False, hash=False)
 
@@ -89,17 +90,18 @@ CONFIGS = {
     "c4_mxfp4": MoEConfig("c4-30b-a3b-prefill-mxfp4", hidden=2048, experts=128, top_k=8,
                           inter=768, expert_bits=4, router_bits=8, group_size=32, layers=2,
                           tokens=16384, seed=4, expert_mode="mxfp4"),
-    # 397B-A17B shapes with 2-bit experts shaped like a 4-bit model requantized
-    # to 2 bits, batched decode M=64
+    # the 397B-A17B-shaped decode's own layers (seed 3) with the routed and
+    # shared experts requantized from 4 to 2 bits (router and shared expert
+    # gate kept at 8 bits), batched decode M=64
     "c5": MoEConfig("c5-397b-a17b-2bit-m64", hidden=4096, experts=512, top_k=4,
                     inter=1024, expert_bits=2, router_bits=8,
                     shared_inter=1024, shared_bits=2, shared_gate_bits=8,
-                    layers=8, tokens=64, seed=5, requant_from=4),
-    # the same batched decode kept at 4-bit
+                    layers=8, tokens=64, seed=3, requant_from=4),
+    # the same batched decode on the same layers kept at 4 bits
     "c5_4bit": MoEConfig("c5-397b-a17b-4bit-m64", hidden=4096, experts=512,
                          top_k=4, inter=1024, expert_bits=4, router_bits=8,
                          shared_inter=1024, shared_bits=4, shared_gate_bits=8,
-                         layers=8, tokens=64, seed=5, requant_from=4),
+                         layers=8, tokens=64, seed=3),
 }
 
 
@@ -168,46 +170,22 @@ def draw_matrix(key, rows: int, cols: int, bits: int, group_size: int = GROUP):
     return words, s_bits, b_bits
 
 
-def _draw_4bit_codes(key, rows, cols, group_size):
-    """4-bit draw with codes uniform on 0..15 drawn one per column, then
-    packed, with the usual scale/bias recipe."""
-    rng = _rng(*key)
-    codes = np.frombuffer(rng.bytes(rows * cols), dtype=np.uint8).reshape(rows, cols) & np.uint8(15)
-    s_bits, b_bits = _scales_biases(rng, rows, cols // group_size, 4)
-    return pack_codes(codes, 4), s_bits, b_bits
-
-
-# inverse CDF of the 2-bit code frequencies 3:5:5:3 (of 16) over a uniform
-# 4-bit value: the frequencies with which requantizing a uniform 4-bit group
-# to 2 bits gives each code
-_CODE_OF_NIBBLE = np.repeat(np.arange(4, dtype=np.uint8), [3, 5, 5, 3])
-
-
-def _draw_2bit_requant_like(key, rows, cols, group_size):
-    """2-bit draw with the statistics of a uniform 4-bit draw requantized to
-    2 bits: codes with the frequencies above, the 4-bit recipe's scale s
-    spread over the 2-bit grid (scale 5s, bias at the 4-bit code midpoint
-    -8s plus N(0, 0.001)), both rounded to bf16."""
-    rng = _rng(*key)
-    nib = np.frombuffer(rng.bytes(rows * cols), dtype=np.uint8).reshape(rows, cols) & np.uint8(15)
-    codes = _CODE_OF_NIBBLE[nib]
-    g = cols // group_size
-    s = rng.uniform(0.005, 0.02, size=(rows, g)).astype(np.float32)
-    noise = rng.normal(0.0, 0.001, size=(rows, g)).astype(np.float32)
-    s_bits = f32_to_bf16_bits((np.float32(5.0) * s).astype(np.float32))
-    b_bits = f32_to_bf16_bits((np.float32(-8.0) * s + noise).astype(np.float32))
-    return pack_codes(codes, 2), s_bits, b_bits
+def source_config(cfg: MoEConfig) -> MoEConfig:
+    """The config whose layers a requantized config's experts come from: the
+    same shapes and seed with the source bit width (the layers of
+    ``CONFIGS["c3"]`` for ``CONFIGS["c5"]``, at that config's token count)."""
+    if not cfg.requant_from:
+        return cfg
+    return replace(cfg, expert_bits=cfg.requant_from,
+                   shared_bits=cfg.requant_from if cfg.has_shared else 0, requant_from=0)
 
 
 def draw_weight(cfg: MoEConfig, layer: int, expert: int, tensor: int, rows: int,
                 cols: int, bits: int):
-    key = (cfg.seed, layer, expert, tensor)
     if cfg.requant_from and tensor in (T_GATE, T_UP, T_DOWN, T_SH_GATE, T_SH_UP, T_SH_DOWN):
-        if bits == 4:
-            return _draw_4bit_codes(key, rows, cols, cfg.group_size)
-        if bits == 2:
-            return _draw_2bit_requant_like(key, rows, cols, cfg.group_size)
-        raise ValueError("requantization-shaped draws are 4- or 2-bit")
+        raise ValueError(f"{cfg.name}: its experts are requantized from the {cfg.requant_from}-bit "
+                         "layer of source_config(cfg); draw that one")
+    key = (cfg.seed, layer, expert, tensor)
     return draw_matrix(key, rows, cols, bits, cfg.group_size)
 
 

@@ -64,3 +64,54 @@ def bf16_dev(bits_u16, device=None):
 
 def bf16_bits_to_f32(bits_u16):
     return (np.asarray(bits_u16, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def oracle_requantized_layer(src_host, experts, threads=16):
+    """The oracle's 2-bit form of a 4-bit host layer, for the experts listed
+    (oracle.requant_2bit_fast per expert matrix) and the shared expert's FFN;
+    the router and the shared expert gate stay as they are.  Stacks are dicts
+    indexed by expert."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    experts = [int(e) for e in experts]
+    out = dict(src_host)
+    jobs = [(name, e) for name in ("gate", "up", "down") for e in experts]
+
+    def one(job):
+        name, e = job
+        return job, oracle.requant_2bit_fast(oracle.expert_slice(src_host[name], e))
+
+    with ThreadPoolExecutor(threads) as ex:
+        done = dict(ex.map(one, jobs))
+    for name in ("gate", "up", "down"):
+        t = src_host[name]
+        out[name] = {"q": {e: done[(name, e)]["q"] for e in experts},
+                     "scales": {e: done[(name, e)]["scales"] for e in experts},
+                     "biases": {e: done[(name, e)]["biases"] for e in experts},
+                     "rows": t["rows"], "cols": t["cols"], "bits": 2,
+                     "group_size": t["group_size"], "batch": t["batch"]}
+    sh = src_host.get("shared")
+    if sh is not None:
+        out["shared"] = {k: (v if k == "expert_gate" else oracle.requant_2bit_fast(v))
+                         for k, v in sh.items()}
+    return out
+
+
+def assert_same_2bit_experts(dev_layer, host2, experts):
+    """The device's requantized words, scales and biases of the listed
+    experts (and of the shared expert) equal the oracle's, bit for bit."""
+    for name in ("gate", "up", "down"):
+        t = getattr(dev_layer, name)
+        for e in experts:
+            e = int(e)
+            assert np.array_equal(t.q[e].cpu().numpy().view(np.uint32), host2[name]["q"][e]), (name, e)
+            assert np.array_equal(t.scales[e].cpu().numpy().view(np.uint16), host2[name]["scales"][e])
+            assert np.array_equal(t.biases[e].cpu().numpy().view(np.uint16), host2[name]["biases"][e])
+    if dev_layer.shared is not None:
+        for name in ("gate", "up", "down"):
+            t, h = dev_layer.shared[name], host2["shared"][name]
+            assert np.array_equal(t.q.cpu().numpy().view(np.uint32).reshape(h["q"].shape), h["q"])
+            assert np.array_equal(t.scales.cpu().numpy().view(np.uint16).reshape(h["scales"].shape),
+                                  h["scales"])
+            assert np.array_equal(t.biases.cpu().numpy().view(np.uint16).reshape(h["biases"].shape),
+                                  h["biases"])

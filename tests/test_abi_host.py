@@ -32,7 +32,8 @@ def test_header_declares_the_four_calls_and_helpers():
     names = declared_functions()
     for n in ("qmatvec", "moe_route", "moe_expert_forward", "moe_gather_qmm", "qdequant",
               "gather_qmm", "requant_2bit", "moe_rms_norm", "moe_forward_norm", "moe_stream_experts",
-              "moe_stream_experts_device", "moe_workspace_size", "moeq_status_string", "moeq_version"):
+              "moe_stream_experts_device", "moe_workspace_size", "moe_workspace_status", "moeq_status_string",
+              "moeq_version"):
         assert n in names
 
 
@@ -340,3 +341,13 @@ def test_route_workspace_covers_the_split_router_partials():
     assert route_bytes(15, 512) < 2 * 15 * 512 * 8
     assert route_bytes(8200, 40) >= 8200 * 40 * 8           # 513 blocks: one part
     assert route_bytes(8200, 40) < 2 * 8200 * 40 * 8
+
+
+def test_workspace_status_validates_before_launching():
+    lib = moeq.lib()
+    assert lib.moe_workspace_status(None, FAKE, None) == -1          # no workspace
+    assert lib.moe_workspace_status(FAKE, None, None) == -1          # no status output
+    assert lib.moe_workspace_status(FAKE + 16, FAKE, None) == -7     # workspace not 256-byte aligned
+    assert lib.moe_workspace_status(FAKE, FAKE + 4, None) == -7      # output not 16-byte aligned
+    assert moeq.STATUS[-12] == "MOEQ_ERR_TIMEOUT"
+    assert b"bounded wait" in lib.moeq_status_string(-12)

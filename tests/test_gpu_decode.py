@@ -12,7 +12,8 @@ import torch
 
 import oracle
 from quantized_moe_expert_unpack_amd import moeq, synth
-from tests.gpu_util import dev, gapped_tokens, rel_l2_rows, say, to_dev
+from tests.gpu_util import (assert_same_2bit_experts, dev, gapped_tokens, oracle_requantized_layer,
+                             rel_l2_rows, say, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -94,12 +95,39 @@ def test_c3_shaped_layer_with_shared_expert():
     assert rel_l2_rows(y.cpu().numpy(), ref).max() <= TOL
 
 
+@functools.lru_cache(maxsize=1)
+def _c5_source(layer_idx):
+    # the 397B-A17B-shaped decode's own 4-bit layer, which both C5 runs use
+    cfg = synth.source_config(synth.CONFIGS["c5"])
+    host = synth.host_layer(cfg, layer_idx, threads=16)
+    return host, moeq.MoELayer.from_host(host, dev())
+
+
 @pytest.mark.parametrize("name", ["c5", "c5_4bit"])
 def test_c5_batched_decode_m64(name):
-    cfg, host, L = _layer(name, 0)
-    say(f"{name} M=64")
-    x = gapped_tokens(cfg, host, 0, 1, m=64)[0]
-    _check_layer(cfg, host, L, x)
+    # C5: the C3 layer's routed and shared experts requantized to 2 bits on
+    # the device (router and shared expert gate kept at 8 bits), 64 tokens
+    # batched; the same layer at 4 bits beside it
+    cfg = synth.CONFIGS[name]
+    host4, L4 = _c5_source(0)
+    say(f"{name} M=64 (layer 0 of {synth.CONFIGS['c3'].name}"
+        f"{', requantized to 2 bits' if cfg.requant_from else ''})")
+    x = gapped_tokens(cfg, host4, 0, 1, m=64)[0]
+    if not cfg.requant_from:
+        _check_layer(cfg, host4, L4, x)
+        return
+    L2 = L4.requantized_2bit()
+    y, idx, w = _decode(cfg, L2, to_dev(x))
+    ridx, rw, _ = oracle.route(oracle.qmatvec(host4["router"], x), cfg.top_k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    assert np.abs(w.cpu().numpy() - rw).max() <= 1e-6
+    touched = np.unique(ridx)
+    host2 = oracle_requantized_layer(host4, touched)
+    assert_same_2bit_experts(L2, host2, touched)        # the device requantization, bit for bit
+    ry = oracle.moe_experts(host2, x, ridx, rw)
+    err = rel_l2_rows(y.cpu().numpy(), ry)
+    say(f"  {len(touched)} experts touched, max rel-L2 {err.max():.3e}")
+    assert err.max() <= TOL, err.max()
 
 
 def test_residual_determinism_and_ragged_m():

@@ -188,3 +188,52 @@ def test_stacks_keep_their_shape_and_reject_bad_sources():
         oracle.requant_2bit(dict(src, group_size=32, scales=np.zeros((6, 4), np.uint16)))
     with pytest.raises(ValueError):
         oracle.requant_2bit(dict(_random_source(4, 64, 1, 64, 1), bits=2))
+
+
+# ---- the integer form used over whole expert stacks (requant_2bit_fast) ----
+
+def _same(a, b):
+    return (np.array_equal(a["q"], b["q"]) and np.array_equal(a["scales"], b["scales"])
+            and np.array_equal(a["biases"], b["biases"]))
+
+
+@pytest.mark.parametrize("bits,gs,seed", [(4, 64, 1), (4, 128, 2), (8, 64, 3), (8, 128, 4),
+                                          (4, 64, 5), (8, 64, 6)])
+def test_fast_form_equals_the_exact_definition(bits, gs, seed):
+    # negative scales, narrow groups (grid ties), random biases
+    src = _random_source(bits, gs, 8, 512, seed=100 + seed)
+    assert _same(oracle.requant_2bit_fast(src), oracle.requant_2bit(src))
+
+
+def test_fast_form_on_degenerate_and_far_apart_groups():
+    rng = np.random.default_rng(9)
+    codes = rng.integers(0, 16, (6, 256))
+    codes[0, :64] = 7                               # one code only: no spread
+    codes[1, 64:128] = rng.choice([3, 4], 64)       # two neighbouring codes
+    codes[2, :64] = rng.choice([0, 15], 64)         # only the two extremes
+    s = [0x3C80] * 24
+    b = [0xBE00] * 24
+    s[1], b[1] = 0x0000, 0x3F00                      # zero scale
+    s[2], b[2] = 0x8000, 0x8000                      # -0 scale and -0 bias
+    s[5], b[5] = 0xBC80, 0x3E00                      # negative scale
+    s[8], b[8] = 0x21C0, 0x3F80                      # s = 1.5 * 2^-60, b = 1: s*q + b inexact in fp64
+    s[9], b[9] = 0xA1C0, 0xBF80                      # the same with both signs flipped
+    s[12], b[12] = 0x0D80, 0x3F80                    # s near 2^-100 against 1
+    src = _qt(codes, s, b, 4, 64)
+    fast, exact = oracle.requant_2bit_fast(src), oracle.requant_2bit(src)
+    assert _same(fast, exact)
+    assert (_codes2(fast)[0, :64] == 0).all() and fast["scales"][0, 0] == 0
+
+
+def test_fast_form_on_stacks_and_rejections():
+    src = _random_source(4, 64, 6, 128, seed=3)
+    st = dict(src, q=src["q"].reshape(2, 3, -1), scales=src["scales"].reshape(2, 3, -1),
+              biases=src["biases"].reshape(2, 3, -1), batch=2, rows=3)
+    r = oracle.requant_2bit_fast(st)
+    assert r["q"].shape == (2, 3, 8) and r["scales"].shape == (2, 3, 2)
+    assert _same({k: v.reshape(6, -1) for k, v in r.items() if k in ("q", "scales", "biases")},
+                 oracle.requant_2bit(src))
+    with pytest.raises(ValueError):
+        oracle.requant_2bit_fast(dict(src, group_size=32, scales=np.zeros((6, 4), np.uint16)))
+    with pytest.raises(ValueError):
+        oracle.requant_2bit_fast(dict(_random_source(4, 64, 1, 64, 1), bits=2))
