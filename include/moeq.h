@@ -260,6 +260,30 @@ int moe_forward(const moeq_moe *L, const float *x, int32_t M, int32_t K, int32_t
                 const float *residual, float *y, int32_t *topk_idx, float *topk_w, void *ws,
                 size_t ws_bytes, moeq_stream_t stream);
 
+/* moe_forward_noalloc: moe_forward with no workspace argument and no
+ * allocation, for callers that cannot allocate device memory around the
+ * call (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).  Same arguments and results as moe_forward; the
+ * workspace is a static device array of the library, 16 MiB on each device,
+ * held from the library's first use on that device until the process ends.
+ *   status_out : nullable device int32 [2], 16-byte aligned: after the call,
+ *                as moe_workspace_status reports for moe_forward's workspace
+ *                ([0] MOEQ_OK or MOEQ_ERR_TIMEOUT, [1] the raw bits); a call
+ *                that reports a timeout also clears the array, so the next
+ *                call starts clean
+ * Returns MOEQ_ERR_WORKSPACE when the call needs more than the array holds
+ * (moe_workspace_size(L, M, K, MOEQ_PATH_FORWARD) > 16 MiB: e.g. more than
+ * about 64 tokens at the 397B-A17B shapes), before anything is launched.
+ * Every call on a device shares that device's array, which keeps the last
+ * call's state: a call whose layer shape or K differs from the previous
+ * call's clears the array first with a fill kernel on `stream`.  Calls on one
+ * device must therefore be ordered (one stream, or streams the caller
+ * synchronizes); calls that overlap on one device race and give wrong
+ * results.  Calls no hipMalloc, hipFree or allocating library routine. */
+int moe_forward_noalloc(const moeq_moe *L, const float *x, int32_t M, int32_t K, int32_t renorm,
+                        const float *residual, float *y, int32_t *topk_idx, float *topk_w,
+                        int32_t *status_out, moeq_stream_t stream);
+
 /* moe_rms_norm: h[m] = x[m] / sqrt(mean_k(x[m][k]^2) + eps) * norm_w, per row.
  *   x : fp32 [M][H];  norm_w : fp32 [H];  h : fp32 [M][H] out;  H % 4 == 0;
  *   eps >= 0 and finite (MOEQ_ERR_SHAPE otherwise)

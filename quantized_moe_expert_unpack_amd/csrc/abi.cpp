@@ -7,8 +7,9 @@
 
 #include <algorithm>
 #include <climits>
-#include <vector>
 #include <cstdint>
+#include <mutex>
+#include <vector>
 
 #include "launch.h"
 #include "stream.h"
@@ -243,6 +244,139 @@ size_t forward_norm_ws_bytes(const moeq::DecodeLayer& dl, int E, int M, int K) {
 
 bool bad_eps(float eps) { return !(eps >= 0.0f) || eps > 3.0e38f; }
 
+// moe_forward's argument checks: 1 when the call has work, 0 (MOEQ_OK) for
+// M == 0, else the error status
+int check_forward(const moeq_moe* L, const float* x, int32_t M, int32_t K, const float* residual,
+                  const float* y, const int32_t* topk_idx, const float* topk_w, moeq::DecodeLayer* dl,
+                  int32_t* E) {
+  LayerDims d;
+  int st = check_experts(L, &d);
+  if (st) return st;
+  if (is_mx(L->gate)) return MOEQ_ERR_UNSUPPORTED;   // mxfp4 experts: gather paths only
+  if ((st = check_qt(&L->router, 1, d.E, d.H))) return st;
+  if (is_mx(L->router)) return MOEQ_ERR_UNSUPPORTED;
+  if (M < 0 || K < 1 || K > kMaxK || K > d.E) return MOEQ_ERR_SHAPE;
+  if (M == 0) return MOEQ_OK;
+  if (!x || !y || !topk_idx || !topk_w) return MOEQ_ERR_NULL_PTR;
+  if (!fits_i32((int64_t)M * d.H) || !fits_i32((int64_t)M * d.E) ||
+      !fits_i32((int64_t)M * K * d.I + (int64_t)M * d.Is + M))
+    return MOEQ_ERR_OVERFLOW;
+  if (!aligned16(x) || !aligned16(y) || !aligned16(topk_idx) || !aligned16(topk_w) ||
+      (residual && !aligned16(residual)))
+    return MOEQ_ERR_ALIGN;
+  *dl = to_decode_layer(L, d);
+  if (!moeq::decode_supported(*dl, K)) return MOEQ_ERR_UNSUPPORTED;
+  *E = d.E;
+  return 1;
+}
+
+// moe_forward after validation, on a workspace of forward_ws_bytes
+int forward_body(const moeq_moe* L, const moeq::DecodeLayer& dl, int32_t E, const float* x, int32_t M,
+                 int32_t K, int32_t renorm, const float* residual, float* y, int32_t* topk_idx,
+                 float* topk_w, void* ws, hipStream_t s) {
+  int st;
+  const QT router = to_qt(L->router);
+  if (moeq::fused_supported(dl, router, M, K)) {
+    const moeq::RouteIn R{router, renorm, topk_idx, topk_w};
+    st = moeq::launch_moe_forward(dl, R, x, M, K, residual, y, ws, s);
+  } else {
+    char* base = reinterpret_cast<char*>(ws);
+    const moeq::DecState ds = moeq::dec_state(dl, K, base);
+    double* l64 = reinterpret_cast<double*>(base + align_up(expert_ws_bytes(dl, M, K)));
+    moeq::launch_route_parts(&router, x, M, E, K, renorm, topk_idx, topk_w, nullptr, l64,
+                             ds.route_ctr, s);
+    st = run_expert_forward(dl, x, topk_idx, topk_w, M, K, residual, y, base, s);
+  }
+  if (st) return MOEQ_ERR_UNSUPPORTED;
+  return launch_status();
+}
+
+}  // namespace
+
+// ---- the allocation-free moe_forward: its workspace is a static array ------
+// One array per device, held until the process ends.  Host code never uses
+// the array's name as an address: each device's address comes from
+// hipGetSymbolAddress (taken once per device, with that device current).
+constexpr size_t kScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+constexpr int kClearBlocks = 512;
+
+// What fixes the layout of the decode state block at the array's front: the
+// layer's shape, its shared expert and K (plus the bit widths and group size,
+// for good measure).  A call with another layout clears the array first.
+struct ScratchKey {
+  int E, H, I, Is, has_shared, K, bits, group_size, router_bits;
+  bool operator==(const ScratchKey& o) const {
+    return E == o.E && H == o.H && I == o.I && Is == o.Is && has_shared == o.has_shared && K == o.K &&
+           bits == o.bits && group_size == o.group_size && router_bits == o.router_bits;
+  }
+};
+
+struct ScratchDev {
+  char* ptr;        // the device's address of `scratch` (null until first use)
+  bool keyed;       // a layout has been set up
+  ScratchKey key;   // the layout of the last call
+  size_t used;      // bytes the calls since the last clear may have touched
+};
+
+std::mutex g_scratch_mu;
+ScratchDev g_scratch[kMaxDevices];
+
+__global__ void k_scratch_zero(uint4* __restrict__ p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// clear the array when the status just written reports a timeout
+__global__ void k_scratch_clear_if(const int32_t* __restrict__ status, uint4* __restrict__ p, size_t n16) {
+  if (status[1] == 0) return;
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+size_t scratch_used_16(const char* ws) {
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  for (auto& d : g_scratch)
+    if (d.ptr == ws) return d.used / 16;
+  return 0;
+}
+
+// The current device's scratch address for a call needing `need` bytes;
+// clears (on `s`, by a fill kernel) what the previous layout used when this
+// call's layout differs, and on the device's first call the whole array.
+int scratch_for_call(const moeq::DecodeLayer& dl, const moeq_qtensor& router, int K, size_t need,
+                     hipStream_t s, char** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return MOEQ_ERR_LAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return MOEQ_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  ScratchDev& d = g_scratch[dev];
+  if (!d.ptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MOEQ_ERR_LAUNCH;
+    d.ptr = static_cast<char*>(p);
+    d.used = kScratchBytes;        // not known to be clear: the first call clears it all
+  }
+  const ScratchKey key{dl.E, dl.H, dl.I, dl.Is, dl.has_shared, K, dl.gate.bits, dl.gate.group_size,
+                       router.bits};
+  if (!d.keyed || !(d.key == key)) {
+    const size_t n = std::max(d.used, need);
+    hipLaunchKernelGGL(k_scratch_zero, dim3(kClearBlocks), dim3(256), 0, s,
+                       reinterpret_cast<uint4*>(d.ptr), (n + 15) / 16);
+    d.key = key;
+    d.keyed = true;
+    d.used = need;
+  } else {
+    d.used = std::max(d.used, need);
+  }
+  *out = d.ptr;
+  return MOEQ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -389,39 +523,37 @@ int moe_expert_forward(const moeq_moe* L, const float* x, const int32_t* topk_id
 int moe_forward(const moeq_moe* L, const float* x, int32_t M, int32_t K, int32_t renorm,
                 const float* residual, float* y, int32_t* topk_idx, float* topk_w, void* ws,
                 size_t ws_bytes, moeq_stream_t stream) {
-  LayerDims d;
-  int st = check_experts(L, &d);
-  if (st) return st;
-  if (is_mx(L->gate)) return MOEQ_ERR_UNSUPPORTED;   // mxfp4 experts: gather paths only
-  if ((st = check_qt(&L->router, 1, d.E, d.H))) return st;
-  if (is_mx(L->router)) return MOEQ_ERR_UNSUPPORTED;
-  if (M < 0 || K < 1 || K > kMaxK || K > d.E) return MOEQ_ERR_SHAPE;
-  if (M == 0) return MOEQ_OK;
-  if (!x || !y || !topk_idx || !topk_w) return MOEQ_ERR_NULL_PTR;
-  if (!fits_i32((int64_t)M * d.H) || !fits_i32((int64_t)M * d.E) ||
-      !fits_i32((int64_t)M * K * d.I + (int64_t)M * d.Is + M))
-    return MOEQ_ERR_OVERFLOW;
-  if (!aligned16(x) || !aligned16(y) || !aligned16(topk_idx) || !aligned16(topk_w) ||
-      (residual && !aligned16(residual)))
-    return MOEQ_ERR_ALIGN;
-  const moeq::DecodeLayer dl = to_decode_layer(L, d);
-  if (!moeq::decode_supported(dl, K)) return MOEQ_ERR_UNSUPPORTED;
-  if (!ws || ws_bytes < forward_ws_bytes(dl, d.E, M, K)) return MOEQ_ERR_WORKSPACE;
+  moeq::DecodeLayer dl;
+  int32_t E = 0;
+  int st = check_forward(L, x, M, K, residual, y, topk_idx, topk_w, &dl, &E);
+  if (st != 1) return st;              // an error, or M == 0 (nothing to do)
+  if (!ws || ws_bytes < forward_ws_bytes(dl, E, M, K)) return MOEQ_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % kAlign) return MOEQ_ERR_ALIGN;
+  return forward_body(L, dl, E, x, M, K, renorm, residual, y, topk_idx, topk_w, ws, (hipStream_t)stream);
+}
+
+int moe_forward_noalloc(const moeq_moe* L, const float* x, int32_t M, int32_t K, int32_t renorm,
+                        const float* residual, float* y, int32_t* topk_idx, float* topk_w,
+                        int32_t* status_out, moeq_stream_t stream) {
+  moeq::DecodeLayer dl;
+  int32_t E = 0;
+  int st = check_forward(L, x, M, K, residual, y, topk_idx, topk_w, &dl, &E);
+  if (st != 1) return st;
+  if (status_out && !aligned16(status_out)) return MOEQ_ERR_ALIGN;
+  const size_t need = forward_ws_bytes(dl, E, M, K);
+  if (need > kScratchBytes) return MOEQ_ERR_WORKSPACE;   // beyond the static array
   hipStream_t s = (hipStream_t)stream;
-  const QT router = to_qt(L->router);
-  if (moeq::fused_supported(dl, router, M, K)) {
-    const moeq::RouteIn R{router, renorm, topk_idx, topk_w};
-    st = moeq::launch_moe_forward(dl, R, x, M, K, residual, y, ws, s);
-  } else {
-    char* base = reinterpret_cast<char*>(ws);
-    const moeq::DecState ds = moeq::dec_state(dl, K, base);
-    double* l64 = reinterpret_cast<double*>(base + align_up(expert_ws_bytes(dl, M, K)));
-    moeq::launch_route_parts(&router, x, M, d.E, K, renorm, topk_idx, topk_w, nullptr, l64,
-                             ds.route_ctr, s);
-    st = run_expert_forward(dl, x, topk_idx, topk_w, M, K, residual, y, base, s);
+  char* ws = nullptr;
+  if ((st = scratch_for_call(dl, L->router, K, need, s, &ws))) return st;
+  st = forward_body(L, dl, E, x, M, K, renorm, residual, y, topk_idx, topk_w, ws, s);
+  if (st) return st;
+  if (status_out) {
+    // the call's timeout status out to the caller; a timed-out call leaves
+    // the array's counters in an unknown state, so then it is cleared
+    moeq::launch_ws_status(ws, status_out, MOEQ_ERR_TIMEOUT, s);
+    hipLaunchKernelGGL(k_scratch_clear_if, dim3(kClearBlocks), dim3(256), 0, s, status_out,
+                       reinterpret_cast<uint4*>(ws), scratch_used_16(ws));
   }
-  if (st) return MOEQ_ERR_UNSUPPORTED;
   return launch_status();
 }
 

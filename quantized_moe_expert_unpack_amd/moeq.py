@@ -90,6 +90,8 @@ _SIGNATURES = {
                                         _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "gather_qmm": (ctypes.c_int, [ctypes.POINTER(QTensorStruct), _P, _P, _I, _I, _P, _P, _SZ, _P]),
     "moe_workspace_status": (ctypes.c_int, [_P, _P, _P]),
+    "moe_forward_noalloc": (ctypes.c_int, [ctypes.POINTER(MoEStruct), _P, _I, _I, _I, _P, _P, _P, _P,
+                                           _P, _P]),
 }
 
 
@@ -377,6 +379,27 @@ def moe_forward(layer: MoELayer, x: torch.Tensor, k: int, renorm: bool = True,
     _check(lib().moe_forward(ctypes.byref(layer.struct()), _ptr(x), m, k, int(bool(renorm)),
                              _ptr(residual), _ptr(y), _ptr(idx), _ptr(w), _ptr(ws), ws.numel(),
                              _stream(stream)), "moe_forward")
+    return y, idx, w
+
+
+def moe_forward_noalloc(layer: MoELayer, x: torch.Tensor, k: int, renorm: bool = True,
+                        residual: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                        idx: Optional[torch.Tensor] = None, w: Optional[torch.Tensor] = None,
+                        status: Optional[torch.Tensor] = None, stream=None):
+    """moe_forward on the library's static per-device workspace (no
+    workspace argument).  ``status``: optional device int32 [>= 2] that
+    receives the call's timeout status.  Returns (y, idx, w)."""
+    m = x.shape[0]
+    dev = x.device
+    if y is None:
+        y = torch.empty((m, layer.hidden), dtype=torch.float32, device=dev)
+    if idx is None:
+        idx = torch.empty((m, k), dtype=torch.int32, device=dev)
+    if w is None:
+        w = torch.empty((m, k), dtype=torch.float32, device=dev)
+    _check(lib().moe_forward_noalloc(ctypes.byref(layer.struct()), _ptr(x), m, k, int(bool(renorm)),
+                                     _ptr(residual), _ptr(y), _ptr(idx), _ptr(w), _ptr(status),
+                                     _stream(stream)), "moe_forward_noalloc")
     return y, idx, w
 
 
