@@ -332,7 +332,8 @@ int moe_forward_norm(const moeq_moe *L, const float *x, int32_t M, int32_t K, in
  *   ws         : the workspace (device, 256-byte aligned)
  *   status_out : device int32 [2], 16-byte aligned: [0] = MOEQ_OK or
  *                MOEQ_ERR_TIMEOUT, [1] = the raw bits (1 ready flag, 2 routing
- *                result, 4 router logits, 8 h or shared gate)
+ *                result, 4 router logits or the slots' expert and weight
+ *                pairs, 8 h or shared gate)
  * One small kernel on `stream`, ordered after the work queued before it (no
  * memset node: the call can be captured in a graph).  The host return value
  * only says whether that kernel was queued; the status itself is in

@@ -37,9 +37,9 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found: the HIP toolchain is required to build libmoeq.so")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [_hipcc(), *FLAGS, *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
         cmd.insert(1, "-xhip")
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,21 +51,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = True) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    os.makedirs(LIBDIR, exist_ok=True)
+TIMELINE_LIB = os.path.join(LIBDIR, "timeline", "libmoeq.so")
+
+
+def build(verbose: bool = True, timeline: bool = False) -> str:
+    """Build lib/libmoeq.so; with ``timeline`` the instrumented variant
+    lib/timeline/libmoeq.so (MOEQ_TIMELINE: the decode kernel records
+    per-unit timestamps, read back by ``timeline.py``)."""
+    build_dir = BUILD + ("_timeline" if timeline else "")
+    lib = TIMELINE_LIB if timeline else LIB
+    defines = ("MOEQ_TIMELINE",) if timeline else ()
+    os.makedirs(build_dir, exist_ok=True)
+    os.makedirs(os.path.dirname(lib), exist_ok=True)
     with ThreadPoolExecutor(max(1, min(len(SOURCES), os.cpu_count() or 1))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, build_dir, defines), SOURCES))
+    tmp = lib + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
     if verbose:
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build()
+    build(timeline="--timeline" in sys.argv)

@@ -58,10 +58,17 @@ constexpr int kRRows = kWaves / 2;         // router rows per R unit (two waves 
 constexpr int kSpinLimit = 1 << 26;
 constexpr int kLine = kLineInts;
 constexpr int kRep = 64;      // copies of every flag that many units poll
+constexpr int kLogitCopies = 32;   // copies of the router logits (one per polling group of units)
+constexpr int kSelCopies = 16;     // copies of the (expert, weight) pairs the down units poll
 // per token: G arrival counter lines, D arrival counter lines
 constexpr int kCtrLines = 2 * (1 + kFan);
 constexpr int kHCopies = 8;   // copies of h (one per XCD; the down units read their XCD's): spreads the
                               // reads of all D units of a token over more memory channels
+static_assert(kHCopies * kGRows % kWave == 0, "a G unit's h copies are written by whole waves");
+// the one-launch form's h buffers: a G unit's kGRows values (one segment) at
+// the front of a 128-byte line of their own, so no line holds two segments
+constexpr int kSegStride = 32;
+static_assert(kSegStride * 4 == 128 && kGRows <= kSegStride, "a segment fills at most one line");
 
 // ---- coherent (agent-scope) loads/stores for data crossing blocks ----------
 __device__ __forceinline__ void st_coh(float* p, float v) {
@@ -78,6 +85,56 @@ __device__ __forceinline__ uint64_t ld_coh64(const uint64_t* p) {
 // cache maintenance: drain this wave's outstanding memory operations before
 // the counter update that announces them.
 __device__ __forceinline__ void drain() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---- per-unit timestamps of one launch (timeline build only) ---------------
+// Built with MOEQ_TIMELINE, every unit's first thread records the constant
+// 100 MHz clock at the steps of its protocol into LDS, and the unit writes
+// them to g_tl[block][event] when it ends (a global store per mark would
+// hold up the unit's next memory wait until the store is acknowledged).
+// Counters add up in LDS and are added to g_tl.  The product build compiles
+// these marks away.
+#ifdef MOEQ_TIMELINE
+constexpr int kTlBlocks = 4096, kTlEvents = 12;
+__device__ uint64_t g_tl[kTlBlocks * kTlEvents];
+__device__ __forceinline__ uint64_t* tl_lds() {
+  __shared__ uint64_t s_tl[2 * kTlEvents];   // marks, then counters
+  return s_tl;
+}
+__device__ __forceinline__ void tl_begin() {
+  if (threadIdx.x < 2 * kTlEvents) tl_lds()[threadIdx.x] = 0ull;
+  __syncthreads();
+}
+__device__ __forceinline__ void tl_mark(int ev) {
+  // the clock is read at this point of the program (nothing is moved across it)
+  __builtin_amdgcn_sched_barrier(0);
+  const uint64_t t = (uint64_t)wall_clock64();
+  __builtin_amdgcn_sched_barrier(0);
+  if (threadIdx.x == 0) {
+    tl_lds()[ev] = t;
+    // with the start mark: which XCD runs the block (hardware register XCC_ID, bits 3:0)
+    if (ev == 0) tl_lds()[kTlEvents - 1] = (uint64_t)__builtin_amdgcn_s_getreg((3 << 11) | 20);
+  }
+}
+// add n to the block's counter in event slot ev
+__device__ __forceinline__ void tl_count(int ev, int n) {
+  if (n) atomicAdd(reinterpret_cast<unsigned long long*>(tl_lds() + kTlEvents + ev), (unsigned long long)n);
+}
+__device__ __forceinline__ void tl_end() {
+  __syncthreads();
+  if (threadIdx.x < kTlEvents && blockIdx.x < kTlBlocks) {
+    const uint64_t* s_tl = tl_lds();
+    uint64_t* g = g_tl + (size_t)blockIdx.x * kTlEvents + threadIdx.x;
+    if (s_tl[threadIdx.x]) *g = s_tl[threadIdx.x];
+    if (s_tl[kTlEvents + threadIdx.x]) atomicAdd(reinterpret_cast<unsigned long long*>(g),
+                                                 (unsigned long long)s_tl[kTlEvents + threadIdx.x]);
+  }
+}
+#else
+__device__ __forceinline__ void tl_begin() {}
+__device__ __forceinline__ void tl_mark(int) {}
+__device__ __forceinline__ void tl_count(int, int) {}
+__device__ __forceinline__ void tl_end() {}
+#endif
 
 
 __device__ __forceinline__ int ld_coh_i(const int* p) {
@@ -123,12 +180,6 @@ __device__ __forceinline__ bool wait_flag(int* flag) {
   return false;
 }
 
-// the token's route line in copy `rep`: word k = (expert + 1) << 32 | the
-// routing weight's fp32 bits, 0 while not routed (one 64-bit store publishes
-// both halves together)
-__device__ __forceinline__ uint64_t* route_line(const DecPlan& P, int rep, int t) {
-  return reinterpret_cast<uint64_t*>(P.idx_c + (size_t)rep * P.rstride + (size_t)t * kLine);
-}
 __device__ __forceinline__ int* ready_line(const DecPlan& P, int rep, int t) {
   return P.ready + (size_t)rep * P.rstride + (size_t)t * kLine;
 }
@@ -167,43 +218,33 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 
 
 // ------------------------------------------------------------------ R unit
-// top-K of at most 64*PER keys by one wave, keys held in registers: K rounds
-// of a wave maximum, the owner of each winner dropping it (keys are unique)
-template <int PER>
-__device__ __forceinline__ void wave_topk(const uint64_t* keys, int E, int K, int lane, int* sel) {
-  uint64_t kk[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int e = lane + kWave * i;
-    kk[i] = e < E ? keys[e] : 0ull;      // 0 is below every key
-  }
-  for (int r = 0; r < K; ++r) {
-    uint64_t mx = kk[0];
-#pragma unroll
-    for (int i = 1; i < PER; ++i) mx = kk[i] > mx ? kk[i] : mx;
-    mx = wave_max_u64(mx);
-#pragma unroll
-    for (int i = 0; i < PER; ++i) kk[i] = kk[i] == mx ? 0ull : kk[i];
-    if (lane == 0) sel[r] = 1023 - (int)(mx & 0x3FFull);
-  }
-}
-
-// top-K of token m from keys/vals in LDS (E <= 1024), all threads of the
-// block: selection by rank as in topk.h, candidates ranked by four threads
-// each; publishes the weights into every route-line copy, drains, then the
-// indices, and writes the caller's outputs.
-// WIDE: allow the one-wave selection up to 512 experts (16 more registers)
-template <bool WIDE>
-__device__ __forceinline__ void route_select(const uint64_t* keys, const double* vals, int E,
-                                             int K, int renorm, const DecPlan& P, const RouteIn& R,
-                                             int m, int par) {
-  __shared__ uint64_t cand[kWaves * kMaxTopK];
-  __shared__ int sel[kMaxTopK];
+// top-K of one token from keys/vals in LDS (E <= 1024), all threads of the
+// block, into sel[0..K) (LDS) in rank order; with wts, also the weights in
+// fp64: p[idx]/sum p[idx] (renorm, summed in slot order) or p[idx]/sum over
+// all E (fixed order), p relative to the maximum, rounded once to fp32.
+// Keys are unique (topk.h), so ranks are too.  Up to 128 keys, every key is
+// ranked against all; above, selection in three short steps instead:
+//   1. the keys fall into 64 groups of g = ceil(E/64) consecutive keys; lane
+//      i of wave 0 takes the maximum of group i;
+//   2. T = the K-th largest of the 64 group maxima.  Exactly K groups have a
+//      maximum >= T, so at least K keys are >= T and every key of the top K
+//      is >= T; a key >= T lies in one of those K groups, so at most K g
+//      keys are (the candidates);
+//   3. the candidates are ranked among themselves: every key above a
+//      candidate is a candidate too, so that rank is the rank among all E.
+__device__ __forceinline__ void route_pick(const uint64_t* keys, const double* vals, int E, int K,
+                                           int renorm, int* sel, float* wts) {
+  constexpr int kMaxCand = kMaxTopK * (kMaxExperts / kWave);
+  __shared__ uint64_t gmax[kWave];
+  __shared__ uint64_t cand[kMaxCand];
+  __shared__ uint64_t s_thr;
+  __shared__ int s_nc;
   __shared__ double ex[kMaxTopK];
   __shared__ double red[kWaves];
   __shared__ double s_tot;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  if (E <= kThreads / 4) {               // up to 128 experts: rank every key, one quad per key
+  if (E <= kThreads / 4) {
+    // up to 128 experts: every key ranked against all, four threads per key
     const int a = tid >> 2, part = tid & 3;
     const uint64_t ka = a < E ? keys[a] : 0ull;
     int rank = 0;
@@ -212,40 +253,55 @@ __device__ __forceinline__ void route_select(const uint64_t* keys, const double*
     rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, false);
     rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, false);
     if (part == 0 && a < E && rank < K) sel[rank] = a;
-  } else if (WIDE && E <= 8 * kWave) {   // up to 512
-    if (wid == 0) wave_topk<8>(keys, E, K, lane, sel);
   } else {
-  const int nc = kWaves * K;             // candidate slots, K per wave
-  if (tid < nc) cand[tid] = 0ull;        // 0 is below every key
-  __syncthreads();
-  // 1) per wave: the keys of its part whose rank inside the part is < K, at
-  //    their rank (keys are unique, so the positions are too)
-  const int q = (E + kWaves - 1) / kWaves;
-  const int lo = min(E, wid * q), hi = min(E, lo + q);
-  for (int a = lo + lane; a < hi; a += kWave) {
-    const uint64_t ka = keys[a];
-    int rank = 0;
-#pragma unroll 4
-    for (int j = lo; j < hi; ++j) rank += keys[j] > ka;
-    if (rank < K) cand[wid * K + rank] = ka;
+  const int g = (E + kWave - 1) / kWave;
+  if (wid == 0) {
+    uint64_t m = 0ull;                   // 0 is below every key (an empty group)
+    const int lo = lane * g, hi = min(E, lo + g);
+    for (int e = lo; e < hi; ++e) m = keys[e] > m ? keys[e] : m;
+    gmax[lane] = m;
+    if (lane == 0) s_nc = 0;
   }
   __syncthreads();
-  // 2) rank of every candidate among the candidates: four threads (one quad)
-  //    per candidate, each over a quarter, summed across the quad
   {
-    const int c = tid >> 2, part = tid & 3;
+    // rank of group maximum c among the 64, eight threads per maximum (at
+    // least K groups are non-empty, so the K-th largest is a key)
+    const int c = tid >> 3, part = tid & 7;
+    if (c < kWave) {
+      const uint64_t kc = gmax[c];
+      int r = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) r += gmax[part * 8 + j] > kc;
+      r += __shfl_xor(r, 1);
+      r += __shfl_xor(r, 2);
+      r += __shfl_xor(r, 4);
+      if (part == 0 && r == K - 1) s_thr = kc;
+    }
+  }
+  __syncthreads();
+  {
+    const uint64_t thr = s_thr;
+    for (int e = tid; e < E; e += kThreads) {
+      const uint64_t k = keys[e];
+      if (k >= thr) cand[atomicAdd(&s_nc, 1)] = k;
+    }
+  }
+  __syncthreads();
+  {
+    // tpc threads per candidate (a power of two, nc * tpc <= kThreads)
+    const int nc = s_nc;
+    int tpc = kWave / 4;
+    while (tpc > 1 && nc * tpc > kThreads) tpc >>= 1;
+    const int c = tid / tpc, part = tid & (tpc - 1);
     const uint64_t kc = c < nc ? cand[c] : 0ull;
-    int rank = 0;
-#pragma unroll 4
-    for (int j = part; j < nc; j += 4) rank += cand[j] > kc;
-    rank += __builtin_amdgcn_mov_dpp(rank, 0xB1, 0xF, 0xF, false);
-    rank += __builtin_amdgcn_mov_dpp(rank, 0x4E, 0xF, 0xF, false);
-    if (part == 0 && c < nc && kc != 0ull && rank < K) sel[rank] = 1023 - (int)(kc & 0x3FFull);
+    int r = 0;
+    for (int j = part; j < nc; j += tpc) r += cand[j] > kc;
+    for (int o = 1; o < tpc; o <<= 1) r += __shfl_xor(r, o);
+    if (part == 0 && c < nc && r < K) sel[r] = 1023 - (int)(kc & 0x3FFull);
   }
   }
   __syncthreads();
-  // 3) weights in fp64: p[idx] / sum p[idx] (renorm, summed in slot order) or
-  //    p[idx] / sum over all E (fixed order), with p relative to the maximum
+  if (!wts) return;
   const double mx = vals[sel[0]];
   if (tid < K) ex[tid] = exp(vals[sel[tid]] - mx);
   if (!renorm) {
@@ -264,47 +320,81 @@ __device__ __forceinline__ void route_select(const uint64_t* keys, const double*
     s_tot = tot;
   }
   __syncthreads();
-  for (int i = tid; i < kRep * K; i += kThreads) {
-    const int rep = i / K, k = i - rep * K;
-    const float w = (float)(ex[k] / s_tot);
-    if (rep == 0) {
-      R.idx_out[(size_t)m * K + k] = sel[k];
-      R.w_out[(size_t)m * K + k] = w;
+  if (tid < K) wts[tid] = (float)(ex[tid] / s_tot);
+  __syncthreads();
+}
+
+// Wave 0 of a G or D unit: wait until every router logit of token t is
+// published (complemented fp64 bits, 0 = not yet), then put the token's keys
+// and logits in LDS; returns the polling rounds it took.  One round loads the
+// whole row and waits for it, so no load is left in flight at the end (a
+// load still in flight would stall the first later use of its registers by
+// a loaded memory latency).  Bounded: on the spin limit the error word gets
+// bit 4 and the logits read as they are.
+// kPer: logits per lane at most (E <= 64 kPer); kSleep: s_sleep between rounds
+template <int kPer, int kSleep>
+__device__ __forceinline__ int poll_logits(const uint64_t* lg, int E, int lane, int* err,
+                                          uint64_t* keys, double* vals) {
+  const int per = (E + kWave - 1) / kWave;
+  uint64_t cur[kPer];
+  int spin = 0;
+  for (;; ++spin) {
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) cur[i] = i < per ? ld_coh_u64(lg + min(lane + kWave * i, E - 1)) : 1ull;
+    bool all = true;
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) all = all && cur[i] != 0ull;
+    if (__all(all)) break;
+    if (spin >= kSpinLimit) {
+      if (lane == 0) atomicOr(err, 4);
+      break;
     }
-    const uint32_t hi = ((uint32_t)par << 31) | (uint32_t)(sel[k] + 1);
-    st_coh_u64(route_line(P, rep, m) + k, ((uint64_t)hi << 32) | __float_as_uint(w));
+    __builtin_amdgcn_s_sleep(kSleep);
   }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int e = lane + kWave * i;
+    if (i < per && e < E) {
+      const double v = __longlong_as_double((long long)~cur[i]);
+      vals[e] = v;
+      keys[e] = route_key(v, e);
+    }
+  }
+  return spin;
 }
 
 // Router rows (8-bit) against x for all M tokens in fp64: the fp32
 // dequantized weight widened exactly, fp64 products and sums, as the oracle
-// defines the logits.  The R unit completing the arrivals selects.
+// defines the logits.  An R unit takes kRRows rows, two waves per row (wave
+// half h takes the row's chunks lane + 64 (2j + h)), and publishes each
+// finished logit into the launch's logits buffer; every G and D unit then
+// selects its token's top-K itself.
 // NORM: the rows see h = r * (x . g) with r = 1/sqrt(mean(x^2) + eps) per token
 // (RMSNorm): x . g is staged, each token's mean square reduced over the block,
 // and r applied to the finished logit.
-template <bool WIDE, bool NORM>
+template <bool NORM, int RCPL2>
 __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P, const RouteIn R,
                                            const float* __restrict__ x, int u) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
-  const int E = L.E, H = L.H, M = P.M, K = P.K;
-  // two waves per row: wave half h takes the row's chunks lane + 64 (2j + h)
+  const int E = L.E, H = L.H, M = P.M;
   const int e = u * kRRows + wid / 2, h = wid & 1;
-  const int nch = H / 16;                 // 16 codes per chunk at 8 bits
+  tl_mark(0);                             // R: start
+  const int nch = H / 16;                 // 16 codes per chunk at 8 bits (nch <= 128 RCPL2)
   const int rsh = __builtin_ctz((unsigned)R.W.group_size);   // log2 of the group size
   const int gpr = H >> rsh;
   const bool row_ok = e < E;
   __shared__ double part[kFusedMaxM][kRRows];
-  // Loads use clamped, always valid addresses and no branches, so they all
-  // issue back to back; lanes past the row's end are never used.
   const int er = min(e, E - 1);
-  // the selector's epoch word (its parity picks the launch's h buffer), read
-  // now so the load overlaps the router rows
-  const int epoch = u == P.r_units - 1 ? ld_coh_i(P.epoch) : 0;
-  uint4 rv[2];
-  uint32_t rsb[2];
+  // the launch's parity picks its logits buffer (read now, so the load
+  // overlaps the router rows)
+  const int epoch = ld_coh_i(P.epoch);
+  // Loads use clamped, always valid addresses and no branches, so they all
+  // issue back to back; chunks past the row's end are never used.
+  uint4 rv[RCPL2];
+  uint32_t rsb[RCPL2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
+  for (int j = 0; j < RCPL2; ++j) {
     const int c = min(lane + kWave * (2 * j + h), nch - 1);
     rv[j] = reinterpret_cast<const uint4*>(R.W.q + (size_t)er * (H / 4))[c];
     rsb[j] = (uint32_t)R.W.scales[(size_t)er * gpr + ((c * 16) >> rsh)] |
@@ -337,113 +427,108 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
       }
     }
   }
-  float rs[2], rb[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    rs[j] = bf16_to_f32(rsb[j] & 0xFFFFu);
-    rb[j] = bf16_to_f32(rsb[j] >> 16);
-  }
   __syncthreads();
-  // per lane and token, its chunks as independent fp64 chains, elements in
-  // order; a weight is dequantized once for all tokens; one chunk at a time
-  // (the scheduling barrier keeps the compiler from hoisting every chunk's
-  // fp64 operands at once)
-  double acc[kFusedMaxM][2];
+  tl_mark(5);                             // R: router rows and x in
+  double acc[kFusedMaxM];
 #pragma unroll
-  for (int m = 0; m < kFusedMaxM; ++m)
+  for (int m = 0; m < kFusedMaxM; ++m) acc[m] = 0.0;
+  if (M == 1) {
+    // one token: the chunk's 16 activations are read from LDS together and
+    // the chunk keeps four independent fp64 chains (one per 4-code word)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[m][j] = 0.0;
+    for (int j = 0; j < RCPL2; ++j) {
+      const int c = lane + kWave * (2 * j + h);
+      const int cc = min(c, nch - 1);
+      const float rs = bf16_to_f32(rsb[j] & 0xFFFFu), rb = bf16_to_f32(rsb[j] >> 16);
+      float4 xv[4];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int c = lane + kWave * (2 * j + h);
-    if (row_ok && c < nch) {
-      const uint32_t wd[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
+      for (int f = 0; f < 4; ++f) xv[f] = xl[f * nch + cc];
+      double a[4];
 #pragma unroll
       for (int f = 0; f < 4; ++f) {
-        double w[4];
+        const uint32_t wd = f == 0 ? rv[j].x : f == 1 ? rv[j].y : f == 2 ? rv[j].z : rv[j].w;
+        double t = (double)fmaf(rs, (float)(wd & 0xFFu), rb) * (double)xv[f].x;
+        t = fma((double)fmaf(rs, (float)((wd >> 8) & 0xFFu), rb), (double)xv[f].y, t);
+        t = fma((double)fmaf(rs, (float)((wd >> 16) & 0xFFu), rb), (double)xv[f].z, t);
+        a[f] = fma((double)fmaf(rs, (float)(wd >> 24), rb), (double)xv[f].w, t);
+      }
+      if (c < nch) acc[0] += (a[0] + a[1]) + (a[2] + a[3]);
+    }
+  } else {
+    // per lane and token, its chunks as independent fp64 chains, elements in
+    // order; a weight is dequantized once for all tokens; one chunk at a time
+    // (the scheduling barrier keeps the compiler from hoisting every chunk's
+    // fp64 operands at once)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) w[q] = (double)fmaf(rs[j], (float)((wd[f] >> (8 * q)) & 0xFFu), rb[j]);
+    for (int j = 0; j < RCPL2; ++j) {
+      const int c = lane + kWave * (2 * j + h);
+      if (c < nch) {
+        const float rs = bf16_to_f32(rsb[j] & 0xFFFFu), rb = bf16_to_f32(rsb[j] >> 16);
+        const uint32_t wd[4] = {rv[j].x, rv[j].y, rv[j].z, rv[j].w};
 #pragma unroll
-        for (int m = 0; m < kFusedMaxM; ++m) {
-          if (m < M) {
-            const float4 xv = xl[m * (H / 4) + f * nch + c];
-            acc[m][j] = fma(w[0], (double)xv.x, acc[m][j]);
-            acc[m][j] = fma(w[1], (double)xv.y, acc[m][j]);
-            acc[m][j] = fma(w[2], (double)xv.z, acc[m][j]);
-            acc[m][j] = fma(w[3], (double)xv.w, acc[m][j]);
+        for (int f = 0; f < 4; ++f) {
+          double w[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) w[q] = (double)fmaf(rs, (float)((wd[f] >> (8 * q)) & 0xFFu), rb);
+#pragma unroll
+          for (int m = 0; m < kFusedMaxM; ++m) {
+            if (m < M) {
+              const float4 xv = xl[m * (H / 4) + f * nch + c];
+              acc[m] = fma(w[0], (double)xv.x, acc[m]);
+              acc[m] = fma(w[1], (double)xv.y, acc[m]);
+              acc[m] = fma(w[2], (double)xv.z, acc[m]);
+              acc[m] = fma(w[3], (double)xv.w, acc[m]);
+            }
           }
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
     }
-    __builtin_amdgcn_sched_barrier(0);
   }
+  tl_mark(1);                             // R: fp64 dot products done
   // the two halves of a row meet in LDS; the even wave publishes the logit
   double wsum[kFusedMaxM];
 #pragma unroll
   for (int m = 0; m < kFusedMaxM; ++m) {
     wsum[m] = 0.0;
     if (m < M) {
-      wsum[m] = wave_sum_d(acc[m][0] + acc[m][1]);
+      wsum[m] = wave_sum_d(acc[m]);
       if (h == 1 && lane == 0) part[m][wid / 2] = wsum[m];
     }
   }
   __syncthreads();
+  // every logit goes to kLogitCopies copies, one per lane (a G or D unit
+  // polls copy blockIdx % kLogitCopies: many units polling one line would
+  // queue on its memory channel)
+  uint64_t* lg = P.logits + ((size_t)(epoch & 1) * kLogitCopies + lane) * P.lstride;
 #pragma unroll
   for (int m = 0; m < kFusedMaxM; ++m) {
-    if (m < M && h == 0 && lane == 0 && row_ok) {
+    if (m < M && h == 0 && lane < kLogitCopies && row_ok) {
       double tot = wsum[m] + part[m][wid / 2];
       if constexpr (NORM) {
         float sq = 0.f;
         for (int w = 0; w < kWaves; ++w) sq += s_ss[w][m];
         tot *= 1.0 / sqrt((double)sq / H + (double)P.norm_eps);
       }
-      // published as the complement of its bits: zero means "not written yet"
-      // (the complement of a finite double is never zero)
-      st_coh_u64(P.logits + (size_t)m * E + e, ~(uint64_t)__double_as_longlong(tot));
+      // published as the complement of its bits: zero means "not written
+      // yet" (the complement of a finite double is never zero)
+      st_coh_u64(lg + (size_t)m * E + e, ~(uint64_t)__double_as_longlong(tot));
     }
   }
-  // the last R unit selects: it polls every logit (no counter round trips),
-  // clears them for the next launch, and runs the top-K of each token
-  if (u != P.r_units - 1) return;
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);
-  double* vals = reinterpret_cast<double*>(keys + E);
-  // (the selector is the only reader and writer of the epoch word)
-  __syncthreads();                       // x in LDS is no longer read
-  for (int m = 0; m < M; ++m) {
-    for (int ee = tid; ee < E; ee += kThreads) {
-      uint64_t* src = P.logits + (size_t)m * E + ee;
-      uint64_t v = 0;
-      for (int i = 0; i < kSpinLimit && v == 0; ++i) {
-        v = ld_coh_u64(src);
-        if (v == 0) __builtin_amdgcn_s_sleep(1);
-      }
-      if (v == 0) atomicOr(P.ctr, 4);
-      st_coh_u64(src, 0);
-      const double lg = __longlong_as_double((long long)~v);
-      vals[ee] = lg;
-      keys[ee] = route_key(lg, ee);
-    }
-    __syncthreads();
-    route_select<WIDE>(keys, vals, E, K, R.renorm, P, R, m, epoch & 1);
-    __syncthreads();
-  }
-  if (tid == 0) {
-    st_coh_i(P.epoch, epoch + 1);
-    // how much of this launch's h buffer it fills (the launch after next
-    // clears that much of it)
-    st_coh_i(P.hext + (epoch & 1), (int)((size_t)kHCopies * P.P * P.Imax / 4));
-  }
+  tl_mark(2);                             // R: logits published
 }
 
 // ------------------------------------------------------------------ G unit
 // LDS: [x, chunk-interleaved][its chunk sums (<= H/16 floats)][bf16 scales and
 // biases of the unit's gate and up rows]
-template <int BITS, int CPL, bool FUSED, bool NORM>
+template <int BITS, int CPL, bool FUSED, bool NORM, bool WIDE, int POLL>
 __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan P,
                                              const float* __restrict__ x,
-                                             const int32_t* __restrict__ idx, int u) {
+                                             const int32_t* __restrict__ idx, int u, int renorm) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
-  __shared__ int s_e, s_par, s_done;
+  __shared__ int s_done;
+  __shared__ int s_sel[kMaxTopK];
+  __shared__ float s_w[kMaxTopK];
   constexpr int kCpc = 128 / BITS;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int S = P.S, K = P.K, H = L.H;
@@ -465,11 +550,17 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
   const int gpr = H >> esh;                         // groups per row
   const int x16 = H / 4;
   const int sb16 = kGRows * gpr * 2 / 16;           // 16-byte words per scale/bias tensor
+  tl_mark(0);                                       // G: start
+  // the launch's parity (its logits and h buffers), read first
+  const int par = FUSED ? (ld_coh_i(P.epoch) & 1) : 0;
   float* xs = smem;
   float* xsum = xs + H;
   // (the sums' region is padded to 16 bytes: the scale words are stored as uint4)
   uint16_t* sbl = reinterpret_cast<uint16_t*>(xsum + pad4(H / 16));   // [4][kGRows * gpr]
   float4* x4 = reinterpret_cast<float4*>(xs);
+  // the token's router keys and logits while it selects (after the scales)
+  uint64_t* keys = reinterpret_cast<uint64_t*>(sbl + 4 * kGRows * gpr);
+  double* vals = reinterpret_cast<double*>(keys + L.E);
 
   uint4 xr[2], gr[2];
 #pragma unroll
@@ -518,15 +609,29 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
     }
     __syncthreads();
     chunk_sums<kCpc>(x4, xsum, nch);
-    if (wid == 0 && !shared) {
-      const uint64_t v = wave_wait_nonzero(route_line(P, u % kRep, t) + k, 1, lane, P.ctr);
-      if (lane == 0) {
-        s_e = (int)((v >> 32) & 0x7FFFFFFFu) - 1;
-        s_par = (int)(v >> 63);
+    tl_mark(1);                                     // G: x staged
+    if (!shared) {
+      // the token's top-K from the published logits; this unit's expert is
+      // the one in its slot
+      if (wid == 0) {
+        const int rounds =
+            poll_logits<POLL, 1>(P.logits + ((size_t)par * kLogitCopies + blockIdx.x % kLogitCopies) * P.lstride +
+                                  (size_t)t * L.E,
+                              L.E, lane, P.ctr, keys, vals);
+        tl_mark(5);                                 // G: logits seen
+        if (lane == 0) tl_count(6, rounds + 1);
       }
+      __syncthreads();
+      tl_mark(7);                                   // G: after the barrier
+      // the slot's first unit also takes the routing weights and publishes
+      // the slot's (expert, weight) pair for the down units, in every copy
+      route_pick(keys, vals, L.E, K, g == 0 ? renorm : 0, s_sel, g == 0 ? s_w : nullptr);
+      if (g == 0 && wid == 0 && lane < kSelCopies)
+        st_coh_u64(P.selw + ((size_t)par * kSelCopies + lane) * P.sstride + (size_t)t * kMaxTopK + k,
+                   ~(((uint64_t)(uint32_t)s_sel[k] << 32) | __float_as_uint(s_w[k])));
     }
-    __syncthreads();
-    if (!shared) erow = (size_t)min(max(s_e, 0), L.E - 1) * L.I;
+    tl_mark(2);                                     // G: expert known
+    if (!shared) erow = (size_t)min(max(s_sel[k], 0), L.E - 1) * L.I;
   } else {
     if (!shared) {
       const int e = idx[(size_t)t * K + k];
@@ -559,12 +664,6 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
       wu[rr][j] = u4[c];
     }
   }
-  // done with the route words: count this reader (the last one clears
-  // them); the counter round trips overlap the loads just issued
-  bool last_reader = false;
-  if (FUSED && !shared && tid == 0)
-    last_reader = arrive(P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines) + (1 + kFan) * kLine, r,
-                         upt + P.nc);
   if constexpr (!FUSED) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
@@ -599,41 +698,43 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
     pg[rr] = ag;
     pu[rr] = au;
   }
+  tl_mark(3);                                       // G: weights in, partial dots done
   const float gsum = treduce<2, 32>(pg, lane);
   const float usum = treduce<2, 32>(pu, lane);
-  if constexpr (FUSED) {
-    if (shared) {
-      // the shared expert does not wait for routing; it learns the launch's
-      // parity from the route words now, and counts itself as their reader
-      if (wid == 0) {
-        const uint64_t v = wave_wait_nonzero(route_line(P, u % kRep, t), 1, lane, P.ctr);
-        if (lane == 0) {
-          s_par = (int)(v >> 63);
-          s_done = arrive(P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines) + (1 + kFan) * kLine, r,
-                          upt + P.nc);
-        }
-      }
-      __syncthreads();
-    }
-  }
   float rn = 1.f;
   if constexpr (NORM) {
     float sq = 0.f;
     for (int w = 0; w < kWaves; ++w) sq += s_gss[w];
     rn = (float)(1.0 / sqrt((double)sq / H + (double)P.norm_eps));
   }
-  if ((lane & 31) < kHCopies) {         // every lane of a half holds its row's sum
+  if constexpr (FUSED) {
+    // the unit's rows meet in LDS, then one wave writes every copy, the
+    // kGRows values of a copy (one 64-byte segment) by one store instruction,
+    // as complemented bits (0 means "not written in this launch"): a down unit
+    // that sees a segment's first value sees the rest of it too, as a rule
+    __shared__ float s_h[kGRows];
+    if ((lane & 31) == 0) {               // every lane of a half holds its row's sum
+      const int i = wid * 2 + tindex<2, 32>(lane);
+      s_h[i] = valid ? silu(rn * gsum) * (rn * usum) : __builtin_nanf("");
+    }
+    __syncthreads();
+    if (wid == 0) {
+#pragma unroll
+      for (int j = 0; j < kHCopies * kGRows / kWave; ++j) {
+        const int q = lane + kWave * j, c = q / kGRows, i = q % kGRows;
+        if (i < nrows)
+          st_coh_i(reinterpret_cast<int*>(P.hb) + (size_t)par * P.hreg + (size_t)c * P.P * P.hstride +
+                       (size_t)p * P.hstride + g * kSegStride + i,
+                   (int)~__float_as_uint(s_h[i]));
+      }
+    }
+  } else if ((lane & 31) < kHCopies) {  // every lane of a half holds its row's sum
     const int i = wid * 2 + tindex<2, 32>(lane);
     const float hv = valid ? silu(rn * gsum) * (rn * usum) : __builtin_nanf("");
-    if (i < nrows) {
-      const size_t at = (size_t)(lane & 31) * P.P * P.Imax + (size_t)p * P.Imax + i_base + i;
-      if constexpr (FUSED)   // complemented bits: 0 means "not written in this launch"
-        st_coh_i(reinterpret_cast<int*>(P.hb) + (size_t)s_par * P.hreg + at,
-                 (int)~__float_as_uint(hv));
-      else
-        st_coh(P.h + at, hv);
-    }
+    if (i < nrows)
+      st_coh(P.h + (size_t)(lane & 31) * P.P * P.Imax + (size_t)p * P.Imax + i_base + i, hv);
   }
+  tl_mark(4);                                       // G: h written
   if (sgu) {
     // the shared_expert_gate logit: this thread's chunk, then the block's sum
     // in wave order
@@ -659,19 +760,14 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
       for (int w = 0; w < kWaves; ++w) tot += sgp[w];
       tot *= rn;
       if constexpr (FUSED)
-        st_coh_i(reinterpret_cast<int*>(P.sgb) + s_par * kFusedMaxM + t, (int)~__float_as_uint(tot));
+        st_coh_i(reinterpret_cast<int*>(P.sgb) + par * kFusedMaxM + t, (int)~__float_as_uint(tot));
       else
         st_coh(P.sg + t, tot);
     }
   }
-  if constexpr (FUSED) {
-    // h goes out with its own "written" marks, so there is nothing to
-    // announce; the last reader of the route words clears them
-    if (!shared && tid == 0) s_done = last_reader;
-    __syncthreads();
-    if (s_done)
-      for (int i = tid; i < kRep * K; i += kThreads) st_coh_u64(route_line(P, i / K, t) + i % K, 0);
-  } else {
+  if constexpr (!FUSED) {
+    // h goes out with the ready flag (the one-launch form's h carries its own
+    // "written" marks instead)
     drain();
     __syncthreads();
     if (tid == 0) s_done = arrive(P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines), r, upt);
@@ -680,11 +776,17 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
   }
 }
 
+// scale/bias words (16 bytes) a D unit stages: all slots, scales and biases
+__host__ __device__ __forceinline__ int d_sb_words_dev(const DecodeLayer& L, int K) {
+  const int egs = L.gate.group_size;
+  return 2 * kDRows * (K * (L.I / egs) + (L.has_shared ? L.Is / egs : 0)) * 2 / 16;
+}
+
 // ------------------------------------------------------------------ D unit
 // LDS: [h of all S slots, chunk-interleaved per slot][their chunk sums][bf16
 // scales then biases of the unit's rows, slot by slot]
-template <int BITS, int DCH, bool FUSED>
-__device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
+template <int BITS, int DCH, bool FUSED, bool WIDE, int POLL>
+__device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, const RouteIn R,
                                           const int32_t* __restrict__ idx,
                                           const float* __restrict__ wts,
                                           const float* __restrict__ residual,
@@ -692,8 +794,10 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float wk[kMaxTopK + 1];
   __shared__ int s_ex[kMaxTopK];
-  __shared__ int bad, s_par, s_done, s_zx;
+  __shared__ int bad, s_done, s_zx;
   constexpr int kCpc = 128 / BITS;
+  // segments of a token a thread may own (DCH chunks per lane of kCpc values)
+  constexpr int kSegPT = (DCH * kCpc + 127) / 128;
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wid = tid / kWave;
   const int K = P.K, H = L.H;
   const int t = d / P.nc;
@@ -705,6 +809,9 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
   const int cpr = I / kCpc;                    // chunks per routed down row
   const int cps = L.has_shared ? Is / kCpc : 0;
   const int tot = K * cpr + cps;               // chunks per output row, all slots
+  tl_mark(0);                                  // D: start
+  // the launch's parity (its logits and h buffers), read first
+  const int par = FUSED ? (ld_coh_i(P.epoch) & 1) : 0;
   int* tl = P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines);
   // slot and chunk of every chunk position of the lane (q = lane + 64 j)
   // (packed in one register: (slot + 1) << 16 | chunk; slot -1 = no chunk)
@@ -730,17 +837,47 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
       if (!ok) atomicOr(&bad, 1);
     }
   }
+  // (the router keys and logits of the token in LDS while it selects, past
+  // the unit's h, chunk sums and scale/bias words)
+  float* hs = smem;                            // [S][Imax]
+  float* hsum = hs + (size_t)P.S * P.Imax;     // [S][Imax/kCpc]
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(hsum + pad4(P.S * P.Imax / 16));   // 16-byte aligned
   if constexpr (FUSED) {
+    // the token's top-K and its weights from the published logits; the
+    // token's first D unit also writes them out for the caller
+    // the token's top-K and its weights: the (expert, weight) pair each
+    // slot's first gate/up unit publishes; the token's first D unit also
+    // writes them out for the caller
     if (wid == 0) {
-      const uint64_t v = wave_wait_nonzero(route_line(P, d % kRep, t), K, lane, P.ctr);
+      const uint64_t* sp = P.selw + ((size_t)par * kSelCopies + blockIdx.x % kSelCopies) * P.sstride +
+                           (size_t)t * kMaxTopK;
+      uint64_t v = 1ull;
+      for (int spin = 0;; ++spin) {
+        v = lane < K ? ld_coh_u64(sp + lane) : 1ull;
+        if (__all(v != 0ull)) break;
+        if (spin >= kSpinLimit) {
+          if (lane == 0) atomicOr(P.ctr, 4);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
+      }
       if (lane < K) {
-        s_ex[lane] = min(max((int)((v >> 32) & 0x7FFFFFFFu) - 1, 0), L.E - 1);
+        v = ~v;
+        s_ex[lane] = (int)(uint32_t)(v >> 32);
         wk[lane] = __uint_as_float((uint32_t)v);
       }
-      if (lane == 0) s_par = (int)(v >> 63);
+    }
+    __syncthreads();
+    if (tid < K) {
+      if (c == 0) {
+        R.idx_out[(size_t)t * K + tid] = s_ex[tid];
+        R.w_out[(size_t)t * K + tid] = wk[tid];
+      }
+      s_ex[tid] = min(max(s_ex[tid], 0), L.E - 1);
     }
   }
   __syncthreads();
+  tl_mark(1);                                  // D: experts known
   // scales and biases of every slot (per slot kDRows rows x groups bf16,
   // contiguous), then the routed chunks
   const int esh = __builtin_ctz((unsigned)L.gate.group_size);  // log2 group size, every expert matrix
@@ -780,17 +917,8 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     wv[j] = reinterpret_cast<const uint4*>(base + (size_t)(r0 + rlc) * wpr)[cj];
   }
   // the extent of the other h buffer's last use (cleared at the end)
-  const int zx = FUSED ? ld_coh_i(P.hext + (s_par ^ 1)) : 0;
-  // done with the route words: count this reader (the last one clears them);
-  // the last wave does it, after its loads are in flight
-  bool last_reader = false;
-  if (FUSED && tid == kThreads - kWave) {
-    const int upt = K * P.ng_routed + (L.has_shared ? P.ng_shared : 0);
-    last_reader = arrive(tl + (1 + kFan) * kLine, upt + c, upt + P.nc);
-  }
-  float* hs = smem;                            // [S][Imax]
-  float* hsum = hs + (size_t)P.S * P.Imax;     // [S][Imax/kCpc]
-  uint16_t* sbl = reinterpret_cast<uint16_t*>(hsum + pad4(P.S * P.Imax / 16));   // 16-byte aligned
+  const int zx = FUSED ? ld_coh_i(P.hext + (par ^ 1)) : 0;
+  float term[DCH];                             // the lane's chunk terms of the wave's row
   if constexpr (FUSED) {
     // h arrives element by element with its "written" marks: once this
     // unit's own loads are in, poll the token's h (copy blockIdx % kHCopies
@@ -800,7 +928,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     if (tid < n_sb) reinterpret_cast<uint4*>(sbl)[tid] = sbr;
     if (tid == 0) s_zx = zx;
     if (wid == 0 && L.has_shared && lane == K) {
-      const uint32_t* sgp = P.sgb + s_par * kFusedMaxM + t;
+      const uint32_t* sgp = P.sgb + par * kFusedMaxM + t;
       uint32_t v = 0;
       for (int i = 0; i < kSpinLimit && v == 0; ++i) {
         v = (uint32_t)ld_coh_i(reinterpret_cast<const int*>(sgp));
@@ -809,83 +937,91 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
       if (v == 0) atomicOr(P.ctr, 8);
       wk[K] = 1.0f / (1.0f + __expf(-__uint_as_float(~v)));
     }
-    // first wait, cheaply, for one marker word per gate/up unit (the first
-    // of its rows; wave 0 alone), so that the whole of h is loaded once it is
-    // almost surely complete: polling all of it would put one copy of h per
-    // poll round and down unit on the memory system while the weights stream
-    const uint32_t* hw = P.hb + (size_t)s_par * P.hreg +
-                         (size_t)(blockIdx.x % kHCopies) * P.P * P.Imax + (size_t)t * P.S * P.Imax;
-    if (wid == 0) {
-      const int nmk = K * P.ng_routed + P.ng_shared;
-      constexpr int kMk = 8;
-      for (int b0 = 0; b0 < nmk; b0 += kWave * kMk) {
-        uint32_t need = 0;
+    __syncthreads();                             // staged scales and biases, wk[K]
+    // h arrives segment by segment: a G unit writes each copy of its kGRows
+    // values (one segment, alone in a 128-byte line) with one store
+    // instruction, as complemented bits (0 = not written).  Every thread
+    // owns segments tid + kThreads i: it polls a segment's first value with a
+    // coherent load and, one round later, loads the whole segment through
+    // L2 into LDS (its line cannot be in L2 from before the segment was
+    // whole: only a D unit that saw its first value reads it).  So h lands in
+    // LDS while the gate/up units are still finishing, and after the last
+    // one only its segment is left to fetch.  Values found unwritten are
+    // re-read with coherent loads.
+    const uint32_t* hw = P.hb + (size_t)par * P.hreg +
+                         (size_t)(blockIdx.x % kHCopies) * P.P * P.hstride +
+                         (size_t)t * P.S * P.hstride;
+    const int nseg = K * P.ng_routed + P.ng_shared;   // segments of the token
+    uint32_t pend = 0, seen = 0, slow = 0;       // this thread's segments q = tid + kThreads i
 #pragma unroll
-        for (int j = 0; j < kMk; ++j)
-          if (b0 + lane + kWave * j < nmk) need |= 1u << j;
-        for (int spin = 0; spin < kSpinLimit; ++spin) {
-          uint32_t v[kMk];
+    for (int i = 0; i < kSegPT; ++i)
+      if (tid + kThreads * i < nseg) pend |= 1u << i;
+    for (int round = 0;; ++round) {
+      if (pend) {
+        uint32_t mk[kSegPT];
+        uint4 body[kSegPT][kGRows / 4];
 #pragma unroll
-          for (int j = 0; j < kMk; ++j) {
-            const int q = min(b0 + lane + kWave * j, nmk - 1);
-            const int k = q < K * P.ng_routed ? q / P.ng_routed : K;
-            const int g = k < K ? q - k * P.ng_routed : q - K * P.ng_routed;
-            v[j] = (need >> j) & 1u ? (uint32_t)ld_coh_i(reinterpret_cast<const int*>(hw) + k * P.Imax + g * kGRows) : 0u;
-          }
+        for (int i = 0; i < kSegPT; ++i) {
+          const int q = min(tid + kThreads * i, nseg - 1);
+          const int k = q < K * P.ng_routed ? q / P.ng_routed : K;
+          const int g = k < K ? q - k * P.ng_routed : q - K * P.ng_routed;
+          const uint32_t* src = hw + (size_t)k * P.hstride + g * kSegStride;
+          mk[i] = 0u;
+          if ((pend >> i) & 1u) {
+            if (!((seen >> i) & 1u)) {
+              mk[i] = (uint32_t)ld_coh_i(reinterpret_cast<const int*>(src));
+            } else if (!((slow >> i) & 1u)) {
 #pragma unroll
-          for (int j = 0; j < kMk; ++j)
-            if (v[j] != 0u) need &= ~(1u << j);
-          if (__all(need == 0u)) break;
-          __builtin_amdgcn_s_sleep(4);
-        }
-      }
-    }
-    __syncthreads();
-    const uint64_t* h2 = reinterpret_cast<const uint64_t*>(hw);
-    const int n2 = P.S * P.Imax / 2;
-    constexpr int kB = 6;
-    for (int b0 = 0; b0 < n2; b0 += kThreads * kB) {
-      uint32_t need = 0;                       // bit j: item j of this batch still missing
+              for (int f = 0; f < kGRows / 4; ++f) body[i][f] = reinterpret_cast<const uint4*>(src)[f];
+            } else {
 #pragma unroll
-      for (int j = 0; j < kB; ++j) {
-        const int i = b0 + tid + kThreads * j;
-        if (i < n2) {
-          const int k = (2 * i) / P.Imax;
-          const int e = 2 * i - k * P.Imax;
-          if (e < (k == K ? Is : I)) need |= 1u << j;
-        }
-      }
-      for (int spin = 0; need && spin < kSpinLimit; ++spin) {
-        // The first pass reads through the XCD's L2: every down unit that
-        // reads this copy of h runs on the same XCD (workgroups are dealt to
-        // the 8 XCDs round robin and the copy is picked by block index), so
-        // one of them fetches a line from memory and the rest hit L2.  A line cached in L2 is never older than this launch (the L2s
-        // are invalidated at kernel start) and values are only trusted when
-        // their "written" mark is set; anything still missing is re-read
-        // with coherent loads, which always go to memory.
-        uint64_t rg[kB];
-#pragma unroll
-        for (int j = 0; j < kB; ++j) {
-          const uint64_t* a = h2 + min(b0 + tid + kThreads * j, n2 - 1);
-          rg[j] = (need >> j) & 1u ? (spin == 0 ? *a : ld_coh64(a)) : 0ull;
-        }
-#pragma unroll
-        for (int j = 0; j < kB; ++j) {
-          const uint32_t lo = (uint32_t)rg[j], hi = (uint32_t)(rg[j] >> 32);
-          if (((need >> j) & 1u) && lo != 0u && hi != 0u) {
-            const int i = b0 + tid + kThreads * j;
-            const int k = (2 * i) / P.Imax;
-            const int e = 2 * i - k * P.Imax;
-            const int nk = (k == K ? Is : I) / kCpc;
-            float* dst = hs + (size_t)k * P.Imax + 4 * ilv<kCpc>(e / 4, nk) + e % 4;
-            dst[0] = __uint_as_float(~lo);
-            dst[1] = __uint_as_float(~hi);
-            need &= ~(1u << j);
+              for (int f = 0; f < kGRows / 4; ++f) {
+                const uint64_t a = ld_coh64(reinterpret_cast<const uint64_t*>(src) + 2 * f);
+                const uint64_t b = ld_coh64(reinterpret_cast<const uint64_t*>(src) + 2 * f + 1);
+                body[i][f] = make_uint4((uint32_t)a, (uint32_t)(a >> 32), (uint32_t)b, (uint32_t)(b >> 32));
+              }
+            }
           }
         }
-        if (need) __builtin_amdgcn_s_sleep(8);
+#pragma unroll
+        for (int i = 0; i < kSegPT; ++i) {
+          if (!((pend >> i) & 1u)) continue;
+          if (!((seen >> i) & 1u)) {
+            if (mk[i] != 0u) seen |= 1u << i;
+            continue;
+          }
+          bool full = true;
+#pragma unroll
+          for (int f = 0; f < kGRows / 4; ++f)
+            full = full && body[i][f].x != 0u && body[i][f].y != 0u && body[i][f].z != 0u && body[i][f].w != 0u;
+          if (!full) {                           // a value not visible yet: re-read from memory
+            if (!((slow >> i) & 1u)) tl_count(5, 1);
+            slow |= 1u << i;
+            continue;
+          }
+          const int q = tid + kThreads * i;
+          const int k = q < K * P.ng_routed ? q / P.ng_routed : K;
+          const int g = k < K ? q - k * P.ng_routed : q - K * P.ng_routed;
+          const int nk = (k == K ? Is : I) / kCpc;
+          float4* dst = reinterpret_cast<float4*>(hs + (size_t)k * P.Imax);
+#pragma unroll
+          for (int f = 0; f < kGRows / 4; ++f)
+            dst[ilv<kCpc>(g * (kGRows / 4) + f, nk)] =
+                make_float4(__uint_as_float(~body[i][f].x), __uint_as_float(~body[i][f].y),
+                            __uint_as_float(~body[i][f].z), __uint_as_float(~body[i][f].w));
+          pend &= ~(1u << i);
+        }
       }
-      if (need) atomicOr(P.ctr, 8);
+      if (__syncthreads_and(pend == 0u)) {
+        tl_mark(2);                              // D: every segment of h in LDS
+        if (tid == 0) tl_count(6, round + 1);    // rounds the unit took
+        break;
+      }
+      if (round >= kSpinLimit / 64) {            // bounded: give up, record it
+        if (tid == 0) atomicOr(P.ctr, 8);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
     }
   } else {
   // wait for token t's h (and the routing weights, the shared gate)
@@ -928,15 +1064,12 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     }
   }
   }
-  if (FUSED && tid == kThreads - kWave) s_done = last_reader;
-  __syncthreads();
-  if (s_done) {
-    if constexpr (FUSED) {
-      for (int i = tid; i < kRep * K; i += kThreads) st_coh_u64(route_line(P, i / K, t) + i % K, 0);
-    } else {
-      if (tid < kRep) st_coh_i(ready_line(P, tid, t), 0);
-    }
+  if constexpr (!FUSED) {
+    __syncthreads();
+    if (s_done && tid < kRep) st_coh_i(ready_line(P, tid, t), 0);
   }
+  tl_mark(3);                                  // D: h of every slot staged
+  {
   // chunk sums of every slot, one (slot, chunk) pair per thread
   for (int q = tid; q < tot; q += kThreads) {
     const int k = q < K * cpr ? q / cpr : K;
@@ -952,25 +1085,33 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     hsum[(size_t)k * (P.Imax / kCpc) + cc] = sum;
   }
   __syncthreads();
-  // the wave's row: per-lane partials over the lane's chunks, then the wave sum
+  // the terms of the wave's row, one per chunk of the lane
+#pragma unroll
+  for (int j = 0; j < DCH; ++j) {
+    const int k = (kc[j] >> 16) - 1, cj = kc[j] & 0xFFFF;
+    term[j] = 0.f;
+    if (k >= 0 && rl < nrows) {
+      const bool sh = k == K;
+      const int Ik = sh ? Is : I;
+      const int gpr = Ik >> esh;
+      const float4* hk = reinterpret_cast<const float4*>(hs + (size_t)k * P.Imax);
+      const float dd = chunk_dot<BITS>(wv[j], hk + cj, Ik / kCpc);
+      const int gi = (sh ? K * kDRows * gr : k * kDRows * gr) + rl * gpr + ((cj * kCpc) >> esh);
+      const int boff = K * kDRows * gr + kDRows * gs;    // biases follow all scales
+      term[j] = fmaf(bf16_to_f32(sbl[gi]), dd,
+                     bf16_to_f32(sbl[boff + gi]) * hsum[(size_t)k * (P.Imax / kCpc) + cj]);
+    }
+  }
+  }
+  // the wave's row: the lane's terms weighted and summed in chunk order, then
+  // the wave sum
   float pv[1];
   {
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < DCH; ++j) {
-      const int k = (kc[j] >> 16) - 1, cj = kc[j] & 0xFFFF;
-      if (k >= 0 && rl < nrows) {
-        const bool sh = k == K;
-        const int Ik = sh ? Is : I;
-        const int gpr = Ik >> esh;
-        const float4* hk = reinterpret_cast<const float4*>(hs + (size_t)k * P.Imax);
-        const float dd = chunk_dot<BITS>(wv[j], hk + cj, Ik / kCpc);
-        const int gi = (sh ? K * kDRows * gr : k * kDRows * gr) + rl * gpr + ((cj * kCpc) >> esh);
-        const int boff = K * kDRows * gr + kDRows * gs;    // biases follow all scales
-        const float part = fmaf(bf16_to_f32(sbl[gi]), dd,
-                                bf16_to_f32(sbl[boff + gi]) * hsum[(size_t)k * (P.Imax / kCpc) + cj]);
-        acc = fmaf(wk[k], part, acc);
-      }
+      const int k = (kc[j] >> 16) - 1;
+      if (k >= 0 && rl < nrows) acc = fmaf(wk[k], term[j], acc);
     }
     pv[0] = acc;
   }
@@ -980,18 +1121,66 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P,
     if (residual) v += resv;
     y[(size_t)t * H + r0 + rl] = v;
   }
+  tl_mark(4);                                  // D: y written
   if constexpr (FUSED) {
-    // clear this unit's share of the other parity's h and shared-gate
-    // buffers: the previous launch used them (as much of the h buffer as its
-    // extent word says, whatever its M), the next one fills them (off the
-    // critical path, at the end)
+    // clear this unit's share of the other parity's h, logits, selection and
+    // shared-gate buffers: the previous launch used them (as much of the h
+    // buffer as its extent word says, whatever its M), the next one fills
+    // them (off the critical path, at the end)
+    const size_t nd = (size_t)P.M * P.nc;
     const size_t nh4 = min((size_t)(unsigned)s_zx, P.hreg / 4);
-    const size_t per = (nh4 + (size_t)P.M * P.nc - 1) / ((size_t)P.M * P.nc);
-    uint4* hz = reinterpret_cast<uint4*>(P.hb + (size_t)(s_par ^ 1) * P.hreg);
+    const size_t per = (nh4 + nd - 1) / nd;
+    uint4* hz = reinterpret_cast<uint4*>(P.hb + (size_t)(par ^ 1) * P.hreg);
     for (size_t i = (size_t)d * per + tid; i < min(nh4, (size_t)(d + 1) * per); i += kThreads)
       hz[i] = make_uint4(0, 0, 0, 0);
-    if (d == 0 && tid < kFusedMaxM) P.sgb[(s_par ^ 1) * kFusedMaxM + tid] = 0u;
+    const size_t nl = (size_t)kLogitCopies * P.lstride;
+    const size_t perl = (nl + nd - 1) / nd;
+    uint64_t* lz = P.logits + (size_t)(par ^ 1) * nl;
+    for (size_t i = (size_t)d * perl + tid; i < min(nl, (size_t)(d + 1) * perl); i += kThreads) lz[i] = 0ull;
+    const size_t ns = (size_t)kSelCopies * P.sstride;
+    const size_t pers = (ns + nd - 1) / nd;
+    uint64_t* sz = P.selw + (size_t)(par ^ 1) * ns;
+    for (size_t i = (size_t)d * pers + tid; i < min(ns, (size_t)(d + 1) * pers); i += kThreads) sz[i] = 0ull;
+    if (d == 0 && tid < kFusedMaxM) P.sgb[(par ^ 1) * kFusedMaxM + tid] = 0u;
+    // how much of this launch's h buffer it fills (the launch after next
+    // clears that much of it)
+    if (d == 0 && tid == 0) st_coh_i(P.hext + par, (int)((size_t)kHCopies * P.P * P.hstride / 4));
+    // the last D unit of the launch to get here moves the launch counter on:
+    // every unit of this launch has read it by then (each D unit has, and
+    // every G and R unit ran before the last D unit could finish)
+    drain();
+    __syncthreads();
+    if (tid == 0 && arrive(P.dctr, d, (int)nd)) st_coh_i(P.epoch, ld_coh_i(P.epoch) + 1);
   }
+}
+
+// Block -> unit (0 R, 1 G, 2 D; *u its index among its kind).  With routing
+// in the launch (r_half != 0) the R units take the first r_half positions on
+// XCDs 0 and 1: workgroups are dealt to the XCDs round robin (block b to XCD
+// b % 8) and the XCDs start dispatching one after another, XCD 0 first, so
+// the router rows and the selector (R unit 0 = block 0) start earliest.  The
+// other blocks, in order, are the G units, then the D units, so on every XCD
+// the units a unit waits for come before it.
+__device__ __forceinline__ int unit_of(int b, const DecPlan& P, int* u) {
+  if (P.r_half) {
+    const int q = b >> 3, xcd = b & 7;
+    if (xcd < 2 && q < P.r_half) {
+      *u = 2 * q + xcd;
+      return 0;
+    }
+    b -= 2 * min(q, P.r_half) + (q < P.r_half ? min(xcd, 2) : 0);
+  } else if (b < P.r_units) {
+    *u = b;
+    return 0;
+  } else {
+    b -= P.r_units;
+  }
+  if (b < P.g_units) {
+    *u = b;
+    return 1;
+  }
+  *u = b - P.g_units;
+  return 2;
 }
 
 // 8-bit layers of up to 2048 columns: at most 80 VGPRs, so three units fit per
@@ -1004,17 +1193,58 @@ __global__ void __launch_bounds__(kThreads)
                                                         const float* __restrict__ wts,
                                                         const float* __restrict__ residual,
                                                         float* __restrict__ y) {
-  int u = blockIdx.x;
-  if constexpr (FUSED) {
-    if (u < P.r_units) {
-      route_unit<!(BITS == 8 && CPL <= 2 && DCH <= 6), NORM>(L, P, R, x, u);
-      return;
-    }
-    u -= P.r_units;
-  }
-  if (u < P.g_units) gate_up_unit<BITS, CPL, FUSED, NORM>(L, P, x, idx, u);
-  else down_unit<BITS, DCH, FUSED>(L, P, idx, wts, residual, y, u - P.g_units);
+  // the 80-register form (8-bit, narrow rows) keeps the one-wave selection
+  // and the logit polls small: E <= 256 there
+  constexpr bool kWide = !(BITS == 8 && CPL <= 2 && DCH <= 6);
+  constexpr int kPoll = kWide ? kMaxExperts / kWave : 4;
+  int u;
+  const int role = unit_of((int)blockIdx.x, P, &u);
+  tl_begin();
+  // router chunks per lane and wave half: H / 2048, from the G units' CPL
+  constexpr int kRc = CPL * 4 / BITS < 1 ? 1 : (CPL * 4 / BITS > 2 ? 2 : CPL * 4 / BITS);
+  if (FUSED && role == 0) route_unit<NORM, kRc>(L, P, R, x, u);
+  else if (role == 1) gate_up_unit<BITS, CPL, FUSED, NORM, kWide, kPoll>(L, P, x, idx, u, R.renorm);
+  else down_unit<BITS, DCH, FUSED, kWide, kPoll>(L, P, R, idx, wts, residual, y, u);
+  tl_end();
 }
+
+#ifdef MOEQ_TIMELINE
+// timeline build only: the last launch's timestamps out to the host
+extern "C" int moeq_timeline_copy(uint64_t* host, size_t n) {
+  if (n > (size_t)kTlBlocks * kTlEvents) n = (size_t)kTlBlocks * kTlEvents;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(g_tl), n * sizeof(uint64_t)) == hipSuccess ? 0 : -10;
+}
+extern "C" int moeq_timeline_clear() {
+  static uint64_t zeros[kTlBlocks * kTlEvents];
+  return hipMemcpyToSymbol(HIP_SYMBOL(g_tl), zeros, sizeof(zeros)) == hipSuccess ? 0 : -10;
+}
+
+// The read ceiling the decode layer streams against: `bytes` read once in
+// 16-byte loads, four in flight per thread, by `blocks` blocks of 256 threads
+// (each block's words folded into one value, stored only if it is a
+// sentinel, so the loads cannot be dropped).
+__global__ void __launch_bounds__(256) k_read_probe(const uint4* __restrict__ p, size_t n16,
+                                                    uint32_t* __restrict__ out) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  uint32_t acc = 0;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const uint4 a = p[i], b = p[i + stride], c = p[i + 2 * stride], d = p[i + 3 * stride];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (; i < n16; i += stride) {
+    const uint4 a = p[i];
+    acc ^= a.x ^ a.y ^ a.z ^ a.w;
+  }
+  if (acc == 0x9E3779B9u) out[blockIdx.x] = acc;
+}
+
+extern "C" int moeq_read_probe(const void* p, size_t bytes, int blocks, uint32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_read_probe, dim3(blocks), dim3(256), 0, s, reinterpret_cast<const uint4*>(p),
+                     bytes / 16, out);
+  return hipGetLastError() == hipSuccess ? 0 : -10;
+}
+#endif
 
 // The error word (the state block's first int, where every bounded wait of
 // the decode launches records a timeout) out to the caller, then cleared.
@@ -1045,11 +1275,20 @@ DecState dec_state(const DecodeLayer& L, int K, void* ws) {
   D.ready = reinterpret_cast<int*>(take(sizeof(int) * (size_t)kRep * D.rstride));
   D.epoch = reinterpret_cast<int*>(take(sizeof(int) * 4));
   D.hext = D.epoch ? D.epoch + 1 : nullptr;
-  D.hreg = (size_t)kHCopies * kFusedMaxM * S * Imax;
+  D.hstride = kSegStride * (L.has_shared && L.Is > L.I ? (L.Is + kGRows - 1) / kGRows
+                                                        : (L.I + kGRows - 1) / kGRows);
+  D.hreg = (size_t)kHCopies * kFusedMaxM * S * D.hstride;
   D.hb = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 2 * D.hreg));
   D.sgb = reinterpret_cast<uint32_t*>(take(sizeof(uint32_t) * 2 * kFusedMaxM));
-  D.logits = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * (size_t)kFusedMaxM * L.E));
-  D.idx_c = reinterpret_cast<int32_t*>(take(sizeof(int) * (size_t)kRep * D.rstride));
+  // logit copies kFusedMaxM x E each, 4 KB + 256 B apart at least (on other channels)
+  D.lstride = (int)((((size_t)kFusedMaxM * L.E * sizeof(uint64_t) + 4095) / 4096 * 4096 + 256) /
+                    sizeof(uint64_t));
+  D.logits = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * 2 * kLogitCopies * (size_t)D.lstride));
+  // selection copies kFusedMaxM x kMaxTopK each, 4 KB + 256 B apart at least
+  D.sstride = (int)((((size_t)kFusedMaxM * kMaxTopK * sizeof(uint64_t) + 4095) / 4096 * 4096 + 256) /
+                    sizeof(uint64_t));
+  D.selw = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * 2 * kSelCopies * (size_t)D.sstride));
+  D.dctr = reinterpret_cast<int*>(take(sizeof(int) * (size_t)kLine * (1 + kFan)));
   D.route_ctr = reinterpret_cast<int*>(take(route_ctr_bytes()));
   D.bcounts = reinterpret_cast<int32_t*>(take(sizeof(int32_t) * (size_t)L.E));
   D.bytes = off;
@@ -1071,6 +1310,17 @@ static DecPlan make_dec_plan(const DecodeLayer& L, int M, int K, bool routed, vo
   P.nc = (L.H + kDRows - 1) / kDRows;
   P.d_units = M * P.nc;
   P.r_units = routed ? (L.E + kRRows - 1) / kRRows : 0;
+  P.r_half = 0;
+  if (routed) {
+    // up to 32 R units on XCDs 0 and 1 (an even count; a unit past the last
+    // row publishes nothing) when the grid reaches their blocks; more are
+    // spread over every XCD in block order
+    const int r2 = (P.r_units + 1) & ~1;
+    if (r2 <= 32 && 8 * (r2 / 2 - 1) + 1 < r2 + P.g_units + P.d_units) {
+      P.r_units = r2;
+      P.r_half = r2 / 2;
+    }
+  }
   const DecState D = dec_state(L, K, ws);
   P.ctr = D.ctr;
   P.ready = D.ready;
@@ -1079,9 +1329,13 @@ static DecPlan make_dec_plan(const DecodeLayer& L, int M, int K, bool routed, vo
   P.hext = D.hext;
   P.hb = D.hb;
   P.hreg = D.hreg;
+  P.hstride = D.hstride;
   P.sgb = D.sgb;
   P.logits = D.logits;
-  P.idx_c = D.idx_c;
+  P.lstride = D.lstride;
+  P.selw = D.selw;
+  P.sstride = D.sstride;
+  P.dctr = D.dctr;
   auto al = [](size_t v) { return (v + 255) / 256 * 256; };
   size_t off = D.bytes;
   char* base = reinterpret_cast<char*>(ws);
@@ -1100,25 +1354,21 @@ size_t decode_ws_bytes(const DecodeLayer& L, int M, int K, bool routed) {
   return b;
 }
 
-// scale/bias words (16 bytes) a D unit stages: all slots, scales and biases
-static int d_sb_words(const DecodeLayer& L, int K) {
-  const int egs = L.gate.group_size;
-  return 2 * kDRows * (K * (L.I / egs) + (L.has_shared ? L.Is / egs : 0)) * 2 / 16;
-}
+static int d_sb_words(const DecodeLayer& L, int K) { return d_sb_words_dev(L, K); }
 
 static size_t dec_lds_bytes(const DecodeLayer& L, int K, bool routed, int M) {
   // G: x (H floats) + chunk sums (<= H/16) + 4 x 16 rows x groups bf16;
   // D: h of all S slots (S x Imax floats) + their chunk sums (<= 1/16 of that)
   //    + the staged scale/bias words;
-  // R (last unit only): E keys and E fp64 logits
-  const size_t g = sizeof(float) * (L.H + pad4(L.H / 16)) + 2 * 4 * kGRows * (L.H / L.gate.group_size);
+  // with routing in the launch, G and D also hold the token's E router keys
+  // and logits while they select, and R units the x of the M tokens
+  const size_t sel = routed ? 16 * (size_t)L.E : 0;
+  const size_t g = sizeof(float) * (L.H + pad4(L.H / 16)) + 2 * 4 * kGRows * (L.H / L.gate.group_size) + sel;
   const int S = K + (L.has_shared ? 1 : 0);
   const int Im = L.has_shared && L.Is > L.I ? L.Is : L.I;
-  const size_t d = sizeof(float) * ((size_t)S * Im + pad4(S * Im / 16)) + 16 * (size_t)d_sb_words(L, K);
-  const size_t r = routed ? 16 * (size_t)L.E : 0;        // + x of the M tokens below
+  const size_t d = sizeof(float) * ((size_t)S * Im + pad4(S * Im / 16)) + 16 * (size_t)d_sb_words(L, K) + sel;
   const size_t rx = routed ? sizeof(float) * (size_t)M * L.H : 0;
   size_t m = g > d ? g : d;
-  m = m > r ? m : r;
   return m > rx ? m : rx;
 }
 
@@ -1155,8 +1405,12 @@ bool decode_supported(const DecodeLayer& L, int K) {
 }
 
 bool fused_supported(const DecodeLayer& L, const QT& router, int M, int K) {
+  // the 80-register form (8-bit, rows of at most 2 chunks per lane, D rows of
+  // at most 6) polls at most 4 logits per lane: E <= 256
+  const bool narrow = L.gate.bits == 8 && g_cpl(L.H, 8) <= 2 && d_ch(L, K) <= 6;
   return decode_supported(L, K) && router.bits == 8 && router.rows == L.E && router.cols == L.H &&
-         M >= 1 && M <= kFusedMaxM && L.E <= kMaxExperts && dec_lds_bytes(L, K, true, M) <= 160 * 1024;
+         M >= 1 && M <= kFusedMaxM && L.E <= (narrow ? 4 * kWave : kMaxExperts) &&
+         dec_lds_bytes(L, K, true, M) <= 160 * 1024;
 }
 
 template <int B, int CPL, int DCH, bool FUSED, bool NORM>

@@ -72,9 +72,14 @@ struct DecState {
   int* hext;         // [2] 16-byte words of each h buffer the last launch using it wrote
   uint32_t* hb;      // [2][hreg] complemented-bit h buffers of the one-launch form
   size_t hreg;       // words per h buffer
+  int hstride;       // words per (copy, pair) row of an h buffer (segments on 128-byte lines)
   uint32_t* sgb;     // [2][kFusedMaxM] shared-gate logits, the same way
-  uint64_t* logits;  // [kFusedMaxM][E] complemented fp64 logits, 0 = not written
-  int32_t* idx_c;    // route-line copies
+  uint64_t* logits;  // [2 parities][copies][lstride] complemented fp64 logits [kFusedMaxM][E], 0 = not written
+  int lstride;       // u64 words per logit copy
+  uint64_t* selw;    // [2 parities][copies][sstride]: [kFusedMaxM][kMaxTopK] complemented
+                     // (expert << 32 | fp32 weight bits) of every slot, 0 = not written
+  int sstride;
+  int* dctr;         // arrival counter lines of the one-launch form's D units (the launch's last one)
   int* route_ctr;    // counters of a separate routing launch
   int32_t* bcounts;  // [E] per-expert pair counts of the batched form
   size_t bytes;      // size of the block (256-byte multiple)
@@ -86,18 +91,25 @@ struct DecPlan {
   int M, K, S, P, Imax;
   int ng_routed, ng_shared, g_units, nc, d_units;
   int r_units;     // router units in front of the expert units (routing in the launch), else 0
+  int r_half;      // R units per XCD on XCDs 0 and 1 (block placement), 0: R units first in order
   int* ctr;        // 128-byte lines: error word, then per token G and D arrival counters
   int* ready;      // ready flags: copies [kRep] of token lines, rstride ints apart
   int rstride;
   float* h;        // [copies][P][Imax] (pair p = token * S + slot)
   float* sg;       // [M]
-  uint64_t* logits;  // [kFusedMaxM][E] router logits as complemented fp64 bits, 0 = not written
+  uint64_t* logits;  // [2 parities][copies][lstride]: router logits [kFusedMaxM][E] as complemented
+                     // fp64 bits, 0 = not written
+  int lstride;
+  uint64_t* selw;    // [2 parities][copies][sstride]: every slot's (expert << 32 | fp32 weight
+                     // bits), complemented, 0 = not written; [kFusedMaxM][kMaxTopK] per copy
+  int sstride;
+  int* dctr;         // arrival counter lines of the D units (the launch's last one moves epoch on)
   int* epoch;        // launch counter (routing in the launch): its parity picks the h buffer
   int* hext;         // [2] extent (16-byte words) of each h buffer's last use
-  uint32_t* hb;      // [2][hreg]: [copies][P][Imax] h as complemented fp32 bits, 0 = not written
+  uint32_t* hb;      // [2][hreg]: [copies][P][hstride] h as complemented fp32 bits, 0 = not written
   size_t hreg;
+  int hstride;       // segments of kGRows values, each at the front of a 128-byte line
   uint32_t* sgb;     // [2][kFusedMaxM] shared-gate logits, the same way
-  int32_t* idx_c;  // route lines: copies [kRep] of token lines (64-bit expert + 1 | weight words)
   const float* norm_w;  // RMSNorm weight [H] of a launch that normalizes x first, else null
   float norm_eps;
 };

@@ -95,6 +95,15 @@ _SIGNATURES = {
 }
 
 
+def use_library(path: str) -> None:
+    """Load the library from ``path`` instead of lib/libmoeq.so (e.g. the
+    instrumented timeline build); only before the first call."""
+    global LIB_PATH
+    if _lib is not None:
+        raise RuntimeError("libmoeq is already loaded")
+    LIB_PATH = path
+
+
 def lib() -> ctypes.CDLL:
     """Load libmoeq.so (once).  Raises if it has not been built."""
     global _lib
