@@ -18,7 +18,9 @@ import numpy as np
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libmoeq.so")
+# MOEQ_LIBRARY names another build of the same library (the AddressSanitizer
+# build of the host front end, for the host tests of the boundary)
+LIB_PATH = os.environ.get("MOEQ_LIBRARY") or os.path.join(_HERE, "lib", "libmoeq.so")
 
 PATH_ROUTE, PATH_DECODE, PATH_GATHER, PATH_GQMM, PATH_FORWARD, PATH_FORWARD_NORM = 0, 1, 2, 3, 4, 5
 MODE_AFFINE, MODE_MXFP4 = 0, 1
