@@ -11,7 +11,10 @@
 // bf16 in LDS and the B codes dequantized to bf16 in LDS (w = scale*code +
 // bias, rounded to nearest even).  LDS holds two stages: while the waves run
 // the MFMAs of one stage, the next steps' global loads land in registers (two
-// steps ahead) and are written to the other stage, one barrier per step.
+// steps ahead), and the step after this one is dequantized and written to
+// the other stage a quarter per 16-wide k slice, between the slices' MFMAs
+// (affine codes; the mxfp4 form writes the whole stage after the MFMAs), one
+// barrier per step.
 // Eight waves, two per SIMD, each own a 128x64 sub-tile (4x2 MFMA 32x32
 // tiles): the two waves of a SIMD hide each other's load, LDS and barrier
 // waits, and a 256-column block re-reads the gathered A rows half as often as
@@ -254,13 +257,67 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
     }
   };
 
+  // codes [8 q, 8 q + 8) of the thread's 32 in a register stage, to four
+  // packed bf16 pairs (one quarter of what MOEQ_LSTORE writes)
+  auto deq8 = [&](const u32x4* BR, int q, float SV, float CV, uint32_t* o4) {
+    if constexpr (MX) {
+      const uint32_t x = BR[0][q] & (SV != 0.f ? 0xFFFFFFFFu : 0u);
+      o4[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, SV, 0));
+      o4[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, SV, 1));
+      o4[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, SV, 2));
+      o4[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(x, SV, 3));
+    } else {
+      constexpr int kPer = 32 / BITS;
+      constexpr uint32_t kMask = (1u << BITS) - 1u;
+#pragma unroll
+      for (int j = 0; j < 8; j += 2) {
+        const int ca = 8 * q + j, cb = ca + 1;
+        const uint32_t xa = BR[(ca / kPer) / 4][(ca / kPer) % 4], xb = BR[(cb / kPer) / 4][(cb / kPer) % 4];
+        o4[j / 2] = pack_bf16(fmaf(SV, (float)((xa >> (BITS * (ca % kPer))) & kMask), CV),
+                              fmaf(SV, (float)((xb >> (BITS * (cb % kPer))) & kMask), CV));
+      }
+    }
+  };
+  // a step's MFMAs on LDS stage rbuf, with the next step (register stage
+  // AR/BR, loaded one step earlier) dequantized and written to the other LDS
+  // stage a quarter per 16-wide k slice, so the dequantization runs between
+  // the MFMAs instead of after them (the other stage was last read before the
+  // previous barrier)
+  auto fused_step = [&](int rbuf, const u32x4* AR, const u32x4* BR, uint32_t SRAW, uint32_t CRAW, float MV) {
+    const float SV = (MX ? e8m0_f32(SRAW) : bf16_to_f32(SRAW)) * MV;
+    const float CV = (MX ? 0.f : bf16_to_f32(CRAW)) * MV;
+    const uint16_t* As = gsm + rbuf * kStage;
+    const uint16_t* Bs = As + kBM * kLds;
+    uint16_t* Aw = gsm + (rbuf ^ 1) * kStage;
+    u32x4* dB = reinterpret_cast<u32x4*>(&Aw[kBM * kLds + bc * kLds + bh * 32]);
+#pragma unroll
+    for (int kk = 0; kk < kBK / 16; ++kk) {
+      const int kof = kk * 16 + 8 * (lane >> 5);
+      bf16x8 af[4], bfr[2];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+        af[mi] = *reinterpret_cast<const bf16x8*>(&As[(wm * 128 + mi * 32 + (lane & 31)) * kLds + kof]);
+#pragma unroll
+      for (int ni = 0; ni < 2; ++ni)
+        bfr[ni] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + ni * 32 + (lane & 31)) * kLds + kof]);
+      uint32_t o4[4];
+      deq8(BR, kk, SV, CV, o4);
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+      *reinterpret_cast<u32x4*>(&Aw[((tid >> 3) + 64 * kk) * kLds + aseg * 8]) = AR[kk];
+      dB[kk] = u32x4{o4[0], o4[1], o4[2], o4[3]};
+    }
+  };
+
   // a step: the loads of step kt+2 go out first (into the register stage step
-  // kt used), the MFMAs of step kt run on LDS stage kt % 2, then step kt+1
+  // kt used), the MFMAs of step kt run on LDS stage kt % 2 while step kt+1
   // (loaded one step earlier) is written to the other LDS stage.  The body
-  // has no branches (loads past the last step re-read it), so the compiler
-  // can interleave the loads, LDS traffic and dequantization with the MFMAs;
-  // both halves always run their MFMAs, and with an odd step count the last
-  // half's B stage is written with zero scale and bias so it adds nothing.
+  // has no branches (loads past the last step re-read it); both halves
+  // always run their MFMAs, and with an odd step count the last half's B
+  // stage is written with zero scale and bias so it adds nothing.
   const int klast = ksteps - 1;
   MOEQ_GLOAD(a0, b0, s0, c0, m0, 0);
   MOEQ_GLOAD(a1, b1, s1, c1, m1, min(1, klast));
@@ -269,16 +326,26 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
   for (int kt = 0; kt < ksteps; kt += 2) {
     const float on = kt + 1 < ksteps ? 1.f : 0.f;
     MOEQ_GLOAD(a0, b0, s0, c0, m0, min(kt + 2, klast));
-    // affine: the loads go out before this step's MFMAs (the scheduler
-    // would sink them; measured faster on 8-bit codes, slower on mxfp4)
-    if constexpr (!MX) __builtin_amdgcn_sched_barrier(0);
-    mfma_step(0);
-    MOEQ_LSTORE(a1, b1, s1, c1, m1 * on, 1);
+    if constexpr (!MX) {
+      // affine: the loads go out before this step's MFMAs (the scheduler
+      // would sink them), the next stage's dequantization between them
+      __builtin_amdgcn_sched_barrier(0);
+      fused_step(0, a1, b1, s1, c1, m1 * on);
+    } else {
+      // mxfp4 (a few conversion instructions per stage): the MFMAs, then
+      // the next stage; measured faster this way than interleaved
+      mfma_step(0);
+      MOEQ_LSTORE(a1, b1, s1, c1, m1 * on, 1);
+    }
     __syncthreads();
     MOEQ_GLOAD(a1, b1, s1, c1, m1, min(kt + 3, klast));
-    if constexpr (!MX) __builtin_amdgcn_sched_barrier(0);
-    mfma_step(1);
-    MOEQ_LSTORE(a0, b0, s0, c0, m0, 0);
+    if constexpr (!MX) {
+      __builtin_amdgcn_sched_barrier(0);
+      fused_step(1, a0, b0, s0, c0, m0);
+    } else {
+      mfma_step(1);
+      MOEQ_LSTORE(a0, b0, s0, c0, m0, 0);
+    }
     __syncthreads();
   }
 #undef MOEQ_GLOAD
