@@ -30,6 +30,8 @@
 //                  a block's columns are 128 rows i of gate and the same
 //                  128 of up (per wave: 32 of each)
 //        2 down    ypair[pair][n] = w_pair * (h[sorted row] . D_e[n]) (bf16)
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -283,7 +285,10 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
   // stage a quarter per 16-wide k slice, so the dequantization runs between
   // the MFMAs instead of after them (the other stage was last read before the
   // previous barrier)
-  auto fused_step = [&](int rbuf, const u32x4* AR, const u32x4* BR, uint32_t SRAW, uint32_t CRAW, float MV) {
+  // MM false: a wave whose 128 rows all lie past the tile's last row (in an
+  // expert's last, partial tile) only stages the next step, no MFMAs
+  auto fused_step = [&](int rbuf, const u32x4* AR, const u32x4* BR, uint32_t SRAW, uint32_t CRAW, float MV,
+                        auto MM) {
     const float SV = (MX ? e8m0_f32(SRAW) : bf16_to_f32(SRAW)) * MV;
     const float CV = (MX ? 0.f : bf16_to_f32(CRAW)) * MV;
     const uint16_t* As = gsm + rbuf * kStage;
@@ -293,20 +298,24 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
 #pragma unroll
     for (int kk = 0; kk < kBK / 16; ++kk) {
       const int kof = kk * 16 + 8 * (lane >> 5);
-      bf16x8 af[4], bfr[2];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-        af[mi] = *reinterpret_cast<const bf16x8*>(&As[(wm * 128 + mi * 32 + (lane & 31)) * kLds + kof]);
-#pragma unroll
-      for (int ni = 0; ni < 2; ++ni)
-        bfr[ni] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + ni * 32 + (lane & 31)) * kLds + kof]);
       uint32_t o4[4];
-      deq8(BR, kk, SV, CV, o4);
+      if constexpr (decltype(MM)::value) {
+        bf16x8 af[4], bfr[2];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+        for (int mi = 0; mi < 4; ++mi)
+          af[mi] = *reinterpret_cast<const bf16x8*>(&As[(wm * 128 + mi * 32 + (lane & 31)) * kLds + kof]);
 #pragma unroll
         for (int ni = 0; ni < 2; ++ni)
-          acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+          bfr[ni] = *reinterpret_cast<const bf16x8*>(&Bs[(wn * 64 + ni * 32 + (lane & 31)) * kLds + kof]);
+        deq8(BR, kk, SV, CV, o4);
+#pragma unroll
+        for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+          for (int ni = 0; ni < 2; ++ni)
+            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[ni], af[mi], acc[mi][ni], 0, 0, 0);
+      } else {
+        deq8(BR, kk, SV, CV, o4);
+      }
       *reinterpret_cast<u32x4*>(&Aw[((tid >> 3) + 64 * kk) * kLds + aseg * 8]) = AR[kk];
       dB[kk] = u32x4{o4[0], o4[1], o4[2], o4[3]};
     }
@@ -323,31 +332,38 @@ __global__ void __launch_bounds__(kThreads, 1) k_gqmm(QT W, QT W2, int N, int Kd
   MOEQ_GLOAD(a1, b1, s1, c1, m1, min(1, klast));
   MOEQ_LSTORE(a0, b0, s0, c0, m0, 0);
   __syncthreads();
-  for (int kt = 0; kt < ksteps; kt += 2) {
-    const float on = kt + 1 < ksteps ? 1.f : 0.f;
-    MOEQ_GLOAD(a0, b0, s0, c0, m0, min(kt + 2, klast));
-    if constexpr (!MX) {
-      // affine: the loads go out before this step's MFMAs (the scheduler
-      // would sink them), the next stage's dequantization between them
-      __builtin_amdgcn_sched_barrier(0);
-      fused_step(0, a1, b1, s1, c1, m1 * on);
-    } else {
-      // mxfp4 (a few conversion instructions per stage): the MFMAs, then
-      // the next stage; measured faster this way than interleaved
-      mfma_step(0);
-      MOEQ_LSTORE(a1, b1, s1, c1, m1 * on, 1);
+  auto kloop = [&](auto MM) {
+    for (int kt = 0; kt < ksteps; kt += 2) {
+      const float on = kt + 1 < ksteps ? 1.f : 0.f;
+      MOEQ_GLOAD(a0, b0, s0, c0, m0, min(kt + 2, klast));
+      if constexpr (!MX) {
+        // affine: the loads go out before this step's MFMAs (the scheduler
+        // would sink them), the next stage's dequantization between them
+        __builtin_amdgcn_sched_barrier(0);
+        fused_step(0, a1, b1, s1, c1, m1 * on, MM);
+      } else {
+        // mxfp4 (a few conversion instructions per stage): the MFMAs, then
+        // the next stage; measured faster this way than interleaved
+        if constexpr (decltype(MM)::value) mfma_step(0);
+        MOEQ_LSTORE(a1, b1, s1, c1, m1 * on, 1);
+      }
+      __syncthreads();
+      MOEQ_GLOAD(a1, b1, s1, c1, m1, min(kt + 3, klast));
+      if constexpr (!MX) {
+        __builtin_amdgcn_sched_barrier(0);
+        fused_step(1, a0, b0, s0, c0, m0, MM);
+      } else {
+        if constexpr (decltype(MM)::value) mfma_step(1);
+        MOEQ_LSTORE(a0, b0, s0, c0, m0, 0);
+      }
+      __syncthreads();
     }
-    __syncthreads();
-    MOEQ_GLOAD(a1, b1, s1, c1, m1, min(kt + 3, klast));
-    if constexpr (!MX) {
-      __builtin_amdgcn_sched_barrier(0);
-      fused_step(1, a0, b0, s0, c0, m0);
-    } else {
-      mfma_step(1);
-      MOEQ_LSTORE(a0, b0, s0, c0, m0, 0);
-    }
-    __syncthreads();
-  }
+  };
+  // a wave whose rows all lie past the tile's count (the lower half of an
+  // expert's last tile of at most 128 rows) skips its MFMAs: they would
+  // multiply rows that are never stored
+  if (wm * 128 < rows) kloop(std::true_type{});
+  else kloop(std::false_type{});
 #undef MOEQ_GLOAD
 #undef MOEQ_LSTORE
 
