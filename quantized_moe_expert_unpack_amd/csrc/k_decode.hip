@@ -1268,7 +1268,6 @@ DecState dec_state(const DecodeLayer& L, int K, void* ws) {
   char* base = reinterpret_cast<char*>(ws);
   auto take = [&](size_t n) { char* p = base ? base + off : nullptr; off += al(n); return p; };
   const int S = K + (L.has_shared ? 1 : 0);
-  const int Imax = L.has_shared && L.Is > L.I ? L.Is : L.I;
   D.ctr = reinterpret_cast<int*>(take(sizeof(int) * (size_t)kLine * (1 + (size_t)kCtrLines * kDecMaxM)));
   // flag copies: kRep blocks of kDecMaxM lines, 4 KB + 256 B apart at least
   D.rstride = (int)((((size_t)kDecMaxM * kLine * sizeof(int) + 4095) / 4096 * 4096 + 256) / sizeof(int));
