@@ -42,10 +42,11 @@ KT_BLOCKS, KT_EVENTS = 4096, 12
 
 
 def plan(cfg, m=1):
-    """Unit counts of the one-launch kernel (16 router rows per R unit, 16
+    """Unit counts of the one-launch kernel (4 router rows per R unit, 16
     gate/up rows per G unit, 8 output rows per D unit) and the kind of every
-    block: R units on XCDs 0 and 1 first (block b runs on XCD b % 8), R unit 0
-    selecting; then G units, then D units, in block order."""
+    block: up to 32 R units (an even count) take the first blocks of XCDs 0
+    and 1 (block b runs on XCD b % 8), more are the first blocks in order;
+    then G units, then D units, in block order."""
     r_units = (cfg.experts + 3) // 4
     ng = (cfg.inter + 15) // 16
     ngs = (cfg.shared_inter + 15) // 16 if cfg.has_shared else 0
