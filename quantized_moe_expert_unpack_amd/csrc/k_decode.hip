@@ -804,7 +804,6 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
   const int c = d - t * P.nc;
   const int r0 = c * kDRows;
   const int nrows = min(kDRows, H - r0);
-  const int rl = wid;                          // the wave's row
   const int I = L.I, Is = L.Is;
   const int cpr = I / kCpc;                    // chunks per routed down row
   const int cps = L.has_shared ? Is / kCpc : 0;
@@ -813,18 +812,16 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
   // the launch's parity (its logits and h buffers), read first
   const int par = FUSED ? (ld_coh_i(P.epoch) & 1) : 0;
   int* tl = P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines);
-  // slot and chunk of every chunk position of the lane (q = lane + 64 j)
-  // (packed in one register: (slot + 1) << 16 | chunk; slot -1 = no chunk)
-  int kc[DCH];
-#pragma unroll
-  for (int j = 0; j < DCH; ++j) {
-    const int q = lane + kWave * j;
-    kc[j] = 0;
-    if (q < tot) {
-      const int k = q < K * cpr ? q / cpr : K;
-      kc[j] = ((k + 1) << 16) | (k < K ? q - k * cpr : q - K * cpr);
-    }
-  }
+  // the thread's chunk and rows: the threads form kTG groups of kThreads/kTG
+  // (kTG = 8/DCH rounded down to a power of two, so a group has a thread
+  // for each of the tot <= 64 DCH chunks of all slots); group gq takes rows
+  // gq kRPT ... + kRPT - 1, its thread lq chunk lq: slot kq (-1: none),
+  // chunk cq within the slot
+  constexpr int kTG = DCH == 1 ? 8 : DCH == 2 ? 4 : DCH <= 4 ? 2 : 1;
+  constexpr int kRPT = kDRows / kTG;
+  const int gq = tid / (kThreads / kTG), lq = tid % (kThreads / kTG);
+  const int kq = lq < tot ? (lq < K * cpr ? lq / cpr : K) : -1;
+  const int cq = kq < 0 ? 0 : (kq < K ? lq - kq * cpr : lq - K * cpr);
 
   if (tid == 0) bad = 0;
   if constexpr (!FUSED) {
@@ -840,8 +837,8 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
   // (the router keys and logits of the token in LDS while it selects, past
   // the unit's h, chunk sums and scale/bias words)
   float* hs = smem;                            // [S][Imax]
-  float* hsum = hs + (size_t)P.S * P.Imax;     // [S][Imax/kCpc]
-  uint16_t* sbl = reinterpret_cast<uint16_t*>(hsum + pad4(P.S * P.Imax / 16));   // 16-byte aligned
+  // (then a region of S * Imax / 16 floats, unused, ahead of the scales)
+  uint16_t* sbl = reinterpret_cast<uint16_t*>(hs + (size_t)P.S * P.Imax + pad4(P.S * P.Imax / 16));
   if constexpr (FUSED) {
     // the token's top-K and its weights from the published logits; the
     // token's first D unit also writes them out for the caller
@@ -899,26 +896,24 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
     const size_t base = k < K ? ((size_t)s_ex[k] * H + r0) * gr : (size_t)r0 * gs;
     sbr = reinterpret_cast<const uint4*>(src + base)[w];
   }
-  // the residual of the wave's row goes out with the unit's other loads, so
-  // the final sum does not wait for it (a wave-uniform address: a scalar
-  // load, held in a scalar register)
+  // the residual of the unit's rows goes out with its other loads, so the
+  // final sum does not wait for it (threads tid < kDRows write the rows)
   float resv = 0.f;
-  if (residual)
-    resv = residual[(size_t)t * H + r0 + __builtin_amdgcn_readfirstlane(min(rl, nrows - 1))];
-  uint4 wv[DCH];
-  const int rlc = min(rl, nrows - 1);
-#pragma unroll
-  for (int j = 0; j < DCH; ++j) {
-    const int kj = (kc[j] >> 16) - 1, cj = kc[j] & 0xFFFF;
-    const bool sh = kj == K;
+  if (residual && tid < kDRows) resv = residual[(size_t)t * H + r0 + min(tid, nrows - 1)];
+  // the thread's chunk of every row (a thread without a chunk reads a valid
+  // one and never uses it)
+  uint4 wr[kRPT];
+  {
+    const bool sh = kq == K;
     const uint32_t* base = sh ? L.sh_down.q
-                              : L.down.q + ((size_t)s_ex[max(kj, 0)] * H) * (I / (32 / BITS));
+                              : L.down.q + ((size_t)s_ex[max(kq, 0)] * H) * (I / (32 / BITS));
     const int wpr = (sh ? Is : I) / (32 / BITS);
-    wv[j] = reinterpret_cast<const uint4*>(base + (size_t)(r0 + rlc) * wpr)[cj];
+#pragma unroll
+    for (int r = 0; r < kRPT; ++r)
+      wr[r] = reinterpret_cast<const uint4*>(base + (size_t)(r0 + min(gq * kRPT + r, nrows - 1)) * wpr)[cq];
   }
   // the extent of the other h buffer's last use (cleared at the end)
   const int zx = FUSED ? ld_coh_i(P.hext + (par ^ 1)) : 0;
-  float term[DCH];                             // the lane's chunk terms of the wave's row
   if constexpr (FUSED) {
     // h arrives element by element with its "written" marks: once this
     // unit's own loads are in, poll the token's h (copy blockIdx % kHCopies
@@ -1069,57 +1064,60 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
     if (s_done && tid < kRep) st_coh_i(ready_line(P, tid, t), 0);
   }
   tl_mark(3);                                  // D: h of every slot staged
-  {
-  // chunk sums of every slot, one (slot, chunk) pair per thread
-  for (int q = tid; q < tot; q += kThreads) {
-    const int k = q < K * cpr ? q / cpr : K;
-    const int cc = k < K ? q - k * cpr : q - K * cpr;
-    const int nk = k < K ? cpr : cps;
-    const float4* a4 = reinterpret_cast<const float4*>(hs + (size_t)k * P.Imax);
-    float sum = 0.f;
+  // every thread: its chunk of h read from LDS (and summed) and applied to
+  // its chunk of its group's kRPT rows; the chunk's term per row is
+  // w_k (s (codes . h) + b (sum of h)), s and b the row's group
+  float part[kRPT];
+#pragma unroll
+  for (int r = 0; r < kRPT; ++r) part[r] = 0.f;
+  if (kq >= 0) {
+    const bool sh = kq == K;
+    const int Ik = sh ? Is : I;
+    const int gpr = Ik >> esh;
+    const int nk = Ik / kCpc;
+    const float4* hk = reinterpret_cast<const float4*>(hs + (size_t)kq * P.Imax);
+    float dd[kRPT];
+#pragma unroll
+    for (int r = 0; r < kRPT; ++r) dd[r] = 0.f;
+    float hsm = 0.f;
 #pragma unroll
     for (int f = 0; f < kCpc / 4; ++f) {
-      const float4 v = a4[f * nk + cc];
-      sum += (v.x + v.y) + (v.z + v.w);
+      const float4 hv = hk[f * nk + cq];
+      hsm += (hv.x + hv.y) + (hv.z + hv.w);
+#pragma unroll
+      for (int r = 0; r < kRPT; ++r) {
+        dd[r] = fmaf((float)chunk_code<BITS>(wr[r], 4 * f + 0), hv.x, dd[r]);
+        dd[r] = fmaf((float)chunk_code<BITS>(wr[r], 4 * f + 1), hv.y, dd[r]);
+        dd[r] = fmaf((float)chunk_code<BITS>(wr[r], 4 * f + 2), hv.z, dd[r]);
+        dd[r] = fmaf((float)chunk_code<BITS>(wr[r], 4 * f + 3), hv.w, dd[r]);
+      }
     }
-    hsum[(size_t)k * (P.Imax / kCpc) + cc] = sum;
+    const int g0 = (sh ? K * kDRows * gr : kq * kDRows * gr) + gq * kRPT * gpr + ((cq * kCpc) >> esh);
+    const int boff = K * kDRows * gr + kDRows * gs;    // biases follow all scales
+    const float wkq = wk[kq];
+#pragma unroll
+    for (int r = 0; r < kRPT; ++r)
+      part[r] = wkq * fmaf(bf16_to_f32(sbl[g0 + r * gpr]), dd[r],
+                           bf16_to_f32(sbl[boff + g0 + r * gpr]) * hsm);
+  }
+  // each row summed over the wave (one transposed reduction of the kRPT
+  // values), then over its group's waves in order: a fixed order, so the
+  // result does not change from run to run
+  __shared__ float s_red[kWaves][kRPT];
+  {
+    const float v = treduce<kRPT, 32>(part, lane);
+    if ((lane & (kWave / kRPT - 1)) == 0) s_red[wid][tindex<kRPT, 32>(lane)] = v;
   }
   __syncthreads();
-  // the terms of the wave's row, one per chunk of the lane
+  if (tid < nrows) {
+    constexpr int kWG = kWaves / kTG;            // waves per group
+    const int g = tid / kRPT, rr = tid % kRPT;
+    float sum = 0.f;
 #pragma unroll
-  for (int j = 0; j < DCH; ++j) {
-    const int k = (kc[j] >> 16) - 1, cj = kc[j] & 0xFFFF;
-    term[j] = 0.f;
-    if (k >= 0 && rl < nrows) {
-      const bool sh = k == K;
-      const int Ik = sh ? Is : I;
-      const int gpr = Ik >> esh;
-      const float4* hk = reinterpret_cast<const float4*>(hs + (size_t)k * P.Imax);
-      const float dd = chunk_dot<BITS>(wv[j], hk + cj, Ik / kCpc);
-      const int gi = (sh ? K * kDRows * gr : k * kDRows * gr) + rl * gpr + ((cj * kCpc) >> esh);
-      const int boff = K * kDRows * gr + kDRows * gs;    // biases follow all scales
-      term[j] = fmaf(bf16_to_f32(sbl[gi]), dd,
-                     bf16_to_f32(sbl[boff + gi]) * hsum[(size_t)k * (P.Imax / kCpc) + cj]);
-    }
-  }
-  }
-  // the wave's row: the lane's terms weighted and summed in chunk order, then
-  // the wave sum
-  float pv[1];
-  {
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < DCH; ++j) {
-      const int k = (kc[j] >> 16) - 1;
-      if (k >= 0 && rl < nrows) acc = fmaf(wk[k], term[j], acc);
-    }
-    pv[0] = acc;
-  }
-  const float tsum = treduce<1, 32>(pv, lane);
-  if (lane == 0 && rl < nrows) {
-    float v = bad ? __builtin_nanf("") : tsum;
+    for (int w = 0; w < kWG; ++w) sum += s_red[g * kWG + w][rr];
+    float v = bad ? __builtin_nanf("") : sum;
     if (residual) v += resv;
-    y[(size_t)t * H + r0 + rl] = v;
+    y[(size_t)t * H + r0 + tid] = v;
   }
   tl_mark(4);                                  // D: y written
   if constexpr (FUSED) {
