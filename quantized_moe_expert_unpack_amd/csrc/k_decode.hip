@@ -794,7 +794,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float wk[kMaxTopK + 1];
   __shared__ int s_ex[kMaxTopK];
-  __shared__ int bad, s_done, s_zx;
+  __shared__ int bad, s_done, s_zx, s_late;
   constexpr int kCpc = 128 / BITS;
   // segments of a token a thread may own (DCH chunks per lane of kCpc values)
   constexpr int kSegPT = (DCH * kCpc + 127) / 128;
@@ -810,7 +810,8 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
   const int tot = K * cpr + cps;               // chunks per output row, all slots
   tl_mark(0);                                  // D: start
   // the launch's parity (its logits and h buffers), read first
-  const int par = FUSED ? (ld_coh_i(P.epoch) & 1) : 0;
+  // (the fused form reads the launch's parity with its first poll below)
+  int par = 0;
   int* tl = P.ctr + (size_t)kLine * (1 + (size_t)t * kCtrLines);
   // the thread's chunk and rows: the threads form kTG groups of kThreads/kTG
   // (kTG = 8/DCH rounded down to a power of two, so a group has a thread
@@ -840,31 +841,46 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
   // (then a region of S * Imax / 16 floats, unused, ahead of the scales)
   uint16_t* sbl = reinterpret_cast<uint16_t*>(hs + (size_t)P.S * P.Imax + pad4(P.S * P.Imax / 16));
   if constexpr (FUSED) {
-    // the token's top-K and its weights from the published logits; the
-    // token's first D unit also writes them out for the caller
     // the token's top-K and its weights: the (expert, weight) pair each
     // slot's first gate/up unit publishes; the token's first D unit also
-    // writes them out for the caller
+    // writes them out for the caller.  The first round reads the launch
+    // counter and both parities' pairs together and keeps the pairs of the
+    // parity the counter names (those were cleared by the previous launch),
+    // so a unit that starts late finds its pairs one memory round trip
+    // earlier.
+    __shared__ int s_par;
     if (wid == 0) {
-      const uint64_t* sp = P.selw + ((size_t)par * kSelCopies + blockIdx.x % kSelCopies) * P.sstride +
-                           (size_t)t * kMaxTopK;
-      uint64_t v = 1ull;
-      for (int spin = 0;; ++spin) {
-        v = lane < K ? ld_coh_u64(sp + lane) : 1ull;
+      const size_t cp = blockIdx.x % kSelCopies;
+      const uint64_t* sp0 = P.selw + cp * P.sstride + (size_t)t * kMaxTopK;
+      const uint64_t* sp1 = P.selw + ((size_t)kSelCopies + cp) * P.sstride + (size_t)t * kMaxTopK;
+      const int ep = ld_coh_i(P.epoch);
+      const uint64_t v0 = lane < K ? ld_coh_u64(sp0 + lane) : 1ull;
+      const uint64_t v1 = lane < K ? ld_coh_u64(sp1 + lane) : 1ull;
+      const int pr = ep & 1;
+      const uint64_t* sp = pr ? sp1 : sp0;
+      uint64_t v = pr ? v1 : v0;
+      int spin = 0;
+      for (;; ++spin) {
         if (__all(v != 0ull)) break;
         if (spin >= kSpinLimit) {
           if (lane == 0) atomicOr(P.ctr, 4);
           break;
         }
         __builtin_amdgcn_s_sleep(2);
+        v = lane < K ? ld_coh_u64(sp + lane) : 1ull;
       }
+      // pairs already there at the first look: the unit started after the
+      // gate/up units' first rows were done, and h is likely complete
+      if (lane == 0) s_late = spin == 0;
       if (lane < K) {
         v = ~v;
         s_ex[lane] = (int)(uint32_t)(v >> 32);
         wk[lane] = __uint_as_float((uint32_t)v);
       }
+      if (lane == 0) s_par = pr;
     }
     __syncthreads();
+    par = s_par;
     if (tid < K) {
       if (c == 0) {
         R.idx_out[(size_t)t * K + tid] = s_ex[tid];
@@ -951,6 +967,10 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
 #pragma unroll
     for (int i = 0; i < kSegPT; ++i)
       if (tid + kThreads * i < nseg) pend |= 1u << i;
+    // a unit that started late reads the segments whole in its first round
+    // (no marker round first): a segment found incomplete that way is re-read
+    // with coherent loads from then on, since its line may now sit in L2
+    if (s_late) seen = pend;
     for (int round = 0;; ++round) {
       if (pend) {
         uint32_t mk[kSegPT];
