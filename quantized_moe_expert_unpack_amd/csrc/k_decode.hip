@@ -53,9 +53,11 @@ namespace moeq {
 constexpr int kThreads = 512;              // every unit is 8 waves
 constexpr int kWaves = kThreads / kWave;
 constexpr int kGRows = 16;                 // intermediate rows per G unit (two per wave)
-constexpr int kDRows = kWaves;             // output rows per D unit (one per wave)
+constexpr int kDRows = kWaves;             // output rows per D unit (one per wave), or 2 kDRows
+                                           // when the layer's units outnumber the resident blocks
 constexpr int kRRows = kWaves / 2;         // router rows per R unit (two waves per row)
 constexpr int kSpinLimit = 1 << 26;
+constexpr int kCUs = 256;                  // compute units of the chip (MI355X)
 constexpr int kLine = kLineInts;
 constexpr int kRep = 64;      // copies of every flag that many units poll
 constexpr int kLogitCopies = 32;   // copies of the router logits (one per polling group of units)
@@ -777,15 +779,15 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
 }
 
 // scale/bias words (16 bytes) a D unit stages: all slots, scales and biases
-__host__ __device__ __forceinline__ int d_sb_words_dev(const DecodeLayer& L, int K) {
+__host__ __device__ __forceinline__ int d_sb_words_dev(const DecodeLayer& L, int K, int dr) {
   const int egs = L.gate.group_size;
-  return 2 * kDRows * (K * (L.I / egs) + (L.has_shared ? L.Is / egs : 0)) * 2 / 16;
+  return 2 * dr * (K * (L.I / egs) + (L.has_shared ? L.Is / egs : 0)) * 2 / 16;
 }
 
 // ------------------------------------------------------------------ D unit
 // LDS: [h of all S slots, chunk-interleaved per slot][their chunk sums][bf16
 // scales then biases of the unit's rows, slot by slot]
-template <int BITS, int DCH, bool FUSED, bool WIDE, int POLL>
+template <int BITS, int DCH, int DR, bool FUSED, bool WIDE, int POLL>
 __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, const RouteIn R,
                                           const int32_t* __restrict__ idx,
                                           const float* __restrict__ wts,
@@ -802,8 +804,8 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
   const int K = P.K, H = L.H;
   const int t = d / P.nc;
   const int c = d - t * P.nc;
-  const int r0 = c * kDRows;
-  const int nrows = min(kDRows, H - r0);
+  const int r0 = c * DR;
+  const int nrows = min(DR, H - r0);
   const int I = L.I, Is = L.Is;
   const int cpr = I / kCpc;                    // chunks per routed down row
   const int cps = L.has_shared ? Is / kCpc : 0;
@@ -819,7 +821,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
   // gq kRPT ... + kRPT - 1, its thread lq chunk lq: slot kq (-1: none),
   // chunk cq within the slot
   constexpr int kTG = DCH == 1 ? 8 : DCH == 2 ? 4 : DCH <= 4 ? 2 : 1;
-  constexpr int kRPT = kDRows / kTG;
+  constexpr int kRPT = DR / kTG;
   const int gq = tid / (kThreads / kTG), lq = tid % (kThreads / kTG);
   const int kq = lq < tot ? (lq < K * cpr ? lq / cpr : K) : -1;
   const int cq = kq < 0 ? 0 : (kq < K ? lq - kq * cpr : lq - K * cpr);
@@ -891,15 +893,15 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
   }
   __syncthreads();
   tl_mark(1);                                  // D: experts known
-  // scales and biases of every slot (per slot kDRows rows x groups bf16,
+  // scales and biases of every slot (per slot DR rows x groups bf16,
   // contiguous), then the routed chunks
   const int esh = __builtin_ctz((unsigned)L.gate.group_size);  // log2 group size, every expert matrix
   const int gr = I >> esh, gs = L.has_shared ? Is >> esh : 0;
-  const int sb_r = kDRows * gr * 2 / 16;       // 16-byte words per slot and tensor
-  const int sb_s = kDRows * gs * 2 / 16;
+  const int sb_r = DR * gr * 2 / 16;       // 16-byte words per slot and tensor
+  const int sb_s = DR * gs * 2 / 16;
   const int n_sb = 2 * (K * sb_r + sb_s);      // all slots, scales and biases
   // (clamped, always valid addresses and no branches: the loads issue back
-  // to back; H is a multiple of kDRows, so every unit has full rows)
+  // to back; H is a multiple of DR, so every unit has full rows)
   uint4 sbr;
   {
     const int tq = min(tid, n_sb - 1);
@@ -913,9 +915,9 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
     sbr = reinterpret_cast<const uint4*>(src + base)[w];
   }
   // the residual of the unit's rows goes out with its other loads, so the
-  // final sum does not wait for it (threads tid < kDRows write the rows)
+  // final sum does not wait for it (threads tid < DR write the rows)
   float resv = 0.f;
-  if (residual && tid < kDRows) resv = residual[(size_t)t * H + r0 + min(tid, nrows - 1)];
+  if (residual && tid < DR) resv = residual[(size_t)t * H + r0 + min(tid, nrows - 1)];
   // the thread's chunk of every row (a thread without a chunk reads a valid
   // one and never uses it)
   uint4 wr[kRPT];
@@ -1112,8 +1114,8 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
         dd[r] = fmaf((float)chunk_code<BITS>(wr[r], 4 * f + 3), hv.w, dd[r]);
       }
     }
-    const int g0 = (sh ? K * kDRows * gr : kq * kDRows * gr) + gq * kRPT * gpr + ((cq * kCpc) >> esh);
-    const int boff = K * kDRows * gr + kDRows * gs;    // biases follow all scales
+    const int g0 = (sh ? K * DR * gr : kq * DR * gr) + gq * kRPT * gpr + ((cq * kCpc) >> esh);
+    const int boff = K * DR * gr + DR * gs;    // biases follow all scales
     const float wkq = wk[kq];
 #pragma unroll
     for (int r = 0; r < kRPT; ++r)
@@ -1203,7 +1205,7 @@ __device__ __forceinline__ int unit_of(int b, const DecPlan& P, int* u) {
 
 // 8-bit layers of up to 2048 columns: at most 80 VGPRs, so three units fit per
 // CU (24 waves) and a 30B-A3B-shaped layer's units are all resident at once
-template <int BITS, int CPL, int DCH, bool FUSED, bool NORM>
+template <int BITS, int CPL, int DCH, int DR, bool FUSED, bool NORM>
 __global__ void __launch_bounds__(kThreads)
     __attribute__((amdgpu_waves_per_eu(BITS == 8 && CPL <= 2 && DCH <= 6 ? 6 : 1))) k_moe_decode(DecodeLayer L, DecPlan P, RouteIn R,
                                                         const float* __restrict__ x,
@@ -1222,7 +1224,7 @@ __global__ void __launch_bounds__(kThreads)
   constexpr int kRc = CPL * 4 / BITS < 1 ? 1 : (CPL * 4 / BITS > 2 ? 2 : CPL * 4 / BITS);
   if (FUSED && role == 0) route_unit<NORM, kRc>(L, P, R, x, u);
   else if (role == 1) gate_up_unit<BITS, CPL, FUSED, NORM, kWide, kPoll>(L, P, x, idx, u, R.renorm);
-  else down_unit<BITS, DCH, FUSED, kWide, kPoll>(L, P, R, idx, wts, residual, y, u);
+  else down_unit<BITS, DCH, DR, FUSED, kWide, kPoll>(L, P, R, idx, wts, residual, y, u);
   tl_end();
 }
 
@@ -1312,6 +1314,24 @@ DecState dec_state(const DecodeLayer& L, int K, void* ws) {
   return D;
 }
 
+// output rows per D unit: 2 kDRows for 2- and 4-bit layers whose units at
+// kDRows rows would outnumber the blocks resident at once (two 8-wave units
+// per CU: those kernels take more than 80 VGPRs), so that most D units are
+// resident from the start and prefetch their rows while the gate/up units
+// stream; kDRows otherwise (and for 8-bit layers, whose 80-VGPR form keeps
+// three units per CU)
+static int d_rows(const DecodeLayer& L, int M, int K, bool routed) {
+  if (L.gate.bits == 8 || L.H % (2 * kDRows) || d_sb_words_dev(L, K, 2 * kDRows) > kThreads) return kDRows;
+  // (a thread's rows double with the unit's; kept where a D row spans more
+  // than 4 chunks per lane, whose threads already hold kDRows rows each)
+  const int cpc = 128 / L.gate.bits;
+  if (K * (L.I / cpc) + (L.has_shared ? L.Is / cpc : 0) > 4 * kWave) return kDRows;
+  const int ng = M * (K * ((L.I + kGRows - 1) / kGRows) + (L.has_shared ? (L.Is + kGRows - 1) / kGRows : 0));
+  const int nr = routed ? (L.E + kRRows - 1) / kRRows : 0;
+  const int nd = M * (L.H / kDRows);
+  return nr + ng + nd > 2 * kCUs ? 2 * kDRows : kDRows;
+}
+
 // the state block, then the launch's own data (h and the shared-gate logits
 // of the launch without routing); M <= kDecMaxM
 static DecPlan make_dec_plan(const DecodeLayer& L, int M, int K, bool routed, void* ws, size_t* bytes) {
@@ -1324,7 +1344,8 @@ static DecPlan make_dec_plan(const DecodeLayer& L, int M, int K, bool routed, vo
   P.ng_routed = (L.I + kGRows - 1) / kGRows;
   P.ng_shared = L.has_shared ? (L.Is + kGRows - 1) / kGRows : 0;
   P.g_units = M * (K * P.ng_routed + P.ng_shared);
-  P.nc = (L.H + kDRows - 1) / kDRows;
+  P.dr = d_rows(L, M, K, routed);
+  P.nc = (L.H + P.dr - 1) / P.dr;
   P.d_units = M * P.nc;
   P.r_units = routed ? (L.E + kRRows - 1) / kRRows : 0;
   P.r_half = 0;
@@ -1371,7 +1392,7 @@ size_t decode_ws_bytes(const DecodeLayer& L, int M, int K, bool routed) {
   return b;
 }
 
-static int d_sb_words(const DecodeLayer& L, int K) { return d_sb_words_dev(L, K); }
+static int d_sb_words(const DecodeLayer& L, int K, int dr) { return d_sb_words_dev(L, K, dr); }
 
 static size_t dec_lds_bytes(const DecodeLayer& L, int K, bool routed, int M) {
   // G: x (H floats) + chunk sums (<= H/16) + 4 x 16 rows x groups bf16;
@@ -1383,7 +1404,8 @@ static size_t dec_lds_bytes(const DecodeLayer& L, int K, bool routed, int M) {
   const size_t g = sizeof(float) * (L.H + pad4(L.H / 16)) + 2 * 4 * kGRows * (L.H / L.gate.group_size) + sel;
   const int S = K + (L.has_shared ? 1 : 0);
   const int Im = L.has_shared && L.Is > L.I ? L.Is : L.I;
-  const size_t d = sizeof(float) * ((size_t)S * Im + pad4(S * Im / 16)) + 16 * (size_t)d_sb_words(L, K) + sel;
+  const size_t d = sizeof(float) * ((size_t)S * Im + pad4(S * Im / 16)) +
+                   16 * (size_t)d_sb_words(L, K, d_rows(L, M, K, routed)) + sel;
   const size_t rx = routed ? sizeof(float) * (size_t)M * L.H : 0;
   size_t m = g > d ? g : d;
   return m > rx ? m : rx;
@@ -1417,7 +1439,7 @@ bool decode_supported(const DecodeLayer& L, int K) {
     if (L.sh_eg.bits != 2 && L.sh_eg.bits != 4 && L.sh_eg.bits != 8) return false;
   }
   if (!d_ch(L, K)) return false;
-  if (d_sb_words(L, K) > kThreads) return false;
+  if (d_sb_words(L, K, 2 * kDRows) > kThreads) return false;
   return dec_lds_bytes(L, K, false, 1) <= 160 * 1024;
 }
 
@@ -1430,12 +1452,12 @@ bool fused_supported(const DecodeLayer& L, const QT& router, int M, int K) {
          dec_lds_bytes(L, K, true, M) <= 160 * 1024;
 }
 
-template <int B, int CPL, int DCH, bool FUSED, bool NORM>
+template <int B, int CPL, int DCH, int DR, bool FUSED, bool NORM>
 static void run_dec(const DecodeLayer& L, const DecPlan& P, const RouteIn& R, const float* x,
                     const int32_t* idx, const float* w, const float* residual, float* y,
                     hipStream_t s) {
   const size_t lds = dec_lds_bytes(L, P.K, FUSED, P.M);
-  hipLaunchKernelGGL((k_moe_decode<B, CPL, DCH, FUSED, NORM>), dim3(P.r_units + P.g_units + P.d_units),
+  hipLaunchKernelGGL((k_moe_decode<B, CPL, DCH, DR, FUSED, NORM>), dim3(P.r_units + P.g_units + P.d_units),
                      dim3(kThreads), lds, s, L, P, R, x, idx, w, residual, y);
 }
 
@@ -1446,10 +1468,13 @@ static int dispatch_dec(const DecodeLayer& L, const DecPlan& P, const RouteIn& R
   const int b = L.gate.bits;
   const int cpl = g_cpl(L.H, b);
   const int dch = d_ch(L, P.K);
-#define MOEQ_DEC(B_, C_, D_)                                              \
-  if (b == B_ && cpl == C_ && dch == D_) {                               \
-    run_dec<B_, C_, D_, FUSED, NORM>(L, P, R, x, idx, w, residual, y, s); \
-    return 0;                                                            \
+#define MOEQ_DEC(B_, C_, D_)                                                            \
+  if (b == B_ && cpl == C_ && dch == D_) {                                             \
+    if (B_ != 8 && P.dr == 2 * kDRows)                                                 \
+      run_dec<B_, C_, D_, (B_ != 8 ? 2 : 1) * kDRows, FUSED, NORM>(L, P, R, x, idx, w, residual, y, s); \
+    else                                                                               \
+      run_dec<B_, C_, D_, kDRows, FUSED, NORM>(L, P, R, x, idx, w, residual, y, s);   \
+    return 0;                                                                          \
   }
 #define MOEQ_DEC_PW(B_, C_) MOEQ_DEC(B_, C_, 1) MOEQ_DEC(B_, C_, 2) MOEQ_DEC(B_, C_, 3) \
   MOEQ_DEC(B_, C_, 4) MOEQ_DEC(B_, C_, 6) MOEQ_DEC(B_, C_, 8)

@@ -90,6 +90,7 @@ DecState dec_state(const DecodeLayer& L, int K, void* ws);
 struct DecPlan {
   int M, K, S, P, Imax;
   int ng_routed, ng_shared, g_units, nc, d_units;
+  int dr;          // output rows per D unit
   int r_units;     // router units in front of the expert units (routing in the launch), else 0
   int r_half;      // R units per XCD on XCDs 0 and 1 (block placement), 0: R units first in order
   int* ctr;        // 128-byte lines: error word, then per token G and D arrival counters

@@ -41,17 +41,38 @@ EVENTS = {
 KT_BLOCKS, KT_EVENTS = 4096, 12
 
 
+def d_rows(cfg, m, routed=True):
+    """Output rows per D unit, as the library chooses them: 16 for 2- and
+    4-bit layers whose units at 8 rows would outnumber two resident units per
+    CU (256 CUs), when the unit's scale/bias words fit one 16-byte word per
+    thread and a D row spans at most 4 chunks per lane; 8 otherwise."""
+    bits, gs = cfg.expert_bits, cfg.group_size
+    if bits == 8 or cfg.hidden % 16:
+        return 8
+    groups = cfg.top_k * (cfg.inter // gs) + (cfg.shared_inter // gs if cfg.has_shared else 0)
+    if 2 * 16 * groups * 2 // 16 > 512:
+        return 8
+    cpc = 128 // bits
+    if cfg.top_k * (cfg.inter // cpc) + (cfg.shared_inter // cpc if cfg.has_shared else 0) > 4 * 64:
+        return 8
+    ng = (cfg.inter + 15) // 16
+    ngs = (cfg.shared_inter + 15) // 16 if cfg.has_shared else 0
+    units8 = ((cfg.experts + 3) // 4 if routed else 0) + m * (cfg.top_k * ng + ngs) + m * (cfg.hidden // 8)
+    return 16 if units8 > 2 * 256 else 8
+
+
 def plan(cfg, m=1):
     """Unit counts of the one-launch kernel (4 router rows per R unit, 16
-    gate/up rows per G unit, 8 output rows per D unit) and the kind of every
-    block: up to 32 R units (an even count) take the first blocks of XCDs 0
-    and 1 (block b runs on XCD b % 8), more are the first blocks in order;
-    then G units, then D units, in block order."""
+    gate/up rows per G unit, d_rows() output rows per D unit) and the kind of
+    every block: up to 32 R units (an even count) take the first blocks of
+    XCDs 0 and 1 (block b runs on XCD b % 8), more are the first blocks in
+    order; then G units, then D units, in block order."""
     r_units = (cfg.experts + 3) // 4
     ng = (cfg.inter + 15) // 16
     ngs = (cfg.shared_inter + 15) // 16 if cfg.has_shared else 0
     g_units = m * (cfg.top_k * ng + ngs)
-    d_units = m * ((cfg.hidden + 7) // 8)
+    dr = d_rows(cfg, m)
+    d_units = m * ((cfg.hidden + dr - 1) // dr)
     r2 = (r_units + 1) & ~1
     half = 0
     if r2 <= 32 and 8 * (r2 // 2 - 1) + 1 < r2 + g_units + d_units:
