@@ -13,17 +13,44 @@ namespace moeq {
 // read becomes a many-way bank conflict).
 //
 // dot of one 16-byte chunk of BITS-bit codes with its activations
+// A word of 2- or 4-bit codes is converted in byte passes: pass m of the
+// word has code 4b + m (2-bit) or 2b + m (4-bit) in byte b, and each byte
+// becomes a float with one byte-to-float instruction (the empty asm keeps
+// the compiler from turning the mask back into one bit-field extract per
+// code); 8-bit words are their own single pass.
+template <int BITS>
+__device__ __forceinline__ uint32_t code_pass(uint32_t w, int m) {
+  uint32_t t = w;
+  if constexpr (BITS == 2) t = (w >> (2 * m)) & 0x03030303u;
+  else if constexpr (BITS == 4) t = (w >> (4 * m)) & 0x0F0F0F0Fu;
+  asm volatile("" : "+v"(t));
+  return t;
+}
+
+__device__ __forceinline__ float f4c(const float4& v, int c) {
+  return c == 0 ? v.x : c == 1 ? v.y : c == 2 ? v.z : v.w;
+}
+
 template <int BITS>
 __device__ __forceinline__ float chunk_dot(const uint4& v, const float4* a4, int stride) {
-  constexpr int kCpc = 128 / BITS;
+  constexpr int kF = 8 / BITS;                 // float4s of activations per word
+  constexpr int kPasses = 8 / BITS;
   float d = 0.f;
 #pragma unroll
-  for (int j = 0; j < kCpc; j += 4) {
-    const float4 av = a4[(j / 4) * stride];
-    d = fmaf((float)chunk_code<BITS>(v, j + 0), av.x, d);
-    d = fmaf((float)chunk_code<BITS>(v, j + 1), av.y, d);
-    d = fmaf((float)chunk_code<BITS>(v, j + 2), av.z, d);
-    d = fmaf((float)chunk_code<BITS>(v, j + 3), av.w, d);
+  for (int wi = 0; wi < 4; ++wi) {
+    const uint32_t w = wi == 0 ? v.x : wi == 1 ? v.y : wi == 2 ? v.z : v.w;
+    float4 av[kF];
+#pragma unroll
+    for (int f = 0; f < kF; ++f) av[f] = a4[(wi * kF + f) * stride];
+#pragma unroll
+    for (int m = 0; m < kPasses; ++m) {
+      const uint32_t t = code_pass<BITS>(w, m);
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const int j = BITS == 2 ? 4 * b + m : BITS == 4 ? 2 * b + m : b;   // code within the word
+        d = fmaf((float)((t >> (8 * b)) & 0xFFu), f4c(av[j / 4], j % 4), d);
+      }
+    }
   }
   return d;
 }

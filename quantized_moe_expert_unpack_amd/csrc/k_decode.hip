@@ -1101,17 +1101,29 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
     float dd[kRPT];
 #pragma unroll
     for (int r = 0; r < kRPT; ++r) dd[r] = 0.f;
+    // (codes converted in byte passes, as in chunk_dot)
     float hsm = 0.f;
+    constexpr int kF = 8 / BITS, kPasses = 8 / BITS;
 #pragma unroll
-    for (int f = 0; f < kCpc / 4; ++f) {
-      const float4 hv = hk[f * nk + cq];
-      hsm += (hv.x + hv.y) + (hv.z + hv.w);
+    for (int wi = 0; wi < 4; ++wi) {
+      float4 hv[kF];
+#pragma unroll
+      for (int f = 0; f < kF; ++f) {
+        hv[f] = hk[(wi * kF + f) * nk + cq];
+        hsm += (hv[f].x + hv[f].y) + (hv[f].z + hv[f].w);
+      }
 #pragma unroll
       for (int r = 0; r < kRPT; ++r) {
-        dd[r] = fmaf((float)chunk_code<BITS>(wr[r], 4 * f + 0), hv.x, dd[r]);
-        dd[r] = fmaf((float)chunk_code<BITS>(wr[r], 4 * f + 1), hv.y, dd[r]);
-        dd[r] = fmaf((float)chunk_code<BITS>(wr[r], 4 * f + 2), hv.z, dd[r]);
-        dd[r] = fmaf((float)chunk_code<BITS>(wr[r], 4 * f + 3), hv.w, dd[r]);
+        const uint32_t w = wi == 0 ? wr[r].x : wi == 1 ? wr[r].y : wi == 2 ? wr[r].z : wr[r].w;
+#pragma unroll
+        for (int m = 0; m < kPasses; ++m) {
+          const uint32_t t = code_pass<BITS>(w, m);
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int j = BITS == 2 ? 4 * b + m : BITS == 4 ? 2 * b + m : b;
+            dd[r] = fmaf((float)((t >> (8 * b)) & 0xFFu), f4c(hv[j / 4], j % 4), dd[r]);
+          }
+        }
       }
     }
     const int g0 = (sh ? K * DR * gr : kq * DR * gr) + gq * kRPT * gpr + ((cq * kCpc) >> esh);
