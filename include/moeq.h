@@ -349,6 +349,13 @@ int moe_workspace_status(void *ws, int32_t *status_out, moeq_stream_t stream);
  * rows run through a bf16 MFMA gate/up GEMM with a SwiGLU epilogue (h kept in
  * bf16) and a down GEMM scaled by the routing weight; each token then sums its
  * K pairs in slot order.  fp32 output; any M >= 1 (no tile-size alignment).
+ * With few rows per expert (M * K <= 4 E, affine experts, layer shapes the
+ * batched decode supports) the MFMA tiles would hold a handful of rows, so
+ * the call instead streams each touched expert once per tile of two pairs
+ * through the batched decode kernels, the activations widened exactly to
+ * fp32 (fp32 accumulation throughout; same outputs to within the tolerance,
+ * same invalid-index NaN rows).  The workspace of moe_workspace_size covers
+ * both forms for every M up to the one it was sized for.
  *   x_bf16 : bf16 bit patterns [M][H];  topk_idx, topk_w as above;  y : fp32 [M][H]
  * has_shared must be 0 (MOEQ_ERR_UNSUPPORTED otherwise).
  * Defines: mlx-lm SwitchGLU through gather_qmm with sorted indices

@@ -461,6 +461,27 @@ __global__ void __launch_bounds__(kRouteThreads) k_topk_wave(const double* __res
     else hipLaunchKernelGGL(KERNEL<2>, GRID, dim3(256), 0, __VA_ARGS__);                   \
   } while (0)
 
+// bf16 -> fp32 (exact: the bf16 bits are the fp32 value's high half), eight
+// values per thread; n is a multiple of 8 and both pointers 16-byte aligned
+__global__ void __launch_bounds__(256) k_bf16_widen(const uint16_t* __restrict__ x, float* __restrict__ y,
+                                                    int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n8) return;
+  const uint4 v = reinterpret_cast<const uint4*>(x)[i];
+  float4* o = reinterpret_cast<float4*>(y) + 2 * i;
+  o[0] = make_float4(__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xFFFF0000u),
+                     __uint_as_float(v.y << 16), __uint_as_float(v.y & 0xFFFF0000u));
+  o[1] = make_float4(__uint_as_float(v.z << 16), __uint_as_float(v.z & 0xFFFF0000u),
+                     __uint_as_float(v.w << 16), __uint_as_float(v.w & 0xFFFF0000u));
+}
+
+int launch_bf16_widen(const uint16_t* x, float* y, int64_t n, hipStream_t s) {
+  const int64_t n8 = n / 8;
+  if (n8 == 0) return 0;
+  hipLaunchKernelGGL(k_bf16_widen, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s, x, y, n8);
+  return 0;
+}
+
 int launch_qdequant(const QT& W, uint8_t* codes, float* deq, hipStream_t s) {
   const int wpr = W.cols * W.bits / 32;
   const int64_t words = (int64_t)W.batch * W.rows * wpr;

@@ -318,6 +318,18 @@ def test_workspace_sizes():
     assert ws(None, 1, 2, moeq.PATH_DECODE) == 0
 
 
+def test_gather_workspace_serves_every_smaller_call():
+    # moe_gather_qmm takes a light form (batched streaming, fp32 buffers) up to
+    # 4 pairs per expert and the GEMM form above; a workspace sized for M must
+    # hold either form for every M' <= M, so the size never decreases with M
+    ws = moeq.lib().moe_workspace_size
+    for kw in (dict(E=128, H=2048, I=768, bits=8), dict(E=8, H=256, I=128, bits=4)):
+        L = _layer(**kw)
+        sizes = [ws(ctypes.byref(L), m, 8 if kw["E"] > 8 else 2, moeq.PATH_GATHER) for m in range(1, 300)]
+        assert all(s > 0 for s in sizes)
+        assert all(b >= a for a, b in zip(sizes, sizes[1:]))
+
+
 def test_binding_fails_loudly_without_the_library(monkeypatch):
     monkeypatch.setattr(moeq, "_lib", None)
     monkeypatch.setattr(moeq, "LIB_PATH", "/nonexistent/libmoeq.so")

@@ -60,6 +60,47 @@ def test_moe_gather_small_m_vs_oracle(m):
     assert err.max() <= TOL
 
 
+# With at most 4 (token, slot) pairs per expert on average (M * K <= 4 E:
+# M <= 64 here) moe_gather_qmm streams every touched expert once per tile of
+# two pairs through the batched decode kernels (fp32 activations widened
+# from bf16) instead of staging 256-row MFMA tiles; M = 65 is the first
+# count that takes the MFMA form.
+@pytest.mark.parametrize("m", [16, 64, 65])
+def test_moe_gather_light_form_both_sides_of_the_switch(m):
+    cfg, host, L = _c4_layer()
+    say(f"moe_gather_qmm M={m} (pairs {m * cfg.top_k}, experts {cfg.experts})")
+    xb = synth.prefill_x_bf16(cfg, m)
+    lg = synth.zipf_logits(cfg, m)
+    y, idx, w = _prefill(cfg, L, xb, lg, poison=POISON[0])
+    y2, _, _ = _prefill(cfg, L, xb, lg, poison=POISON[1])
+    assert torch.equal(y, y2)                   # nothing unwritten, bitwise rerun
+    ridx, rw, _ = oracle.route(lg.astype(np.float64), cfg.top_k)
+    assert np.array_equal(idx.cpu().numpy(), ridx)
+    ref = oracle.moe_experts(host, bf16_bits_to_f32(xb), ridx, rw)
+    err = rel_l2_rows(y.cpu().numpy(), ref)
+    say(f"  max rel-L2 {err.max():.3e}")
+    assert err.max() <= (1e-4 if m <= 64 else TOL)   # the light form accumulates in fp32
+
+
+def test_moe_gather_light_and_gemm_forms_share_one_workspace():
+    # one workspace sized for the largest call serves both forms in any
+    # order: the GEMM form's per-expert counts (2000 tokens: 16000 pairs, the
+    # multi-block sort) must still be zero after light calls, and each
+    # result equals the same call on a fresh workspace bit for bit
+    cfg, host, L = _c4_layer()
+    seq = [2000, 16, 2000, 64, 1, 2000]
+    ws = moeq.workspace(L, max(seq), cfg.top_k, moeq.PATH_GATHER, dev())
+    for i, m in enumerate(seq):
+        say(f"shared workspace call {i}: M={m}")
+        xb = synth.prefill_x_bf16(cfg, m)
+        lg = to_dev(synth.zipf_logits(cfg, m))
+        idx, w = moeq.moe_route(None, lg, cfg.experts, cfg.top_k)
+        y = moeq.moe_gather_qmm(L, bf16_dev(xb), idx, w, ws=ws)
+        yf = moeq.moe_gather_qmm(L, bf16_dev(xb), idx, w)
+        torch.cuda.synchronize()
+        assert torch.equal(y, yf)
+
+
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_moe_gather_widths_off_the_tile_grid(bits):
     # H = 320 (not a multiple of the 256-column down tile) and I = 192 (not a
