@@ -76,6 +76,22 @@ def test_c3_shared_expert_one_and_two_tokens():
             say(f"c3 layer {layer_idx} M={m}: max rel-L2 {e:.3e}")
 
 
+# above 128 experts the one-launch kernel's gate/up units select through a
+# threshold: the K-th largest of 64 group maxima (groups of ceil(E/64) keys),
+# then the keys at or above it ranked among themselves.  E = 130 leaves 20 of
+# the 64 groups empty, E = 1024 gives groups of 16 and with K = 16 up to 256
+# candidates; K = 1 is the plain maximum
+@pytest.mark.parametrize("E,K", [(130, 16), (136, 4), (512, 8), (1024, 16), (1024, 1)])
+def test_one_launch_selection_above_128_experts(E, K):
+    cfg = synth.scaled(synth.CONFIGS["c1"], experts=E, top_k=K, seed=70 + K)
+    host = synth.host_layer(cfg, 0, threads=16)
+    L = moeq.MoELayer.from_host(host, dev())
+    x = gapped_tokens(cfg, host, 0, 2)[:, 0]
+    ws = moeq.workspace(L, 2, K, moeq.PATH_FORWARD, dev())
+    _, e = _check(cfg, host, L, x, ws)
+    say(f"E={E} K={K}: max rel-L2 {e:.3e}")
+
+
 def test_residual_and_bitwise_reruns():
     cfg, host, L = _layer("c2", 0)
     ws = moeq.workspace(L, 2, cfg.top_k, moeq.PATH_FORWARD, dev())
