@@ -385,7 +385,6 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
   const int nch = H / 16;                 // 16 codes per chunk at 8 bits (nch <= 128 RCPL2)
   const int rsh = __builtin_ctz((unsigned)R.W.group_size);   // log2 of the group size
   const int gpr = H >> rsh;
-  const bool row_ok = e < E;
   __shared__ double part[kFusedMaxM][kRRows];
   const int er = min(e, E - 1);
   // the launch's parity picks its logits buffer (read now, so the load
@@ -502,10 +501,13 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
   // every logit goes to kLogitCopies copies, one per lane (a G or D unit
   // polls copy blockIdx % kLogitCopies: many units polling one line would
   // queue on its memory channel)
-  uint64_t* lg = P.logits + ((size_t)(epoch & 1) * kLogitCopies + lane) * P.lstride;
+  // the unit's kRRows logits of a token are staged, then written to every
+  // copy as one run of kRRows consecutive values: adjacent lanes take the
+  // rows of one copy, so each copy's run is one coalesced write
+  __shared__ uint64_t s_pub[kFusedMaxM][kRRows];
 #pragma unroll
   for (int m = 0; m < kFusedMaxM; ++m) {
-    if (m < M && h == 0 && lane < kLogitCopies && row_ok) {
+    if (m < M && h == 0 && lane == 0) {
       double tot = wsum[m] + part[m][wid / 2];
       if constexpr (NORM) {
         float sq = 0.f;
@@ -514,7 +516,20 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
       }
       // published as the complement of its bits: zero means "not written
       // yet" (the complement of a finite double is never zero)
-      st_coh_u64(lg + (size_t)m * E + e, ~(uint64_t)__double_as_longlong(tot));
+      s_pub[m][wid / 2] = ~(uint64_t)__double_as_longlong(tot);
+    }
+  }
+  __syncthreads();
+  if (wid == 0) {
+    const int r = lane % kRRows, e0 = u * kRRows;
+    constexpr int kCpI = kWave / kRRows;           // copies per store instruction
+#pragma unroll
+    for (int j = 0; j < kLogitCopies / kCpI; ++j) {
+      const int c = lane / kRRows + kCpI * j;
+      uint64_t* lg = P.logits + ((size_t)(epoch & 1) * kLogitCopies + c) * P.lstride;
+#pragma unroll
+      for (int m = 0; m < kFusedMaxM; ++m)
+        if (m < M && e0 + r < E) st_coh_u64(lg + (size_t)m * E + e0 + r, s_pub[m][r]);
     }
   }
   tl_mark(2);                             // R: logits published
