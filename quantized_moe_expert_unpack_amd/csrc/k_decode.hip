@@ -60,7 +60,9 @@ constexpr int kSpinLimit = 1 << 26;
 constexpr int kCUs = 256;                  // compute units of the chip (MI355X)
 constexpr int kLine = kLineInts;
 constexpr int kRep = 64;      // copies of every flag that many units poll
-constexpr int kLogitCopies = 32;   // copies of the router logits (one per polling group of units)
+constexpr int kLogitCopies = 16;   // copies of the router logits (one per polling group of units)
+static_assert(kLogitCopies % (kWave / kRRows) == 0,
+              "a router unit writes its rows' logits to kWave / kRRows copies per store instruction");
 constexpr int kSelCopies = 16;     // copies of the (expert, weight) pairs the down units poll
 // per token: G arrival counter lines, D arrival counter lines
 constexpr int kCtrLines = 2 * (1 + kFan);
