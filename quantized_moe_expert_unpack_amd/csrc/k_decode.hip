@@ -66,8 +66,8 @@ static_assert(kLogitCopies % (kWave / kRRows) == 0,
 constexpr int kSelCopies = 16;     // copies of the (expert, weight) pairs the down units poll
 // per token: G arrival counter lines, D arrival counter lines
 constexpr int kCtrLines = 2 * (1 + kFan);
-constexpr int kHCopies = 8;   // copies of h (one per XCD; the down units read their XCD's): spreads the
-                              // reads of all D units of a token over more memory channels
+constexpr int kHCopies = 4;   // copies of h (down unit d reads copy d % kHCopies): spreads the reads of
+                              // all D units of a token over more memory channels
 static_assert(kHCopies * kGRows % kWave == 0, "a G unit's h copies are written by whole waves");
 // the one-launch form's h buffers: a G unit's kGRows values (one segment) at
 // the front of a 128-byte line of their own, so no line holds two segments
