@@ -64,6 +64,7 @@ constexpr int kLogitCopies = 16;   // copies of the router logits (one per polli
 static_assert(kLogitCopies % (kWave / kRRows) == 0,
               "a router unit writes its rows' logits to kWave / kRRows copies per store instruction");
 constexpr int kSelCopies = 16;     // copies of the (expert, weight) pairs the down units poll
+constexpr int kSelLine = 16;       // u64 words from one slot's pair to the next (a 128-byte line each)
 // per token: G arrival counter lines, D arrival counter lines
 constexpr int kCtrLines = 2 * (1 + kFan);
 constexpr int kHCopies = 4;   // copies of h (down unit d reads copy d % kHCopies): spreads the reads of
@@ -328,7 +329,7 @@ __device__ __forceinline__ void route_pick(const uint64_t* keys, const double* v
   __syncthreads();
 }
 
-// Wave 0 of a G or D unit: wait until every router logit of token t is
+// Wave 0 of a G unit: wait until every router logit of token t is
 // published (complemented fp64 bits, 0 = not yet), then put the token's keys
 // and logits in LDS; returns the polling rounds it took.  One round loads the
 // whole row and waits for it, so no load is left in flight at the end (a
@@ -371,8 +372,9 @@ __device__ __forceinline__ int poll_logits(const uint64_t* lg, int E, int lane, 
 // dequantized weight widened exactly, fp64 products and sums, as the oracle
 // defines the logits.  An R unit takes kRRows rows, two waves per row (wave
 // half h takes the row's chunks lane + 64 (2j + h)), and publishes each
-// finished logit into the launch's logits buffer; every G and D unit then
-// selects its token's top-K itself.
+// finished logit into the launch's logits buffer; every G unit then selects
+// its token's top-K itself (the D units take the slots' pairs from the G
+// units).
 // NORM: the rows see h = r * (x . g) with r = 1/sqrt(mean(x^2) + eps) per token
 // (RMSNorm): x . g is staged, each token's mean square reduced over the block,
 // and r applied to the finished logit.
@@ -500,7 +502,7 @@ __device__ __forceinline__ void route_unit(const DecodeLayer L, const DecPlan P,
     }
   }
   __syncthreads();
-  // every logit goes to kLogitCopies copies, one per lane (a G or D unit
+  // every logit goes to kLogitCopies copies, one per lane (a G unit
   // polls copy blockIdx % kLogitCopies: many units polling one line would
   // queue on its memory channel)
   // the unit's kRRows logits of a token are staged, then written to every
@@ -646,7 +648,7 @@ __device__ __forceinline__ void gate_up_unit(const DecodeLayer L, const DecPlan 
       // the slot's (expert, weight) pair for the down units, in every copy
       route_pick(keys, vals, L.E, K, g == 0 ? renorm : 0, s_sel, g == 0 ? s_w : nullptr);
       if (g == 0 && wid == 0 && lane < kSelCopies)
-        st_coh_u64(P.selw + ((size_t)par * kSelCopies + lane) * P.sstride + (size_t)t * kMaxTopK + k,
+        st_coh_u64(P.selw + ((size_t)par * kSelCopies + lane) * P.sstride + ((size_t)t * kMaxTopK + k) * kSelLine,
                    ~(((uint64_t)(uint32_t)s_sel[k] << 32) | __float_as_uint(s_w[k])));
     }
     tl_mark(2);                                     // G: expert known
@@ -870,11 +872,11 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
     __shared__ int s_par;
     if (wid == 0) {
       const size_t cp = blockIdx.x % kSelCopies;
-      const uint64_t* sp0 = P.selw + cp * P.sstride + (size_t)t * kMaxTopK;
-      const uint64_t* sp1 = P.selw + ((size_t)kSelCopies + cp) * P.sstride + (size_t)t * kMaxTopK;
+      const uint64_t* sp0 = P.selw + cp * P.sstride + (size_t)t * kMaxTopK * kSelLine;
+      const uint64_t* sp1 = P.selw + ((size_t)kSelCopies + cp) * P.sstride + (size_t)t * kMaxTopK * kSelLine;
       const int ep = ld_coh_i(P.epoch);
-      const uint64_t v0 = lane < K ? ld_coh_u64(sp0 + lane) : 1ull;
-      const uint64_t v1 = lane < K ? ld_coh_u64(sp1 + lane) : 1ull;
+      const uint64_t v0 = lane < K ? ld_coh_u64(sp0 + lane * kSelLine) : 1ull;
+      const uint64_t v1 = lane < K ? ld_coh_u64(sp1 + lane * kSelLine) : 1ull;
       const int pr = ep & 1;
       const uint64_t* sp = pr ? sp1 : sp0;
       uint64_t v = pr ? v1 : v0;
@@ -886,7 +888,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
           break;
         }
         __builtin_amdgcn_s_sleep(2);
-        v = lane < K ? ld_coh_u64(sp + lane) : 1ull;
+        v = lane < K ? ld_coh_u64(sp + lane * kSelLine) : 1ull;
       }
       // pairs already there at the first look: the unit started after the
       // gate/up units' first rows were done, and h is likely complete
@@ -1332,8 +1334,10 @@ DecState dec_state(const DecodeLayer& L, int K, void* ws) {
   D.lstride = (int)((((size_t)kFusedMaxM * L.E * sizeof(uint64_t) + 4095) / 4096 * 4096 + 256) /
                     sizeof(uint64_t));
   D.logits = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * 2 * kLogitCopies * (size_t)D.lstride));
-  // selection copies kFusedMaxM x kMaxTopK each, 4 KB + 256 B apart at least
-  D.sstride = (int)((((size_t)kFusedMaxM * kMaxTopK * sizeof(uint64_t) + 4095) / 4096 * 4096 + 256) /
+  // selection copies kFusedMaxM x kMaxTopK pairs each (every pair on a line
+  // of its own: each slot's is written by another unit), 4 KB + 256 B apart
+  // at least
+  D.sstride = (int)((((size_t)kFusedMaxM * kMaxTopK * kSelLine * sizeof(uint64_t) + 4095) / 4096 * 4096 + 256) /
                     sizeof(uint64_t));
   D.selw = reinterpret_cast<uint64_t*>(take(sizeof(uint64_t) * 2 * kSelCopies * (size_t)D.sstride));
   D.dctr = reinterpret_cast<int*>(take(sizeof(int) * (size_t)kLine * (1 + kFan)));
@@ -1427,14 +1431,14 @@ static size_t dec_lds_bytes(const DecodeLayer& L, int K, bool routed, int M) {
   // G: x (H floats) + chunk sums (<= H/16) + 4 x 16 rows x groups bf16;
   // D: h of all S slots (S x Imax floats) + their chunk sums (<= 1/16 of that)
   //    + the staged scale/bias words;
-  // with routing in the launch, G and D also hold the token's E router keys
-  // and logits while they select, and R units the x of the M tokens
+  // with routing in the launch, G also holds the token's E router keys and
+  // logits while it selects, and R units the x of the M tokens
   const size_t sel = routed ? 16 * (size_t)L.E : 0;
   const size_t g = sizeof(float) * (L.H + pad4(L.H / 16)) + 2 * 4 * kGRows * (L.H / L.gate.group_size) + sel;
   const int S = K + (L.has_shared ? 1 : 0);
   const int Im = L.has_shared && L.Is > L.I ? L.Is : L.I;
   const size_t d = sizeof(float) * ((size_t)S * Im + pad4(S * Im / 16)) +
-                   16 * (size_t)d_sb_words(L, K, d_rows(L, M, K, routed)) + sel;
+                   16 * (size_t)d_sb_words(L, K, d_rows(L, M, K, routed));
   const size_t rx = routed ? sizeof(float) * (size_t)M * L.H : 0;
   size_t m = g > d ? g : d;
   return m > rx ? m : rx;

@@ -77,7 +77,8 @@ struct DecState {
   uint64_t* logits;  // [2 parities][copies][lstride] complemented fp64 logits [kFusedMaxM][E], 0 = not written
   int lstride;       // u64 words per logit copy
   uint64_t* selw;    // [2 parities][copies][sstride]: [kFusedMaxM][kMaxTopK] complemented
-                     // (expert << 32 | fp32 weight bits) of every slot, 0 = not written
+                     // (expert << 32 | fp32 weight bits) of every slot, 0 = not written,
+                     // each pair at the start of a 128-byte line of its own
   int sstride;
   int* dctr;         // arrival counter lines of the one-launch form's D units (the launch's last one)
   int* route_ctr;    // counters of a separate routing launch
@@ -102,7 +103,8 @@ struct DecPlan {
                      // fp64 bits, 0 = not written
   int lstride;
   uint64_t* selw;    // [2 parities][copies][sstride]: every slot's (expert << 32 | fp32 weight
-                     // bits), complemented, 0 = not written; [kFusedMaxM][kMaxTopK] per copy
+                     // bits), complemented, 0 = not written; [kFusedMaxM][kMaxTopK] per copy,
+                     // each pair at the start of a 128-byte line of its own
   int sstride;
   int* dctr;         // arrival counter lines of the D units (the launch's last one moves epoch on)
   int* epoch;        // launch counter (routing in the launch): its parity picks the h buffer
