@@ -887,7 +887,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
           if (lane == 0) atomicOr(P.ctr, 4);
           break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(1);
         v = lane < K ? ld_coh_u64(sp + lane * kSelLine) : 1ull;
       }
       // pairs already there at the first look: the unit started after the
@@ -1057,7 +1057,7 @@ __device__ __forceinline__ void down_unit(const DecodeLayer L, const DecPlan P, 
         if (tid == 0) atomicOr(P.ctr, 8);
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
     }
   } else {
   // wait for token t's h (and the routing weights, the shared gate)
